@@ -1,0 +1,189 @@
+/*
+ * dsa.h — C ABI of libdsa.so, the MI355X (gfx950) DeepSeek-Sparse-Attention
+ * hot path: lightning-indexer exact top-k, query-block union tables, and
+ * sparse absorbed-MLA attention for decode and chunked-prefill extend.
+ *
+ * Sources: the sglang-jax DSA pages — "ref.py" (streamindex_topk_ref,
+ * sparse_mla_ref), "sparse_mla_prefill_qblock.py" (build_block_unit_tables,
+ * _qblock_kernel, sparse_mla_attention_qblock) and "dsa_sparse_backend.py"
+ * (DSASparseAttentionBackend: _fixed_stride_pages, _scatter_paged, the
+ * default sm_scale).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *   allocates nothing, keeps no pointer after a call returns, and never
+ *   synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
+ *   default stream) and results are visible after the caller's sync.
+ * - bf16 tensors are raw IEEE bfloat16 (uint16 bit patterns); all layouts
+ *   are dense row-major with the shapes given.
+ * - Ragged batches (packed along the token axis T):
+ *     seq_lens [S]     int32, kv length of sequence s INCLUDING its current
+ *                      query chunk ("dsa_sparse_backend.py", _scatter_paged);
+ *     cu_q_lens [S+1]  int32, row range [cu_q_lens[s], cu_q_lens[s+1]) of s;
+ *     page_table [S,MP] int32, physical page of seq-local page p of s
+ *                      (fixed stride MP, as built by _fixed_stride_pages).
+ *   Row t of sequence s sits at absolute position
+ *     abs_q(t) = seq_lens[s] - q_len(s) + (t - cu_q_lens[s])
+ *   ("ref.py", streamindex_topk_ref). Rows t >= cu_q_lens[S] belong to no
+ *   sequence. Positions are seq-local token indices: position j of s lives in
+ *   page page_table[s, j / PS] at offset j % PS.
+ * - Caller preconditions, not checked on the host (checking would need a
+ *   device sync): cu_q_lens non-decreasing with cu_q_lens[0] = 0 and
+ *   cu_q_lens[S] <= T; q_len(s) <= seq_lens[s] <= MP * PS; every page id
+ *   reachable below seq_lens[s] lies in [0, num_pages). Kernels clamp what
+ *   they read so that a violation yields unspecified values, not a fault.
+ * - Host validation happens before any launch. On an error nothing is
+ *   launched and nothing is written; dsa_last_error() describes the cause.
+ *   DSA_ERR_HIP reports a launch failure (hipGetLastError); asynchronous
+ *   faults surface at the caller's next synchronisation.
+ * - Each entry point takes a caller-provided device workspace of at least
+ *   the size its *_workspace() query returns (any alignment >= 256 B).
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* a size or pointer argument is out of range */
+  DSA_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement */
+  DSA_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than required */
+  DSA_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+};
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+/* Detail of the most recent failure in this thread ("" if none). */
+const char* dsa_last_error(void);
+/* ABI revision; bumps on any signature or semantic change. */
+int dsa_abi_version(void);
+
+/*
+ * dsa_indexer_topk — lightning-indexer exact top-k.
+ * "ref.py", streamindex_topk_ref (decode is the q_len = 1 case).
+ *
+ * For each row t of sequence s with a = abs_q(t) and every position j with
+ * j < seq_lens[s] and j <= a:
+ *     score[t, j] = sum_h w[t, h] * relu( sum_d q_idx[t, h, d] * K[j, d] )
+ * with K[j] = idx_cache[page_table[s, j / PS], j % PS, :], computed with
+ * bf16 products and fp32 accumulation. topk[t, :] receives the first
+ * min(k, n_valid) positions ordered by score descending, equal scores by
+ * position ascending (-0.0 equals +0.0), then -1 up to k. Rows outside every
+ * sequence are all -1. topk is fully written for rows 0..T-1.
+ *
+ *   q_idx      bf16 [T, H, D]
+ *   w          fp32 [T, H]
+ *   idx_cache  bf16 [num_pages, PS, D]  one key per token, shared by heads
+ *   topk       int32 [T, k]             output
+ *   max_q_len  host upper bound on q_len(s) over the batch (a hint that picks
+ *              the streaming per-row kernel when <= 1 and the MFMA tile
+ *              kernel otherwise; any value gives the same result)
+ * Supported: H in {1..64} with H % 32 == 0 or H <= 32, D % 32 == 0 and
+ * D <= 256, PS % 16 == 0, 1 <= k <= 4096.
+ */
+size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
+                                  int max_q_len);
+int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
+                     const int32_t* page_table, const int32_t* seq_lens,
+                     const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                     int k, int max_q_len, int32_t* topk, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_block_union — per query-block union of selected pages and per-token
+ * membership. "sparse_mla_prefill_qblock.py", build_block_unit_tables, with
+ * the ragged lifting of sparse_mla_attention_qblock.
+ *
+ * Rows are grouped into nQB = ceil(T / QB) blocks of QB consecutive packed
+ * rows (blocks may straddle sequences; the last block is padded with empty
+ * rows). A selected position j >= 0 of row t in sequence s names the page
+ * key s * MP + j / PS; entries j < 0 or j >= MP * PS and rows outside every
+ * sequence are ignored. Per block b:
+ *   blk_counts[b]        number of distinct keys (TRUE size, not capped);
+ *   blk_units[b, i]      the i-th smallest key for i < min(count, u_max),
+ *                        -1 after;
+ *   blk_member[b, i, q]  bit r set iff row b*QB+q selected position
+ *                        (key % MP) * PS + r of that page; 0 for padding
+ *                        rows and for slots i >= min(count, u_max).
+ * A count above u_max is data, not an error: the tables then hold only the
+ * smallest u_max keys (lossy). min(QB * k, S * MP) slots are always enough.
+ *
+ *   topk        int32 [T, k]
+ *   blk_units   int32 [nQB, u_max]       output
+ *   blk_counts  int32 [nQB]              output
+ *   blk_member  uint64 [nQB, u_max, QB]  output
+ * Supported: PS in {16, 32, 48, 64}, S * MP <= 2^20, u_max <= 16384,
+ * QB <= 1024.
+ */
+size_t dsa_block_union_workspace(int T, int S, int MP, int QB, int u_max);
+int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t* cu_q_lens,
+                    int T, int S, int k, int PS, int MP, int QB, int u_max,
+                    int32_t* blk_units, int32_t* blk_counts, uint64_t* blk_member,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_decode — sparse absorbed-MLA attention, one query row per
+ * selection list. "ref.py", sparse_mla_ref.
+ *
+ * For each row t of sequence s (a = abs_q(t)) and head h, over
+ * V = { j in topk[t, :] : 0 <= j < seq_lens[s], j <= a }:
+ *     l_j = sm_scale * sum_{d < 576} q[t, h, d] * R_j[d]
+ *     out[t, h, :] = sum_j softmax(l)_j * R_j[0:512]
+ * with R_j = kv_cache[page_table[s, j / PS], j % PS, 0:576] (the packed
+ * [c_kv 512 | k_rope 64] latent row). Logits and softmax in fp32, bf16
+ * products, fp32 accumulation, bf16 output. Empty V or a row outside every
+ * sequence gives zeros. Selections must be duplicate-free (a duplicate would
+ * be counted twice). Any ragged layout is accepted; "decode" names the
+ * per-row execution (split over the selection list, then a combine).
+ *
+ *   q          bf16 [T, H, 576]  = [q_nope absorbed (512) | q_rope (64)]
+ *   kv_cache   bf16 [num_pages, PS, row_stride], row_stride >= 576
+ *   topk       int32 [T, k]
+ *   out        bf16 [T, H, 512]  output
+ * Supported: H in {16, 32, 48, 64} or H <= 16, PS % 16 == 0, k <= 65536.
+ */
+size_t dsa_sparse_mla_decode_workspace(int T, int H, int k);
+int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, const int32_t* topk, int T, int S, int H,
+                          int k, int PS, int MP, float sm_scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_extend — query-block sparse absorbed-MLA attention.
+ * "sparse_mla_prefill_qblock.py", _qblock_kernel / sparse_mla_attention_qblock.
+ *
+ * Block b walks its union slots i < min(blk_counts[b], u_max) in ascending
+ * key order, fetching each page once for all its QB * H rows. A key r of
+ * that page (position j = (key % MP) * PS + r of sequence key / MP) counts
+ * for row (q, h) iff bit r of blk_member[b, i, q] is set, j <= abs_q and
+ * j < seq_lens. The masked online softmax then gives, per query, exactly the
+ * dsa_sparse_mla_decode result for the selection the tables were built
+ * from (up to fp32 summation order), when no block overflowed u_max.
+ *
+ *   q, kv_cache, out   as in dsa_sparse_mla_decode
+ *   blk_*              as produced by dsa_block_union with the same
+ *                      (T, QB, u_max, PS, MP)
+ * Supported: H == 16 or H == 32 ... (H % 16 == 0, H <= 64), PS in
+ * {16, 32, 48, 64}, QB * H % 64 == 0 or QB * H <= 64.
+ */
+size_t dsa_sparse_mla_extend_workspace(int T, int H, int QB, int u_max);
+int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, const int32_t* blk_units,
+                          const int32_t* blk_counts, const uint64_t* blk_member, int T, int S,
+                          int H, int PS, int MP, int QB, int u_max, float sm_scale, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,22 @@
+"""DeepSeek-Sparse-Attention hot path for MI355X (gfx950).
+
+Python face of ``libdsa.so`` (C ABI in ``include/dsa.h``): exact
+lightning-indexer top-k, query-block union tables, and sparse absorbed-MLA
+attention for decode and chunked-prefill extend. All compute runs in the HIP
+kernels; this package only marshals torch tensors into the C calls.
+"""
+from ._lib import (  # noqa: F401
+    DsaError,
+    block_union,
+    block_union_workspace,
+    header_functions,
+    indexer_topk,
+    indexer_topk_workspace,
+    last_error,
+    load,
+    sparse_mla_decode,
+    sparse_mla_decode_workspace,
+    sparse_mla_extend,
+    sparse_mla_extend_workspace,
+    status_string,
+)

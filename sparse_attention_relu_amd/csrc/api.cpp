@@ -1,0 +1,264 @@
+// C-ABI entry points of libdsa.so: host-side validation, workspace carving
+// and kernel launches. Every argument is checked before anything is
+// launched; on an error nothing is written and dsa_last_error() says why.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/dsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kMaxCap = 1 << 24;  // positions per sequence (MP * PS)
+
+long scores_ld(int MP, int PS) { return (((long)MP * PS) + 63) / 64 * 64; }
+
+int check_ragged(int T, int S, int PS, int MP, int num_pages) {
+  if (T < 0) return fail(DSA_ERR_INVALID_ARG, "T=%d must be >= 0", T);
+  if (S < 0) return fail(DSA_ERR_INVALID_ARG, "S=%d must be >= 0", S);
+  if (PS < 1 || PS > 4096) return fail(DSA_ERR_INVALID_ARG, "PS=%d out of [1, 4096]", PS);
+  if (MP < 1) return fail(DSA_ERR_INVALID_ARG, "MP=%d must be >= 1", MP);
+  if ((long)MP * PS > kMaxCap)
+    return fail(DSA_ERR_UNSUPPORTED, "MP*PS=%ld exceeds %d positions", (long)MP * PS, kMaxCap);
+  if (num_pages < 1) return fail(DSA_ERR_INVALID_ARG, "num_pages=%d must be >= 1", num_pages);
+  return DSA_OK;
+}
+
+size_t decode_ws(int T, int H, int k) {
+  const int ch = dsa::mla_decode_chunk(T, k);
+  const size_t nch = (size_t)((k + ch - 1) / ch);
+  return align256((size_t)T * nch * H * 512 * 4) + align256((size_t)T * nch * H * 2 * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------------------
+size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
+                                  int max_q_len) {
+  (void)S; (void)H; (void)D; (void)k; (void)max_q_len;
+  if (T <= 0 || PS <= 0 || MP <= 0) return 0;
+  return align256((size_t)T * scores_ld(MP, PS) * 4);
+}
+
+int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
+                     const int32_t* page_table, const int32_t* seq_lens,
+                     const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP, int k,
+                     int max_q_len, int32_t* topk, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (H < 1 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "indexer H=%d not in [1, 64]", H);
+  if (D != 32 && D != 64 && D != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer D=%d not in {32, 64, 128}", D);
+  if (k < 1 || k > 4096) return fail(DSA_ERR_UNSUPPORTED, "k=%d not in [1, 4096]", k);
+  if (T == 0) return ok();
+  if (!q_idx || !w || !idx_cache || !page_table || !seq_lens || !cu_q_lens || !topk)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_idx) || !aligned16(idx_cache))
+    return fail(DSA_ERR_INVALID_ARG, "q_idx and idx_cache must be 16-byte aligned");
+  const size_t need = dsa_indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "indexer workspace %zu < %zu bytes", workspace_bytes, need);
+  dsa::IndexerArgs a;
+  a.q = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.cache = static_cast<const uint16_t*>(idx_cache);
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.T = T; a.S = S; a.H = H; a.D = D; a.PS = PS; a.MP = MP; a.k = k;
+  a.max_q_len = max_q_len;
+  a.scores = static_cast<float*>(workspace);
+  a.ld = scores_ld(MP, PS);
+  a.topk = topk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::indexer_score(a, s);
+  if (e != hipSuccess) return hip_status(e, "indexer score launch");
+  return hip_status(dsa::indexer_select(a, s), "indexer top-k launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t dsa_block_union_workspace(int T, int S, int MP, int QB, int u_max) {
+  (void)u_max;
+  if (T <= 0 || QB <= 0 || S <= 0 || MP <= 0) return 0;
+  const size_t nqb = (size_t)((T + QB - 1) / QB);
+  const size_t nw = (size_t)dsa::union_words(S, MP);
+  return align256(nqb * nw * 8) + align256(nqb * nw * 4);
+}
+
+int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t* cu_q_lens,
+                    int T, int S, int k, int PS, int MP, int QB, int u_max, int32_t* blk_units,
+                    int32_t* blk_counts, uint64_t* blk_member, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_ragged(T, S, PS, MP, 1);
+  if (st) return st;
+  if (S < 1) return fail(DSA_ERR_INVALID_ARG, "S=%d must be >= 1", S);
+  if (PS > 64) return fail(DSA_ERR_UNSUPPORTED, "union PS=%d > 64 (one 64-bit word per page)", PS);
+  if (k < 1) return fail(DSA_ERR_INVALID_ARG, "k=%d must be >= 1", k);
+  if (QB < 1 || QB > 1024) return fail(DSA_ERR_UNSUPPORTED, "QB=%d not in [1, 1024]", QB);
+  if (u_max < 1 || (size_t)u_max * 8 > dsa::kUnionTileBytes)
+    return fail(DSA_ERR_UNSUPPORTED, "u_max=%d not in [1, %zu]", u_max, dsa::kUnionTileBytes / 8);
+  if ((long)S * MP > (1L << 18))
+    return fail(DSA_ERR_UNSUPPORTED, "S*MP=%ld page keys exceed 2^18", (long)S * MP);
+  if (T == 0) return ok();
+  if (!topk || !seq_lens || !cu_q_lens || !blk_units || !blk_counts || !blk_member)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const size_t need = dsa_block_union_workspace(T, S, MP, QB, u_max);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "union workspace %zu < %zu bytes", workspace_bytes, need);
+  const size_t nqb = (size_t)((T + QB - 1) / QB);
+  const size_t nw = (size_t)dsa::union_words(S, MP);
+  dsa::UnionArgs a;
+  a.topk = topk;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.T = T; a.S = S; a.k = k; a.PS = PS; a.MP = MP; a.QB = QB; a.u_max = u_max;
+  a.units = blk_units;
+  a.counts = blk_counts;
+  a.member = blk_member;
+  a.bits = static_cast<uint64_t*>(workspace);
+  a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(nqb * nw * 8));
+  return hip_status(dsa::block_union(a, static_cast<hipStream_t>(stream)), "union launch");
+}
+
+// ---------------------------------------------------------------------------
+static int check_mla_common(const void* q, const void* kv, int row_stride, int H, int PS,
+                            void* out) {
+  if (H < 1 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "MLA H=%d not in [1, 64]", H);
+  if (row_stride < 576 || row_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "row_stride=%d must be >= 576 and a multiple of 8",
+                row_stride);
+  if (!q || !kv || !out) return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(kv))
+    return fail(DSA_ERR_INVALID_ARG, "q and kv_cache must be 16-byte aligned");
+  (void)PS;
+  return DSA_OK;
+}
+
+size_t dsa_sparse_mla_decode_workspace(int T, int H, int k) {
+  if (T <= 0 || H <= 0 || k <= 0) return 0;
+  return decode_ws(T, H, k);
+}
+
+int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, const int32_t* topk, int T, int S, int H,
+                          int k, int PS, int MP, float sm_scale, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_UNSUPPORTED, "k=%d not in [1, 65536]", k);
+  if (T == 0) return ok();
+  st = check_mla_common(q, kv_cache, row_stride, H, PS, out);
+  if (st) return st;
+  if (!page_table || !seq_lens || !cu_q_lens || !topk)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const size_t need = dsa_sparse_mla_decode_workspace(T, H, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", workspace_bytes, need);
+  const int ch = dsa::mla_decode_chunk(T, k);
+  const size_t nch = (size_t)((k + ch - 1) / ch);
+  dsa::MlaArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv_cache);
+  a.row_stride = row_stride;
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.topk = topk;
+  a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((size_t)T * nch * H * 512 * 4));
+  return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+size_t dsa_sparse_mla_extend_workspace(int T, int H, int QB, int u_max) {
+  (void)T; (void)H; (void)QB; (void)u_max;
+  return 0;
+}
+
+int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, const int32_t* blk_units,
+                          const int32_t* blk_counts, const uint64_t* blk_member, int T, int S,
+                          int H, int PS, int MP, int QB, int u_max, float sm_scale, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (S < 1) return fail(DSA_ERR_INVALID_ARG, "S=%d must be >= 1", S);
+  if (H % 16 != 0) return fail(DSA_ERR_UNSUPPORTED, "extend H=%d must be a multiple of 16", H);
+  if (PS > 64) return fail(DSA_ERR_UNSUPPORTED, "extend PS=%d > 64", PS);
+  if (QB < 1 || QB > 1024) return fail(DSA_ERR_UNSUPPORTED, "QB=%d not in [1, 1024]", QB);
+  if (u_max < 1) return fail(DSA_ERR_INVALID_ARG, "u_max=%d must be >= 1", u_max);
+  if ((long)S * MP > (1L << 24)) return fail(DSA_ERR_UNSUPPORTED, "S*MP too large");
+  if (T == 0) return ok();
+  st = check_mla_common(q, kv_cache, row_stride, H, PS, out);
+  if (st) return st;
+  if (!page_table || !seq_lens || !cu_q_lens || !blk_units || !blk_counts || !blk_member)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  dsa::MlaArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv_cache);
+  a.row_stride = row_stride;
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.units = blk_units;
+  a.counts = blk_counts;
+  a.member = blk_member;
+  a.T = T; a.S = S; a.H = H; a.PS = PS; a.MP = MP; a.QB = QB; a.u_max = u_max;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  return hip_status(dsa::mla_extend(a, static_cast<hipStream_t>(stream)), "extend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kTopkCandCap = 4096;              // boundary-bin candidates kept in LDS
+constexpr size_t kUnionTileBytes = 64 * 1024;   // LDS membership tile per workgroup
+
+struct IndexerArgs {
+  const uint16_t* q;
+  const float* w;
+  const uint16_t* cache;
+  int num_pages;
+  const int32_t* pt;
+  const int32_t* seq_lens;
+  const int32_t* cu;
+  int T, S, H, D, PS, MP, k, max_q_len;
+  float* scores;  // workspace [T, ld]
+  long ld;
+  int32_t* topk;
+};
+
+hipError_t indexer_score(const IndexerArgs& a, hipStream_t st);
+hipError_t indexer_select(const IndexerArgs& a, hipStream_t st);
+size_t topk_select_lds_bytes(int k);
+
+struct UnionArgs {
+  const int32_t* topk;
+  const int32_t* seq_lens;
+  const int32_t* cu;
+  int T, S, k, PS, MP, QB, u_max;
+  int32_t* units;
+  int32_t* counts;
+  uint64_t* member;
+  uint64_t* bits;    // workspace [nQB, NW]
+  int32_t* prefix;   // workspace [nQB, NW]
+};
+
+int union_words(int S, int MP);
+int union_member_qpw(int QB, int u_max);
+hipError_t block_union(const UnionArgs& a, hipStream_t st);
+
+struct MlaArgs {
+  const uint16_t* q;
+  const uint16_t* kv;
+  int row_stride, num_pages;
+  const int32_t* pt;
+  const int32_t* seq_lens;
+  const int32_t* cu;
+  const int32_t* topk;  // decode
+  const int32_t* units;  // extend
+  const int32_t* counts;
+  const uint64_t* member;
+  int T, S, H, k, PS, MP, QB, u_max;
+  float sm_scale;
+  uint16_t* out;
+  float* part_o;   // decode workspace
+  float* part_ml;
+};
+
+int mla_decode_chunk(int T, int k);
+hipError_t mla_decode(const MlaArgs& a, hipStream_t st);
+hipError_t mla_extend(const MlaArgs& a, hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,111 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its host
+validation rejects bad arguments before touching the GPU (no compute call
+is made here)."""
+import ctypes
+import os
+
+import pytest
+
+import sparse_attention_relu_amd as dsa
+from sparse_attention_relu_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_relu_amd import build
+
+        build.build(verbose=False)
+    return dsa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _lib.header_functions()
+    assert len(declared) == 11
+    for name in declared:
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, f"binding lacks {name}"
+    assert sorted(_lib.SIGNATURES) == declared
+
+
+def test_status_strings(lib):
+    assert dsa.status_string(0) == "ok"
+    assert "workspace" in dsa.status_string(3)
+    assert lib.dsa_abi_version() == 1
+
+
+def _idx_call(lib, **kw):
+    a = dict(q=1 << 12, w=1 << 12, cache=1 << 12, P=4, pt=1 << 12, sl=1 << 12, cu=1 << 12,
+             T=2, S=1, H=32, D=128, PS=64, MP=4, k=16, mql=1, out=1 << 12, ws=None, wsb=0)
+    a.update(kw)
+    return lib.dsa_indexer_topk(a["q"], a["w"], a["cache"], a["P"], a["pt"], a["sl"], a["cu"],
+                                a["T"], a["S"], a["H"], a["D"], a["PS"], a["MP"], a["k"],
+                                a["mql"], a["out"], a["ws"], a["wsb"], None)
+
+
+def test_indexer_validation(lib):
+    assert _idx_call(lib, D=96) == _lib.DSA_ERR_UNSUPPORTED
+    assert _idx_call(lib, k=0) == _lib.DSA_ERR_UNSUPPORTED
+    assert _idx_call(lib, k=5000) == _lib.DSA_ERR_UNSUPPORTED
+    assert _idx_call(lib, H=65) == _lib.DSA_ERR_UNSUPPORTED
+    assert _idx_call(lib, T=-1) == _lib.DSA_ERR_INVALID_ARG
+    assert _idx_call(lib, q=None) == _lib.DSA_ERR_INVALID_ARG
+    assert _idx_call(lib, q=(1 << 12) + 2) == _lib.DSA_ERR_INVALID_ARG  # misaligned
+    assert _idx_call(lib) == _lib.DSA_ERR_WORKSPACE  # no workspace given
+    assert "workspace" in dsa.last_error()
+    assert _idx_call(lib, T=0) == _lib.DSA_OK  # nothing to do: no launch
+    need = dsa.indexer_topk_workspace(2, 1, 32, 128, 64, 4, 16, 1)
+    assert need >= 2 * 4 * 64 * 4
+    assert _idx_call(lib, ws=1 << 12, wsb=need - 1) == _lib.DSA_ERR_WORKSPACE
+
+
+def test_union_validation(lib):
+    def call(**kw):
+        a = dict(T=8, S=2, k=4, PS=64, MP=8, QB=4, u_max=16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.dsa_block_union(1 << 12, 1 << 12, 1 << 12, a["T"], a["S"], a["k"], a["PS"],
+                                   a["MP"], a["QB"], a["u_max"], 1 << 12, 1 << 12, 1 << 12,
+                                   a["ws"], a["wsb"], None)
+
+    assert call(PS=128) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(QB=0) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(u_max=0) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(u_max=100000) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(S=64, MP=8192) == _lib.DSA_ERR_UNSUPPORTED
+    assert call() == _lib.DSA_ERR_WORKSPACE
+    assert call(T=0) == _lib.DSA_OK
+
+
+def test_mla_validation(lib):
+    def dec(**kw):
+        a = dict(rs=576, H=16, k=64, T=2, q=1 << 12)
+        a.update(kw)
+        return lib.dsa_sparse_mla_decode(a["q"], 1 << 12, a["rs"], 8, 1 << 12, 1 << 12, 1 << 12,
+                                         1 << 12, a["T"], 2, a["H"], a["k"], 64, 4, 0.1,
+                                         1 << 12, None, 0, None)
+
+    assert dec(rs=500) == _lib.DSA_ERR_INVALID_ARG
+    assert dec(rs=580) == _lib.DSA_ERR_INVALID_ARG
+    assert dec(H=0) == _lib.DSA_ERR_UNSUPPORTED
+    assert dec(q=(1 << 12) + 8) == _lib.DSA_ERR_INVALID_ARG
+    assert dec() == _lib.DSA_ERR_WORKSPACE
+    assert dec(T=0) == _lib.DSA_OK
+
+    def ext(**kw):
+        a = dict(H=16, PS=64, QB=64, u_max=32)
+        a.update(kw)
+        return lib.dsa_sparse_mla_extend(1 << 12, 1 << 12, 576, 8, 1 << 12, 1 << 12, 1 << 12,
+                                         1 << 12, 1 << 12, 1 << 12, 4, 2, a["H"], a["PS"], 4,
+                                         a["QB"], a["u_max"], 0.1, 1 << 12, None, 0, None)
+
+    assert ext(H=8) == _lib.DSA_ERR_UNSUPPORTED
+    assert ext(PS=128) == _lib.DSA_ERR_UNSUPPORTED
+    assert ext(QB=2048) == _lib.DSA_ERR_UNSUPPORTED
+    assert ext(u_max=0) == _lib.DSA_ERR_INVALID_ARG
+
+
+def test_decode_workspace_formula(lib):
+    # partial (m, l, O) per (row, chunk, head)
+    ws = dsa.sparse_mla_decode_workspace(8, 16, 2048)
+    assert ws > 0 and ws % 256 == 0
+    assert dsa.sparse_mla_decode_workspace(0, 16, 2048) == 0

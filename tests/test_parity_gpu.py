@@ -1,0 +1,324 @@
+"""GPU parity: every entry point of libdsa.so against the fp64 oracle.
+
+Top-k and union tables are compared bit for bit (the indexer inputs are
+integer-valued, so fp32 scores are exact in any summation order); attention
+outputs within max-abs 2e-2 and relative-L2 5e-3. Shapes here are small
+enough for the oracle to finish in seconds while spanning several tiles,
+ragged tails and the degenerate cases.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import (Dev, bf16, check_attention, check_topk_rows_valid, f32, i32, log,
+                         to_np, torch_mod)
+from workloads import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_relu_amd as m
+
+    m.load()  # fails loudly when the library is missing
+    return m
+
+
+def _oracle_topk(wl, b, k=None, q_idx=None, w=None, cu=None):
+    q_idx = b.q_idx if q_idx is None else q_idx
+    w = b.w if w is None else w
+    cu = b.cu_q_lens if cu is None else cu
+    return oracle.indexer_topk(bf16_to_f64(q_idx), w.astype(np.float64),
+                               bf16_to_f64(wl.idx_cache), wl.page_table, wl.seq_lens, cu,
+                               wl.k if k is None else k)
+
+
+def _gpu_topk(dsa, d, q_idx, w, cu, k, max_q_len):
+    torch = torch_mod()
+    out = dsa.indexer_topk(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache, d.page_table,
+                           d.seq_lens, i32(cu, "cuda"), k, max_q_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _max_q_len(cu):
+    cu = np.asarray(cu)
+    return int(np.diff(cu).max(initial=0))
+
+
+# ----------------------------------------------------------------------------
+# Indexer
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bname", ["decode", "extend"])
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+def test_indexer_tiny(dsa, bname, path):
+    wl = W.config(1)
+    b = wl.batches[bname]
+    log(f"indexer tiny {bname} path={path}")
+    d = Dev(wl)
+    mql = 1 if path == "rows" else max(2, _max_q_len(b.cu_q_lens))
+    got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, mql)
+    exp = _oracle_topk(wl, b)
+    assert np.array_equal(got, exp)
+
+
+INDEXER_EDGE = {
+    # name: (S, kv_lens, PS, MP, q_lens, H, D, k, extra_rows)
+    "mixed_empty_seq_tail_rows": (3, [37, 200, 64], 16, 16, [1, 5, 0], 4, 32, 48, 3),
+    "h64_d128_ragged": (2, [1000, 4097], 64, 80, [40, 33], 64, 128, 256, 0),
+    "h1_d64_k1": (2, [77, 300], 32, 10, [3, 70], 1, 64, 1, 1),
+    "k4096_short_rows": (2, [100, 2500], 64, 40, [1, 2], 32, 128, 4096, 0),
+    "k4096_long_rows": (1, [10000], 64, 160, [3], 32, 128, 4096, 0),
+    "h32_d128_chunk_straddle": (4, [700, 64, 1500, 33], 64, 24, [33, 64, 47, 33], 32, 128, 128, 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(INDEXER_EDGE))
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+def test_indexer_edges(dsa, name, path):
+    S, kv, PS, MP, ql, H, D, k, extra = INDEXER_EDGE[name]
+    cu = np.concatenate([[0], np.cumsum(ql)]).tolist()
+    wl = W.build(name=name, seed=77, S=S, kv_lens=kv, PS=PS, MP=MP, batches={"b": cu}, H_idx=H,
+                 D_idx=D, k=k, with_mla=False, extra_pages=2)
+    b = wl.batches["b"]
+    q_idx, w = b.q_idx, b.w
+    if extra:  # rows past cu_q_lens[S] belong to no sequence
+        q_idx = np.concatenate([q_idx, q_idx[:1].repeat(extra, 0)])
+        w = np.concatenate([w, w[:1].repeat(extra, 0)])
+    log(f"indexer edge {name} path={path} T={q_idx.shape[0]}")
+    d = Dev(wl)
+    mql = 1 if path == "rows" else max(2, max(ql))
+    got = _gpu_topk(dsa, d, q_idx, w, cu, k, mql)
+    exp = _oracle_topk(wl, b, k=k, q_idx=q_idx, w=w, cu=np.array(cu))
+    assert np.array_equal(got, exp)
+    check_topk_rows_valid(got, wl.seq_lens, cu, k)
+
+
+def test_indexer_ties_and_negative_zero(dsa):
+    """All-zero queries (every score ties at 0) and negative weights (scores
+    of -0.0 mixed with +0.0): order is by position."""
+    wl = W.build(name="ties", seed=5, S=2, kv_lens=[300, 129], PS=16, MP=20,
+                 batches={"b": [0, 4, 9]}, H_idx=8, D_idx=32, k=64, with_mla=False)
+    b = wl.batches["b"]
+    q = b.q_idx.copy()
+    q[::2] = W.f32_to_bf16(np.zeros(q[::2].shape, np.float32))
+    w = b.w.copy()
+    w[1::2] *= -1.0
+    d = Dev(wl)
+    for mql in (1, 5):
+        log(f"indexer ties mql={mql}")
+        got = _gpu_topk(dsa, d, q, w, b.cu_q_lens, 64, mql)
+        exp = _oracle_topk(wl, b, k=64, q_idx=q, w=w)
+        assert np.array_equal(got, exp)
+
+
+def test_indexer_zero_rows(dsa):
+    """T > 0 with no sequence rows at all (cu_q_lens = 0...): all -1."""
+    wl = W.build(name="none", seed=6, S=2, kv_lens=[50, 60], PS=16, MP=4,
+                 batches={"b": [0, 0, 0]}, H_idx=4, D_idx=32, k=8, with_mla=False)
+    d = Dev(wl)
+    q = W.f32_to_bf16(np.ones((5, 4, 32), np.float32))
+    got = _gpu_topk(dsa, d, q, np.ones((5, 4), np.float32), [0, 0, 0], 8, 1)
+    assert (got == -1).all()
+
+
+# ----------------------------------------------------------------------------
+# Union
+# ----------------------------------------------------------------------------
+def _gpu_union(dsa, topk, wl, cu, QB, u_max):
+    torch = torch_mod()
+    u, c, m = dsa.block_union(i32(topk, "cuda"), i32(wl.seq_lens, "cuda"), i32(cu, "cuda"),
+                              wl.PS, wl.MP, QB, u_max)
+    torch.cuda.synchronize()
+    return u.cpu().numpy(), c.cpu().numpy(), m.cpu().numpy()
+
+
+@pytest.mark.parametrize("QB", [16, 64])
+def test_union_tiny(dsa, QB):
+    wl = W.config(1, with_mla=False)
+    b = wl.batches["extend"]
+    tk = _oracle_topk(wl, b)
+    log(f"union tiny QB={QB}")
+    u, c, m = _gpu_union(dsa, tk, wl, b.cu_q_lens, QB, wl.u_max)
+    eu, ec, em = oracle.block_union(tk, wl.seq_lens, b.cu_q_lens, wl.PS, wl.MP, QB, wl.u_max)
+    assert np.array_equal(u, eu) and np.array_equal(c, ec) and np.array_equal(m, em)
+
+
+UNION_CASES = {
+    # name: (S, kv, PS, MP, q_lens, k, QB, u_max, fill)
+    "ps16_qb3": (3, [100, 7, 64], 16, 8, [5, 2, 9], 12, 3, 64, 0.6),
+    "ps48_qb8_lossless": (2, [400, 250], 48, 9, [20, 13], 40, 8, 18, 0.9),
+    "ps64_qb64_lossy": (4, [900, 1200, 64, 333], 64, 20, [17, 30, 1, 40], 64, 64, 9, 0.8),
+    "ps32_qb1": (2, [90, 150], 32, 5, [4, 6], 16, 1, 5, 1.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(UNION_CASES))
+def test_union_cases(dsa, name):
+    S, kv, PS, MP, ql, k, QB, u_max, fill = UNION_CASES[name]
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    wl = W.build(name=name, seed=11, S=S, kv_lens=kv, PS=PS, MP=MP, batches={"b": cu}, H_idx=4,
+                 D_idx=32, k=k, with_mla=False)
+    tk = W.random_selection(wl.seq_lens, cu, k, 3, fill=fill, allow_out_of_range=True)
+    tk = np.concatenate([tk, np.full((2, k), 5, np.int32)])  # rows past cu[S]: ignored
+    log(f"union {name}")
+    u, c, m = _gpu_union(dsa, tk, wl, cu, QB, u_max)
+    eu, ec, em = oracle.block_union(tk, wl.seq_lens, cu, PS, MP, QB, u_max)
+    assert np.array_equal(c, ec)
+    assert np.array_equal(u, eu)
+    assert np.array_equal(m, em)
+
+
+# ----------------------------------------------------------------------------
+# Sparse MLA
+# ----------------------------------------------------------------------------
+def _gpu_decode(dsa, d, q, kv, cu, topk, scale):
+    torch = torch_mod()
+    out = dsa.sparse_mla_decode(q, kv, d.page_table, d.seq_lens, i32(cu, "cuda"),
+                                i32(topk, "cuda"), scale)
+    torch.cuda.synchronize()
+    return to_np(out)
+
+
+def _gpu_extend(dsa, d, q, kv, cu, topk, scale, QB, u_max):
+    torch = torch_mod()
+    wl = d.wl
+    cu_t = i32(cu, "cuda")
+    u, c, m = dsa.block_union(i32(topk, "cuda"), d.seq_lens, cu_t, wl.PS, wl.MP, QB, u_max)
+    out = dsa.sparse_mla_extend(q, kv, d.page_table, d.seq_lens, cu_t, u, c, m, QB, scale)
+    torch.cuda.synchronize()
+    return to_np(out), u.cpu().numpy(), c.cpu().numpy()
+
+
+def _oracle_mla(wl, b, topk, layer=0, q=None, cu=None, kv=None):
+    q = b.q_mla[layer] if q is None else q
+    kv = wl.kv_cache[layer] if kv is None else kv
+    return oracle.sparse_mla(bf16_to_f64(q), bf16_to_f64(kv), wl.page_table, wl.seq_lens,
+                             b.cu_q_lens if cu is None else cu, topk, wl.sm_scale, wl.Dv)
+
+
+@pytest.mark.parametrize("bname", ["decode", "extend"])
+def test_mla_decode_tiny(dsa, bname):
+    wl = W.config(1)
+    b = wl.batches[bname]
+    tk = _oracle_topk(wl, b)
+    d = Dev(wl)
+    log(f"mla decode tiny {bname}")
+    got = _gpu_decode(dsa, d, bf16(b.q_mla[0], "cuda"), d.kv_cache[0], b.cu_q_lens, tk,
+                      wl.sm_scale)
+    check_attention(got, _oracle_mla(wl, b, tk), what=f"decode tiny {bname}")
+
+
+MLA_CASES = {
+    # name: (S, kv, PS, MP, q_lens, H, k, extra_rows, row_pad)
+    "h16_ps64_multi": (3, [700, 64, 1500], 64, 24, [1, 3, 6], 16, 200, 2, 0),
+    "h4_ps16": (2, [90, 333], 16, 24, [2, 5], 4, 40, 0, 64),
+    "h32_ps32": (2, [500, 260], 32, 16, [4, 4], 32, 96, 1, 0),
+    "h64_ps64": (1, [3000], 64, 50, [3], 64, 300, 0, 0),
+}
+
+
+def _mla_case(name, seed=21):
+    S, kv, PS, MP, ql, H, k, extra, pad = MLA_CASES[name]
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    wl = W.build(name=name, seed=seed, S=S, kv_lens=kv, PS=PS, MP=MP, batches={"b": cu},
+                 H_idx=4, D_idx=32, k=k, H_mla=H, extra_pages=1)
+    b = wl.batches["b"]
+    tk = W.random_selection(wl.seq_lens, cu, k, seed, fill=0.5, allow_out_of_range=True)
+    q = b.q_mla[0]
+    if extra:
+        q = np.concatenate([q, q[:1].repeat(extra, 0)])
+        tk = np.concatenate([tk, np.zeros((extra, k), np.int32)])
+    tk[0, :] = -1  # an empty selection
+    kvc = wl.kv_cache[0]
+    if pad:
+        kvc = kvc.with_columns(pad)
+    return wl, b, cu, q, tk, kvc
+
+
+@pytest.mark.parametrize("name", sorted(MLA_CASES))
+def test_mla_decode_cases(dsa, name):
+    wl, b, cu, q, tk, kvc = _mla_case(name)
+    log(f"mla decode {name} T={q.shape[0]} row_stride={kvc.shape[-1]}")
+    d = Dev(wl)
+    got = _gpu_decode(dsa, d, bf16(q, "cuda"), kvc.to_torch("cuda"), cu, tk, wl.sm_scale)
+    exp = oracle.sparse_mla(bf16_to_f64(q), bf16_to_f64(kvc), wl.page_table, wl.seq_lens, cu, tk,
+                            wl.sm_scale, wl.Dv)
+    assert (got[0] == 0).all()
+    check_attention(got, exp, what=f"decode {name}")
+
+
+@pytest.mark.parametrize("QB", [16, 64])
+def test_mla_extend_tiny(dsa, QB):
+    wl = W.config(1)
+    b = wl.batches["extend"]
+    tk = _oracle_topk(wl, b)
+    d = Dev(wl)
+    log(f"mla extend tiny QB={QB}")
+    got, _, _ = _gpu_extend(dsa, d, bf16(b.q_mla[0], "cuda"), d.kv_cache[0], b.cu_q_lens, tk,
+                            wl.sm_scale, QB, wl.u_max)
+    check_attention(got, _oracle_mla(wl, b, tk), what=f"extend tiny QB={QB}")
+
+
+EXTEND_CASES = {
+    # name: (mla case, QB, u_max)  u_max=None -> lossless bound S*MP
+    "h16_multi_qb4": ("h16_ps64_multi", 4, None),
+    "h32_qb5_partial_tile": ("h32_ps32", 5, None),
+    "h64_qb2": ("h64_ps64", 2, None),
+    "h16_lossy_umax": ("h16_ps64_multi", 8, 5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXTEND_CASES))
+def test_mla_extend_cases(dsa, name):
+    case, QB, u_max = EXTEND_CASES[name]
+    wl, b, cu, q, tk, kvc = _mla_case(case, seed=31)
+    if u_max is None:
+        u_max = wl.S * wl.MP
+    log(f"mla extend {name} QB={QB} u_max={u_max}")
+    d = Dev(wl)
+    got, units, counts = _gpu_extend(dsa, d, bf16(q, "cuda"), kvc.to_torch("cuda"), cu, tk,
+                                     wl.sm_scale, QB, u_max)
+    # the attended selection: entries whose page key survived the cap
+    tk_eff = tk.copy()
+    seq, _ = oracle.query_rows(wl.seq_lens, cu, tk.shape[0])
+    for t in range(tk.shape[0]):
+        bq = t // QB
+        kept = set(units[bq, : min(int(counts[bq]), u_max)].tolist())
+        for i, j in enumerate(tk[t]):
+            if j >= 0 and (seq[t] < 0 or int(seq[t]) * wl.MP + int(j) // wl.PS not in kept):
+                tk_eff[t, i] = -1
+    if u_max < wl.S * wl.MP:
+        assert (counts > u_max).any(), "lossy case did not overflow"
+    exp = oracle.sparse_mla(bf16_to_f64(q), bf16_to_f64(kvc), wl.page_table, wl.seq_lens, cu,
+                            tk_eff, wl.sm_scale, wl.Dv)
+    check_attention(got, exp, what=f"extend {name}")
+
+
+def test_extend_matches_decode(dsa):
+    """The query-block kernel reproduces the per-row result for one selection."""
+    wl, b, cu, q, tk, kvc = _mla_case("h16_ps64_multi", seed=41)
+    d = Dev(wl)
+    qd, kd = bf16(q, "cuda"), kvc.to_torch("cuda")
+    dec = _gpu_decode(dsa, d, qd, kd, cu, tk, wl.sm_scale)
+    ext, _, _ = _gpu_extend(dsa, d, qd, kd, cu, tk, wl.sm_scale, 4, wl.S * wl.MP)
+    check_attention(ext, dec, what="extend vs decode")
+
+
+def test_repeat_determinism(dsa):
+    """Same inputs twice give identical bits (no races in LDS staging)."""
+    wl = W.config(1)
+    b = wl.batches["extend"]
+    d = Dev(wl)
+    tk1 = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, 32)
+    tk2 = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, 32)
+    assert np.array_equal(tk1, tk2)
+    q = bf16(b.q_mla[0], "cuda")
+    o1, _, _ = _gpu_extend(dsa, d, q, d.kv_cache[0], b.cu_q_lens, tk1, wl.sm_scale, 16, 32)
+    o2, _, _ = _gpu_extend(dsa, d, q, d.kv_cache[0], b.cu_q_lens, tk1, wl.sm_scale, 16, 32)
+    assert np.array_equal(o1, o2)

@@ -37,8 +37,24 @@ def test_tiny_recipe():
 def test_seed_determinism():
     a = W.config(1)
     b = W.config(1)
-    assert (a.idx_cache == b.idx_cache).all() and (a.kv_cache[0] == b.kv_cache[0]).all()
+    assert (a.idx_cache.rows == b.idx_cache.rows).all()
+    assert (a.kv_cache[0].rows == b.kv_cache[0].rows).all()
+    assert (a.idx_cache.dense() == b.idx_cache.dense()).all()
     assert (a.batches["extend"].q_idx == b.batches["extend"].q_idx).all()
+
+
+def test_paged_cache_views():
+    wl = W.config(1)
+    dense = W.bf16_to_f64(wl.kv_cache[0].dense())
+    view = wl.kv_cache[0].f64_view()
+    pages = np.array([0, 3, 31, 7])
+    offs = np.array([0, 15, 2, 9])
+    got = view[pages, offs]
+    exp = dense[pages, offs]
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    assert np.array_equal(got[~np.isnan(got)], exp[~np.isnan(exp)])
+    wide = wl.kv_cache[0].with_columns(64)
+    assert wide.shape == (32, 16, 640) and np.isnan(W.bf16_to_f32(wide.dense()[..., 576:])).all()
 
 
 def test_locality_selection():

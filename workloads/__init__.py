@@ -35,9 +35,15 @@ BF16_NAN = np.uint16(0x7FC0)
 def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round-to-nearest-even); returns uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # round half to even on the dropped 16 bits; finite values cannot overflow
+    # 32 bits here, NaN patterns are fixed below
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         out[nan] = BF16_NAN
@@ -55,6 +61,76 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 _INT_BF16 = f32_to_bf16(np.arange(-2, 3, dtype=np.float32))  # bits of -2..2
 _W_CHOICES = np.array([0.25, 0.5, 1.0, 2.0], dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Paged caches, stored compactly
+# ----------------------------------------------------------------------------
+class PagedCache:
+    """A paged bf16 cache [num_pages, PS, D] kept as its live rows only.
+
+    ``slots`` holds the ascending flat slot ids (page * PS + offset) of live
+    tokens and ``rows`` their bf16 bits; every other slot is NaN. The full
+    pool is materialised on demand: ``dense()`` on the host (small cases),
+    ``to_torch()`` directly on the device, ``f64_view()`` as a read-only
+    float64 view indexable like ``cache[pages, offsets]``.
+    """
+
+    def __init__(self, num_pages: int, PS: int, D: int, slots: np.ndarray, rows: np.ndarray):
+        self.num_pages, self.PS, self.D = int(num_pages), int(PS), int(D)
+        self.slots = np.asarray(slots, dtype=np.int64)
+        self.rows = rows
+        self.shape = (self.num_pages, self.PS, self.D)
+
+    @property
+    def nbytes(self) -> int:
+        return self.num_pages * self.PS * self.D * 2
+
+    def dense(self) -> np.ndarray:
+        out = np.full((self.num_pages * self.PS, self.D), BF16_NAN, dtype=np.uint16)
+        out[self.slots] = self.rows
+        return out.reshape(self.shape)
+
+    def __array__(self, dtype=None, copy=None):
+        a = self.dense()
+        return a if dtype is None else a.astype(dtype)
+
+    def f64_view(self) -> "_F64Rows":
+        return _F64Rows(self)
+
+    def with_columns(self, extra: int) -> "PagedCache":
+        """Same cache with ``extra`` NaN columns appended to every row."""
+        pad = np.full((self.rows.shape[0], extra), BF16_NAN, dtype=np.uint16)
+        return PagedCache(self.num_pages, self.PS, self.D + extra, self.slots,
+                          np.concatenate([self.rows, pad], axis=1))
+
+    def to_torch(self, device):
+        import torch
+
+        t = torch.full((self.num_pages * self.PS, self.D), float("nan"), dtype=torch.bfloat16,
+                       device=device)
+        rows = torch.from_numpy(np.ascontiguousarray(self.rows).view(np.int16)).view(torch.bfloat16)
+        idx = torch.from_numpy(self.slots)
+        t.index_copy_(0, idx.to(device), rows.to(device))
+        return t.view(self.num_pages, self.PS, self.D)
+
+
+class _F64Rows:
+    """float64 view of a PagedCache: ``view[pages, offsets] -> [n, D]``."""
+
+    def __init__(self, pc: PagedCache):
+        self.pc = pc
+        self.shape = pc.shape
+
+    def __getitem__(self, idx):
+        pages, offs = idx
+        flat = np.asarray(pages, dtype=np.int64) * self.pc.PS + np.asarray(offs, dtype=np.int64)
+        slots = self.pc.slots
+        pos = np.minimum(np.searchsorted(slots, flat), max(slots.size - 1, 0))
+        hit = slots[pos] == flat if slots.size else np.zeros(flat.shape, bool)
+        out = bf16_to_f64(self.pc.rows[pos]) if slots.size else np.zeros(flat.shape + (self.pc.D,))
+        out[~hit] = np.nan
+        return out
 
 
 # ----------------------------------------------------------------------------
@@ -82,8 +158,8 @@ class Workload:
     MP: int
     seq_lens: np.ndarray      # int32 [S]
     page_table: np.ndarray    # int32 [S, MP]
-    idx_cache: np.ndarray     # uint16 [P, PS, D_idx]
-    kv_cache: List[np.ndarray]  # per layer: uint16 [P, PS, Dk]
+    idx_cache: PagedCache     # bf16 [P, PS, D_idx]
+    kv_cache: List[PagedCache]  # per layer: bf16 [P, PS, Dk]
     H_idx: int
     D_idx: int
     k: int
@@ -98,7 +174,7 @@ class Workload:
 
     @property
     def num_pages(self) -> int:
-        return int(self.idx_cache.shape[0])
+        return self.idx_cache.num_pages
 
 
 # ----------------------------------------------------------------------------
@@ -124,19 +200,22 @@ def _used_mask(seq_lens, page_table, num_pages, PS):
 
 def _int_cache(rng, used, D):
     P, PS = used.shape
-    out = np.full((P, PS, D), BF16_NAN, dtype=np.uint16)
-    n = int(used.sum())
-    vals = rng.integers(0, 5, size=(n, D), dtype=np.int8)
-    out[used] = _INT_BF16[vals]
-    return out
+    slots = np.flatnonzero(used.reshape(-1))
+    vals = rng.integers(0, 5, size=(slots.size, D), dtype=np.int8)
+    return PagedCache(P, PS, D, slots, _INT_BF16[vals])
+
+
+_CHUNK_ROWS = 1 << 15  # rows drawn per call; fixed so the stream is reproducible
 
 
 def _normal_cache(rng, used, D):
     P, PS = used.shape
-    out = np.full((P, PS, D), BF16_NAN, dtype=np.uint16)
-    n = int(used.sum())
-    out[used] = f32_to_bf16(rng.standard_normal((n, D), dtype=np.float32))
-    return out
+    slots = np.flatnonzero(used.reshape(-1))
+    rows = np.empty((slots.size, D), dtype=np.uint16)
+    for i in range(0, slots.size, _CHUNK_ROWS):
+        m = min(_CHUNK_ROWS, slots.size - i)
+        rows[i : i + m] = f32_to_bf16(rng.standard_normal((m, D), dtype=np.float32))
+    return PagedCache(P, PS, D, slots, rows)
 
 
 def _int_tensor(rng, shape):
