@@ -234,7 +234,6 @@ int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, i
   int st = check_ragged(T, S, PS, MP, num_pages);
   if (st) return st;
   if (S < 1) return fail(DSA_ERR_INVALID_ARG, "S=%d must be >= 1", S);
-  if (H % 16 != 0) return fail(DSA_ERR_UNSUPPORTED, "extend H=%d must be a multiple of 16", H);
   if (PS > 64) return fail(DSA_ERR_UNSUPPORTED, "extend PS=%d > 64", PS);
   if (QB < 1 || QB > 1024) return fail(DSA_ERR_UNSUPPORTED, "QB=%d not in [1, 1024]", QB);
   if (u_max < 1) return fail(DSA_ERR_INVALID_ARG, "u_max=%d must be >= 1", u_max);

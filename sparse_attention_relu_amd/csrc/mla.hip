@@ -259,12 +259,14 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Extend (query block): grid = (nQB, ceil(QB * H / 64)), block = 256.
-// A workgroup owns 64 consecutive rows (row = q * H + h) of block b. Wave w
-// computes logits and the online softmax for rows 16 w .. 16 w + 15 (one
-// query, 16 heads, query fragment resident in registers), and P.V for value
-// columns 128 w .. 128 w + 127 of all 64 rows. Union pages are walked in
-// ascending key order, 32 positions at a time; a step whose positions no
-// row of the workgroup selected is skipped without fetching.
+// A workgroup owns 64 consecutive rows (row = q * H + h) of block b; rows of
+// several queries may share a wave when H < 16. Wave w computes logits and
+// the online softmax for rows 16 w .. 16 w + 15 (query fragments resident in
+// registers), and P.V for value columns 128 w .. 128 w + 127 of all 64 rows.
+// Union pages are walked in ascending key order, 32 positions at a time;
+// each row carries its own 64-bit validity mask per page (membership AND
+// causal AND kv_len), and a step no row of the workgroup selected is skipped
+// without fetching.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mla_extend_qblock(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
@@ -275,7 +277,9 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
   __shared__ __attribute__((aligned(16))) uint16_t kvs[NR * KRS];
   __shared__ __attribute__((aligned(16))) uint16_t ps[64 * PRS];
   __shared__ float s_alpha[64], s_l[64];
-  __shared__ uint32_t s_hm[4];
+  __shared__ uint64_t s_mask[64];
+  __shared__ int s_rt[64], s_rseq[64], s_rabs[64], s_rq[64];
+  __shared__ uint32_t s_any[2], s_mbany[4];
   __shared__ int s_src[NR];
 
   const int b = blockIdx.x;
@@ -285,24 +289,31 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
   const int cap = MP * PS;
   const int rows_total = QB * H;
 
-  // this wave's softmax rows: query qloc, heads h0 .. h0 + 15
-  const int rw = r0 + 16 * wave;
-  const bool wact = rw < rows_total;
-  const int qloc = wact ? rw / H : 0;
-  const int h0 = wact ? rw % H : 0;
-  const int t = b * QB + qloc;
-  RowInfo ri;
-  ri.seq = -1;
-  ri.abs_q = -1;
-  if (wact && t < T) ri = row_info(cu, seq_lens, S, t, cap);
+  if (tid < 64) {  // per-row bookkeeping
+    const int r = r0 + tid;
+    const int qloc = r / H;
+    const int t = b * QB + qloc;
+    RowInfo ri;
+    ri.seq = -1;
+    ri.abs_q = -1;
+    const bool live = r < rows_total && t < T;
+    if (live) ri = row_info(cu, seq_lens, S, t, cap);
+    s_rt[tid] = live ? t : -1;
+    s_rseq[tid] = ri.seq;
+    s_rabs[tid] = ri.abs_q;
+    s_rq[tid] = qloc < QB ? qloc : 0;
+  }
+  __syncthreads();
 
   bf16x8 qa[DK / 32];
   {
-    const bool okq = ri.seq >= 0;
-    const uint16_t* qrow = q + ((size_t)(okq ? t : 0) * H + h0 + col) * DK + 8 * g;
+    const int row = 16 * wave + col;
+    const int tq = s_rseq[row] >= 0 ? s_rt[row] : -1;
+    const int h = (r0 + row) % H;
+    const uint16_t* qrow = q + ((size_t)(tq >= 0 ? tq : 0) * H + h) * DK + 8 * g;
 #pragma unroll
     for (int i = 0; i < DK / 32; ++i)
-      qa[i] = as_bf16x8(okq ? *reinterpret_cast<const uint4*>(qrow + 32 * i) : zero_u4());
+      qa[i] = as_bf16x8(tq >= 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * i) : zero_u4());
   }
   float m_run[4], l_run[4];
 #pragma unroll
@@ -325,28 +336,40 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
     int kvp = seq_lens[sp];
     kvp = kvp < 0 ? 0 : (kvp > cap ? cap : kvp);
     const int page = clamp_page(pt[key], num_pages);
-    uint64_t mask = 0;
-    if (ri.seq == sp) {
-      const uint64_t mem = member[((size_t)b * u_max + slot) * QB + qloc];
-      const int lim = min(ri.abs_q + 1, kvp) - lp * PS;  // valid offsets [0, lim)
-      if (lim > 0) mask = lim >= 64 ? mem : (mem & ((1ull << lim) - 1));
-      if (PS < 64) mask &= (1ull << PS) - 1;
+    __syncthreads();  // every reader of the previous slot's LDS state is done
+    if (tid < 64) {
+      uint64_t mk = 0;
+      if (s_rseq[tid] == sp) {
+        const uint64_t mem = member[((size_t)b * u_max + slot) * QB + s_rq[tid]];
+        const int lim = min(s_rabs[tid] + 1, kvp) - lp * PS;  // valid offsets [0, lim)
+        if (lim > 0) mk = lim >= 64 ? mem : (mem & ((1ull << lim) - 1));
+        if (PS < 64) mk &= (1ull << PS) - 1;
+      }
+      s_mask[tid] = mk;
+      const uint64_t any0 = __ballot((uint32_t)mk != 0u);
+      const uint64_t any1 = __ballot((uint32_t)(mk >> 32) != 0u);
+      if (tid == 0) {
+        s_any[0] = any0 != 0;
+        s_any[1] = any1 != 0;
+      }
     }
+    __syncthreads();
     for (int hv = 0; hv < halves; ++hv) {
-      const uint32_t hm = (uint32_t)(mask >> (NR * hv));
-      __syncthreads();  // previous step's readers of kvs / ps / s_hm are done
-      if (l == 0) s_hm[wave] = hm;
+      if (!s_any[hv]) continue;
       if (tid < NR) {
         const int off = NR * hv + tid;
         const int pos = lp * PS + off;
         s_src[tid] = (off < PS && pos < kvp) ? page * PS + off : -1;
       }
-      __syncthreads();
-      const uint32_t any = s_hm[0] | s_hm[1] | s_hm[2] | s_hm[3];
-      if (!any) continue;
+      __syncthreads();  // also: the previous half's P.V readers are done
       stage_rows(kvs, kv, row_stride, s_src, 256);
+      uint32_t hm[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hm[r] = (uint32_t)(s_mask[16 * wave + 4 * g + r] >> (NR * hv));
+      const bool wave_any = __ballot((hm[0] | hm[1] | hm[2] | hm[3]) != 0u) != 0;
+      if (l == 0) s_mbany[wave] = wave_any;
       __syncthreads();
-      if (hm) {
+      if (wave_any) {
         f32x4 sacc[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
@@ -357,11 +380,10 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
             sacc[nb] = mfma16(qa[i], bk, sacc[nb]);
           }
         }
-        const bool v0 = (hm >> col) & 1u, v1 = (hm >> (16 + col)) & 1u;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float x0 = v0 ? sacc[0][r] * sm_scale : -INFINITY;
-          const float x1 = v1 ? sacc[1][r] * sm_scale : -INFINITY;
+          const float x0 = ((hm[r] >> col) & 1u) ? sacc[0][r] * sm_scale : -INFINITY;
+          const float x1 = ((hm[r] >> (16 + col)) & 1u) ? sacc[1][r] * sm_scale : -INFINITY;
           float mx = fmaxf(x0, x1);
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
@@ -390,7 +412,7 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
         const bf16x8 bv = load_v_col(kvs, 8 * g, 128 * wave + 16 * nb + col);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          if (s_hm[mb] == 0) continue;
+          if (!s_mbany[mb]) continue;
           const bf16x8 ap = as_bf16x8(*reinterpret_cast<const uint4*>(&ps[(16 * mb + col) * PRS + 8 * g]));
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[mb][nb][r] *= s_alpha[16 * mb + 4 * g + r];
@@ -409,12 +431,11 @@ __global__ __launch_bounds__(256) void mla_extend_qblock(
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 16 * mb + 4 * g + r;
-      if (row >= rows_total) continue;
-      const int tq = b * QB + row / H;
-      if (tq >= T) continue;
-      const int h = row % H;
-      const float lsum = s_l[16 * mb + 4 * g + r];
+      const int row = 16 * mb + 4 * g + r;
+      const int tq = s_rt[row];
+      if (tq < 0) continue;
+      const int h = (r0 + row) % H;
+      const float lsum = s_l[row];
       const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
       uint16_t* orow = out + ((size_t)tq * H + h) * DV + 128 * wave + col;
 #pragma unroll

@@ -98,7 +98,7 @@ def test_mla_validation(lib):
                                          1 << 12, 1 << 12, 1 << 12, 4, 2, a["H"], a["PS"], 4,
                                          a["QB"], a["u_max"], 0.1, 1 << 12, None, 0, None)
 
-    assert ext(H=8) == _lib.DSA_ERR_UNSUPPORTED
+    assert ext(H=65) == _lib.DSA_ERR_UNSUPPORTED
     assert ext(PS=128) == _lib.DSA_ERR_UNSUPPORTED
     assert ext(QB=2048) == _lib.DSA_ERR_UNSUPPORTED
     assert ext(u_max=0) == _lib.DSA_ERR_INVALID_ARG
