@@ -1,0 +1,371 @@
+#!/usr/bin/env python3
+"""Benchmark of the DeepSeek-Sparse-Attention hot path on one MI355X.
+
+One step = one DSA layer of the workload:
+  decode  (default, 8 sequences x 8192 tokens): exact indexer top-k, then
+          sparse absorbed-MLA decode over the selected positions;
+  extend  (4 requests x (12288 + 1024), reported beside it): indexer top-k,
+          query-block union tables, query-block sparse MLA.
+Inputs are seeded synthetic tensors already resident in HBM when the timed
+region starts. Prints ONE JSON line (rank 0).
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+                  [--extend-config 4|5|0] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s & extend ms/layer (indexer top-k + sparse MLA), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+DK, DV = 576, 512
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3],
+                   help="decode workload (1 tiny, 2 8x8192, 3 ragged 64x[4K,32K])")
+    p.add_argument("--extend-config", type=int, default=4, choices=[0, 1, 4, 5],
+                   help="extend workload measured beside it (0 = none)")
+    p.add_argument("--qb", type=int, default=256, help="query block of the extend layer")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    return p.parse_args(argv)
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+def _dev_inputs(wl, bname, layers=1):
+    import numpy as np
+    import torch
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    b = wl.batches[bname]
+    return dict(
+        page_table=i32(wl.page_table), seq_lens=i32(wl.seq_lens), cu=i32(b.cu_q_lens),
+        idx_cache=wl.idx_cache.to_torch("cuda"),
+        kv_cache=[wl.kv_cache[i].to_torch("cuda") for i in range(layers)],
+        q_idx=bf16(b.q_idx), w=torch.from_numpy(b.w).cuda(),
+        q=[bf16(b.q_mla[i]) for i in range(layers)],
+        max_q_len=int(np.diff(b.cu_q_lens).max()),
+    )
+
+
+def _row_valid_counts(wl, cu):
+    """n_valid per packed row (positions j < kv and j <= abs_q)."""
+    import numpy as np
+
+    T = int(cu[-1])
+    n = np.zeros(T, dtype=np.int64)
+    for s in range(wl.S):
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        a = int(wl.seq_lens[s]) - (q1 - q0) + np.arange(q1 - q0)
+        n[q0:q1] = np.clip(np.minimum(a + 1, int(wl.seq_lens[s])), 0, None)
+    return n
+
+
+def _timed(step, steps, warmup):
+    """Average ms per step over `steps` calls, events on the current stream."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _kernel_times(dsa, step, steps):
+    """Per-kernel average launch duration (ms) from the library's event timer."""
+    import torch
+
+    torch.cuda.synchronize()
+    dsa.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    prof = dsa.profile_read()
+    dsa.profile_enable(False)
+    return {k: (n, tot / n) for k, (n, tot) in prof.items()}
+
+
+def _roofline_entry(bound, work, ms, per_step_launches=1):
+    """work = algorithmic bytes (hbm) or flops (mfma) of ONE launch."""
+    if bound == "hbm":
+        achieved = work / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = work / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def bench_decode(dsa, wl, args):
+    import numpy as np
+    import torch
+
+    d = _dev_inputs(wl, "decode")
+    b = wl.batches["decode"]
+    T, k, H = b.T, wl.k, wl.H_mla
+    topk = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
+    ws_i = torch.empty(max(1, dsa.indexer_topk_workspace(T, wl.S, wl.H_idx, wl.D_idx, wl.PS,
+                                                         wl.MP, k, 1)), dtype=torch.uint8,
+                       device="cuda")
+    ws_d = torch.empty(max(1, dsa.sparse_mla_decode_workspace(T, H, k)), dtype=torch.uint8,
+                       device="cuda")
+
+    def step():
+        dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"], d["seq_lens"],
+                         d["cu"], k, 1, out=topk, workspace=ws_i)
+        dsa.sparse_mla_decode(d["q"][0], d["kv_cache"][0], d["page_table"], d["seq_lens"],
+                              d["cu"], topk, wl.sm_scale, out=out, workspace=ws_d)
+
+    ms = _timed(step, args.steps, args.warmup)
+    kt = _kernel_times(dsa, step, args.steps)
+
+    # algorithmic work per launch
+    nval = _row_valid_counts(wl, b.cu_q_lens)
+    sel = topk.cpu().numpy()
+    n_sel = int((sel >= 0).sum())
+    D, Hi, PS = wl.D_idx, wl.H_idx, wl.PS
+    work = {
+        "idx_score_rows": ("hbm", int(nval.sum()) * (D * 2 + 4) + T * Hi * (D * 2 + 4)
+                           + int(np.ceil(nval / PS).sum()) * 4),
+        "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
+        "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
+        "mla_decode_combine": ("hbm", T * H * DV * 2),
+    }
+    kernels = {}
+    for name, (n, avg) in kt.items():
+        bound, w = work.get(name, ("hbm", 0))
+        e = {"avg_us": round(avg * 1e3, 2), "launches_per_step": n // args.steps}
+        if w:
+            e.update(_roofline_entry(bound, w, avg))
+            e["work"] = w
+        kernels[name] = e
+    dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
+    bound, w = work[dom]
+    roof = _roofline_entry(bound, w, kt[dom][1])
+    roof.update({"kernel": dom, "traffic": None,
+                 "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+    return dict(ms=ms, tok_s=T / (ms * 1e-3), kernels=kernels, roofline=roof,
+                selected=n_sel, keys=int(nval.sum()))
+
+
+# ----------------------------------------------------------------------------
+# extend
+# ----------------------------------------------------------------------------
+def bench_extend(dsa, wl, args, QB):
+    import numpy as np
+    import torch
+
+    layers = len(wl.kv_cache)
+    d = _dev_inputs(wl, "extend", layers=layers)
+    b = wl.batches["extend"]
+    T, k, H = b.T, wl.k, wl.H_mla
+    u_max = wl.u_max
+    nqb = (T + QB - 1) // QB
+    topk = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    units = torch.empty((nqb, u_max), dtype=torch.int32, device="cuda")
+    counts = torch.empty((nqb,), dtype=torch.int32, device="cuda")
+    member = torch.empty((nqb, u_max, QB), dtype=torch.uint64, device="cuda")
+    outs = [torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
+    ws_i = torch.empty(dsa.indexer_topk_workspace(T, wl.S, wl.H_idx, wl.D_idx, wl.PS, wl.MP, k,
+                                                  d["max_q_len"]), dtype=torch.uint8,
+                       device="cuda")
+    ws_u = torch.empty(max(1, dsa.block_union_workspace(T, wl.S, wl.MP, QB, u_max)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"], d["seq_lens"],
+                         d["cu"], k, d["max_q_len"], out=topk, workspace=ws_i)
+        dsa.block_union(topk, d["seq_lens"], d["cu"], wl.PS, wl.MP, QB, u_max,
+                        out=(units, counts, member), workspace=ws_u)
+        for i in range(layers):  # the full layer, then IndexShare layers reuse the tables
+            dsa.sparse_mla_extend(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
+                                  d["cu"], units, counts, member, QB, wl.sm_scale, out=outs[i])
+
+    steps = max(2, args.steps // 4)
+    ms = _timed(step, steps, min(args.warmup, 2))
+    kt = _kernel_times(dsa, step, steps)
+    cnt = counts.cpu().numpy()
+    sel = topk.cpu().numpy()
+    nval = _row_valid_counts(wl, b.cu_q_lens)
+    exec_flops = int(np.minimum(cnt, u_max).sum()) * QB * H * wl.PS * (DK + DV) * 2
+    useful_flops = int((sel >= 0).sum()) * H * (DK + DV) * 2
+    idx_flops = 2 * wl.H_idx * wl.D_idx * int(nval.sum())
+    work = {
+        "idx_score_tiles": ("mfma", idx_flops),
+        "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
+        "mla_extend_qblock": ("mfma", exec_flops),
+        "union_member": ("hbm", T * k * 4 + nqb * u_max * QB * 8),
+        "union_mark": ("hbm", T * k * 4),
+    }
+    kernels = {}
+    for name, (n, avg) in kt.items():
+        e = {"avg_us": round(avg * 1e3, 2), "launches_per_step": n // steps}
+        if name in work:
+            bound, w = work[name]
+            e.update(_roofline_entry(bound, w, avg))
+            e["work"] = w
+        kernels[name] = e
+    # redundant-fetch ratios: per-query pages vs block unions vs distinct pages
+    seq, _ = _rows_seq(wl, b.cu_q_lens)
+    keys = np.where(sel >= 0, seq[:, None] * wl.MP + sel // wl.PS, -1)
+    per_query_pages = sum(len(np.unique(r[r >= 0])) for r in keys)
+    distinct = len(np.unique(keys[keys >= 0]))
+    res = dict(ms_per_step=round(ms, 4), layers=layers, QB=QB,
+               ms_full_layer=round(ms - (layers - 1) * kt["mla_extend_qblock"][1], 4)
+               if layers > 1 else round(ms, 4),
+               ms_shared_layer=round(kt["mla_extend_qblock"][1], 4),
+               indexer_ms=round(kt.get("idx_score_tiles", (0, 0))[1]
+                                + kt.get("topk_select", (0, 0))[1], 4),
+               union_per_block={"min": int(cnt.min()), "mean": round(float(cnt.mean()), 1),
+                                "max": int(cnt.max())},
+               redundant_fetch={"per_query": round(per_query_pages / max(distinct, 1), 1),
+                                "qblock": round(float(cnt.sum()) / max(distinct, 1), 2)},
+               mfma_executed_tflop=round(exec_flops / 1e12, 3),
+               mfma_useful_tflop=round(useful_flops / 1e12, 3),
+               kernels=kernels)
+    dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
+    if dom in work:
+        bound, w = work[dom]
+        roof = _roofline_entry(bound, w, kt[dom][1])
+        roof.update({"kernel": dom, "traffic": None, "work_per_launch": w,
+                     "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+        res["roofline"] = roof
+    return res
+
+
+def _rows_seq(wl, cu):
+    import numpy as np
+
+    T = int(cu[-1])
+    seq = np.full(T, -1, dtype=np.int64)
+    pos = np.full(T, -1, dtype=np.int64)
+    for s in range(wl.S):
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        seq[q0:q1] = s
+        pos[q0:q1] = int(wl.seq_lens[s]) - (q1 - q0) + np.arange(q1 - q0)
+    return seq, pos
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores
+# ----------------------------------------------------------------------------
+def cpu_baseline(wl, seconds):
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workloads import bf16_to_f64
+
+    b = wl.batches["decode"]
+    q_idx = bf16_to_f64(b.q_idx)
+    w = b.w.astype(np.float64)
+    icache = wl.idx_cache.f64_view()
+    kv = wl.kv_cache[0].f64_view()
+    q = bf16_to_f64(b.q_mla[0])
+    rows_done = 0
+    t0 = time.perf_counter()
+    t_end = t0 + seconds
+    r = 0
+    while True:
+        rows = [r % b.T]
+        tk = oracle.indexer_topk(q_idx, w, icache, wl.page_table, wl.seq_lens, b.cu_q_lens, wl.k,
+                                 rows=rows)
+        oracle.sparse_mla(q, kv, wl.page_table, wl.seq_lens, b.cu_q_lens, tk, wl.sm_scale, wl.Dv,
+                          rows=rows)
+        rows_done += 1
+        r += 1
+        if time.perf_counter() >= t_end and rows_done >= 1:
+            break
+    dt = time.perf_counter() - t0
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    return {"value": round(rows_done / dt, 3), "unit": "tok/s", "cores": max(threads, 1),
+            "kind": "oracle",
+            "sample": f"{rows_done} decode rows (indexer top-k + sparse MLA, fp64 NumPy) of the "
+                      f"{wl.name} workload in {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path runs on a single MI355X here)", file=sys.stderr)
+        return 2
+    import torch
+
+    import sparse_attention_relu_amd as dsa
+    import workloads as W
+
+    dsa.load()
+    torch.cuda.set_device(0)
+    wl = W.config(args.config)
+    dec = bench_decode(dsa, wl, args)
+    result = {
+        "metric": METRIC,
+        "value": round(dec["tok_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "seqs": wl.S, "kv_len": int(wl.seq_lens.max()),
+                   "page_size": wl.PS, "index_topk": wl.k, "indexer_heads": wl.H_idx,
+                   "indexer_dim": wl.D_idx, "mla_heads": wl.H_mla, "dk": DK, "dv": DV,
+                   "step": "one DSA decode layer: indexer top-k + sparse MLA"},
+        "roofline": dec["roofline"],
+        "kernels": dec["kernels"],
+    }
+    if args.extend_config:
+        wle = W.config(args.extend_config)
+        qb = args.qb if args.qb in wle.QB else wle.QB[0]
+        ext = bench_extend(dsa, wle, args, qb)
+        ext["workload"] = wle.name
+        result["extend"] = ext
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

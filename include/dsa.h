@@ -182,6 +182,21 @@ int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, i
                           int H, int PS, int MP, int QB, int u_max, float sm_scale, void* out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing (diagnostics). dsa_profile_enable(1) clears earlier records
+ * and makes every subsequent kernel launch of the entry points above record
+ * a pair of HIP events on its own stream; dsa_profile_enable(0) stops it.
+ * dsa_profile_read() waits for the recorded events, reduces them per kernel
+ * name in first-launch order and fills up to max_kernels entries:
+ * names (max_kernels * name_len bytes, NUL-terminated, truncated to
+ * name_len - 1), launches[i], total_ms[i]; *n_kernels gets the count. The
+ * records are consumed. Not meant for use under graph capture.
+ * Returns DSA_ERR_INVALID_ARG for bad sizes, DSA_ERR_HIP if an event failed.
+ */
+int dsa_profile_enable(int on);
+int dsa_profile_read(int max_kernels, char* names, int name_len, int* launches,
+                     double* total_ms, int* n_kernels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     indexer_topk_workspace,
     last_error,
     load,
+    profile_enable,
+    profile_read,
     sparse_mla_decode,
     sparse_mla_decode_workspace,
     sparse_mla_extend,

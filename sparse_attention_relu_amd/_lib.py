@@ -40,6 +40,8 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
                               + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_sparse_mla_extend_workspace": (_c_size, [_c_int] * 4),
+    "dsa_profile_enable": (_c_int, [_c_int]),
+    "dsa_profile_read": (_c_int, [_c_int, ctypes.c_char_p, _c_int, _vp, _vp, _vp]),
     "dsa_sparse_mla_extend": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]
                               + [_c_int] * 7 + [_c_float, _vp, _vp, _c_size, _vp]),
 }
@@ -145,6 +147,32 @@ def _ragged(page_table, seq_lens, cu_q_lens, device):
     if page_table.shape[0] != S or cu_q_lens.shape[0] != S + 1:
         raise ValueError("page_table [S, MP], seq_lens [S], cu_q_lens [S+1] disagree on S")
     return S, page_table.shape[1]
+
+
+# ----------------------------------------------------------------------------
+# Kernel timing
+# ----------------------------------------------------------------------------
+def profile_enable(on: bool = True) -> None:
+    """Start (and clear) or stop per-kernel event timing in the library."""
+    _check("dsa_profile_enable", load().dsa_profile_enable(1 if on else 0))
+
+
+def profile_read(max_kernels: int = 32):
+    """{kernel name: (launches, total_ms)} of the launches since enabling."""
+    name_len = 64
+    names = ctypes.create_string_buffer(max_kernels * name_len)
+    launches = (ctypes.c_int * max_kernels)()
+    total = (ctypes.c_double * max_kernels)()
+    n = ctypes.c_int(0)
+    st = load().dsa_profile_read(max_kernels, names, name_len, ctypes.addressof(launches),
+                                 ctypes.addressof(total), ctypes.addressof(n))
+    _check("dsa_profile_read", st)
+    raw = names.raw
+    out = {}
+    for i in range(n.value):
+        nm = raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (launches[i], total[i])
+    return out
 
 
 # ----------------------------------------------------------------------------

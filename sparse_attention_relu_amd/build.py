@@ -20,12 +20,15 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "indexer.hip", "union.hip", "mla.hip"]
-HEADERS = ["common.h", "kernels.h"]
+SOURCES = ["api.cpp", "profile.cpp", "indexer.hip", "union.hip", "mla.hip"]
+HEADERS = ["common.h", "kernels.h", "profile.h"]
 
 COMMON_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
                 f"--offload-arch={ARCH}", "-I", os.path.join(os.path.dirname(PKG), "include")]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# per-source extras: the query-block attention keeps 256 accumulator registers
+# live, which only fits when MFMA results may be placed in the VGPR form
+EXTRA_FLAGS = {"mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def hipcc() -> str:
@@ -40,7 +43,7 @@ def _compile(src: str) -> str:
     cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
-        cmd += DEVICE_FLAGS
+        cmd += DEVICE_FLAGS + EXTRA_FLAGS.get(src, [])
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")

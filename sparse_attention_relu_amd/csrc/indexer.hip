@@ -9,8 +9,11 @@
 // top-k per row with a 64-bit radix select over (score, position) keys.
 #include <atomic>
 
+#include <rocprim/block/block_radix_sort.hpp>
+
 #include "common.h"
 #include "kernels.h"
+#include "profile.h"
 
 namespace dsa {
 
@@ -82,29 +85,36 @@ __global__ __launch_bounds__(256) void idx_score_rows(
   const int32_t* ptrow = pt + (size_t)ri.seq * MP;
   float* srow = scores + (size_t)t * ld;
 
-  for (int jb = j_begin; jb < j_end; jb += 32) {
-    const int j = jb + m;
+  // issue every key load of this wave before the first MFMA
+  constexpr int NB = KPW / 32;
+  bf16x8 b[NB][KS];
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int j = j_begin + 32 * blk + m;
     const bool ok = j < j_end;
     const uint16_t* kp = cache;
     if (ok) {
       const int page = clamp_page(ptrow[j / PS], num_pages);
       kp = cache + ((size_t)page * PS + (j % PS)) * D + hf * HALF;
     }
-    bf16x8 b[KS];
 #pragma unroll
     for (int i = 0; i < KS; ++i)
-      b[i] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(kp + 8 * i) : zero_u4());
+      b[blk][i] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(kp + 8 * i) : zero_u4());
+  }
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int j = j_begin + 32 * blk + m;
     float part = 0.0f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
       f32x16 acc = {};
 #pragma unroll
       for (int i = 0; i < KS; ++i)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[i], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[blk][i], acc, 0, 0, 0);
       part += relu_weighted_sum(acc, wv[hb]);
     }
     part += shfl_xor_f(part, 32);
-    if (hf == 0 && ok) srow[j] = part;
+    if (hf == 0 && j < j_end) srow[j] = part;
   }
 }
 
@@ -266,65 +276,79 @@ __global__ __launch_bounds__(NW * 64) void idx_score_tiles(
 }
 
 // ---------------------------------------------------------------------------
-// Exact top-k per row: radix select over 64-bit keys
-//   key(j) = order_bits(score[j]) << 32 | (2^32 - 1 - j)
-// (distinct per position; larger key = earlier in the canonical order).
-// 12-bit digits from the top narrow the search until the boundary bin fits
-// the candidate buffer; a collect pass then moves every key above the
-// boundary bin into the output list and the boundary bin's keys into the
-// candidate list, which is sorted to take the missing ones. The k winners
-// are finally sorted in LDS (bitonic, descending key) and written as
-// positions, -1 padded.
-// grid = T, block = NT, dynamic LDS = (kp2 + cand_cap) * 8 + 4096 * 4.
+// Exact top-k per row.
+//
+// Every score maps to a 32-bit order key (larger key = larger score, -0.0
+// folded onto +0.0). Radix select finds the boundary: a 12-bit histogram of
+// the key's top bits over the row picks the bin holding the k-th largest
+// key, further 12-bit digits narrow it while the bin is larger than the
+// candidate buffer. A collect pass then compacts, in POSITION order, the
+// keys above the bin into the output list and the bin's keys into the
+// candidate list; the remaining digits are resolved inside LDS, and the
+// candidates above the exact k-th key plus the first ties (lowest
+// positions) are appended, still in position order. One stable descending
+// block radix sort of the k (key, position) pairs then yields score
+// descending, position ascending.
+// grid = T, block = 1024, dynamic LDS = 4096 * 4 + cand_cap * 8 + 1024 * IPT * 8.
 // ---------------------------------------------------------------------------
-template <int NT>
-__device__ void bitonic_sort_desc(uint64_t* a, int n) {
-  for (int k2 = 2; k2 <= n; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += NT) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo + j;
-        const uint64_t x = a[lo], y = a[hi];
-        const bool desc = (lo & k2) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          a[lo] = y;
-          a[hi] = x;
-        }
+constexpr int kSelNT = 1024;
+constexpr int kSelM = 16;  // consecutive positions per thread in a collect chunk
+
+// Bin d of an nb-bin histogram holding the need-th largest key (counting
+// from the top bin down); writes (d, count above d) to out[0..1].
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int need, int* s_scan,
+                                           int* out) {
+  constexpr int BPT = 4096 / kSelNT;
+  const int tid = threadIdx.x;
+  int local = 0;
+#pragma unroll
+  for (int c = 0; c < BPT; ++c) {
+    const int b = nb - 1 - tid * BPT - c;
+    if (b >= 0) local += (int)hist[b];
+  }
+  int total;
+  const int incl = block_inclusive_scan<kSelNT>(local, s_scan, &total);
+  const int excl = incl - local;
+  if (excl < need && need <= incl) {
+    int run = excl;
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      const int b = nb - 1 - tid * BPT - c;
+      if (b < 0) break;
+      const int h = (int)hist[b];
+      if (run + h >= need) {
+        out[0] = b;
+        out[1] = run;
+        break;
       }
-      __syncthreads();
+      run += h;
     }
   }
+  __syncthreads();
 }
 
-__device__ __forceinline__ int next_pow2(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+__device__ __forceinline__ uint32_t row_key(const float* row, int j) {
+  return score_order_bits(row[j]);
 }
 
-// wave-aggregated append to an LDS counter; returns this lane's slot
-__device__ __forceinline__ int wave_append(bool pred, int* counter) {
-  const uint64_t mask = __ballot(pred);
-  if (mask == 0) return -1;
-  const int leader = __ffsll((unsigned long long)mask) - 1;
-  int base = 0;
-  if (lane_id() == leader) base = atomicAdd(counter, __popcll(mask));
-  base = __shfl(base, leader, DSA_WAVE);
-  return pred ? base + ballot_rank(mask) : -1;
-}
-
-template <int NT>
-__global__ __launch_bounds__(NT) void topk_select(const float* __restrict__ scores, long ld,
-                                                  const int32_t* __restrict__ cu,
-                                                  const int32_t* __restrict__ seq_lens, int S,
-                                                  int cap, int k, int kp2, int cand_cap,
-                                                  int32_t* __restrict__ topk) {
-  extern __shared__ uint64_t smem64[];
-  uint64_t* outk = smem64;
-  uint64_t* cand = outk + kp2;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(cand + cand_cap);
-  __shared__ int s_cnt[4];
+template <int IPT>
+__global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
+                                                      const int32_t* __restrict__ cu,
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      int S, int cap, int k, int cand_cap,
+                                                      int32_t* __restrict__ topk) {
+  constexpr int NT = kSelNT;
+  using Sorter = rocprim::block_radix_sort<uint32_t, NT, IPT, int>;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  uint32_t* hist = lds;                      // 4096
+  uint32_t* cand_key = hist + 4096;          // cand_cap
+  uint32_t* cand_pos = cand_key + cand_cap;  // cand_cap
+  uint32_t* sel_key = cand_pos + cand_cap;   // NT * IPT
+  uint32_t* sel_pos = sel_key + NT * IPT;    // NT * IPT
+  // the sort's scratch reuses the histogram / candidate region once it is dead
+  auto& sort_storage = *reinterpret_cast<typename Sorter::storage_type*>(lds);
   __shared__ int s_scan[NT / 64];
+  __shared__ int s_dig[2];
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -336,103 +360,179 @@ __global__ __launch_bounds__(NT) void topk_select(const float* __restrict__ scor
     for (int i = tid; i < k; i += NT) orow[i] = -1;
     return;
   }
-  if (tid == 0) {
-    s_cnt[0] = 0;
-    s_cnt[1] = 0;
-    s_cnt[2] = 0;
-    s_cnt[3] = 0;
-  }
-  __syncthreads();
 
   int count;
   if (n <= k) {
-    for (int j = tid; j < n; j += NT) outk[j] = topk_key(row[j], j);
+    for (int j = tid; j < n; j += NT) {
+      sel_key[j] = row_key(row, j);
+      sel_pos[j] = (uint32_t)j;
+    }
     count = n;
   } else {
-    uint64_t prefix = 0;
+    // ---- global digits until the boundary bin fits the candidate buffer
+    uint32_t prefix = 0;
     int pbits = 0;
     int need = k;
-    while (true) {
-      const int width = min(12, 64 - pbits);
-      const int shift = 64 - pbits - width;
-      const int nb = 1 << width;
-      for (int i = tid; i < 4096; i += NT) hist[i] = 0;
+    int nbin = n;
+    while (pbits == 0 || (nbin > cand_cap && pbits < 32)) {
+      const int w = min(12, 32 - pbits);
+      const int nb = 1 << w;
+      for (int i = tid; i < nb; i += NT) hist[i] = 0;
       __syncthreads();
-      for (int j = tid; j < n; j += NT) {
-        const uint64_t key = topk_key(row[j], j);
-        if (pbits == 0 || (key >> (64 - pbits)) == prefix)
-          atomicAdd(&hist[(key >> shift) & (uint64_t)(nb - 1)], 1u);
-      }
-      __syncthreads();
-      // suffix counts from the highest bin down: thread tid owns the
-      // 4096 / NT bins nb-1-tid*BPT .. nb-BPT-tid*BPT
-      constexpr int BPT = 4096 / NT;
-      int local = 0;
+      const int shift = 32 - pbits - w;
+      const int n4 = n & ~3;
+      for (int j = tid * 4; j < n4; j += NT * 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j);
+        const float vs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int c = 0; c < BPT; ++c) {
-        const int b = nb - 1 - tid * BPT - c;
-        if (b >= 0) local += (int)hist[b];
-      }
-      int total;
-      const int incl = block_inclusive_scan<NT>(local, s_scan, &total);
-      const int excl = incl - local;
-      if (excl < need && need <= incl) {
-        int run = excl;
-#pragma unroll
-        for (int c = 0; c < BPT; ++c) {
-          const int b = nb - 1 - tid * BPT - c;
-          if (b < 0) break;
-          const int h = (int)hist[b];
-          if (run + h >= need) {
-            s_cnt[2] = b;
-            s_cnt[3] = run;
-            break;
-          }
-          run += h;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t key = score_order_bits(vs[e]);
+          if (pbits == 0 || (key >> (32 - pbits)) == prefix)
+            atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
         }
       }
-      __syncthreads();
-      const int dstar = s_cnt[2];
-      const int above = s_cnt[3];
-      need -= above;
-      prefix = (pbits == 0 ? 0ull : (prefix << width)) | (uint64_t)dstar;
-      pbits += width;
-      const int bin = (int)hist[dstar];
-      __syncthreads();
-      if (bin <= cand_cap || pbits >= 64) break;
-    }
-    // collect
-    for (int j0 = 0; j0 < n; j0 += NT) {
-      const int j = j0 + tid;
-      uint64_t key = 0;
-      uint64_t v = 0;
-      const bool in = j < n;
-      if (in) {
-        key = topk_key(row[j], j);
-        v = pbits >= 64 ? key : (key >> (64 - pbits));
+      for (int j = n4 + tid; j < n; j += NT) {
+        const uint32_t key = row_key(row, j);
+        if (pbits == 0 || (key >> (32 - pbits)) == prefix)
+          atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
       }
-      const int io = wave_append(in && v > prefix, &s_cnt[0]);
-      if (io >= 0 && io < kp2) outk[io] = key;
-      const int ic = wave_append(in && v == prefix, &s_cnt[1]);
-      if (ic >= 0 && ic < cand_cap) cand[ic] = key;
+      __syncthreads();
+      find_digit(hist, nb, need, s_scan, s_dig);
+      const int d = s_dig[0];
+      need -= s_dig[1];
+      prefix = (pbits == 0 ? 0u : (prefix << w)) | (uint32_t)d;
+      pbits += w;
+      nbin = (int)hist[d];
+      __syncthreads();
+    }
+    // ---- collect in position order: above -> output list, boundary bin ->
+    // candidates (or, when all 32 bits are fixed, its first `need` ties)
+    const bool exact = pbits >= 32;
+    int nabove = 0, nbnd = 0;
+    for (int c0 = 0; c0 < n; c0 += NT * kSelM) {
+      const int j0 = c0 + tid * kSelM;
+      uint32_t keys[kSelM];
+      if (j0 + kSelM <= n) {
+#pragma unroll
+        for (int e = 0; e < kSelM; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(row + j0 + e);
+          keys[e] = score_order_bits(v.x);
+          keys[e + 1] = score_order_bits(v.y);
+          keys[e + 2] = score_order_bits(v.z);
+          keys[e + 3] = score_order_bits(v.w);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kSelM; ++e) keys[e] = (j0 + e < n) ? row_key(row, j0 + e) : 0u;
+      }
+      int fa = 0, fb = 0;
+#pragma unroll
+      for (int e = 0; e < kSelM; ++e) {
+        if (j0 + e >= n) break;
+        const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
+        fa += v > prefix;
+        fb += v == prefix;
+      }
+      int total;
+      const int packed = fa | (fb << 16);
+      const int excl = block_inclusive_scan<NT>(packed, s_scan, &total) - packed;
+      int ia = nabove + (excl & 0xffff);
+      int ib = nbnd + (excl >> 16);
+#pragma unroll
+      for (int e = 0; e < kSelM; ++e) {
+        const int j = j0 + e;
+        if (j >= n) break;
+        const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
+        if (v > prefix) {
+          if (ia < NT * IPT) {
+            sel_key[ia] = keys[e];
+            sel_pos[ia] = (uint32_t)j;
+          }
+          ++ia;
+        } else if (v == prefix) {
+          if (exact) {  // ties of the k-th key: the first `need` in position order
+            const int dst = (k - need) + ib;
+            if (ib < need && dst < NT * IPT) {
+              sel_key[dst] = keys[e];
+              sel_pos[dst] = (uint32_t)j;
+            }
+          } else if (ib < cand_cap) {
+            cand_key[ib] = keys[e];
+            cand_pos[ib] = (uint32_t)j;
+          }
+          ++ib;
+        }
+      }
+      nabove += total & 0xffff;
+      nbnd += total >> 16;
     }
     __syncthreads();
-    const int nc = min(s_cnt[1], cand_cap);
-    const int base = min(s_cnt[0], k);
-    need = min(need, min(nc, k - base));
-    const int cp2 = next_pow2(nc);
-    for (int i = nc + tid; i < cp2; i += NT) cand[i] = 0;
-    __syncthreads();
-    bitonic_sort_desc<NT>(cand, cp2);
-    for (int i = tid; i < need; i += NT) outk[base + i] = cand[i];
-    count = base + need;
+    if (!exact) {
+      // ---- resolve the remaining digits among the candidates (LDS)
+      const int C = min(nbnd, cand_cap);
+      uint32_t cpre = prefix;
+      int cbits = pbits;
+      int cneed = need;
+      while (cbits < 32) {
+        const int w = min(12, 32 - cbits);
+        const int nb = 1 << w;
+        for (int i = tid; i < nb; i += NT) hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < C; i += NT) {
+          const uint32_t key = cand_key[i];
+          if ((key >> (32 - cbits)) == cpre)
+            atomicAdd(&hist[(key >> (32 - cbits - w)) & (uint32_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_digit(hist, nb, cneed, s_scan, s_dig);
+        cneed -= s_dig[1];
+        cpre = (cpre << w) | (uint32_t)s_dig[0];
+        cbits += w;
+        __syncthreads();
+      }
+      // candidates above the k-th key, then its first `cneed` ties, in order
+      const uint32_t kth = cpre;
+      const int base = k - need;
+      int ngt = 0, ntie = 0;
+      for (int c0 = 0; c0 < C; c0 += NT) {
+        const int i = c0 + tid;
+        const uint32_t key = i < C ? cand_key[i] : 0u;
+        const int gt = (i < C) && key > kth;
+        const int tie = (i < C) && key == kth;
+        int total;
+        const int packed = gt | (tie << 16);
+        const int excl = block_inclusive_scan<NT>(packed, s_scan, &total) - packed;
+        const int gt_before = ngt + (excl & 0xffff);
+        const int tie_before = ntie + (excl >> 16);
+        if (gt || (tie && tie_before < cneed)) {
+          const int dst = base + gt_before + min(tie_before, cneed);
+          if (dst < NT * IPT) {
+            sel_key[dst] = key;
+            sel_pos[dst] = cand_pos[i];
+          }
+        }
+        ngt += total & 0xffff;
+        ntie += total >> 16;
+      }
+    }
+    count = k;
   }
   __syncthreads();
-  const int op2 = next_pow2(count);
-  for (int i = count + tid; i < op2; i += NT) outk[i] = 0;
+  uint32_t keys[IPT];
+  int vals[IPT];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    keys[i] = idx < count ? sel_key[idx] : 0u;
+    vals[i] = idx < count ? (int)sel_pos[idx] : -1;
+  }
   __syncthreads();
-  bitonic_sort_desc<NT>(outk, op2);
-  for (int i = tid; i < k; i += NT) orow[i] = i < count ? topk_key_pos(outk[i]) : -1;
+  Sorter().sort_desc(keys, vals, sort_storage);
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    if (idx < k) orow[idx] = vals[i];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -443,6 +543,7 @@ static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
   constexpr int KPW = 64;
   const int cap = a.MP * a.PS;
   dim3 grid((cap + 4 * KPW - 1) / (4 * KPW), a.T);
+  ProfScope prof("idx_score_rows", st);
   hipLaunchKernelGGL((idx_score_rows<D, HB, KPW>), grid, dim3(256), 0, st, a.q, a.w, a.cache,
                      a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
                      a.ld);
@@ -455,6 +556,7 @@ static hipError_t launch_tiles(const IndexerArgs& a, hipStream_t st) {
   const int cap = a.MP * a.PS;
   const int RK = 2048;
   dim3 grid((cap + RK - 1) / RK, (a.T + TR - 1) / TR);
+  ProfScope prof("idx_score_tiles", st);
   hipLaunchKernelGGL((idx_score_tiles<D, HB, QPW, NW>), grid, dim3(NW * 64), 0, st, a.q, a.w,
                      a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, RK,
                      a.scores, a.ld);
@@ -476,32 +578,42 @@ hipError_t indexer_score(const IndexerArgs& a, hipStream_t st) {
   }
 }
 
+static int select_ipt(int k) { return k <= 1024 ? 1 : (k <= 2048 ? 2 : 4); }
+
 size_t topk_select_lds_bytes(int k) {
-  int kp2 = 1;
-  while (kp2 < k) kp2 <<= 1;
-  return (size_t)(kp2 + kTopkCandCap) * 8 + 4096 * 4;
+  return (size_t)4096 * 4 + (size_t)kTopkCandCap * 8 + (size_t)kSelNT * select_ipt(k) * 8;
 }
 
-hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
-  constexpr int NT = 1024;
-  int kp2 = 1;
-  while (kp2 < a.k) kp2 <<= 1;
+template <int IPT>
+static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
+  static_assert(sizeof(typename rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>::storage_type)
+                    <= (4096 + 2 * kTopkCandCap) * 4,
+                "sort scratch must fit the histogram and candidate region");
   const size_t lds = topk_select_lds_bytes(a.k);
-  // raise the dynamic-LDS limit of the select kernel once per device
+  // raise the dynamic-LDS limit once per device
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<NT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<IPT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit);
   }
-  hipLaunchKernelGGL((topk_select<NT>), dim3(a.T), dim3(NT), lds, st, a.scores, a.ld, a.cu,
-                     a.seq_lens, a.S, a.MP * a.PS, a.k, kp2, kTopkCandCap, a.topk);
+  ProfScope prof("topk_select", st);
+  hipLaunchKernelGGL((topk_select<IPT>), dim3(a.T), dim3(kSelNT), lds, st, a.scores, a.ld, a.cu,
+                     a.seq_lens, a.S, a.MP * a.PS, a.k, kTopkCandCap, a.topk);
   return hipGetLastError();
+}
+
+hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
+  switch (select_ipt(a.k)) {
+    case 1: return launch_select<1>(a, st);
+    case 2: return launch_select<2>(a, st);
+    default: return launch_select<4>(a, st);
+  }
 }
 
 }  // namespace dsa

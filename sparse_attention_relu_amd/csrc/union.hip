@@ -11,6 +11,7 @@
 // built in LDS per group of queries and written slot-major.
 #include "common.h"
 #include "kernels.h"
+#include "profile.h"
 
 namespace dsa {
 
@@ -142,18 +143,28 @@ hipError_t block_union(const UnionArgs& a, hipStream_t st) {
   const long nbits = (long)nqb * NW;
   long nblk = (nbits + 255) / 256;
   if (nblk > 4096) nblk = 4096;
-  hipLaunchKernelGGL(union_clear, dim3((unsigned)nblk), dim3(256), 0, st, a.bits, nbits);
+  {
+    ProfScope prof("union_clear", st);
+    hipLaunchKernelGGL(union_clear, dim3((unsigned)nblk), dim3(256), 0, st, a.bits, nbits);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int RPW = 16;
-  hipLaunchKernelGGL(union_mark, dim3(nqb, (a.QB + RPW - 1) / RPW), dim3(256),
-                     (size_t)NW * 8, st, a.topk, a.seq_lens, a.cu, a.T, a.S, a.k, a.PS, a.MP,
-                     a.QB, RPW, NW, a.bits);
+  {
+    ProfScope prof("union_mark", st);
+    hipLaunchKernelGGL(union_mark, dim3(nqb, (a.QB + RPW - 1) / RPW), dim3(256),
+                       (size_t)NW * 8, st, a.topk, a.seq_lens, a.cu, a.T, a.S, a.k, a.PS, a.MP,
+                       a.QB, RPW, NW, a.bits);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(union_compact, dim3(nqb), dim3(256), 0, st, a.bits, NW, a.u_max, a.prefix,
-                     a.units, a.counts);
+  {
+    ProfScope prof("union_compact", st);
+    hipLaunchKernelGGL(union_compact, dim3(nqb), dim3(256), 0, st, a.bits, NW, a.u_max, a.prefix,
+                       a.units, a.counts);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int qpw = union_member_qpw(a.QB, a.u_max);
+  ProfScope prof("union_member", st);
   hipLaunchKernelGGL(union_member, dim3(nqb, (a.QB + qpw - 1) / qpw), dim3(256),
                      (size_t)a.u_max * qpw * 8, st, a.topk, a.seq_lens, a.cu, a.T, a.S, a.k,
                      a.PS, a.MP, a.QB, a.u_max, qpw, NW, a.bits, a.prefix, a.counts, a.member);

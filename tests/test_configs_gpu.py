@@ -1,0 +1,191 @@
+"""GPU parity at the five named workloads' full sizes, in the launch
+configuration bench.py times.
+
+Decode workloads are checked on every row. For the two extend workloads the
+oracle computes sampled rows and blocks one by one; every row and block is
+also checked against properties that hold at any size (padding count,
+causality, distinct positions, union ordering and membership popcounts).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import Dev, check_attention, check_topk_rows_valid, i32, log, to_np, torch_mod
+from workloads import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_relu_amd as m
+
+    m.load()
+    return m
+
+
+def _topk(dsa, d, bt, k, mql):
+    torch = torch_mod()
+    out = dsa.indexer_topk(bt["q_idx"], bt["w"], d.idx_cache, d.page_table, d.seq_lens, bt["cu"],
+                           k, mql)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_rows_topk(wl, b, rows):
+    return oracle.indexer_topk(bf16_to_f64(b.q_idx), b.w.astype(np.float64),
+                               wl.idx_cache.f64_view(), wl.page_table, wl.seq_lens, b.cu_q_lens,
+                               wl.k, rows=rows)
+
+
+def _oracle_rows_mla(wl, b, topk, rows, layer=0):
+    return oracle.sparse_mla(bf16_to_f64(b.q_mla[layer]), wl.kv_cache[layer].f64_view(),
+                             wl.page_table, wl.seq_lens, b.cu_q_lens, topk, wl.sm_scale, wl.Dv,
+                             rows=rows)
+
+
+def _sample_rows(T, cu, n_random, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1}
+    for c in cu[1:-1]:
+        rows.update({int(c) - 1, int(c)})
+    rows.update(rng.choice(T, size=min(n_random, T), replace=False).tolist())
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+def _decode_config(dsa, cid):
+    torch = torch_mod()
+    log(f"config {cid}: generating")
+    wl = W.config(cid)
+    b = wl.batches["decode"]
+    d = Dev(wl)
+    bt = d.batch("decode")
+    log(f"config {cid}: indexer top-k, T={b.T}")
+    tk = _topk(dsa, d, bt, wl.k, 1).cpu().numpy()
+    rows = list(range(b.T))
+    exp = _oracle_rows_topk(wl, b, rows)
+    assert np.array_equal(tk, exp), "top-k differs from the oracle"
+    log(f"config {cid}: sparse MLA decode")
+    out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"],
+                                i32(tk, "cuda"), wl.sm_scale)
+    torch.cuda.synchronize()
+    check_attention(to_np(out), _oracle_rows_mla(wl, b, exp, rows), what=f"config {cid} decode")
+
+
+def test_config2_decode_batch(dsa):
+    _decode_config(dsa, 2)
+
+
+@pytest.mark.timeout(600)
+def test_config3_ragged_decode(dsa):
+    _decode_config(dsa, 3)
+
+
+def _check_union_all_blocks(units, counts, member, topk, QB, u_max):
+    """Properties of every block: sorted unique units, -1 tail, and per query
+    popcount = number of selections (lossless caps)."""
+    nqb = units.shape[0]
+    T = topk.shape[0]
+    assert (counts <= u_max).all(), "a block overflowed a lossless cap"
+    for b in range(nqb):
+        n = int(counts[b])
+        assert (np.diff(units[b, :n]) > 0).all() and (units[b, n:] == -1).all()
+    bytes_ = member.view(np.uint8).reshape(nqb, u_max, QB, 8)
+    table = np.array([bin(i).count("1") for i in range(256)], dtype=np.uint8)
+    pop = table[bytes_].sum(axis=(1, 3), dtype=np.int64)  # [nQB, QB]
+    sel = np.zeros(nqb * QB, dtype=np.int64)
+    sel[:T] = (topk >= 0).sum(axis=1)
+    assert np.array_equal(pop.reshape(-1), sel), "membership popcount != selections"
+
+
+def _extend_config(dsa, cid, QB, n_random, n_blocks):
+    torch = torch_mod()
+    log(f"config {cid}: generating")
+    wl = W.config(cid)
+    b = wl.batches["extend"]
+    cu = b.cu_q_lens
+    d = Dev(wl)
+    bt = d.batch("extend")
+    T = b.T
+    mql = int(np.diff(cu).max())
+    log(f"config {cid}: indexer top-k (tile path), T={T}")
+    tk_t = _topk(dsa, d, bt, wl.k, mql)
+    tk = tk_t.cpu().numpy()
+    check_topk_rows_valid(tk, wl.seq_lens, cu, wl.k)
+    rows = _sample_rows(T, cu, n_random, cid)
+    log(f"config {cid}: oracle top-k on {len(rows)} rows")
+    exp = _oracle_rows_topk(wl, b, rows)
+    assert np.array_equal(tk[rows], exp[rows]), "top-k differs from the oracle"
+
+    log(f"config {cid}: union QB={QB}")
+    u_max = wl.u_max
+    units, counts, member = dsa.block_union(tk_t, d.seq_lens, bt["cu"], wl.PS, wl.MP, QB, u_max)
+    torch.cuda.synchronize()
+    un, cn, mn = units.cpu().numpy(), counts.cpu().numpy(), member.cpu().numpy()
+    _check_union_all_blocks(un, cn, mn, tk, QB, u_max)
+    nqb = un.shape[0]
+    blocks = sorted({0, nqb - 1} | set(np.random.default_rng(cid).choice(nqb, n_blocks).tolist()))
+    eu, ec, em = oracle.block_union(tk, wl.seq_lens, cu, wl.PS, wl.MP, QB, u_max, blocks=blocks)
+    for blk in blocks:
+        assert np.array_equal(un[blk], eu[blk]) and cn[blk] == ec[blk]
+        assert np.array_equal(mn[blk], em[blk])
+    log(f"config {cid}: union sizes min/mean/max {cn.min()}/{cn.mean():.1f}/{cn.max()}")
+
+    for layer in range(len(wl.kv_cache)):
+        log(f"config {cid}: extend attend layer {layer} (indexer selection)")
+        out = dsa.sparse_mla_extend(bt["q"] if layer == 0 else d.batch("extend", layer)["q"],
+                                    d.kv_cache[layer], d.page_table, d.seq_lens, bt["cu"], units,
+                                    counts, member, QB, wl.sm_scale)
+        torch.cuda.synchronize()
+        got = to_np(out)
+        ref = _oracle_rows_mla(wl, b, tk, rows, layer=layer)
+        check_attention(got, ref, rows=rows, what=f"config {cid} QB={QB} layer {layer}")
+
+    log(f"config {cid}: extend attend with the locality selection")
+    loc = W.locality_selection(wl.seq_lens, cu, wl.k, 100 + cid)
+    lt = i32(loc, "cuda")
+    u2, c2, m2 = dsa.block_union(lt, d.seq_lens, bt["cu"], wl.PS, wl.MP, QB, u_max)
+    out = dsa.sparse_mla_extend(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"], u2,
+                                c2, m2, QB, wl.sm_scale)
+    torch.cuda.synchronize()
+    ref = _oracle_rows_mla(wl, b, loc, rows)
+    check_attention(to_np(out), ref, rows=rows, what=f"config {cid} QB={QB} locality")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("QB", [64, 256])
+def test_config4_chunked_extend(dsa, QB):
+    _extend_config(dsa, 4, QB, n_random=24, n_blocks=2)
+
+
+@pytest.mark.timeout(900)
+def test_config5_long_indexshare(dsa):
+    _extend_config(dsa, 5, 256, n_random=6, n_blocks=1)
+
+
+def test_config1_tiny_all_paths(dsa):
+    """Tiny workload at its stated sizes: both indexer kernels, both QB."""
+    torch = torch_mod()
+    wl = W.config(1)
+    d = Dev(wl)
+    for bname in ("decode", "extend"):
+        b = wl.batches[bname]
+        bt = d.batch(bname)
+        exp = _oracle_rows_topk(wl, b, list(range(b.T)))
+        for mql in (1, 32):
+            assert np.array_equal(_topk(dsa, d, bt, wl.k, mql).cpu().numpy(), exp)
+    b = wl.batches["extend"]
+    bt = d.batch("extend")
+    tk = _oracle_rows_topk(wl, b, list(range(b.T)))
+    ref = _oracle_rows_mla(wl, b, tk, list(range(b.T)))
+    for QB in wl.QB:
+        u, c, m = dsa.block_union(i32(tk, "cuda"), d.seq_lens, bt["cu"], wl.PS, wl.MP, QB,
+                                  wl.u_max)
+        out = dsa.sparse_mla_extend(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"],
+                                    u, c, m, QB, wl.sm_scale)
+        torch.cuda.synchronize()
+        check_attention(to_np(out), ref, what=f"tiny QB={QB}")
