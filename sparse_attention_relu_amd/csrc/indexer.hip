@@ -279,17 +279,15 @@ __global__ __launch_bounds__(NW * 64) void idx_score_tiles(
 // Exact top-k per row.
 //
 // Every score maps to a 32-bit order key (larger key = larger score, -0.0
-// folded onto +0.0). Radix select finds the boundary: a 12-bit histogram of
-// the key's top bits over the row picks the bin holding the k-th largest
-// key, further 12-bit digits narrow it while the bin is larger than the
-// candidate buffer. A collect pass then compacts, in POSITION order, the
-// keys above the bin into the output list and the bin's keys into the
-// candidate list; the remaining digits are resolved inside LDS, and the
-// candidates above the exact k-th key plus the first ties (lowest
-// positions) are appended, still in position order. One stable descending
-// block radix sort of the k (key, position) pairs then yields score
-// descending, position ascending.
-// grid = T, block = 1024, dynamic LDS = 4096 * 4 + cand_cap * 8 + 1024 * IPT * 8.
+// folded onto +0.0). Radix select narrows down the boundary: 12-bit digits
+// from the top, each a histogram pass over the row, until the keys above the
+// boundary bin plus the bin itself fit the sort capacity (or all 32 bits are
+// fixed). A collect pass then compacts those keys, in POSITION order, into
+// one list; when the bin is a single exact key, only its first ties (lowest
+// positions) are taken. One stable descending block radix sort of the list
+// yields score descending, position ascending among equal scores, and the
+// first k entries are the answer.
+// grid = T, block = 1024, dynamic LDS = select_lds_bytes(k).
 // ---------------------------------------------------------------------------
 constexpr int kSelNT = 1024;
 constexpr int kSelM = 16;  // consecutive positions per thread in a collect chunk
@@ -332,21 +330,32 @@ __device__ __forceinline__ uint32_t row_key(const float* row, int j) {
 }
 
 template <int IPT>
+struct SelectCfg {
+  static constexpr int CAP = kSelNT * IPT;  // sort capacity
+  using Sorter = rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>;
+  static constexpr size_t LIST_BYTES = (size_t)CAP * 8;
+  static constexpr size_t HIST_BYTES = 4096 * 4;
+  static constexpr size_t BYTES =
+      LIST_BYTES + HIST_BYTES > sizeof(typename Sorter::storage_type)
+          ? LIST_BYTES + HIST_BYTES
+          : sizeof(typename Sorter::storage_type);
+};
+
+template <int IPT>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ seq_lens,
-                                                      int S, int cap, int k, int cand_cap,
+                                                      int S, int cap, int k,
                                                       int32_t* __restrict__ topk) {
   constexpr int NT = kSelNT;
-  using Sorter = rocprim::block_radix_sort<uint32_t, NT, IPT, int>;
+  using Cfg = SelectCfg<IPT>;
+  constexpr int CAP = Cfg::CAP;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  uint32_t* hist = lds;                      // 4096
-  uint32_t* cand_key = hist + 4096;          // cand_cap
-  uint32_t* cand_pos = cand_key + cand_cap;  // cand_cap
-  uint32_t* sel_key = cand_pos + cand_cap;   // NT * IPT
-  uint32_t* sel_pos = sel_key + NT * IPT;    // NT * IPT
-  // the sort's scratch reuses the histogram / candidate region once it is dead
-  auto& sort_storage = *reinterpret_cast<typename Sorter::storage_type*>(lds);
+  uint32_t* list_key = lds;                // CAP
+  uint32_t* list_pos = list_key + CAP;     // CAP
+  uint32_t* hist = list_pos + CAP;         // 4096
+  // the sort's scratch reuses the whole region once the list is in registers
+  auto& sort_storage = *reinterpret_cast<typename Cfg::Sorter::storage_type*>(lds);
   __shared__ int s_scan[NT / 64];
   __shared__ int s_dig[2];
 
@@ -362,19 +371,19 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   }
 
   int count;
-  if (n <= k) {
+  if (n <= CAP) {  // everything fits the sort: no selection needed
     for (int j = tid; j < n; j += NT) {
-      sel_key[j] = row_key(row, j);
-      sel_pos[j] = (uint32_t)j;
+      list_key[j] = row_key(row, j);
+      list_pos[j] = (uint32_t)j;
     }
     count = n;
   } else {
-    // ---- global digits until the boundary bin fits the candidate buffer
+    // ---- global digits until (above + boundary bin) fits, or the key is exact
     uint32_t prefix = 0;
     int pbits = 0;
     int need = k;
     int nbin = n;
-    while (pbits == 0 || (nbin > cand_cap && pbits < 32)) {
+    while (pbits == 0 || ((k - need) + nbin > CAP && pbits < 32)) {
       const int w = min(12, 32 - pbits);
       const int nb = 1 << w;
       for (int i = tid; i < nb; i += NT) hist[i] = 0;
@@ -405,9 +414,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       nbin = (int)hist[d];
       __syncthreads();
     }
-    // ---- collect in position order: above -> output list, boundary bin ->
-    // candidates (or, when all 32 bits are fixed, its first `need` ties)
-    const bool exact = pbits >= 32;
+    const bool exact = pbits >= 32;  // the bin is one key: take its first `need` ties
+    const int above = k - need;
+    // ---- collect in position order: above -> [0, above), bin -> [above, ...)
     int nabove = 0, nbnd = 0;
     for (int c0 = 0; c0 < n; c0 += NT * kSelM) {
       const int j0 = c0 + tid * kSelM;
@@ -444,21 +453,16 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
         if (j >= n) break;
         const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
         if (v > prefix) {
-          if (ia < NT * IPT) {
-            sel_key[ia] = keys[e];
-            sel_pos[ia] = (uint32_t)j;
+          if (ia < CAP) {
+            list_key[ia] = keys[e];
+            list_pos[ia] = (uint32_t)j;
           }
           ++ia;
         } else if (v == prefix) {
-          if (exact) {  // ties of the k-th key: the first `need` in position order
-            const int dst = (k - need) + ib;
-            if (ib < need && dst < NT * IPT) {
-              sel_key[dst] = keys[e];
-              sel_pos[dst] = (uint32_t)j;
-            }
-          } else if (ib < cand_cap) {
-            cand_key[ib] = keys[e];
-            cand_pos[ib] = (uint32_t)j;
+          const int dst = above + ib;
+          if ((!exact || ib < need) && dst < CAP) {
+            list_key[dst] = keys[e];
+            list_pos[dst] = (uint32_t)j;
           }
           ++ib;
         }
@@ -466,56 +470,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       nabove += total & 0xffff;
       nbnd += total >> 16;
     }
-    __syncthreads();
-    if (!exact) {
-      // ---- resolve the remaining digits among the candidates (LDS)
-      const int C = min(nbnd, cand_cap);
-      uint32_t cpre = prefix;
-      int cbits = pbits;
-      int cneed = need;
-      while (cbits < 32) {
-        const int w = min(12, 32 - cbits);
-        const int nb = 1 << w;
-        for (int i = tid; i < nb; i += NT) hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < C; i += NT) {
-          const uint32_t key = cand_key[i];
-          if ((key >> (32 - cbits)) == cpre)
-            atomicAdd(&hist[(key >> (32 - cbits - w)) & (uint32_t)(nb - 1)], 1u);
-        }
-        __syncthreads();
-        find_digit(hist, nb, cneed, s_scan, s_dig);
-        cneed -= s_dig[1];
-        cpre = (cpre << w) | (uint32_t)s_dig[0];
-        cbits += w;
-        __syncthreads();
-      }
-      // candidates above the k-th key, then its first `cneed` ties, in order
-      const uint32_t kth = cpre;
-      const int base = k - need;
-      int ngt = 0, ntie = 0;
-      for (int c0 = 0; c0 < C; c0 += NT) {
-        const int i = c0 + tid;
-        const uint32_t key = i < C ? cand_key[i] : 0u;
-        const int gt = (i < C) && key > kth;
-        const int tie = (i < C) && key == kth;
-        int total;
-        const int packed = gt | (tie << 16);
-        const int excl = block_inclusive_scan<NT>(packed, s_scan, &total) - packed;
-        const int gt_before = ngt + (excl & 0xffff);
-        const int tie_before = ntie + (excl >> 16);
-        if (gt || (tie && tie_before < cneed)) {
-          const int dst = base + gt_before + min(tie_before, cneed);
-          if (dst < NT * IPT) {
-            sel_key[dst] = key;
-            sel_pos[dst] = cand_pos[i];
-          }
-        }
-        ngt += total & 0xffff;
-        ntie += total >> 16;
-      }
-    }
-    count = k;
+    count = exact ? k : min(above + nbnd, CAP);
   }
   __syncthreads();
   uint32_t keys[IPT];
@@ -523,11 +478,11 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int idx = tid * IPT + i;
-    keys[i] = idx < count ? sel_key[idx] : 0u;
-    vals[i] = idx < count ? (int)sel_pos[idx] : -1;
+    keys[i] = idx < count ? list_key[idx] : 0u;
+    vals[i] = idx < count ? (int)list_pos[idx] : -1;
   }
   __syncthreads();
-  Sorter().sort_desc(keys, vals, sort_storage);
+  typename Cfg::Sorter().sort_desc(keys, vals, sort_storage);
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int idx = tid * IPT + i;
@@ -578,18 +533,21 @@ hipError_t indexer_score(const IndexerArgs& a, hipStream_t st) {
   }
 }
 
-static int select_ipt(int k) { return k <= 1024 ? 1 : (k <= 2048 ? 2 : 4); }
+// sort capacity 2k (at least 2048): room for the keys above the boundary bin
+// plus the bin itself in the common case
+static int select_ipt(int k) { return k <= 1024 ? 2 : (k <= 2048 ? 4 : 8); }
 
 size_t topk_select_lds_bytes(int k) {
-  return (size_t)4096 * 4 + (size_t)kTopkCandCap * 8 + (size_t)kSelNT * select_ipt(k) * 8;
+  switch (select_ipt(k)) {
+    case 2: return SelectCfg<2>::BYTES;
+    case 4: return SelectCfg<4>::BYTES;
+    default: return SelectCfg<8>::BYTES;
+  }
 }
 
 template <int IPT>
 static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
-  static_assert(sizeof(typename rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>::storage_type)
-                    <= (4096 + 2 * kTopkCandCap) * 4,
-                "sort scratch must fit the histogram and candidate region");
-  const size_t lds = topk_select_lds_bytes(a.k);
+  const size_t lds = SelectCfg<IPT>::BYTES;
   // raise the dynamic-LDS limit once per device
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
@@ -604,15 +562,15 @@ static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
   }
   ProfScope prof("topk_select", st);
   hipLaunchKernelGGL((topk_select<IPT>), dim3(a.T), dim3(kSelNT), lds, st, a.scores, a.ld, a.cu,
-                     a.seq_lens, a.S, a.MP * a.PS, a.k, kTopkCandCap, a.topk);
+                     a.seq_lens, a.S, a.MP * a.PS, a.k, a.topk);
   return hipGetLastError();
 }
 
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
   switch (select_ipt(a.k)) {
-    case 1: return launch_select<1>(a, st);
     case 2: return launch_select<2>(a, st);
-    default: return launch_select<4>(a, st);
+    case 4: return launch_select<4>(a, st);
+    default: return launch_select<8>(a, st);
   }
 }
 

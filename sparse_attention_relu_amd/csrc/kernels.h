@@ -7,7 +7,6 @@
 
 namespace dsa {
 
-constexpr int kTopkCandCap = 4096;              // boundary-bin candidates kept in LDS
 constexpr size_t kUnionTileBytes = 64 * 1024;   // LDS membership tile per workgroup
 
 struct IndexerArgs {

@@ -367,17 +367,24 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
 constexpr int XW = 4;                          // waves per workgroup (2 pairs)
 constexpr int XROWS = 64;                      // rows per workgroup
 constexpr int PROWS = 64;                      // rows per staged page (PS <= 64)
-constexpr int CHUNKS = DK / 8;                 // 16-byte chunks per latent row
-constexpr int ROWB = DK * 2;                   // bytes per staged row
-constexpr int PAGE_BYTES = PROWS * ROWB;       // 73728
-constexpr int GLL_N = PROWS * CHUNKS / 64 / XW;  // direct loads per wave per page (18)
+constexpr int NOPE_B = 1024;                   // staged bytes per row, columns 0..511
+constexpr int ROPE_B = 128;                    // staged bytes per row, columns 512..575
+constexpr int ROPE_OFF = PROWS * NOPE_B;       // rope region after the 64 nope rows
+constexpr int PAGE_BYTES = PROWS * (NOPE_B + ROPE_B);  // 73728
+constexpr int GLL_N = PAGE_BYTES / 1024 / XW;  // direct loads per wave per page (18)
 constexpr float kLazyMax = 8.0f;
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row, int c) { return c < 64 ? (c ^ (row & 15)) : c; }
+// Swizzles of 16-byte chunks. Nope row r keeps chunk c (0..63) at slot
+// c ^ nope_x(r), nope_x(r) = 2 (r & 7) + ((r >> 3) & 1): any 16 consecutive
+// rows read at one chunk hit 16 distinct bank groups (S^T reads), and the 4
+// consecutive rows x 2 adjacent chunks of one transposed read hit 8 (V^T
+// reads). Rope row r keeps chunk c (0..7) at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int nope_x(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -410,26 +417,36 @@ __device__ __forceinline__ PageMeta page_meta(const int32_t* __restrict__ units,
   return pm;
 }
 
-// issue this wave's GLL_N direct loads of one page into an LDS buffer
+// Issue this wave's GLL_N direct loads of one page into an LDS buffer. Load
+// I of the page (I = GLL_N * wave + n) fills LDS bytes [1024 I, 1024 I + 1024),
+// 16 bytes per lane: loads 0..63 are the nope rows (one row each), loads
+// 64..71 the rope rows (8 rows each). Rows beyond the page or at positions
+// >= kv_len read the page's row 0 instead.
 __device__ __forceinline__ void stage_page(unsigned char* buf, const uint16_t* __restrict__ kv,
                                            int row_stride, const PageMeta& pm, int PS,
                                            int wave, int) {
-  // lane id from a volatile instruction: keeps the per-lane address math
-  // next to its use instead of 18 hoisted values held across the page loop
+  // lane id from a volatile instruction keeps this cheap arithmetic at its use
   int l;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  const uint16_t* pg = kv + (size_t)pm.page * PS * row_stride;
+  const int valid_rows = min(PS, pm.kvp - pm.lp * PS);  // rows [0, valid_rows) are live
 #pragma unroll
   for (int n = 0; n < GLL_N; ++n) {
-    const int pos = (GLL_N * wave + n) * 64 + l;
-    const int r = pos / CHUNKS, cs = pos % CHUNKS;
-    const int c = swz(r, cs);  // the chunk stored at LDS slot cs of row r
-    const int use = (r < PS && pm.lp * PS + r < pm.kvp) ? r : 0;
-    const uint16_t* src = kv + ((size_t)pm.page * PS + use) * row_stride + 8 * c;
-    // 16 bytes per lane to LDS base + 16 * lane. Issued as inline assembly so
-    // that the compiler does not make every later LDS read wait for these
-    // loads; their completion is awaited explicitly (wait_vmcnt).
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(lds_void*)(buf + (GLL_N * wave + n) * 1024));
+    const int I = GLL_N * wave + n;  // wave-uniform
+    int r, c;
+    if (I < PROWS) {
+      r = I;
+      c = l ^ nope_x(r);
+    } else {
+      r = ((I - PROWS) << 3) + (l >> 3);
+      c = 64 + ((l & 7) ^ rope_x(r));
+    }
+    const int use = r < valid_rows ? r : 0;
+    const uint16_t* src = pg + (size_t)use * row_stride + 8 * c;
+    // issued as inline assembly so that the compiler does not make every
+    // later LDS read wait for these loads; completion is awaited explicitly
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(buf + I * 1024));
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(src), "s"(dst)
@@ -457,6 +474,8 @@ struct ExtArgs {
 
 struct ExtLane {
   int wave, l, pr, role, g, m, qloc;
+  int soff[12];    // S^T reads: byte offsets of this lane's 36 chunks (see ext_offsets)
+  int toff[2][4];  // V^T transposed reads: per-lane parts of the byte offsets
   RowInfo ri;
   bf16x8 qb[DK / 16];
   f32x16 o[8];
@@ -496,13 +515,19 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, int slot,
   f32x16 sacc = {};
   float mx = -INFINITY;
   if (pair_any) {
-    // ---- S^T tile: keys 32 role + m (A from LDS), rows m (B = resident q)
-    const int krow = 32 * role + m;
-    const unsigned char* krp = cur + krow * ROWB;
+    // ---- S^T tile: keys 32 role + m (A from LDS), rows m (B = resident q);
+    // step i reads chunk 2 i + g of key row 32 role + m
+    auto s_off = [&](int i) { return i < 32 ? X.soff[i & 7] + 256 * (i >> 3) : X.soff[8 + (i - 32)]; };
+    // operands are read two steps ahead of the MFMA that consumes them
+    bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(0)));
+    bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(1)));
 #pragma unroll
     for (int i = 0; i < DK / 16; ++i) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(krp + swz(krow, 2 * i + g) * 16));
-      sacc = mfma32(a, X.qb[i], sacc);
+      bf16x8 a2 = a1;
+      if (i + 2 < DK / 16) a2 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(i + 2)));
+      sacc = mfma32(a0, X.qb[i], sacc);
+      a0 = a1;
+      a1 = a2;
     }
     // accumulator r of this lane holds key 8 (r / 4) + 4 g + (r % 4) of the half
 #pragma unroll
@@ -545,36 +570,65 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, int slot,
 #pragma unroll
         for (int r = 0; r < 16; ++r) X.o[d][r] *= alpha;
     }
-    // ---- O^T += V^T P^T: four 16-key steps, value columns 256 role + 32 d + ...
-    const int G = l >> 4, jq = l & 15, kq = jq >> 2, qq = jq & 3;
-    const int c0 = 2 * (G & 1) + (qq >> 1);
-    const int boff = 8 * (qq & 1);
+    // ---- O^T += V^T P^T: four 16-key steps (own key half first, its P^T
+    // fragments are in registers), value columns 256 role + 32 d + ...
+    auto vfrag = [&](int kh, int st, int d) {
+      const int dc = (32 * kh + 16 * st) * NOPE_B + 512 * role + 256 * (d >> 2);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[0][d & 3]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[1][d & 3]));
+      bf16x8 a;
+      __builtin_memcpy(&a, &lo, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+      return a;
+    };
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kh = kk ? (role ^ 1) : role;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 other = pf[((pr * 2 + kh) * 2 + st) * 64 + l];
-        const bf16x8 pbk = (kh == role) ? pb[st] : other;
-        const int key0 = 32 * kh + 16 * st + 4 * g + kq;  // row this lane supplies, read 0
-        const int key1 = key0 + 8;                          // read 1
-        // chunk(d) = 32 role + 4 d + c0 (c0 < 4): the swizzle splits into a
-        // per-lane low part and (4 d) ^ (key & 12)
-        const int x0 = key0 & 15, x1 = key1 & 15;
-        const unsigned char* b0 = cur + key0 * ROWB + ((c0 ^ (x0 & 3)) << 4) + boff;
-        const unsigned char* b1 = cur + key1 * ROWB + ((c0 ^ (x1 & 3)) << 4) + boff;
-        const int hi0 = x0 & 12, hi1 = x1 & 12;
+        const bf16x8 pbk = kk ? pf[((pr * 2 + kh) * 2 + st) * 64 + l] : pb[st];
+        bf16x8 v0 = vfrag(kh, st, 0);
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-          const int cb = 32 * role + 4 * d;
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b0 + ((cb ^ hi0) << 4)));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(b1 + ((cb ^ hi1) << 4)));
-          bf16x8 a;
-          __builtin_memcpy(&a, &lo, 8);
-          __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
-          X.o[d] = mfma32(a, pbk, X.o[d]);
+          bf16x8 v1 = v0;
+          if (d + 1 < 8) v1 = vfrag(kh, st, d + 1);
+          X.o[d] = mfma32(v0, pbk, X.o[d]);
+          v0 = v1;
         }
       }
     }
+  }
+}
+
+// Per-lane LDS byte offsets, fixed for the whole kernel.
+// S^T reads: lane (m, g) of wave `role` reads key row kr = 32 role + m,
+// chunk 2 i + g. For i < 32 the slot is (2 i + g) ^ nope_x(kr) = 16 (i >> 3)
+// + ((2 (i & 7)) ^ y), y = g ^ nope_x(kr), so 8 per-lane values plus a
+// constant; for i >= 32 the rope chunk 2 (i - 32) + g of row kr.
+// V^T reads: the lane supplies row key0 = 32 kh + 16 st + 4 g + kq (read 0)
+// or key0 + 8 (read 1), 16-byte chunk 32 role + 4 d + c0 and byte boff, with
+// kq = (l & 15) >> 2, c0 = 2 ((l >> 4) & 1) + ((l & 3) >> 1), boff =
+// 8 (l & 1). Its slot is 32 role + 4 (d ^ z) + (c0 ^ w_e) with z = 2 g +
+// (kq >> 1), w_e = 2 (kq & 1) + e, so 4 per-lane values per read plus the
+// constants 1024 (32 kh + 16 st), 512 role and 256 (d >> 2).
+__device__ __forceinline__ void ext_offsets(ExtLane& X) {
+  const int kr = 32 * X.role + X.m;
+  const int y = X.g ^ nope_x(kr);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) X.soff[j] = kr * NOPE_B + 16 * ((2 * j) ^ y);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) X.soff[8 + j] = ROPE_OFF + kr * ROPE_B + 16 * ((2 * j + X.g) ^ rope_x(kr));
+  const int l = X.l;
+  const int kq = (l & 15) >> 2, qq = l & 3;
+  const int c0 = 2 * ((l >> 4) & 1) + (qq >> 1);
+  const int boff = 8 * (qq & 1);
+  const int z = 2 * X.g + (kq >> 1);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int key = 4 * X.g + kq + 8 * e;
+    const int w = c0 ^ (2 * (kq & 1) + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) X.toff[e][j] = key * NOPE_B + 64 * (j ^ z) + 16 * w + boff;
   }
 }
 
@@ -611,6 +665,7 @@ void mla_extend_qblock(
   const int row = tile * XROWS + X.pr * 32 + X.m;
   const bool row_live = row < QB * H;
   X.qloc = row_live ? row / H : 0;
+  ext_offsets(X);
   const int h = row_live ? row % H : 0;
   const int t = b * QB + X.qloc;
   X.ri.seq = -1;
@@ -653,9 +708,10 @@ void mla_extend_qblock(
     const PageMeta pm0 = page_meta(units, pt, seq_lens, b, u_max, 0, S, MP, cap, num_pages);
     stage_page(page0, kv, row_stride, pm0, PS, X.wave, X.l);
   }
-  for (int slot = 0; slot < A.u_lim; slot += 2) {
-    ext_step(A, X, slot, page0, page1, pfrag, s_max);
-    if (slot + 1 < A.u_lim) ext_step(A, X, slot + 1, page1, page0, pfrag, s_max);
+  for (int slot = 0; slot < A.u_lim; ++slot) {
+    unsigned char* cur = (slot & 1) ? page1 : page0;
+    unsigned char* nxt = (slot & 1) ? page0 : page1;
+    ext_step(A, X, slot, cur, nxt, pfrag, s_max);
   }
   // ---- row sums over both key halves, then normalise and store this
   // wave's value columns 256 role + 32 d + 8 (r / 4) + 4 g + (r % 4)
