@@ -51,6 +51,47 @@ __device__ __forceinline__ RowInfo row_info(const int32_t* __restrict__ cu,
   return r;
 }
 
+// Same result as row_info for a row index t that is uniform across the wave,
+// called with every lane active: each lane loads one sequence's bounds and
+// length, so the owner is found with one round of loads (per 64 sequences)
+// and a ballot instead of a chain of dependent loads.
+__device__ __forceinline__ RowInfo row_info_wave(const int32_t* __restrict__ cu,
+                                                 const int32_t* __restrict__ seq_lens, int S,
+                                                 int t, int cap) {
+  RowInfo r;
+  r.seq = -1;
+  r.abs_q = -1;
+  r.kv = 0;
+  r.n_valid = 0;
+  const int l = threadIdx.x & (DSA_WAVE - 1);
+  for (int base = 0; base < S; base += DSA_WAVE) {
+    const int i = base + l;
+    const bool in = i < S;
+    const int q0 = in ? cu[i] : 0;
+    const int q1 = in ? cu[i + 1] : 0;
+    const int kv = in ? seq_lens[i] : 0;
+    // sequences of this group that end at or before t (cu is non-decreasing)
+    const uint64_t done = __ballot(in && q1 <= t);
+    const int c = __popcll(done);
+    const int last = (S - base < DSA_WAVE ? S - base : DSA_WAVE);
+    if (c < last) {
+      const int s0 = __shfl(q0, c, DSA_WAVE);
+      const int s1 = __shfl(q1, c, DSA_WAVE);
+      const int sk = __shfl(kv, c, DSA_WAVE);
+      if (t < s0) return r;  // before the owner's first row: no sequence
+      r.seq = base + c;
+      r.abs_q = sk - (s1 - s0) + (t - s0);
+      const int kc = sk < 0 ? 0 : (sk > cap ? cap : sk);
+      r.kv = kc;
+      int n = r.abs_q + 1;
+      n = n < kc ? n : kc;
+      r.n_valid = n < 0 ? 0 : n;
+      return r;
+    }
+  }
+  return r;
+}
+
 __device__ __forceinline__ int clamp_page(int p, int num_pages) {
   return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
 }

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void idx_score_rows(
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int m = l & 31, hf = l >> 5;
-  const RowInfo ri = row_info(cu, seq_lens, S, t, MP * PS);
+  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int j_begin = (blockIdx.x * 4 + wave) * KPW;
   if (ri.seq < 0 || j_begin >= ri.n_valid) return;
   const int j_end = min(j_begin + KPW, ri.n_valid);
@@ -286,11 +286,18 @@ __global__ __launch_bounds__(NW * 64) void idx_score_tiles(
 // one list; when the bin is a single exact key, only its first ties (lowest
 // positions) are taken. One stable descending block radix sort of the list
 // yields score descending, position ascending among equal scores, and the
-// first k entries are the answer.
+// first k entries are the answer. The sort only looks at the bits in which
+// the listed keys differ (the others are common to all of them, so they
+// cannot change any comparison).
+//
+// Each thread owns kSelM consecutive positions of a chunk; the first chunk
+// (the whole row when it has at most kSelNT * kSelM positions) is read once
+// and kept in registers for every pass.
 // grid = T, block = 1024, dynamic LDS = select_lds_bytes(k).
 // ---------------------------------------------------------------------------
 constexpr int kSelNT = 1024;
-constexpr int kSelM = 16;  // consecutive positions per thread in a collect chunk
+constexpr int kSelM = 16;  // consecutive positions per thread in a chunk
+constexpr int kSelChunk = kSelNT * kSelM;
 
 // Bin d of an nb-bin histogram holding the need-th largest key (counting
 // from the top bin down); writes (d, count above d) to out[0..1].
@@ -325,13 +332,29 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int nee
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t row_key(const float* row, int j) {
-  return score_order_bits(row[j]);
+// Keys of positions c0 + kSelM * tid + e (e < kSelM); positions >= n get 0.
+__device__ __forceinline__ void load_keys(const float* row, int n, int c0,
+                                          uint32_t (&keys)[kSelM]) {
+  const int j0 = c0 + threadIdx.x * kSelM;
+  if (j0 + kSelM <= n) {
+#pragma unroll
+    for (int e = 0; e < kSelM; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + j0 + e);
+      keys[e] = score_order_bits(v.x);
+      keys[e + 1] = score_order_bits(v.y);
+      keys[e + 2] = score_order_bits(v.z);
+      keys[e + 3] = score_order_bits(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSelM; ++e) keys[e] = (j0 + e < n) ? score_order_bits(row[j0 + e]) : 0u;
+  }
 }
 
 template <int IPT>
 struct SelectCfg {
   static constexpr int CAP = kSelNT * IPT;  // sort capacity
+  static_assert(CAP <= kSelChunk, "the short-row path keeps the row in one chunk");
   using Sorter = rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>;
   static constexpr size_t LIST_BYTES = (size_t)CAP * 8;
   static constexpr size_t HIST_BYTES = 4096 * 4;
@@ -358,10 +381,11 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   auto& sort_storage = *reinterpret_cast<typename Cfg::Sorter::storage_type*>(lds);
   __shared__ int s_scan[NT / 64];
   __shared__ int s_dig[2];
+  __shared__ uint32_t s_bits[2][NT / 64];
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
-  const RowInfo ri = row_info(cu, seq_lens, S, t, cap);
+  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
   const int n = ri.n_valid;
   const float* row = scores + (size_t)t * ld;
   int32_t* orow = topk + (size_t)t * k;
@@ -370,11 +394,22 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     return;
   }
 
+  uint32_t k0[kSelM];  // chunk 0, resident for all passes
+  load_keys(row, n, 0, k0);
+  uint32_t bor = 0u, band = ~0u;  // OR / AND of the keys this thread lists
+
   int count;
   if (n <= CAP) {  // everything fits the sort: no selection needed
-    for (int j = tid; j < n; j += NT) {
-      list_key[j] = row_key(row, j);
-      list_pos[j] = (uint32_t)j;
+    const int j0 = tid * kSelM;
+#pragma unroll
+    for (int e = 0; e < kSelM; ++e) {
+      const int j = j0 + e;
+      if (j < n) {
+        list_key[j] = k0[e];
+        list_pos[j] = (uint32_t)j;
+        bor |= k0[e];
+        band &= k0[e];
+      }
     }
     count = n;
   } else {
@@ -389,21 +424,21 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       for (int i = tid; i < nb; i += NT) hist[i] = 0;
       __syncthreads();
       const int shift = 32 - pbits - w;
-      const int n4 = n & ~3;
-      for (int j = tid * 4; j < n4; j += NT * 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row + j);
-        const float vs[4] = {v.x, v.y, v.z, v.w};
+      for (int c0 = 0; c0 < n; c0 += kSelChunk) {
+        uint32_t keys[kSelM];
+        if (c0 == 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t key = score_order_bits(vs[e]);
-          if (pbits == 0 || (key >> (32 - pbits)) == prefix)
+          for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
+        } else {
+          load_keys(row, n, c0, keys);
+        }
+        const int j0 = c0 + tid * kSelM;
+#pragma unroll
+        for (int e = 0; e < kSelM; ++e) {
+          const uint32_t key = keys[e];
+          if (j0 + e < n && (pbits == 0 || (key >> (32 - pbits)) == prefix))
             atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
         }
-      }
-      for (int j = n4 + tid; j < n; j += NT) {
-        const uint32_t key = row_key(row, j);
-        if (pbits == 0 || (key >> (32 - pbits)) == prefix)
-          atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
       find_digit(hist, nb, need, s_scan, s_dig);
@@ -418,29 +453,22 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     const int above = k - need;
     // ---- collect in position order: above -> [0, above), bin -> [above, ...)
     int nabove = 0, nbnd = 0;
-    for (int c0 = 0; c0 < n; c0 += NT * kSelM) {
-      const int j0 = c0 + tid * kSelM;
+    for (int c0 = 0; c0 < n; c0 += kSelChunk) {
       uint32_t keys[kSelM];
-      if (j0 + kSelM <= n) {
+      if (c0 == 0) {
 #pragma unroll
-        for (int e = 0; e < kSelM; e += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(row + j0 + e);
-          keys[e] = score_order_bits(v.x);
-          keys[e + 1] = score_order_bits(v.y);
-          keys[e + 2] = score_order_bits(v.z);
-          keys[e + 3] = score_order_bits(v.w);
-        }
+        for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
       } else {
-#pragma unroll
-        for (int e = 0; e < kSelM; ++e) keys[e] = (j0 + e < n) ? row_key(row, j0 + e) : 0u;
+        load_keys(row, n, c0, keys);
       }
+      const int j0 = c0 + tid * kSelM;
       int fa = 0, fb = 0;
 #pragma unroll
       for (int e = 0; e < kSelM; ++e) {
-        if (j0 + e >= n) break;
         const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
-        fa += v > prefix;
-        fb += v == prefix;
+        const bool ok = j0 + e < n;
+        fa += ok && v > prefix;
+        fb += ok && v == prefix;
       }
       int total;
       const int packed = fa | (fb << 16);
@@ -450,19 +478,22 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 #pragma unroll
       for (int e = 0; e < kSelM; ++e) {
         const int j = j0 + e;
-        if (j >= n) break;
         const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
-        if (v > prefix) {
+        if (j < n && v > prefix) {
           if (ia < CAP) {
             list_key[ia] = keys[e];
             list_pos[ia] = (uint32_t)j;
+            bor |= keys[e];
+            band &= keys[e];
           }
           ++ia;
-        } else if (v == prefix) {
+        } else if (j < n && v == prefix) {
           const int dst = above + ib;
           if ((!exact || ib < need) && dst < CAP) {
             list_key[dst] = keys[e];
             list_pos[dst] = (uint32_t)j;
+            bor |= keys[e];
+            band &= keys[e];
           }
           ++ib;
         }
@@ -472,7 +503,27 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     }
     count = exact ? k : min(above + nbnd, CAP);
   }
+  // ---- bits in which the listed keys differ
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    bor |= (uint32_t)__shfl_xor((int)bor, o, DSA_WAVE);
+    band &= (uint32_t)__shfl_xor((int)band, o, DSA_WAVE);
+  }
+  if (lane_id() == 0) {
+    s_bits[0][tid >> 6] = bor;
+    s_bits[1][tid >> 6] = band;
+  }
   __syncthreads();
+  uint32_t diff;
+  {
+    uint32_t o = 0u, a = ~0u;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      o |= s_bits[0][i];
+      a &= s_bits[1][i];
+    }
+    diff = o ^ a;
+  }
   uint32_t keys[IPT];
   int vals[IPT];
 #pragma unroll
@@ -481,8 +532,14 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     keys[i] = idx < count ? list_key[idx] : 0u;
     vals[i] = idx < count ? (int)list_pos[idx] : -1;
   }
-  __syncthreads();
-  typename Cfg::Sorter().sort_desc(keys, vals, sort_storage);
+  if (diff != 0u) {
+    // entries past `count` carry key 0 and sit after every listed key, so a
+    // stable sort keeps them last whatever their bits in the sorted range
+    __syncthreads();
+    const unsigned lo = (unsigned)__builtin_ctz(diff);
+    const unsigned hi = 32u - (unsigned)__builtin_clz(diff);
+    typename Cfg::Sorter().sort_desc(keys, vals, sort_storage, lo, hi);
+  }
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int idx = tid * IPT + i;

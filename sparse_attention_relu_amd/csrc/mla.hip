@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void mla_decode_partial(
   const int c = blockIdx.x, t = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
   const int g = l >> 4, col = l & 15;
-  const RowInfo ri = row_info(cu, seq_lens, S, t, MP * PS);
+  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int i_begin = c * CH, i_end = min(i_begin + CH, k);
   const int nst = ri.seq >= 0 ? (i_end - i_begin + NR - 1) / NR : 0;
   if (tid < NH) {
