@@ -4,13 +4,14 @@
 One step = one DSA layer of the workload:
   decode  (default, 8 sequences x 8192 tokens): exact indexer top-k, then
           sparse absorbed-MLA decode over the selected positions;
+  ragged decode (64 sequences, 4K..32K tokens, reported beside it);
   extend  (4 requests x (12288 + 1024), reported beside it): indexer top-k,
           query-block union tables, query-block sparse MLA.
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts. Prints ONE JSON line (rank 0).
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
-                  [--extend-config 4|5|0] [--no-cpu-baseline]
+                  [--ragged-config 3|0] [--extend-config 4|5|0] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -39,6 +40,8 @@ def parse_args(argv=None):
                    help="decode workload (1 tiny, 2 8x8192, 3 ragged 64x[4K,32K])")
     p.add_argument("--extend-config", type=int, default=4, choices=[0, 1, 4, 5],
                    help="extend workload measured beside it (0 = none)")
+    p.add_argument("--ragged-config", type=int, default=3, choices=[0, 3],
+                   help="ragged decode workload reported beside it (0 = none)")
     p.add_argument("--qb", type=int, default=256, help="query block of the extend layer")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -177,8 +180,13 @@ def bench_decode(dsa, wl, args):
     roof = _roofline_entry(bound, w, kt[dom][1])
     roof.update({"kernel": dom, "traffic": None,
                  "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+    def part(names):
+        return sum(kt[nm][1] * kt[nm][0] for nm in names if nm in kt) / args.steps
+
     return dict(ms=ms, tok_s=T / (ms * 1e-3), kernels=kernels, roofline=roof,
-                selected=n_sel, keys=int(nval.sum()))
+                selected=n_sel, keys=int(nval.sum()),
+                indexer_ms=round(part(("idx_score_rows", "topk_select")), 4),
+                attend_ms=round(part(("mla_decode_partial", "mla_decode_combine")), 4))
 
 
 # ----------------------------------------------------------------------------
@@ -355,6 +363,14 @@ def main(argv=None):
         "roofline": dec["roofline"],
         "kernels": dec["kernels"],
     }
+    if args.ragged_config and args.ragged_config != args.config:
+        wlr = W.config(args.ragged_config)
+        rd = bench_decode(dsa, wlr, args)
+        result["ragged_decode"] = {
+            "workload": wlr.name, "seqs": wlr.S, "tokens": int(wlr.seq_lens.sum()),
+            "tok_s": round(rd["tok_s"], 1), "ms_per_step": round(rd["ms"], 5),
+            "indexer_ms": rd["indexer_ms"], "attend_ms": rd["attend_ms"],
+            "roofline": rd["roofline"], "kernels": rd["kernels"]}
     if args.extend_config:
         wle = W.config(args.extend_config)
         qb = args.qb if args.qb in wle.QB else wle.QB[0]

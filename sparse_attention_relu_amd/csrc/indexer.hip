@@ -53,11 +53,24 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
 
 // ---------------------------------------------------------------------------
 // Streaming per-row scorer (decode and any ragged layout). One wave scores
-// KPW consecutive positions of one row; keys go straight from HBM to the
-// MFMA B operand, the query fragment stays in registers.
-// grid = (ceil(cap / (4 * KPW)), T), block = 256.
+// NSUB blocks of 64 consecutive positions of one row: the page of every key
+// it will touch is looked up first, then the keys of block s + 1 are loaded
+// straight into MFMA B-operand registers while block s is multiplied. The
+// query fragment and head weights stay in registers.
+// grid = (ceil(cap / (4 * 64 * NSUB)), T), block = 256.
 // ---------------------------------------------------------------------------
-template <int D, int HB, int KPW>
+template <int D>
+__device__ __forceinline__ void load_key_frags(const uint16_t* __restrict__ cache, int pg, int PS,
+                                               int j, int hf, bf16x8 (&b)[D / 16]) {
+  constexpr int HALF = D / 2;
+  const bool ok = pg >= 0;
+  const uint16_t* kp = cache + ((size_t)(ok ? pg : 0) * PS + (j % PS)) * D + hf * HALF;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i)
+    b[i] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(kp + 8 * i) : zero_u4());
+}
+
+template <int D, int HB, int NSUB>
 __global__ __launch_bounds__(256) void idx_score_rows(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
@@ -65,6 +78,7 @@ __global__ __launch_bounds__(256) void idx_score_rows(
     int PS, int MP, float* __restrict__ scores, long ld) {
   constexpr int KS = D / 16;
   constexpr int HALF = D / 2;
+  constexpr int KPW = 64 * NSUB;
   const int t = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
@@ -73,7 +87,17 @@ __global__ __launch_bounds__(256) void idx_score_rows(
   const int j_begin = (blockIdx.x * 4 + wave) * KPW;
   if (ri.seq < 0 || j_begin >= ri.n_valid) return;
   const int j_end = min(j_begin + KPW, ri.n_valid);
+  const int32_t* ptrow = pt + (size_t)ri.seq * MP;
 
+  // pages of every key of this wave (-1: past the row's end)
+  int pg[NSUB][2];
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j = j_begin + 64 * sb + 32 * blk + m;
+      pg[sb][blk] = j < j_end ? clamp_page(ptrow[j / PS], num_pages) : -1;
+    }
   bf16x8 a[HB][KS];
   float wv[HB][16];
 #pragma unroll
@@ -82,39 +106,35 @@ __global__ __launch_bounds__(256) void idx_score_rows(
     load_q_frag<D>(q + ((size_t)t * H + (head < H ? head : 0)) * D + hf * HALF, head < H, a[hb]);
     load_head_weights(w + (size_t)t * H, H, hb, hf, wv[hb]);
   }
-  const int32_t* ptrow = pt + (size_t)ri.seq * MP;
   float* srow = scores + (size_t)t * ld;
 
-  // issue every key load of this wave before the first MFMA
-  constexpr int NB = KPW / 32;
-  bf16x8 b[NB][KS];
+  bf16x8 b[2][2][KS];
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    const int j = j_begin + 32 * blk + m;
-    const bool ok = j < j_end;
-    const uint16_t* kp = cache;
-    if (ok) {
-      const int page = clamp_page(ptrow[j / PS], num_pages);
-      kp = cache + ((size_t)page * PS + (j % PS)) * D + hf * HALF;
+  for (int blk = 0; blk < 2; ++blk)
+    load_key_frags<D>(cache, pg[0][blk], PS, j_begin + 32 * blk + m, hf, b[0][blk]);
+#pragma unroll
+  for (int sb = 0; sb < NSUB; ++sb) {
+    if (sb + 1 < NSUB) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        load_key_frags<D>(cache, pg[sb + 1][blk], PS, j_begin + 64 * (sb + 1) + 32 * blk + m, hf,
+                          b[(sb + 1) & 1][blk]);
     }
 #pragma unroll
-    for (int i = 0; i < KS; ++i)
-      b[blk][i] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(kp + 8 * i) : zero_u4());
-  }
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j = j_begin + 64 * sb + 32 * blk + m;
+      float part = 0.0f;
 #pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    const int j = j_begin + 32 * blk + m;
-    float part = 0.0f;
+      for (int hb = 0; hb < HB; ++hb) {
+        f32x16 acc = {};
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int i = 0; i < KS; ++i)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[blk][i], acc, 0, 0, 0);
-      part += relu_weighted_sum(acc, wv[hb]);
+        for (int i = 0; i < KS; ++i)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[sb & 1][blk][i], acc, 0, 0, 0);
+        part += relu_weighted_sum(acc, wv[hb]);
+      }
+      part += shfl_xor_f(part, 32);
+      if (hf == 0 && j < j_end) srow[j] = part;
     }
-    part += shfl_xor_f(part, 32);
-    if (hf == 0 && j < j_end) srow[j] = part;
   }
 }
 
@@ -281,14 +301,16 @@ __global__ __launch_bounds__(NW * 64) void idx_score_tiles(
 // Every score maps to a 32-bit order key (larger key = larger score, -0.0
 // folded onto +0.0). Radix select narrows down the boundary: 12-bit digits
 // from the top, each a histogram pass over the row, until the keys above the
-// boundary bin plus the bin itself fit the sort capacity (or all 32 bits are
+// boundary bin plus the bin itself fit the list capacity (or all 32 bits are
 // fixed). A collect pass then compacts those keys, in POSITION order, into
 // one list; when the bin is a single exact key, only its first ties (lowest
-// positions) are taken. One stable descending block radix sort of the list
-// yields score descending, position ascending among equal scores, and the
-// first k entries are the answer. The sort only looks at the bits in which
-// the listed keys differ (the others are common to all of them, so they
-// cannot change any comparison).
+// positions) are taken. The answer is the list ordered by key descending,
+// list index ascending (for equal keys that is position ascending), cut at k:
+// entries are bucketed by key (at most 4096 buckets over the listed keys'
+// span) and each one's place is its bucket's start plus the number of bucket
+// members ahead of it. Should a bucket hold more than kRankBucketMax entries,
+// a stable block radix sort over the bits in which the keys differ orders the
+// list instead.
 //
 // Each thread owns kSelM consecutive positions of a chunk; the first chunk
 // (the whole row when it has at most kSelNT * kSelM positions) is read once
@@ -353,16 +375,24 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int c0,
 
 template <int IPT>
 struct SelectCfg {
-  static constexpr int CAP = kSelNT * IPT;  // sort capacity
+  static constexpr int CAP = kSelNT * IPT;  // list capacity
   static_assert(CAP <= kSelChunk, "the short-row path keeps the row in one chunk");
   using Sorter = rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>;
+  // LDS: list key/pos [CAP] | hist/cursor [4096] | bucket start [4096 + 64]
+  //      | bucket-ordered key [CAP] | bucket-ordered list index (u16) [CAP]
   static constexpr size_t LIST_BYTES = (size_t)CAP * 8;
-  static constexpr size_t HIST_BYTES = 4096 * 4;
-  static constexpr size_t BYTES =
-      LIST_BYTES + HIST_BYTES > sizeof(typename Sorter::storage_type)
-          ? LIST_BYTES + HIST_BYTES
-          : sizeof(typename Sorter::storage_type);
+  static constexpr size_t HIST_OFF = LIST_BYTES;
+  static constexpr size_t START_OFF = HIST_OFF + 4096 * 4;
+  static constexpr size_t SKEY_OFF = START_OFF + (4096 + 64) * 4;
+  static constexpr size_t SIDX_OFF = SKEY_OFF + (size_t)CAP * 4;
+  static constexpr size_t RANK_BYTES = SIDX_OFF + (size_t)CAP * 2;
+  static constexpr size_t BYTES = RANK_BYTES > sizeof(typename Sorter::storage_type)
+                                      ? RANK_BYTES
+                                      : sizeof(typename Sorter::storage_type);
 };
+
+// Largest bucket the rank phase handles; beyond it the list is sorted.
+constexpr int kRankBucketMax = 256;
 
 template <int IPT>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
@@ -381,7 +411,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   auto& sort_storage = *reinterpret_cast<typename Cfg::Sorter::storage_type*>(lds);
   __shared__ int s_scan[NT / 64];
   __shared__ int s_dig[2];
-  __shared__ uint32_t s_bits[2][NT / 64];
+  __shared__ uint32_t s_bits[4][NT / 64];
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -396,7 +426,8 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 
   uint32_t k0[kSelM];  // chunk 0, resident for all passes
   load_keys(row, n, 0, k0);
-  uint32_t bor = 0u, band = ~0u;  // OR / AND of the keys this thread lists
+  // OR / AND / min / max of the keys this thread lists
+  uint32_t bor = 0u, band = ~0u, kmin = ~0u, kmax = 0u;
 
   int count;
   if (n <= CAP) {  // everything fits the sort: no selection needed
@@ -409,6 +440,8 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
         list_pos[j] = (uint32_t)j;
         bor |= k0[e];
         band &= k0[e];
+        kmin = min(kmin, k0[e]);
+        kmax = max(kmax, k0[e]);
       }
     }
     count = n;
@@ -485,6 +518,8 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
             list_pos[ia] = (uint32_t)j;
             bor |= keys[e];
             band &= keys[e];
+            kmin = min(kmin, keys[e]);
+            kmax = max(kmax, keys[e]);
           }
           ++ia;
         } else if (j < n && v == prefix) {
@@ -494,6 +529,8 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
             list_pos[dst] = (uint32_t)j;
             bor |= keys[e];
             band &= keys[e];
+            kmin = min(kmin, keys[e]);
+            kmax = max(kmax, keys[e]);
           }
           ++ib;
         }
@@ -503,27 +540,110 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     }
     count = exact ? k : min(above + nbnd, CAP);
   }
-  // ---- bits in which the listed keys differ
+  // ---- reduce OR / AND / min / max of the listed keys
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     bor |= (uint32_t)__shfl_xor((int)bor, o, DSA_WAVE);
     band &= (uint32_t)__shfl_xor((int)band, o, DSA_WAVE);
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, DSA_WAVE));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, DSA_WAVE));
   }
   if (lane_id() == 0) {
     s_bits[0][tid >> 6] = bor;
     s_bits[1][tid >> 6] = band;
+    s_bits[2][tid >> 6] = kmin;
+    s_bits[3][tid >> 6] = kmax;
   }
   __syncthreads();
-  uint32_t diff;
   {
-    uint32_t o = 0u, a = ~0u;
+    uint32_t o = 0u, an = ~0u, mn = ~0u, mx = 0u;
 #pragma unroll
     for (int i = 0; i < NT / 64; ++i) {
       o |= s_bits[0][i];
-      a &= s_bits[1][i];
+      an &= s_bits[1][i];
+      mn = min(mn, s_bits[2][i]);
+      mx = max(mx, s_bits[3][i]);
     }
-    diff = o ^ a;
+    bor = o;
+    band = an;
+    kmin = mn;
+    kmax = mx;
   }
+  const uint32_t diff = bor ^ band;  // bits in which the listed keys differ
+  const int nout = min(count, k);
+  for (int i = nout + tid; i < k; i += NT) orow[i] = -1;
+  if (diff == 0u) {  // one key: the list (position order) is the order
+    for (int i = tid; i < nout; i += NT) orow[i] = (int)list_pos[i];
+    return;
+  }
+  // ---- rank: bucket b = (kmax - key) >> sh (ascending b = descending key,
+  // at most 4096 buckets; one key per bucket whenever the keys' span allows).
+  // An entry's place is its bucket's start plus the number of bucket members
+  // that precede it (larger key, or equal key and smaller list index, which
+  // for equal keys is the smaller position).
+  const int lo = __builtin_ctz(diff);
+  const uint32_t span = (kmax - kmin) >> lo;
+  const int nbits = 32 - __builtin_clz(span);
+  const int sh = lo + (nbits > 12 ? nbits - 12 : 0);
+  const int nbk = (int)((kmax - kmin) >> sh) + 1;
+  uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + Cfg::HIST_OFF);
+  int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + Cfg::START_OFF);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + Cfg::SKEY_OFF);
+  uint16_t* sidx = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(lds) + Cfg::SIDX_OFF);
+  for (int b = tid; b < 4096; b += NT) cursor[b] = 0u;
+  __syncthreads();
+  for (int i = tid; i < count; i += NT) atomicAdd(&cursor[(kmax - list_key[i]) >> sh], 1u);
+  __syncthreads();
+  {
+    constexpr int BPT = 4096 / NT;
+    int c[BPT], local = 0, big = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      c[u] = (int)cursor[tid * BPT + u];
+      local += c[u];
+      big = max(big, c[u]);
+    }
+    int total;
+    int run = block_inclusive_scan<NT>(local, s_scan, &total) - local;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      bstart[tid * BPT + u] = run;
+      cursor[tid * BPT + u] = (uint32_t)run;
+      run += c[u];
+    }
+    if (tid == 0) {
+      bstart[4096] = total;
+      s_dig[0] = 0;
+    }
+    __syncthreads();
+    if (big > 0) atomicMax(&s_dig[0], big);
+    __syncthreads();
+  }
+  if (s_dig[0] <= kRankBucketMax) {
+    for (int i = tid; i < count; i += NT) {
+      const uint32_t key = list_key[i];
+      const uint32_t slot = atomicAdd(&cursor[(kmax - key) >> sh], 1u);
+      skey[slot] = key;
+      sidx[slot] = (uint16_t)i;
+    }
+    __syncthreads();
+    for (int sl = tid; sl < count; sl += NT) {
+      const uint32_t key = skey[sl];
+      const int idx = sidx[sl];
+      const int b = (int)((kmax - key) >> sh);
+      const int b0 = bstart[b], b1 = bstart[b + 1];
+      int r = 0;
+      for (int u = b0; u < b1; ++u) {
+        const uint32_t ku = skey[u];
+        r += (ku > key) | ((ku == key) & ((int)sidx[u] < idx));
+      }
+      if (b0 + r < k) orow[b0 + r] = (int)list_pos[idx];
+    }
+    return;
+  }
+  // ---- a crowded bucket: stable descending radix sort of the list over the
+  // bits in which its keys differ (entries past `count` carry key 0 and stay
+  // last: they sort below or, on ties, after every listed key)
   uint32_t keys[IPT];
   int vals[IPT];
 #pragma unroll
@@ -532,34 +652,37 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     keys[i] = idx < count ? list_key[idx] : 0u;
     vals[i] = idx < count ? (int)list_pos[idx] : -1;
   }
-  if (diff != 0u) {
-    // entries past `count` carry key 0 and sit after every listed key, so a
-    // stable sort keeps them last whatever their bits in the sorted range
-    __syncthreads();
-    const unsigned lo = (unsigned)__builtin_ctz(diff);
-    const unsigned hi = 32u - (unsigned)__builtin_clz(diff);
-    typename Cfg::Sorter().sort_desc(keys, vals, sort_storage, lo, hi);
-  }
+  __syncthreads();
+  typename Cfg::Sorter().sort_desc(keys, vals, sort_storage, (unsigned)lo,
+                                   32u - (unsigned)__builtin_clz(diff));
 #pragma unroll
   for (int i = 0; i < IPT; ++i) {
     const int idx = tid * IPT + i;
-    if (idx < k) orow[idx] = vals[i];
+    if (idx < nout) orow[idx] = vals[i];
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-template <int D, int HB>
-static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
-  constexpr int KPW = 64;
+template <int D, int HB, int NSUB>
+static hipError_t launch_rows_n(const IndexerArgs& a, hipStream_t st) {
+  constexpr int KPW = 64 * NSUB;
   const int cap = a.MP * a.PS;
   dim3 grid((cap + 4 * KPW - 1) / (4 * KPW), a.T);
   ProfScope prof("idx_score_rows", st);
-  hipLaunchKernelGGL((idx_score_rows<D, HB, KPW>), grid, dim3(256), 0, st, a.q, a.w, a.cache,
+  hipLaunchKernelGGL((idx_score_rows<D, HB, NSUB>), grid, dim3(256), 0, st, a.q, a.w, a.cache,
                      a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
                      a.ld);
   return hipGetLastError();
+}
+
+// One 64-key block per wave: the key loads of a wave then live in registers
+// only once, which keeps three waves per SIMD in flight (a software
+// pipelined multi-block wave holds fewer waves and moves fewer bytes).
+template <int D, int HB>
+static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
+  return launch_rows_n<D, HB, 1>(a, st);
 }
 
 template <int D, int HB>

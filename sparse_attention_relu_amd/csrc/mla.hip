@@ -7,11 +7,6 @@
 // kernel follows "sparse_mla_prefill_qblock.py", _qblock_kernel: one fetch per
 // union page for all QB * H rows of a block, per-row validity = membership
 // bit AND causal AND kv_len, flash-style online softmax.
-//
-// MFMA v_mfma_f32_16x16x32_bf16 is used for both products. Operand layout
-// (per lane l, group g = l / 16, column c = l % 16):
-//   A: row c, k-values 8 g .. 8 g + 7 of the step;  B: column c, same k;
-//   C: rows 4 g + r (r < 4), column c.
 #include <atomic>
 
 #include "common.h"
@@ -20,315 +15,378 @@
 
 namespace dsa {
 
+// ---------------------------------------------------------------------------
+// Staged latent rows. A staged row keeps its 512 "nope" columns (1024 bytes)
+// and its 64 rope columns (128 bytes) in two separate regions, so that 16-byte
+// chunk c of a row sits at a power-of-two stride and can be XOR-swizzled:
+// nope row r keeps chunk c (0..63) at slot c ^ nope_x(r),
+// nope_x(r) = 2 (r & 7) + ((r >> 3) & 1), so any 16 consecutive rows read at
+// one chunk hit 16 distinct bank groups, and the 4 consecutive rows x 2
+// adjacent chunks of one transposed read hit 8; rope row r keeps chunk c
+// (0..7) at c ^ ((r >> 1) & 7). Rows are filled by direct global->LDS 16-byte
+// loads (global_load_lds_dwordx4): one wave instruction writes 1024
+// consecutive LDS bytes, 16 per lane, so a lane simply fetches the chunk that
+// belongs at its slot.
+// ---------------------------------------------------------------------------
 constexpr int DK = 576;
 constexpr int DV = 512;
-constexpr int NR = 32;        // latent rows staged per step
-constexpr int KRS = DK + 8;   // LDS row stride in bf16 (1168 B) -> conflict-free b128 reads
-constexpr int PRS = NR + 8;   // P row stride in bf16
+constexpr int NOPE_B = 1024;  // staged bytes per row, columns 0..511
+constexpr int ROPE_B = 128;   // staged bytes per row, columns 512..575
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int nope_x(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// B operand of P.V: 8 consecutive staged rows (keys) of one value column.
-__device__ __forceinline__ bf16x8 load_v_col(const uint16_t* kvs, int key0, int col) {
-  uint16_t v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = kvs[(key0 + e) * KRS + col];
-  bf16x8 r;
-  __builtin_memcpy(&r, v, 16);
-  return r;
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Stage NR latent rows into LDS; rows with pos < 0 are zero-filled (never read
-// from HBM, so poisoned or unmapped slots cannot leak in).
-__device__ __forceinline__ void stage_rows(uint16_t* kvs, const uint16_t* __restrict__ kv,
-                                           int row_stride, const int* s_src, int nthreads) {
-  constexpr int CPR = DK / 8;  // 72 chunks of 16 B per row
-  for (int idx = threadIdx.x; idx < NR * CPR; idx += nthreads) {
-    const int row = idx / CPR, c = idx % CPR;
-    const int src = s_src[row];
-    uint4 v = zero_u4();
-    if (src >= 0) v = *reinterpret_cast<const uint4*>(kv + (size_t)src * row_stride + 8 * c);
-    *reinterpret_cast<uint4*>(&kvs[row * KRS + 8 * c]) = v;
-  }
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// [15:14], expcnt[6:4] and lgkmcnt[11:8] left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that publishes this wave's LDS writes but, unlike
+// __syncthreads(), does not wait for outstanding global->LDS loads (their
+// completion is awaited explicitly with wait_vmcnt where it matters).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Lane id from a volatile instruction, which keeps cheap address arithmetic
+// next to its use instead of live across a loop.
+__device__ __forceinline__ int lane_id_volatile() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// One direct 16-byte global->LDS load per lane into the 1024 LDS bytes at
+// `dst` (wave-uniform), lane l writing dst + 16 l. Issued as inline assembly
+// so that the compiler does not make later LDS reads wait for it; completion
+// is awaited explicitly.
+__device__ __forceinline__ void gll16(const void* src, unsigned char* dst) {
+  const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(d)
+               : "memory", "m0");
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid = (nch, T), block = 256. Workgroup (c, t) attends row t over
-// selections [c * CH, (c + 1) * CH) in stages of NR rows, and leaves its
-// partial (row max m, sum l, unnormalised O) per head for the combine
-// kernel. The source slot of every selection is resolved first; each stage's
-// rows are then staged through registers one stage ahead, so the next
-// stage's HBM reads are in flight while the current one is computed.
+// Decode: grid = (nch * HB, T), block = 256. Workgroup (c, hb, t) attends row
+// t over selections [c * CH, (c + 1) * CH) for heads 16 hb .. 16 hb + 15 and
+// leaves its partial (max m, sum l, unnormalised O) per head for the combine
+// kernel. The source slot of every selection is resolved first; stages of
+// kDecRows selected rows then stream through a two-buffer LDS ring (stage
+// s + 2 is loaded while stage s + 1 is in flight and stage s is used).
+// Every wave computes, for all 16 heads and the stage's 32 keys,
+//   S^T = K . Q^T  (v_mfma_f32_16x16x32_bf16: M = keys, N = heads, K = 576)
+// and its own 128 value columns of O^T += V^T . P^T. The S^T accumulator of
+// a lane holds keys 4 g .. 4 g + 3 (+16) of one head, which is exactly its
+// P^T operand (k slot j of lane group g = key 4 g + j, or 16 + 4 g + j - 4),
+// so V^T is read with the same key order through transposed 16-bit LDS
+// reads. Invalid selections load a valid row of the same stage and are
+// masked to probability 0; stages without any valid selection are skipped.
 // ---------------------------------------------------------------------------
-constexpr int kDecMaxCH = 256;
-constexpr int kStageLoads = NR * (DK / 8) / 256;  // 16-byte loads per thread per stage
+constexpr int kDecRows = 32;                                  // selections per stage
+constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
+constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
+constexpr int kDecGll = kDecStage / 1024 / 4;                 // loads per wave per stage (9)
+constexpr int kDecMaxCH = 512;
 
-__device__ __forceinline__ void fetch_stage(uint4 (&r)[kStageLoads], const uint16_t* __restrict__ kv,
-                                            int row_stride, const int* s_src) {
-  constexpr int CPR = DK / 8;
+// This wave's kDecGll direct loads of one stage. Load I (= 9 wave + n) fills
+// LDS bytes [1024 I, 1024 I + 1024): loads 0..31 are nope rows, 32..35 hold
+// the rope parts of rows 8 (I - 32) .. 8 (I - 32) + 7.
+__device__ __forceinline__ void stage_rows(unsigned char* buf, const uint16_t* __restrict__ kv,
+                                           int row_stride, const int* s_src, int wave) {
+  const int l = lane_id_volatile();
 #pragma unroll
-  for (int i = 0; i < kStageLoads; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int row = idx / CPR, c = idx % CPR;
-    const int src = s_src[row];
-    r[i] = src >= 0 ? *reinterpret_cast<const uint4*>(kv + (size_t)src * row_stride + 8 * c)
-                    : zero_u4();
+  for (int n = 0; n < kDecGll; ++n) {
+    const int I = kDecGll * wave + n;  // wave-uniform
+    int r, e;
+    if (I < kDecRows) {
+      r = I;
+      e = 8 * (l ^ nope_x(r));
+    } else {
+      r = ((I - kDecRows) << 3) + (l >> 3);
+      e = 512 + 8 * ((l & 7) ^ rope_x(r));
+    }
+    gll16(kv + (size_t)s_src[r] * row_stride + e, buf + I * 1024);
   }
 }
 
-__device__ __forceinline__ void commit_stage(const uint4 (&r)[kStageLoads], uint16_t* kvs) {
-  constexpr int CPR = DK / 8;
-#pragma unroll
-  for (int i = 0; i < kStageLoads; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int row = idx / CPR, c = idx % CPR;
-    *reinterpret_cast<uint4*>(&kvs[row * KRS + 8 * c]) = r[i];
-  }
-}
-
-template <int HB>
-__global__ __launch_bounds__(256) void mla_decode_partial(
+template <int dummy = 0>
+__global__ __launch_bounds__(256, 2) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int T, int S, int H, int k,
-    int PS, int MP, float sm_scale, int CH, int nch, float* __restrict__ part_o,
+    int PS, int MP, float sm_scale, int CH, int nch, int HB, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  constexpr int NH = HB * 16;
-  __shared__ __attribute__((aligned(16))) uint16_t kvs[NR * KRS];
-  __shared__ __attribute__((aligned(16))) uint16_t ps[NH * PRS];
-  __shared__ float s_logit[NH][NR + 1];
-  __shared__ float s_m[NH], s_l[NH], s_alpha[NH];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][kDecStage];
   __shared__ int s_src[kDecMaxCH];
-  __shared__ int s_any[kDecMaxCH / NR];
+  __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
 
-  const int c = blockIdx.x, t = blockIdx.y;
+  const int c = blockIdx.x / HB, hb = blockIdx.x - c * HB, t = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
   const int g = l >> 4, col = l & 15;
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int i_begin = c * CH, i_end = min(i_begin + CH, k);
-  const int nst = ri.seq >= 0 ? (i_end - i_begin + NR - 1) / NR : 0;
-  if (tid < NH) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.0f;
-  }
-  if (tid < kDecMaxCH / NR) s_any[tid] = 0;
-  __syncthreads();
-  if (ri.seq >= 0) {
+  const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
+
+  // ---- resolve sources and per-stage validity masks (64 entries per wave pass)
+  if (nst > 0) {
     const int32_t* sel = topk + (size_t)t * k;
     const int32_t* ptrow = pt + (size_t)ri.seq * MP;
-    for (int i = tid; i < nst * NR; i += 256) {
-      const int ii = i_begin + i;
+    for (int i0 = wave * 64; i0 < nst * kDecRows; i0 += 256) {
+      const int i = i0 + l, ii = i_begin + i;
       int src = -1;
-      if (ii < i_end) {
+      if (i < nst * kDecRows && ii < i_end) {
         const int j = sel[ii];
         if (j >= 0 && j < ri.kv && j <= ri.abs_q)
           src = clamp_page(ptrow[j / PS], num_pages) * PS + (j % PS);
       }
-      s_src[i] = src;
-      if (src >= 0) s_any[i / NR] = 1;
+      const uint64_t m = __ballot(src >= 0);
+      const uint32_t m32 = (uint32_t)(m >> (l & 32));
+      const int first = m32 ? (l & 32) + __builtin_ctz(m32) : l;
+      const int fsrc = __shfl(src, first, DSA_WAVE);
+      if (i < nst * kDecRows) {
+        s_src[i] = src >= 0 ? src : fsrc;
+        if ((l & 31) == 0) s_mask[i / kDecRows] = m32;
+      }
     }
   }
+  // ---- this lane's query fragments: head 16 hb + col, k values 32 i + 8 g ..
+  const int head = 16 * hb + col;
+  bf16x8 qf[DK / 32];
+  {
+    const uint16_t* qrow = q + ((size_t)t * H + (head < H ? head : 0)) * DK + 8 * g;
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i)
+      qf[i] = as_bf16x8(head < H && nst > 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * i)
+                                            : zero_u4());
+    // complete these loads here: a first use inside the stage loop would make
+    // the compiler wait for every outstanding load there, ring loads included
+#pragma unroll
+    for (int i = 0; i < DK / 32; ++i) asm volatile("" : : "v"(qf[i]));
+  }
   __syncthreads();
-  f32x4 acc[HB][8];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[hb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint4 stage[kStageLoads];
-  if (nst > 0) fetch_stage(stage, kv, row_stride, s_src);
+  // per-lane LDS offsets: S^T reads (key row col of a 16-key tile, chunk 4 i + g)
+  const int nx = nope_x(col), rx = rope_x(col);
+  int soff[4], roff[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) soff[j] = col * NOPE_B + 64 * (j ^ (nx >> 2)) + 16 * ((g ^ nx) & 3);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    roff[j] = kDecRopeOff + col * ROPE_B + 16 * ((4 * j + g) ^ rx);
+  // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
+  const int vr = 4 * g + (col >> 2), vq = col & 3;
+  const int vx = nope_x(vr);
+  const int vbase = vr * NOPE_B + 256 * wave + 16 * ((vq >> 1) ^ (vx & 1)) + 8 * (vq & 1);
+  const int vxor = 32 * (vx >> 1);
+
+  f32x4 o[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (nst > 0 && s_mask[0]) stage_rows(ring[0], kv, row_stride, s_src, wave);
+  if (nst > 1 && s_mask[1]) stage_rows(ring[1], kv, row_stride, s_src + kDecRows, wave);
   for (int st = 0; st < nst; ++st) {
-    const int* src_st = s_src + st * NR;
-    if (!s_any[st]) {  // nothing valid here; keep the pipeline moving
-      if (st + 1 < nst) fetch_stage(stage, kv, row_stride, src_st + NR);
-      continue;
+    const uint32_t mask = s_mask[st];
+    unsigned char* buf = ring[st & 1];
+    if (mask) {
+      if (st + 1 < nst && s_mask[st + 1]) wait_vmcnt<kDecGll>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      // S^T for keys 0..15 and 16..31
+      f32x4 s[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const unsigned char* kb = buf + tt * 16 * NOPE_B;
+        const unsigned char* rb = buf + tt * 16 * ROPE_B;
+#pragma unroll
+        for (int i = 0; i < DK / 32; ++i) {
+          const int off = i < 16 ? soff[i & 3] + 256 * (i >> 2) : roff[i - 16];
+          const bf16x8 a =
+              as_bf16x8(*reinterpret_cast<const uint4*>((i < 16 ? kb : rb) + off));
+          s[tt] = mfma16(a, qf[i], s[tt]);
+        }
+      }
+      // masked online softmax over the head's 32 keys (4 lane groups x 8)
+      float x[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * tt + 4 * g + r;
+          const float v = ((mask >> key) & 1u) ? s[tt][r] * sm_scale : -INFINITY;
+          x[4 * tt + r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __expf(x[e] - m_new);
+        ps += p[e];
+      }
+      ps += shfl_xor_f(ps, 16);
+      ps += shfl_xor_f(ps, 32);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      uint4 pk;
+      pk.x = pack_bf16x2(p[0], p[1]);
+      pk.y = pack_bf16x2(p[2], p[3]);
+      pk.z = pack_bf16x2(p[4], p[5]);
+      pk.w = pack_bf16x2(p[6], p[7]);
+      const bf16x8 pb = as_bf16x8(pk);
+      // O^T (value columns 128 wave + 16 ct + 4 g + r, head col) += V^T P^T
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const int off = vbase + ((32 * ct) ^ vxor);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
+        const v4s hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off + 16 * NOPE_B));
+        bf16x8 va;
+        __builtin_memcpy(&va, &lo, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
+        o[ct] = mfma16(va, pb, o[ct]);
+      }
     }
-    __syncthreads();  // previous stage's readers of kvs / ps are done
-    commit_stage(stage, kvs);
-    if (st + 1 < nst) fetch_stage(stage, kv, row_stride, src_st + NR);
-    __syncthreads();
-    // logits: tiles (hb, nb) of 16 heads x 16 keys, spread over the waves
-    for (int tile = wave; tile < HB * 2; tile += 4) {
-      const int hb = tile >> 1, nb = tile & 1;
-      const int head = hb * 16 + col;
-      const uint16_t* qrow = q + ((size_t)t * H + (head < H ? head : 0)) * DK + 8 * g;
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 6
-      for (int i = 0; i < DK / 32; ++i) {
-        const bf16x8 a = as_bf16x8(head < H ? *reinterpret_cast<const uint4*>(qrow + 32 * i) : zero_u4());
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(&kvs[(16 * nb + col) * KRS + 32 * i + 8 * g]));
-        sacc = mfma16(a, b, sacc);
-      }
-      const bool kvalid = src_st[16 * nb + col] >= 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s_logit[hb * 16 + 4 * g + r][16 * nb + col] = kvalid ? sacc[r] * sm_scale : -INFINITY;
-    }
-    __syncthreads();
-    // online softmax: 16 threads per head, 2 keys each
-    for (int hh = tid >> 4; hh < NH; hh += 16) {
-      const int kk = (tid & 15) * 2;
-      const float x0 = s_logit[hh][kk], x1 = s_logit[hh][kk + 1];
-      float mx = fmaxf(x0, x1);
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-      const float m_old = s_m[hh];
-      const float m_new = fmaxf(m_old, mx);
-      float p0 = 0.f, p1 = 0.f, alpha = 1.f;
-      if (m_new != -INFINITY) {
-        p0 = __expf(x0 - m_new);
-        p1 = __expf(x1 - m_new);
-        alpha = __expf(m_old - m_new);
-      }
-      float sum = p0 + p1;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sum += shfl_xor_f(sum, o);
-      *reinterpret_cast<uint32_t*>(&ps[hh * PRS + kk]) = pack_bf16x2(p0, p1);
-      if ((tid & 15) == 0) {
-        s_alpha[hh] = alpha;
-        s_m[hh] = m_new;
-        s_l[hh] = s_l[hh] * alpha + sum;
-      }
-    }
-    __syncthreads();
-    // P.V for this wave's 128 value columns
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&ps[(hb * 16 + col) * PRS + 8 * g]));
-      float al[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = s_alpha[hb * 16 + 4 * g + r];
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[hb][nb][r] *= al[r];
-        const bf16x8 b = load_v_col(kvs, 8 * g, 128 * wave + 16 * nb + col);
-        acc[hb][nb] = mfma16(a, b, acc[hb][nb]);
-      }
+    if (st + 2 < nst && s_mask[st + 2]) {
+      lds_barrier();  // every wave is done with this buffer
+      stage_rows(buf, kv, row_stride, s_src + (st + 2) * kDecRows, wave);
     }
   }
-  __syncthreads();
+  // ---- partials: m, l per head; O rows as float4 (4 consecutive columns)
   const size_t base = ((size_t)t * nch + c) * H;
-  if (tid < H) {
-    part_ml[(base + tid) * 2 + 0] = s_m[tid];
-    part_ml[(base + tid) * 2 + 1] = s_l[tid];
-  }
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int head = hb * 16 + 4 * g + r;
-      if (head >= H) continue;
-      float* orow = part_o + (base + head) * DV + 128 * wave + col;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) orow[16 * nb] = acc[hb][nb][r];
+  if (head < H) {
+    if (wave == 0 && g == 0) {
+      part_ml[(base + head) * 2 + 0] = m_run;
+      part_ml[(base + head) * 2 + 1] = l_run;
     }
+    float* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      *reinterpret_cast<float4*>(orow + 16 * ct) = make_float4(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+  }
 }
 
-// grid = (T, H), block = 128 (4 value columns per thread): merge the nch
-// partials of (t, h): out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c.
-__global__ __launch_bounds__(128) void mla_decode_combine(const float* __restrict__ part_o,
+// grid = (T, H), block = 256: merge the nch partials of (t, h),
+//   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0.
+// Thread (g, d4) = (tid / 128, tid % 128) folds chunks g, g + 2, ... for value
+// columns 4 d4 .. 4 d4 + 3 with a running maximum, issuing all loads of a batch
+// of kCombU chunks at once; the two halves then merge through LDS.
+constexpr int kCombU = 16;
+
+__device__ __forceinline__ void merge_partial(float& M, float& L, float4& o, float m, float l,
+                                              const float4& v) {
+  if (!(l > 0.f)) return;
+  const float mn = fmaxf(M, m);
+  const float a = M == -INFINITY ? 0.f : __expf(M - mn);
+  const float b = __expf(m - mn);
+  L = L * a + l * b;
+  o.x = o.x * a + v.x * b;
+  o.y = o.y * a + v.y * b;
+  o.z = o.z * a + v.z * b;
+  o.w = o.w * a + v.w * b;
+  M = mn;
+}
+
+__global__ __launch_bounds__(256) void mla_decode_combine(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int H, int nch,
                                                           uint16_t* __restrict__ out) {
-  extern __shared__ float s_w[];  // nch weights
-  __shared__ float s_red[2];
+  __shared__ float4 s_o[128];
+  __shared__ float s_ml[2];
   const int t = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int g = threadIdx.x >> 7, d4 = threadIdx.x & 127;
   const size_t base = (size_t)t * nch * H;
-  // row maximum over chunks with mass
-  float mx = -INFINITY;
-  for (int c = tid; c < nch; c += 128) {
-    const float m = part_ml[(base + (size_t)c * H + h) * 2];
-    const float l = part_ml[(base + (size_t)c * H + h) * 2 + 1];
-    if (l > 0.f) mx = fmaxf(mx, m);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
-  if (lane_id() == 0) s_red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  const float M = fmaxf(s_red[0], s_red[1]);
-  __syncthreads();
-  float L = 0.f;
-  for (int c = tid; c < nch; c += 128) {
-    const float m = part_ml[(base + (size_t)c * H + h) * 2];
-    const float l = part_ml[(base + (size_t)c * H + h) * 2 + 1];
-    const float wgt = l > 0.f ? __expf(m - M) : 0.f;
-    s_w[c] = wgt;
-    L += wgt * l;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) L += shfl_xor_f(L, o);
-  if (lane_id() == 0) s_red[threadIdx.x >> 6] = L;
-  __syncthreads();
-  const float Lt = s_red[0] + s_red[1];
-  const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
-  const int d = 4 * tid;
+  float M = -INFINITY, L = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  // batches of independent loads so the partials stream instead of one
-  // dependent round trip per chunk
-  constexpr int U = 8;
-  for (int c0 = 0; c0 < nch; c0 += U) {
-    float4 v[U];
+  for (int c0 = g; c0 < nch; c0 += 2 * kCombU) {
+    float m[kCombU], l[kCombU];
+    float4 v[kCombU];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u;
-      v[u] = (c < nch && s_w[c] != 0.f)
-                 ? *reinterpret_cast<const float4*>(part_o + (base + (size_t)c * H + h) * DV + d)
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < kCombU; ++u) {
+      const int c = c0 + 2 * u;
+      if (c < nch) {
+        const size_t r = base + (size_t)c * H + h;
+        m[u] = part_ml[r * 2];
+        l[u] = part_ml[r * 2 + 1];
+        v[u] = *reinterpret_cast<const float4*>(part_o + r * DV + 4 * d4);
+      } else {
+        m[u] = -INFINITY;
+        l[u] = 0.f;
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wgt = c0 + u < nch ? s_w[c0 + u] : 0.f;
-      o.x += wgt * v[u].x;
-      o.y += wgt * v[u].y;
-      o.z += wgt * v[u].z;
-      o.w += wgt * v[u].w;
+    for (int u = 0; u < kCombU; ++u) merge_partial(M, L, o, m[u], l[u], v[u]);
+  }
+  if (g == 1) {
+    s_o[d4] = o;
+    if (d4 == 0) {
+      s_ml[0] = M;
+      s_ml[1] = L;
     }
   }
-  uint2 packed;
-  packed.x = pack_bf16x2(o.x * inv, o.y * inv);
-  packed.y = pack_bf16x2(o.z * inv, o.w * inv);
-  *reinterpret_cast<uint2*>(out + ((size_t)t * H + h) * DV + d) = packed;
+  __syncthreads();
+  if (g == 0) {
+    merge_partial(M, L, o, s_ml[0], s_ml[1], s_o[d4]);
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    uint2 packed;
+    packed.x = pack_bf16x2(o.x * inv, o.y * inv);
+    packed.y = pack_bf16x2(o.z * inv, o.w * inv);
+    *reinterpret_cast<uint2*>(out + ((size_t)t * H + h) * DV + 4 * d4) = packed;
+  }
 }
 
 int mla_decode_chunk(int T, int k) {
-  // aim at about one workgroup per compute unit, 32 .. kDecMaxCH selections each
-  const int nsub = (k + NR - 1) / NR;
-  long per = ((long)T * nsub) / 256;
-  if (per < 1) per = 1;
-  if (per > kDecMaxCH / NR) per = kDecMaxCH / NR;
-  return (int)per * NR;
+  // about two workgroups per compute unit, 2 .. 16 stages of kDecRows each:
+  // at least two stages so that a workgroup's loads overlap, at most 16 to
+  // bound the partial (m, l, O) traffic of the combine
+  const long nsub = (k + kDecRows - 1) / kDecRows;
+  long per = ((long)T * nsub + 511) / 512;
+  if (per < 2) per = 2;
+  if (per > kDecMaxCH / kDecRows) per = kDecMaxCH / kDecRows;
+  return (int)per * kDecRows;
 }
 
 hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
   const int CH = mla_decode_chunk(a.T, a.k);
   const int nch = (a.k + CH - 1) / CH;
-  if (a.T == 0) return hipSuccess;
-  dim3 grid(nch, a.T);
   const int HB = (a.H + 15) / 16;
-#define DSA_DEC(hb)                                                                           \
-  hipLaunchKernelGGL((mla_decode_partial<hb>), grid, dim3(256), 0, st, a.q, a.kv, a.row_stride, \
-                     a.num_pages, a.pt, a.seq_lens, a.cu, a.topk, a.T, a.S, a.H, a.k, a.PS,    \
-                     a.MP, a.sm_scale, CH, nch, a.part_o, a.part_ml)
   {
     ProfScope prof("mla_decode_partial", st);
-    switch (HB) {
-      case 1: DSA_DEC(1); break;
-      case 2: DSA_DEC(2); break;
-      case 3: DSA_DEC(3); break;
-      case 4: DSA_DEC(4); break;
-      default: return hipErrorInvalidValue;
-    }
+    hipLaunchKernelGGL((mla_decode_partial<0>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q, a.kv,
+                       a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk, a.T, a.S, a.H,
+                       a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB, a.part_o, a.part_ml);
   }
-#undef DSA_DEC
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ProfScope prof("mla_decode_combine", st);
-  hipLaunchKernelGGL(mla_decode_combine, dim3(a.T, a.H), dim3(128), (size_t)nch * sizeof(float),
-                     st, a.part_o, a.part_ml, a.H, nch, a.out);
+  hipLaunchKernelGGL(mla_decode_combine, dim3(a.T, a.H), dim3(256), 0, st, a.part_o, a.part_ml,
+                     a.H, nch, a.out);
   return hipGetLastError();
 }
 
@@ -367,35 +425,10 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
 constexpr int XW = 4;                          // waves per workgroup (2 pairs)
 constexpr int XROWS = 64;                      // rows per workgroup
 constexpr int PROWS = 64;                      // rows per staged page (PS <= 64)
-constexpr int NOPE_B = 1024;                   // staged bytes per row, columns 0..511
-constexpr int ROPE_B = 128;                    // staged bytes per row, columns 512..575
 constexpr int ROPE_OFF = PROWS * NOPE_B;       // rope region after the 64 nope rows
 constexpr int PAGE_BYTES = PROWS * (NOPE_B + ROPE_B);  // 73728
 constexpr int GLL_N = PAGE_BYTES / 1024 / XW;  // direct loads per wave per page (18)
 constexpr float kLazyMax = 8.0f;
-
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Swizzles of 16-byte chunks. Nope row r keeps chunk c (0..63) at slot
-// c ^ nope_x(r), nope_x(r) = 2 (r & 7) + ((r >> 3) & 1): any 16 consecutive
-// rows read at one chunk hit 16 distinct bank groups (S^T reads), and the 4
-// consecutive rows x 2 adjacent chunks of one transposed read hit 8 (V^T
-// reads). Rope row r keeps chunk c (0..7) at c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int nope_x(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
-// [15:14], expcnt[6:4] and lgkmcnt[11:8] left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 struct PageMeta {
   int page, lp, sp, kvp;
@@ -425,9 +458,7 @@ __device__ __forceinline__ PageMeta page_meta(const int32_t* __restrict__ units,
 __device__ __forceinline__ void stage_page(unsigned char* buf, const uint16_t* __restrict__ kv,
                                            int row_stride, const PageMeta& pm, int PS,
                                            int wave, int) {
-  // lane id from a volatile instruction keeps this cheap arithmetic at its use
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  const int l = lane_id_volatile();
   const uint16_t* pg = kv + (size_t)pm.page * PS * row_stride;
   const int valid_rows = min(PS, pm.kvp - pm.lp * PS);  // rows [0, valid_rows) are live
 #pragma unroll
@@ -442,25 +473,10 @@ __device__ __forceinline__ void stage_page(unsigned char* buf, const uint16_t* _
       c = 64 + ((l & 7) ^ rope_x(r));
     }
     const int use = r < valid_rows ? r : 0;
-    const uint16_t* src = pg + (size_t)use * row_stride + 8 * c;
-    // issued as inline assembly so that the compiler does not make every
-    // later LDS read wait for these loads; completion is awaited explicitly
-    const uint32_t dst =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(buf + I * 1024));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(dst)
-                 : "memory", "m0");
+    gll16(pg + (size_t)use * row_stride + 8 * c, buf + I * 1024);
   }
 }
 
-// Workgroup barrier that publishes this wave's LDS writes but, unlike
-// __syncthreads(), does not wait for outstanding global->LDS loads (their
-// completion is awaited explicitly with wait_vmcnt where it matters).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
 
 struct ExtArgs {
   const uint16_t* __restrict__ kv;

@@ -117,6 +117,28 @@ def test_indexer_ties_and_negative_zero(dsa):
         assert np.array_equal(got, exp)
 
 
+@pytest.mark.parametrize("k", [200, 512])
+def test_indexer_crowded_ties(dsa, k):
+    """About 2980 keys share one vector (exactly equal scores) and 20 keys are
+    its double: the top-k is the 20 large scores, then the tied positions in
+    ascending order. With k=200 the ties fill one bucket of the select's rank
+    phase; with k=512 that bucket overflows and the list is sorted instead."""
+    wl = W.build(name="crowded", seed=11, S=1, kv_lens=[3000], PS=64, MP=48,
+                 batches={"b": [0, 3]}, H_idx=8, D_idx=64, k=k, with_mla=False)
+    b = wl.batches["b"]
+    rows = wl.idx_cache.rows
+    v = b.q_idx[0, 0].copy()
+    rows[:] = v
+    big = np.random.default_rng(3).choice(rows.shape[0], 20, replace=False)
+    rows[big] = W.f32_to_bf16(2.0 * W.bf16_to_f32(v))
+    d = Dev(wl)
+    exp = _oracle_topk(wl, b, k=k)
+    for mql in (1, 3):
+        log(f"indexer crowded ties k={k} mql={mql}")
+        got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, k, mql)
+        assert np.array_equal(got, exp)
+
+
 def test_indexer_zero_rows(dsa):
     """T > 0 with no sequence rows at all (cu_q_lens = 0...): all -1."""
     wl = W.build(name="none", seed=6, S=2, kv_lens=[50, 60], PS=16, MP=4,
