@@ -43,6 +43,10 @@ def parse_args(argv=None):
     p.add_argument("--ragged-config", type=int, default=3, choices=[0, 3],
                    help="ragged decode workload reported beside it (0 = none)")
     p.add_argument("--qb", type=int, default=256, help="query block of the extend layer")
+    p.add_argument("--only", choices=["all", "decode", "ragged", "extend", "copy"],
+                   default="all",
+                   help="run one workload alone (for per-workload profiles); 'copy' times a "
+                        "plain 256 MiB device copy, the scale of the HBM byte counters")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample")
@@ -128,6 +132,49 @@ def _roofline_entry(bound, work, ms, per_step_launches=1):
             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+# Sources whose text decides each kernel's machine code.
+KERNEL_SOURCES = {
+    "idx_score_rows": "indexer.hip", "idx_score_tiles": "indexer.hip",
+    "topk_select": "indexer.hip", "mla_decode_partial": "mla.hip",
+    "mla_decode_combine": "mla.hip", "mla_extend_qblock": "mla.hip",
+    "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
+    "union_member": "union.hip",
+}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the kernel's source file and the shared device header."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "sparse_attention_relu_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "common.h"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary
+    profiles/traffic_<kernel>_<workload>.txt, or None when there is none or
+    the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
@@ -178,8 +225,9 @@ def bench_decode(dsa, wl, args):
     dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
     bound, w = work[dom]
     roof = _roofline_entry(bound, w, kt[dom][1])
-    roof.update({"kernel": dom, "traffic": None,
+    roof.update({"kernel": dom, "traffic": measured_traffic(dom, wl.name),
                  "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+
     def part(names):
         return sum(kt[nm][1] * kt[nm][0] for nm in names if nm in kt) / args.steps
 
@@ -268,8 +316,8 @@ def bench_extend(dsa, wl, args, QB):
     if dom in work:
         bound, w = work[dom]
         roof = _roofline_entry(bound, w, kt[dom][1])
-        roof.update({"kernel": dom, "traffic": None, "work_per_launch": w,
-                     "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+        roof.update({"kernel": dom, "traffic": measured_traffic(dom, wl.name),
+                     "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
         res["roofline"] = roof
     return res
 
@@ -328,6 +376,29 @@ def cpu_baseline(wl, seconds):
 
 
 # ----------------------------------------------------------------------------
+def copy_calibration(mib=256, reps=5):
+    """A plain device copy of known size: under a counter profiler its
+    FETCH_SIZE / WRITE_SIZE per dispatch give the counters' byte scale."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"only": "copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": round(ms, 4), "GB_s": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}),
+          flush=True)
+    return 0
+
+
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
@@ -341,6 +412,22 @@ def main(argv=None):
 
     dsa.load()
     torch.cuda.set_device(0)
+    if args.only == "copy":
+        return copy_calibration()
+    if args.only in ("ragged", "extend"):  # one side workload alone, its own line
+        if args.only == "ragged":
+            wlr = W.config(args.ragged_config or 3)
+            rd = bench_decode(dsa, wlr, args)
+            line = {"workload": wlr.name, "tok_s": round(rd["tok_s"], 1),
+                    "ms_per_step": round(rd["ms"], 5), "roofline": rd["roofline"],
+                    "kernels": rd["kernels"]}
+        else:
+            wle = W.config(args.extend_config or 4)
+            qb = args.qb if args.qb in wle.QB else wle.QB[0]
+            line = bench_extend(dsa, wle, args, qb)
+            line["workload"] = wle.name
+        print(json.dumps({"only": args.only, **line}), flush=True)
+        return 0
     wl = W.config(args.config)
     dec = bench_decode(dsa, wl, args)
     result = {
@@ -363,7 +450,7 @@ def main(argv=None):
         "roofline": dec["roofline"],
         "kernels": dec["kernels"],
     }
-    if args.ragged_config and args.ragged_config != args.config:
+    if args.only == "all" and args.ragged_config and args.ragged_config != args.config:
         wlr = W.config(args.ragged_config)
         rd = bench_decode(dsa, wlr, args)
         result["ragged_decode"] = {
@@ -371,7 +458,7 @@ def main(argv=None):
             "tok_s": round(rd["tok_s"], 1), "ms_per_step": round(rd["ms"], 5),
             "indexer_ms": rd["indexer_ms"], "attend_ms": rd["attend_ms"],
             "roofline": rd["roofline"], "kernels": rd["kernels"]}
-    if args.extend_config:
+    if args.only == "all" and args.extend_config:
         wle = W.config(args.extend_config)
         qb = args.qb if args.qb in wle.QB else wle.QB[0]
         ext = bench_extend(dsa, wle, args, qb)

@@ -314,7 +314,7 @@ CONFIG_NAMES = {
     1: "tiny",
     2: "decode_batch_8x8192",
     3: "ragged_decode_64x4k-32k",
-    4: "chunked_extend_4x(12288+1024)",
+    4: "chunked_extend_4x13312_T4096",
     5: "long_extend_131072_T8192_indexshare4",
 }
 
