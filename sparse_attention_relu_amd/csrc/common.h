@@ -159,9 +159,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 
 __device__ __forceinline__ uint4 zero_u4() { return make_uint4(0u, 0u, 0u, 0u); }
 
-// Pack two floats into one dword of two bf16 (low = a).
+// Pack two floats into one dword of two bf16 (low = a), round to nearest
+// even (one v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------------------

@@ -82,6 +82,21 @@ __device__ __forceinline__ void gll16(const void* src, unsigned char* dst) {
                : "memory", "m0");
 }
 
+// The same load with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset (the "saddr" form), so a lane's address costs one
+// 32-bit VALU operation instead of 64-bit arithmetic. lds_addr is the LDS
+// byte address (wave-uniform).
+__device__ __forceinline__ void gll16_s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
 // ---------------------------------------------------------------------------
 // Decode: grid = (nch * HB, T), block = 256. Workgroup (c, hb, t) attends row
 // t over selections [c * CH, (c + 1) * CH) for heads 16 hb .. 16 hb + 15 and
@@ -411,24 +426,27 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
 // of the page serves both products.
 //
 // Pages are staged with direct global->LDS 16-byte loads into two 72 KB
-// buffers (double buffering: page s+1 is in flight while page s is used).
-// Within a 1152-byte row, 16-byte chunk c < 64 is stored at c ^ (row & 15)
-// so that the rows read by a lane group hit distinct banks. Rows beyond the
-// page or at positions >= kv_len are filled from the page's row 0 (a valid
-// row whenever the page has any); their keys are masked, so they only ever
-// meet probability 0 on finite data.
+// buffers (double buffering: page s+1 is in flight while page s is used),
+// in the swizzled nope/rope layout described at the top of this file. Rows
+// beyond the page or at positions >= kv_len are filled from the page's row 0
+// (a valid row whenever the page has any); their keys are masked, so they
+// only ever meet probability 0 on finite data. The metadata of a union slot
+// (page, sequence, length, membership word) is loaded a step or two before
+// its page is used.
 //
-// The softmax offset is updated lazily: the accumulator is rescaled only
-// when a row's maximum grows by more than kLazyMax (probabilities stay below
-// e^8 before normalisation), which leaves the normalised result unchanged.
+// Logits are kept in log2 units (sm_scale * log2 e folded in, exp2 on the
+// hardware). The softmax offset is updated lazily: the accumulator is
+// rescaled only when a row's maximum grows by more than e^8 (probabilities
+// stay below e^8 before normalisation), which leaves the normalised result
+// unchanged.
 // ---------------------------------------------------------------------------
 constexpr int XW = 4;                          // waves per workgroup (2 pairs)
 constexpr int XROWS = 64;                      // rows per workgroup
 constexpr int PROWS = 64;                      // rows per staged page (PS <= 64)
 constexpr int ROPE_OFF = PROWS * NOPE_B;       // rope region after the 64 nope rows
 constexpr int PAGE_BYTES = PROWS * (NOPE_B + ROPE_B);  // 73728
-constexpr int GLL_N = PAGE_BYTES / 1024 / XW;  // direct loads per wave per page (18)
-constexpr float kLazyMax = 8.0f;
+constexpr float kLazyMax2 = 11.5415603f;  // 8 nats in log2 units: rescale when the
+                                          // offset would grow by more than e^8
 
 struct PageMeta {
   int page, lp, sp, kvp;
@@ -450,33 +468,67 @@ __device__ __forceinline__ PageMeta page_meta(const int32_t* __restrict__ units,
   return pm;
 }
 
-// Issue this wave's GLL_N direct loads of one page into an LDS buffer. Load
-// I of the page (I = GLL_N * wave + n) fills LDS bytes [1024 I, 1024 I + 1024),
-// 16 bytes per lane: loads 0..63 are the nope rows (one row each), loads
-// 64..71 the rope rows (8 rows each). Rows beyond the page or at positions
-// >= kv_len read the page's row 0 instead.
-__device__ __forceinline__ void stage_page(unsigned char* buf, const uint16_t* __restrict__ kv,
-                                           int row_stride, const PageMeta& pm, int PS,
-                                           int wave, int) {
-  const int l = lane_id_volatile();
-  const uint16_t* pg = kv + (size_t)pm.page * PS * row_stride;
-  const int valid_rows = min(PS, pm.kvp - pm.lp * PS);  // rows [0, valid_rows) are live
-#pragma unroll
-  for (int n = 0; n < GLL_N; ++n) {
-    const int I = GLL_N * wave + n;  // wave-uniform
-    int r, c;
-    if (I < PROWS) {
-      r = I;
-      c = l ^ nope_x(r);
-    } else {
-      r = ((I - PROWS) << 3) + (l >> 3);
-      c = 64 + ((l & 7) ^ rope_x(r));
-    }
-    const int use = r < valid_rows ? r : 0;
-    gll16(pg + (size_t)use * row_stride + 8 * c, buf + I * 1024);
-  }
+// Metadata of a union slot as loaded (clamped key, its page-table entry and
+// its sequence length), fetched a step ahead of its use.
+struct SlotRaw {
+  int key, ptv, slv;
+};
+
+__device__ __forceinline__ int clamp_key(int key, int S, int MP) {
+  return key < 0 ? 0 : (key >= S * MP ? S * MP - 1 : key);
 }
 
+__device__ __forceinline__ SlotRaw slot_raw(const int32_t* __restrict__ pt,
+                                            const int32_t* __restrict__ seq_lens, int key,
+                                            int MP) {
+  SlotRaw r;
+  r.key = key;
+  r.ptv = pt[key];
+  r.slv = seq_lens[key / MP];
+  return r;
+}
+
+__device__ __forceinline__ PageMeta meta_from_raw(const SlotRaw& r, int MP, int cap,
+                                                  int num_pages) {
+  PageMeta pm;
+  pm.sp = r.key / MP;
+  pm.lp = r.key % MP;
+  pm.kvp = r.slv < 0 ? 0 : (r.slv > cap ? cap : r.slv);
+  pm.page = clamp_page(r.ptv, num_pages);
+  return pm;
+}
+
+// Issue this wave's direct loads of one page into the LDS buffer at byte
+// address `buf`: wave w fills nope rows r = 4 n + w (n < 16, LDS bytes
+// [1024 r, 1024 r + 1024)) and the rope parts of rows 8 G .. 8 G + 7 for
+// G = w and w + 4 (bytes ROPE_OFF + 1024 G ..). Rows beyond the page or at
+// positions >= kv_len read the page's row 0 instead. `wave` must be
+// wave-uniform to the compiler (readfirstlane), so that the row choices and
+// the row base addresses are scalar.
+__device__ __forceinline__ void stage_page(uint32_t buf, const uint16_t* __restrict__ kv,
+                                           int row_stride, const PageMeta& pm, int PS,
+                                           int wave) {
+  const int l = lane_id_volatile();
+  const unsigned char* pg =
+      reinterpret_cast<const unsigned char*>(kv + (size_t)pm.page * PS * row_stride);
+  const int valid_rows = min(PS, pm.kvp - pm.lp * PS);  // rows [0, valid_rows) are live
+  const size_t rs = (size_t)row_stride * 2;
+  const uint32_t l16 = 16u * (uint32_t)l;
+#pragma unroll
+  for (int n = 0; n < PROWS / XW; ++n) {
+    const int r = XW * n + wave;
+    const int use = r < valid_rows ? r : 0;
+    gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), pg + use * rs, buf + r * NOPE_B);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int G = wave + XW * j;
+    const int r = 8 * G + (l >> 3);
+    const int use = r < valid_rows ? r : 0;
+    gll16_s((uint32_t)(use * (int)rs) + 2 * DV + 16u * (uint32_t)((l & 7) ^ rope_x(r)), pg,
+            buf + ROPE_OFF + G * 1024);
+  }
+}
 
 struct ExtArgs {
   const uint16_t* __restrict__ kv;
@@ -485,7 +537,7 @@ struct ExtArgs {
   const int32_t* __restrict__ units;
   const uint64_t* __restrict__ member;
   int row_stride, num_pages, S, PS, MP, QB, u_max, cap, b, u_lim;
-  float sm_scale;
+  float scale2;  // sm_scale * log2(e)
 };
 
 struct ExtLane {
@@ -498,33 +550,49 @@ struct ExtLane {
   float m_used, l_part;
 };
 
+// Metadata carried from step to step: slot s's page (complete), slot s + 1's
+// raw entries, slot s + 2's key, and this lane's membership word of slot s.
+struct ExtPipe {
+  PageMeta cur;
+  SlotRaw next;
+  int key2;
+  uint64_t mem;
+};
+
 // One union page: `cur` holds it, `nxt` receives the next one meanwhile.
 // The __restrict__ LDS pointers let the compiler see that reads of `cur`
 // and of the exchange buffers never alias the loads in flight into `nxt`.
-__device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, int slot,
-                                         unsigned char* __restrict__ cur,
-                                         unsigned char* __restrict__ nxt,
+// Every global load issued here is consumed one step later, after that
+// step's wait, so no load latency is exposed inside a step.
+__device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& P, int slot,
+                                         const unsigned char* __restrict__ cur, uint32_t nxt,
                                          bf16x8* __restrict__ pf, float* __restrict__ smax) {
   const int l = X.l, g = X.g, m = X.m, pr = X.pr, role = X.role;
-  const PageMeta pm = page_meta(A.units, A.pt, A.seq_lens, A.b, A.u_max, slot, A.S, A.MP, A.cap,
-                                A.num_pages);
-  // membership word of this lane's query (loaded unconditionally so that the
-  // wait below provably covers it)
-  const uint64_t mem = A.member[((size_t)A.b * A.u_max + slot) * A.QB + X.qloc];
-  const int lim = min(X.ri.abs_q + 1, pm.kvp) - pm.lp * A.PS;
-  uint64_t mk = 0;
-  if (X.ri.seq == pm.sp && lim > 0) mk = lim >= 64 ? mem : (mem & ((1ull << lim) - 1));
-  if (A.PS < 64) mk &= (1ull << A.PS) - 1;
   // this wave's loads of page `slot` (issued one step earlier) and the
-  // metadata above have landed; after the barrier every wave's have, and
-  // nobody reads `nxt` (the previous page) any more
+  // metadata loads of the previous step have landed; after the barrier
+  // every wave's have, and nobody reads `nxt` (the previous page) any more
   wait_vmcnt<0>();
   lds_barrier();
-  if (slot + 1 < A.u_lim) {
-    const PageMeta pn = page_meta(A.units, A.pt, A.seq_lens, A.b, A.u_max, slot + 1, A.S, A.MP,
-                                  A.cap, A.num_pages);
-    stage_page(nxt, A.kv, A.row_stride, pn, A.PS, X.wave, X.l);  // overlaps this page's math
-  }
+  const PageMeta pm = P.cur;
+  const PageMeta pn = meta_from_raw(P.next, A.MP, A.cap, A.num_pages);
+  if (slot + 1 < A.u_lim)
+    stage_page(nxt, A.kv, A.row_stride, pn, A.PS, X.wave);  // overlaps this page's math
+  // metadata for the coming steps
+  uint64_t mem_n = 0;
+  if (slot + 1 < A.u_lim) mem_n = A.member[((size_t)A.b * A.u_max + slot + 1) * A.QB + X.qloc];
+  SlotRaw raw2 = P.next;
+  if (slot + 2 < A.u_lim) raw2 = slot_raw(A.pt, A.seq_lens, clamp_key(P.key2, A.S, A.MP), A.MP);
+  int key3 = 0;
+  if (slot + 3 < A.u_lim) key3 = A.units[(size_t)A.b * A.u_max + slot + 3];
+
+  const int lim = min(X.ri.abs_q + 1, pm.kvp) - pm.lp * A.PS;
+  uint64_t mk = 0;
+  if (X.ri.seq == pm.sp && lim > 0) mk = lim >= 64 ? P.mem : (P.mem & ((1ull << lim) - 1));
+  if (A.PS < 64) mk &= (1ull << A.PS) - 1;
+  P.cur = pn;
+  P.next = raw2;
+  P.key2 = key3;
+  P.mem = mem_n;
   // both waves of a pair hold the same rows, hence the same masks
   const bool pair_any = __ballot(mk != 0ull) != 0;
   const uint32_t hm = (uint32_t)(mk >> (32 * role));
@@ -545,11 +613,13 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, int slot,
       a0 = a1;
       a1 = a2;
     }
-    // accumulator r of this lane holds key 8 (r / 4) + 4 g + (r % 4) of the half
+    // accumulator r of this lane holds key 8 (r / 4) + 4 g + (r % 4) of the
+    // half; logits are kept in log2 units (sm_scale * log2 e folded in)
+    const uint32_t hg = hm >> (4 * g);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = 8 * (r >> 2) + 4 * g + (r & 3);
-      sacc[r] = ((hm >> key) & 1u) ? sacc[r] * A.sm_scale : -INFINITY;
+      const int key = 8 * (r >> 2) + (r & 3);
+      sacc[r] = ((hg >> key) & 1u) ? sacc[r] * A.scale2 : -INFINITY;
       mx = fmaxf(mx, sacc[r]);
     }
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
@@ -560,16 +630,19 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, int slot,
   float alpha = 1.f;
   if (pair_any) {
     mx = fmaxf(mx, smax[(pr * 2 + (role ^ 1)) * 32 + m]);
-    if (mx > X.m_used + kLazyMax) {
-      alpha = __expf(X.m_used - mx);  // 0 while nothing was accumulated
+    if (mx > X.m_used + kLazyMax2) {
+      alpha = __builtin_amdgcn_exp2f(X.m_used - mx);  // 0 while nothing was accumulated
       X.m_used = mx;
       X.l_part *= alpha;
     }
+    // exp2(-inf) is 0, so masked keys need no test; a row with no offset
+    // yet has only masked keys and subtracts 0 instead of -inf
+    const float off = X.m_used == -INFINITY ? 0.f : X.m_used;
     uint32_t w[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = sacc[r] != -INFINITY ? __expf(sacc[r] - X.m_used) : 0.f;
-      const float p1 = sacc[r + 1] != -INFINITY ? __expf(sacc[r + 1] - X.m_used) : 0.f;
+      const float p0 = __builtin_amdgcn_exp2f(sacc[r] - off);
+      const float p1 = __builtin_amdgcn_exp2f(sacc[r + 1] - off);
       X.l_part += p0 + p1;
       w[r >> 1] = pack_bf16x2(p0, p1);
     }
@@ -671,7 +744,7 @@ void mla_extend_qblock(
   if (b >= nqb) return;
 
   ExtLane X;
-  X.wave = threadIdx.x >> 6;
+  X.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   X.l = lane_id();
   X.pr = X.wave >> 1;
   X.role = X.wave & 1;
@@ -718,16 +791,23 @@ void mla_extend_qblock(
   A.cap = cap;
   A.b = b;
   A.u_lim = min(counts[b], u_max);
-  A.sm_scale = sm_scale;
+  A.scale2 = sm_scale * 1.44269504088896341f;
 
+  ExtPipe P;
+  P.mem = 0;
+  P.key2 = 0;
   if (A.u_lim > 0) {
-    const PageMeta pm0 = page_meta(units, pt, seq_lens, b, u_max, 0, S, MP, cap, num_pages);
-    stage_page(page0, kv, row_stride, pm0, PS, X.wave, X.l);
+    P.cur = page_meta(units, pt, seq_lens, b, u_max, 0, S, MP, cap, num_pages);
+    stage_page(lds_addr_of(page0), kv, row_stride, P.cur, PS, X.wave);
+    P.mem = member[(size_t)b * u_max * QB + X.qloc];
+    const int k1 = A.u_lim > 1 ? clamp_key(units[(size_t)b * u_max + 1], S, MP) : 0;
+    P.next = slot_raw(pt, seq_lens, k1, MP);
+    if (A.u_lim > 2) P.key2 = units[(size_t)b * u_max + 2];
   }
+  const uint32_t lds0 = lds_addr_of(page0), lds1 = lds_addr_of(page1);
   for (int slot = 0; slot < A.u_lim; ++slot) {
-    unsigned char* cur = (slot & 1) ? page1 : page0;
-    unsigned char* nxt = (slot & 1) ? page0 : page1;
-    ext_step(A, X, slot, cur, nxt, pfrag, s_max);
+    const unsigned char* cur = (slot & 1) ? page1 : page0;
+    ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max);
   }
   // ---- row sums over both key halves, then normalise and store this
   // wave's value columns 256 role + 32 d + 8 (r / 4) + 4 g + (r % 4)
