@@ -411,19 +411,22 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
 //
 // Workgroup = 2 wave pairs x 32 rows (row = q * H + h of the block). Both
 // waves of a pair keep the same 32 rows' query fragments in registers; per
-// page, wave `role` of the pair computes
-//   S^T = K . Q^T for keys 32 role .. 32 role + 31 of the page
-//     (v_mfma_f32_32x32x16_bf16: M = keys, N = rows, K = 576), and
-//   O^T += V^T . P^T for value columns 256 role .. 256 role + 255 over all
-//     64 keys (M = value columns, N = rows, K = keys).
-// The two halves meet through LDS twice per page: the row maxima (for the
-// shared online-softmax offset) and the bf16 P^T fragments. A lane's S^T
-// accumulator holds 16 keys of ONE row, which is exactly the layout of the
-// P^T operand, so P is packed in place. V^T fragments come from the
-// row-major page through transposed 16-bit LDS reads (ds_read_b64_tr_b16:
-// inside each 16-lane group, lanes 4k..4k+3 supply 16 consecutive values of
-// row k and lane j receives column j of the 4 rows), so one row-major copy
-// of the page serves both products.
+// page, wave `role` of pair `pr` computes
+//   S^T = K . Q^T for keys 32 role .. 32 role + 31 of the page and the rows
+//     of its pair (v_mfma_f32_32x32x16_bf16: M = keys, N = rows, K = 576);
+// the pair meets through LDS for the row maxima (the shared online-softmax
+// offset). A lane's S^T accumulator holds 16 keys of ONE row, which is
+// exactly the layout of a P^T operand, so P is packed in place and published
+// in LDS. Then wave w computes
+//   O^T += V^T . P^T for value columns 128 w .. 128 w + 127 and all 64 rows
+//     (M = value columns, N = rows of one pair, K = keys),
+// so each V^T fragment serves the MFMAs of both pairs. V^T fragments come
+// from the row-major page through transposed 16-bit LDS reads
+// (ds_read_b64_tr_b16: inside each 16-lane group, lanes 4k..4k+3 supply 16
+// consecutive values of row k and lane j receives column j of the 4 rows),
+// so one row-major copy of the page serves both products; transposed reads
+// move about half the bytes per clock of 16-byte reads, which is why each
+// one is used twice.
 //
 // Pages are staged with direct global->LDS 16-byte loads into two 72 KB
 // buffers (double buffering: page s+1 is in flight while page s is used),
@@ -530,6 +533,45 @@ __device__ __forceinline__ void stage_page(uint32_t buf, const uint16_t* __restr
   }
 }
 
+// The same page staging split into its 18 loads (n < 16: nope row 4 n + wave;
+// n = 16, 17: rope groups wave, wave + 4), so that they can be spread over
+// the matrix work of a step instead of stalling the wave in one burst.
+struct StageCtx {
+  const unsigned char* pg;
+  size_t rs;
+  uint32_t buf;
+  int valid_rows, wave;
+};
+
+__device__ __forceinline__ StageCtx stage_ctx(uint32_t buf, const uint16_t* __restrict__ kv,
+                                              int row_stride, const PageMeta& pm, int PS,
+                                              int wave) {
+  StageCtx c;
+  c.pg = reinterpret_cast<const unsigned char*>(kv + (size_t)pm.page * PS * row_stride);
+  c.rs = (size_t)row_stride * 2;
+  c.buf = buf;
+  c.valid_rows = min(PS, pm.kvp - pm.lp * PS);
+  c.wave = wave;
+  return c;
+}
+
+__device__ __forceinline__ void stage_one(const StageCtx& c, int n, int l) {
+  if (n < PROWS / XW) {
+    const int r = XW * n + c.wave;
+    const int use = r < c.valid_rows ? r : 0;
+    gll16_s((16u * (uint32_t)l) ^ (16u * (uint32_t)nope_x(r)), c.pg + use * c.rs,
+            c.buf + r * NOPE_B);
+  } else {
+    const int G = c.wave + XW * (n - PROWS / XW);
+    const int r = 8 * G + (l >> 3);
+    const int use = r < c.valid_rows ? r : 0;
+    gll16_s((uint32_t)(use * (int)c.rs) + 2 * DV + 16u * (uint32_t)((l & 7) ^ rope_x(r)), c.pg,
+            c.buf + ROPE_OFF + G * 1024);
+  }
+}
+
+constexpr int kStageLoads = PROWS / XW + 2;  // 18 direct loads per wave per page
+
 struct ExtArgs {
   const uint16_t* __restrict__ kv;
   const int32_t* __restrict__ pt;
@@ -546,7 +588,7 @@ struct ExtLane {
   int toff[2][4];  // V^T transposed reads: per-lane parts of the byte offsets
   RowInfo ri;
   bf16x8 qb[DK / 16];
-  f32x16 o[8];
+  f32x16 o[2][4];  // O^T tiles: [pair of the rows][32-column block of this wave]
   float m_used, l_part;
 };
 
@@ -566,7 +608,8 @@ struct ExtPipe {
 // step's wait, so no load latency is exposed inside a step.
 __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& P, int slot,
                                          const unsigned char* __restrict__ cur, uint32_t nxt,
-                                         bf16x8* __restrict__ pf, float* __restrict__ smax) {
+                                         bf16x8* __restrict__ pf, float* __restrict__ smax,
+                                         float* __restrict__ salpha) {
   const int l = X.l, g = X.g, m = X.m, pr = X.pr, role = X.role;
   // this wave's loads of page `slot` (issued one step earlier) and the
   // metadata loads of the previous step have landed; after the barrier
@@ -575,8 +618,9 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
   lds_barrier();
   const PageMeta pm = P.cur;
   const PageMeta pn = meta_from_raw(P.next, A.MP, A.cap, A.num_pages);
-  if (slot + 1 < A.u_lim)
-    stage_page(nxt, A.kv, A.row_stride, pn, A.PS, X.wave);  // overlaps this page's math
+  // the next page's loads are issued during this page's S^T products
+  const bool do_stage = slot + 1 < A.u_lim;
+  const StageCtx sc = stage_ctx(nxt, A.kv, A.row_stride, pn, A.PS, X.wave);
   // metadata for the coming steps
   uint64_t mem_n = 0;
   if (slot + 1 < A.u_lim) mem_n = A.member[((size_t)A.b * A.u_max + slot + 1) * A.QB + X.qloc];
@@ -595,6 +639,10 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
   P.mem = mem_n;
   // both waves of a pair hold the same rows, hence the same masks
   const bool pair_any = __ballot(mk != 0ull) != 0;
+  if (!pair_any && do_stage) {
+#pragma unroll
+    for (int n = 0; n < kStageLoads; ++n) stage_one(sc, n, l);
+  }
   const uint32_t hm = (uint32_t)(mk >> (32 * role));
   f32x16 sacc = {};
   float mx = -INFINITY;
@@ -610,6 +658,7 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
       bf16x8 a2 = a1;
       if (i + 2 < DK / 16) a2 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(i + 2)));
       sacc = mfma32(a0, X.qb[i], sacc);
+      if (do_stage && (i & 1) == 0 && (i >> 1) < kStageLoads) stage_one(sc, i >> 1, l);
       a0 = a1;
       a1 = a2;
     }
@@ -648,43 +697,51 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
     }
     __builtin_memcpy(&pb[0], w, 16);
     __builtin_memcpy(&pb[1], w + 4, 16);
-    pf[((pr * 2 + role) * 2 + 0) * 64 + l] = pb[0];
-    pf[((pr * 2 + role) * 2 + 1) * 64 + l] = pb[1];
+  } else {
+    pb[0] = as_bf16x8(zero_u4());
+    pb[1] = pb[0];
   }
+  pf[((pr * 2 + role) * 2 + 0) * 64 + l] = pb[0];
+  pf[((pr * 2 + role) * 2 + 1) * 64 + l] = pb[1];
+  if (role == 0 && g == 0) salpha[pr * 32 + m] = alpha;
   lds_barrier();
-  if (pair_any) {
-    if (__ballot(alpha != 1.f && alpha != 0.f) != 0) {
+  // ---- rescale the O rows whose softmax offset moved (rows m of both pairs)
+  const float a0 = salpha[m], a1 = salpha[32 + m];
+  if (__ballot(a0 != 1.f || a1 != 1.f) != 0) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) X.o[d][r] *= alpha;
-    }
-    // ---- O^T += V^T P^T: four 16-key steps (own key half first, its P^T
-    // fragments are in registers), value columns 256 role + 32 d + ...
-    auto vfrag = [&](int kh, int st, int d) {
-      const int dc = (32 * kh + 16 * st) * NOPE_B + 512 * role + 256 * (d >> 2);
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[0][d & 3]));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[1][d & 3]));
-      bf16x8 a;
-      __builtin_memcpy(&a, &lo, 8);
-      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
-      return a;
-    };
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kh = kk ? (role ^ 1) : role;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 pbk = kk ? pf[((pr * 2 + kh) * 2 + st) * 64 + l] : pb[st];
-        bf16x8 v0 = vfrag(kh, st, 0);
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          bf16x8 v1 = v0;
-          if (d + 1 < 8) v1 = vfrag(kh, st, d + 1);
-          X.o[d] = mfma32(v0, pbk, X.o[d]);
-          v0 = v1;
-        }
+      for (int r = 0; r < 16; ++r) {
+        X.o[0][ct][r] *= a0;
+        X.o[1][ct][r] *= a1;
       }
+  }
+  // ---- O^T += V^T P^T for value columns 128 wave + 32 ct + ..., all 64 rows:
+  // four 16-key steps; each V^T fragment feeds the MFMAs of both pairs
+  auto vfrag = [&](int j) {  // j = (kh * 2 + st) * 4 + ct
+    const int kh = j >> 3, st = (j >> 2) & 1, ct = j & 3;
+    const int dc = (32 * kh + 16 * st) * NOPE_B + 256 * X.wave;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[0][ct]));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + dc + X.toff[1][ct]));
+    bf16x8 a;
+    __builtin_memcpy(&a, &lo, 8);
+    __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+    return a;
+  };
+  bf16x8 v0 = vfrag(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kh = ks >> 1, st = ks & 1;
+    const bf16x8 b0 = pf[((0 * 2 + kh) * 2 + st) * 64 + l];
+    const bf16x8 b1 = pf[((1 * 2 + kh) * 2 + st) * 64 + l];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int j = ks * 4 + ct;
+      bf16x8 v1 = v0;
+      if (j + 1 < 16) v1 = vfrag(j + 1);
+      X.o[0][ct] = mfma32(v0, b0, X.o[0][ct]);
+      X.o[1][ct] = mfma32(v0, b1, X.o[1][ct]);
+      v0 = v1;
     }
   }
 }
@@ -695,11 +752,12 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
 // + ((2 (i & 7)) ^ y), y = g ^ nope_x(kr), so 8 per-lane values plus a
 // constant; for i >= 32 the rope chunk 2 (i - 32) + g of row kr.
 // V^T reads: the lane supplies row key0 = 32 kh + 16 st + 4 g + kq (read 0)
-// or key0 + 8 (read 1), 16-byte chunk 32 role + 4 d + c0 and byte boff, with
-// kq = (l & 15) >> 2, c0 = 2 ((l >> 4) & 1) + ((l & 3) >> 1), boff =
-// 8 (l & 1). Its slot is 32 role + 4 (d ^ z) + (c0 ^ w_e) with z = 2 g +
-// (kq >> 1), w_e = 2 (kq & 1) + e, so 4 per-lane values per read plus the
-// constants 1024 (32 kh + 16 st), 512 role and 256 (d >> 2).
+// or key0 + 8 (read 1), 16-byte chunk 16 wave + 4 ct + c0 and byte boff,
+// with kq = (l & 15) >> 2, c0 = 2 ((l >> 4) & 1) + ((l & 3) >> 1), boff =
+// 8 (l & 1). Since nope_x(key) = 8 g + 2 kq + e, its slot is 16 wave +
+// 4 (ct ^ z) + (c0 ^ w_e) with z = 2 g + (kq >> 1), w_e = 2 (kq & 1) + e,
+// so 4 per-lane values per read plus the constants 1024 (32 kh + 16 st) and
+// 256 wave.
 __device__ __forceinline__ void ext_offsets(ExtLane& X) {
   const int kr = 32 * X.role + X.m;
   const int y = X.g ^ nope_x(kr);
@@ -734,6 +792,7 @@ void mla_extend_qblock(
   __shared__ __attribute__((aligned(1024))) unsigned char page1[PAGE_BYTES];
   __shared__ bf16x8 pfrag[2 * 2 * 2 * 64];  // P^T fragments [pair][role][step][lane]
   __shared__ float s_max[2 * 2 * 32];        // row maxima [pair][role][row]
+  __shared__ float s_alpha[2 * 32];          // offset rescale factors [pair][row]
   const int TPB = (QB * H + XROWS - 1) / XROWS;
   const int nqb = (T + QB - 1) / QB;
   // the TPB workgroups of a block get ids of one residue mod 8, i.e. one XCD
@@ -771,7 +830,9 @@ void mla_extend_qblock(
     }
   }
 #pragma unroll
-  for (int d = 0; d < 8; ++d) X.o[d] = f32x16{};
+  for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) X.o[p2][ct] = f32x16{};
   X.m_used = -INFINITY;
   X.l_part = 0.f;
 
@@ -807,26 +868,32 @@ void mla_extend_qblock(
   const uint32_t lds0 = lds_addr_of(page0), lds1 = lds_addr_of(page1);
   for (int slot = 0; slot < A.u_lim; ++slot) {
     const unsigned char* cur = (slot & 1) ? page1 : page0;
-    ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max);
+    ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max, s_alpha);
   }
   // ---- row sums over both key halves, then normalise and store this
-  // wave's value columns 256 role + 32 d + 8 (r / 4) + 4 g + (r % 4)
+  // wave's value columns 128 wave + 32 ct + 8 (r / 4) + 4 g + (r % 4) of the
+  // rows m of both pairs
   const float lw = X.l_part + shfl_xor_f(X.l_part, 32);
   __syncthreads();
   if (X.g == 0) s_max[(X.pr * 2 + X.role) * 32 + X.m] = lw;
   __syncthreads();
-  const float lt = s_max[(X.pr * 2 + 0) * 32 + X.m] + s_max[(X.pr * 2 + 1) * 32 + X.m];
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (out_live) {
-    uint16_t* orow = out + ((size_t)t * H + h) * DV + 256 * X.role;
 #pragma unroll
-    for (int d = 0; d < 8; ++d)
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const float lt = s_max[(p2 * 2 + 0) * 32 + X.m] + s_max[(p2 * 2 + 1) * 32 + X.m];
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int row2 = tile * XROWS + p2 * 32 + X.m;
+    if (row2 >= QB * H) continue;
+    const int t2 = b * QB + row2 / H, h2 = row2 % H;
+    if (t2 >= T) continue;
+    uint16_t* orow = out + ((size_t)t2 * H + h2) * DV + 128 * X.wave;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         uint2 v;
-        v.x = pack_bf16x2(X.o[d][4 * r4] * inv, X.o[d][4 * r4 + 1] * inv);
-        v.y = pack_bf16x2(X.o[d][4 * r4 + 2] * inv, X.o[d][4 * r4 + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * d + 8 * r4 + 4 * X.g) = v;
+        v.x = pack_bf16x2(X.o[p2][ct][4 * r4] * inv, X.o[p2][ct][4 * r4 + 1] * inv);
+        v.y = pack_bf16x2(X.o[p2][ct][4 * r4 + 2] * inv, X.o[p2][ct][4 * r4 + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * ct + 8 * r4 + 4 * X.g) = v;
       }
   }
 }
