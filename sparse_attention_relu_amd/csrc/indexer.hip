@@ -44,10 +44,18 @@ __device__ __forceinline__ void load_head_weights(const float* __restrict__ wrow
   }
 }
 
+// relu(x) as one integer max on the bit pattern: every negative float
+// (-0.0 included) is a negative integer, so max(bits, 0) gives +0.0 for
+// them and leaves non-negative values unchanged (fmaxf would first quiet a
+// possible signalling NaN, a second instruction per element).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const float (&wv)[16]) {
   float part = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) part += wv[r] * fmaxf(acc[r], 0.0f);
+  for (int r = 0; r < 16; ++r) part = fmaf(wv[r], relu_bits(acc[r]), part);
   return part;
 }
 
