@@ -394,13 +394,142 @@ struct SelectCfg {
   static constexpr size_t SKEY_OFF = START_OFF + (4096 + 64) * 4;
   static constexpr size_t SIDX_OFF = SKEY_OFF + (size_t)CAP * 4;
   static constexpr size_t RANK_BYTES = SIDX_OFF + (size_t)CAP * 2;
-  static constexpr size_t BYTES = RANK_BYTES > sizeof(typename Sorter::storage_type)
-                                      ? RANK_BYTES
-                                      : sizeof(typename Sorter::storage_type);
+  static constexpr size_t SEL_BYTES = RANK_BYTES > sizeof(typename Sorter::storage_type)
+                                          ? RANK_BYTES
+                                          : sizeof(typename Sorter::storage_type);
+  // direct rank of a short row (the same LDS, used before the select path):
+  // cursor [4096] | bucket start [4096 + 64] | (key, position) composite
+  // [CAP + 64] for the positions whose bucket starts below k (k <= CAP / 2)
+  static constexpr size_t D_CUR_OFF = 0;
+  static constexpr size_t D_START_OFF = 4096 * 4;
+  static constexpr size_t D_KEY_OFF = D_START_OFF + (4096 + 64) * 4;
+  static constexpr size_t D_POS_OFF = 0;  // unused
+  static constexpr size_t DIRECT_BYTES = D_KEY_OFF + ((size_t)CAP + 64) * 8;
+  static constexpr size_t BYTES = SEL_BYTES > DIRECT_BYTES ? SEL_BYTES : DIRECT_BYTES;
 };
 
 // Largest bucket the rank phase handles; beyond it the list is sorted.
 constexpr int kRankBucketMax = 256;
+// Largest bucket of the direct rank of a short row; beyond it the row takes
+// the radix-select path.
+constexpr int kDirectBucketMax = 64;
+
+__device__ __forceinline__ float order_key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Direct rank of a row of n <= kSelChunk positions whose keys are in registers
+// (thread tid holds positions kSelM * tid + e): scores are bucketed by value,
+// b = (vmax - v) * 4095.5 / (vmax - vmin) (monotone, so equal scores share a
+// bucket and a larger score never lands in a later bucket). Only positions
+// whose bucket starts below k can be in the answer; each one's place is its
+// bucket's start plus the number of bucket members ahead of it (larger key,
+// or equal key and smaller position: one comparison of the composite
+// key << 16 | (0xffff - position)). Returns false, having written nothing,
+// when the spread is degenerate or a bucket holds more than kDirectBucketMax
+// positions.
+template <int NT>
+__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], int n, int k,
+                                            uint32_t* lds, size_t cur_off, size_t start_off,
+                                            size_t key_off, int* s_scan,
+                                            uint32_t (*s_red)[NT / 64], int* s_flag,
+                                            int32_t* __restrict__ orow) {
+  const int tid = threadIdx.x;
+  const int j0 = tid * kSelM;
+  uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < kSelM; ++e)
+    if (j0 + e < n) {
+      kmin = min(kmin, k0[e]);
+      kmax = max(kmax, k0[e]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, DSA_WAVE));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, DSA_WAVE));
+  }
+  if (lane_id() == 0) {
+    s_red[0][tid >> 6] = kmin;
+    s_red[1][tid >> 6] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    kmin = min(kmin, s_red[0][i]);
+    kmax = max(kmax, s_red[1][i]);
+  }
+  const float vmax = order_key_value(kmax), vmin = order_key_value(kmin);
+  const float scale = 4095.5f / (vmax - vmin);
+  if (kmin == kmax || !(scale > 0.f) || !(scale < 3.0e38f)) return false;
+  auto bucket = [&](uint32_t key) {
+    const float b = (vmax - order_key_value(key)) * scale;
+    return min(4095, (int)b);
+  };
+  uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + cur_off);
+  int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + start_off);
+  uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
+  for (int b = tid; b < 4096; b += NT) cursor[b] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kSelM; ++e)
+    if (j0 + e < n) atomicAdd(&cursor[bucket(k0[e])], 1u);
+  __syncthreads();
+  {
+    constexpr int BPT = 4096 / NT;
+    int c[BPT], local = 0, big = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      c[u] = (int)cursor[tid * BPT + u];
+      local += c[u];
+    }
+    int total;
+    int run = block_inclusive_scan<NT>(local, s_scan, &total) - local;
+    if (tid == 0) {
+      s_flag[0] = 0;
+      s_flag[1] = min(n, k);  // end of the positions that are scattered
+    }
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      bstart[tid * BPT + u] = run;
+      cursor[tid * BPT + u] = (uint32_t)run;
+      if (run < k) big = max(big, c[u]);
+      run += c[u];
+    }
+    if (tid == 0) bstart[4096] = total;
+    __syncthreads();
+    if (big > 0) atomicMax(&s_flag[0], big);
+    // the bucket holding place k - 1 ends the scattered range
+    int r2 = run;
+#pragma unroll
+    for (int u = BPT - 1; u >= 0; --u) {
+      r2 -= c[u];
+      if (r2 < k && r2 + c[u] >= k) s_flag[1] = r2 + c[u];
+    }
+    __syncthreads();
+  }
+  if (s_flag[0] > kDirectBucketMax) return false;
+  const int lim = s_flag[1];
+#pragma unroll
+  for (int e = 0; e < kSelM; ++e)
+    if (j0 + e < n) {
+      const int b = bucket(k0[e]);
+      if (bstart[b] < k) {
+        const uint32_t slot = atomicAdd(&cursor[b], 1u);
+        scomp[slot] = ((uint64_t)k0[e] << 16) | (uint64_t)(0xffffu - (uint32_t)(j0 + e));
+      }
+    }
+  __syncthreads();
+  for (int sl = tid; sl < lim; sl += NT) {
+    const uint64_t cm = scomp[sl];
+    const int b = bucket((uint32_t)(cm >> 16));
+    const int b0 = bstart[b], b1 = bstart[b + 1];
+    int r = 0;
+    for (int u = b0; u < b1; ++u) r += scomp[u] > cm;
+    if (b0 + r < k) orow[b0 + r] = (int)(0xffffu - (uint32_t)(cm & 0xffffu));
+  }
+  for (int i = n + tid; i < k; i += NT) orow[i] = -1;
+  return true;
+}
 
 template <int IPT>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
@@ -434,6 +563,11 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 
   uint32_t k0[kSelM];  // chunk 0, resident for all passes
   load_keys(row, n, 0, k0);
+  if (n <= kSelChunk &&
+      topk_direct<NT>(k0, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF, s_scan,
+                      s_bits, s_dig, orow))
+    return;
+  __syncthreads();  // the select path reuses the LDS
   // OR / AND / min / max of the keys this thread lists
   uint32_t bor = 0u, band = ~0u, kmin = ~0u, kmax = 0u;
 
