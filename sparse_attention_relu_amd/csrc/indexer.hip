@@ -418,31 +418,47 @@ __device__ __forceinline__ float order_key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-// Direct rank of a row of n <= kSelChunk positions whose keys are in registers
-// (thread tid holds positions kSelM * tid + e): scores are bucketed by value,
-// b = (vmax - v) * 4095.5 / (vmax - vmin) (monotone, so equal scores share a
-// bucket and a larger score never lands in a later bucket). Only positions
-// whose bucket starts below k can be in the answer; each one's place is its
-// bucket's start plus the number of bucket members ahead of it (larger key,
-// or equal key and smaller position: one comparison of the composite
-// key << 16 | (0xffff - position)). Returns false, having written nothing,
-// when the spread is degenerate or a bucket holds more than kDirectBucketMax
-// positions.
+// Direct rank of a row of n <= kDirectMaxN positions. Thread tid owns
+// positions c0 + kSelM * tid + e of every chunk c0; the first chunk's keys
+// are in registers, later chunks are read again from the row. Scores are
+// bucketed by value, b = (vmax - v) * 4095.5 / (vmax - vmin) (monotone, so
+// equal scores share a bucket and a larger score never lands in a later
+// bucket). Only positions whose bucket starts below k can be in the answer;
+// each one's place is its bucket's start plus the number of bucket members
+// ahead of it (larger key, or equal key and smaller position: one comparison
+// of the composite key << 32 | ~position). Returns false, having written
+// nothing, when the spread is degenerate or a candidate bucket holds more
+// than kDirectBucketMax positions.
+constexpr int kDirectMaxN = 1 << 17;
+
 template <int NT>
-__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], int n, int k,
-                                            uint32_t* lds, size_t cur_off, size_t start_off,
-                                            size_t key_off, int* s_scan,
+__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const float* row, int n,
+                                            int k, uint32_t* lds, size_t cur_off,
+                                            size_t start_off, size_t key_off, int* s_scan,
                                             uint32_t (*s_red)[NT / 64], int* s_flag,
                                             int32_t* __restrict__ orow) {
   const int tid = threadIdx.x;
-  const int j0 = tid * kSelM;
-  uint32_t kmin = ~0u, kmax = 0u;
+  // keys of chunk c0 (the first one from registers)
+  auto chunk_keys = [&](int c0, uint32_t (&keys)[kSelM]) {
+    if (c0 == 0) {
 #pragma unroll
-  for (int e = 0; e < kSelM; ++e)
-    if (j0 + e < n) {
-      kmin = min(kmin, k0[e]);
-      kmax = max(kmax, k0[e]);
+      for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
+    } else {
+      load_keys(row, n, c0, keys);
     }
+  };
+  uint32_t kmin = ~0u, kmax = 0u;
+  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
+    uint32_t keys[kSelM];
+    chunk_keys(c0, keys);
+    const int j0 = c0 + tid * kSelM;
+#pragma unroll
+    for (int e = 0; e < kSelM; ++e)
+      if (j0 + e < n) {
+        kmin = min(kmin, keys[e]);
+        kmax = max(kmax, keys[e]);
+      }
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, DSA_WAVE));
@@ -470,9 +486,14 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], int n, 
   uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
   for (int b = tid; b < 4096; b += NT) cursor[b] = 0u;
   __syncthreads();
+  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
+    uint32_t keys[kSelM];
+    chunk_keys(c0, keys);
+    const int j0 = c0 + tid * kSelM;
 #pragma unroll
-  for (int e = 0; e < kSelM; ++e)
-    if (j0 + e < n) atomicAdd(&cursor[bucket(k0[e])], 1u);
+    for (int e = 0; e < kSelM; ++e)
+      if (j0 + e < n) atomicAdd(&cursor[bucket(keys[e])], 1u);
+  }
   __syncthreads();
   {
     constexpr int BPT = 4096 / NT;
@@ -509,23 +530,28 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], int n, 
   }
   if (s_flag[0] > kDirectBucketMax) return false;
   const int lim = s_flag[1];
+  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
+    uint32_t keys[kSelM];
+    chunk_keys(c0, keys);
+    const int j0 = c0 + tid * kSelM;
 #pragma unroll
-  for (int e = 0; e < kSelM; ++e)
-    if (j0 + e < n) {
-      const int b = bucket(k0[e]);
-      if (bstart[b] < k) {
-        const uint32_t slot = atomicAdd(&cursor[b], 1u);
-        scomp[slot] = ((uint64_t)k0[e] << 16) | (uint64_t)(0xffffu - (uint32_t)(j0 + e));
+    for (int e = 0; e < kSelM; ++e)
+      if (j0 + e < n) {
+        const int b = bucket(keys[e]);
+        if (bstart[b] < k) {
+          const uint32_t slot = atomicAdd(&cursor[b], 1u);
+          scomp[slot] = ((uint64_t)keys[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
+        }
       }
-    }
+  }
   __syncthreads();
   for (int sl = tid; sl < lim; sl += NT) {
     const uint64_t cm = scomp[sl];
-    const int b = bucket((uint32_t)(cm >> 16));
+    const int b = bucket((uint32_t)(cm >> 32));
     const int b0 = bstart[b], b1 = bstart[b + 1];
     int r = 0;
     for (int u = b0; u < b1; ++u) r += scomp[u] > cm;
-    if (b0 + r < k) orow[b0 + r] = (int)(0xffffu - (uint32_t)(cm & 0xffffu));
+    if (b0 + r < k) orow[b0 + r] = (int)(~(uint32_t)cm);
   }
   for (int i = n + tid; i < k; i += NT) orow[i] = -1;
   return true;
@@ -563,9 +589,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 
   uint32_t k0[kSelM];  // chunk 0, resident for all passes
   load_keys(row, n, 0, k0);
-  if (n <= kSelChunk &&
-      topk_direct<NT>(k0, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF, s_scan,
-                      s_bits, s_dig, orow))
+  if (n <= kDirectMaxN &&
+      topk_direct<NT>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
+                      s_scan, s_bits, s_dig, orow))
     return;
   __syncthreads();  // the select path reuses the LDS
   // OR / AND / min / max of the keys this thread lists
