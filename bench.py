@@ -10,7 +10,7 @@ One step = one DSA layer of the workload:
 Inputs are seeded synthetic tensors already resident in HBM when the timed
 region starts. Prints ONE JSON line (rank 0).
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
                   [--ragged-config 3|0] [--extend-config 4|5|0] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -34,8 +34,8 @@ DK, DV = 576, 512
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=2, choices=[1, 2, 3],
                    help="decode workload (1 tiny, 2 8x8192, 3 ragged 64x[4K,32K])")
     p.add_argument("--extend-config", type=int, default=4, choices=[0, 1, 4, 5],

@@ -70,26 +70,25 @@ __device__ __forceinline__ int lane_id_volatile() {
   return l;
 }
 
-// One direct 16-byte global->LDS load per lane into the 1024 LDS bytes at
-// `dst` (wave-uniform), lane l writing dst + 16 l. Issued as inline assembly
-// so that the compiler does not make later LDS reads wait for it; completion
-// is awaited explicitly.
-__device__ __forceinline__ void gll16(const void* src, unsigned char* dst) {
-  const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)dst);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(d)
-               : "memory", "m0");
-}
-
-// The same load with a wave-uniform 64-bit base in SGPRs and a 32-bit
-// per-lane byte offset (the "saddr" form), so a lane's address costs one
-// 32-bit VALU operation instead of 64-bit arithmetic. lds_addr is the LDS
-// byte address (wave-uniform).
+// One direct 16-byte global->LDS load per lane (global_load_lds_dwordx4):
+// lane l writes LDS bytes lds_addr + 16 l .. + 15 (lds_addr wave-uniform).
+// Issued as inline assembly so that the compiler does not make later LDS
+// reads wait for it; completion is awaited explicitly. This form takes a
+// wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset (the
+// "saddr" form), so a lane's address costs one 32-bit VALU operation.
 __device__ __forceinline__ void gll16_s(uint32_t voff, const void* sbase, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// The same load with a full 64-bit per-lane source address and a
+// wave-uniform LDS byte address.
+__device__ __forceinline__ void gll16_a(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
                : "memory", "m0");
 }
 
@@ -101,47 +100,49 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // Decode: grid = (nch * HB, T), block = 256. Workgroup (c, hb, t) attends row
 // t over selections [c * CH, (c + 1) * CH) for heads 16 hb .. 16 hb + 15 and
 // leaves its partial (max m, sum l, unnormalised O) per head for the combine
-// kernel. The source slot of every selection is resolved first; stages of
-// kDecRows selected rows then stream through a two-buffer LDS ring (stage
-// s + 2 is loaded while stage s + 1 is in flight and stage s is used).
-// Every wave computes, for all 16 heads and the stage's 32 keys,
-//   S^T = K . Q^T  (v_mfma_f32_16x16x32_bf16: M = keys, N = heads, K = 576)
-// and its own 128 value columns of O^T += V^T . P^T. The S^T accumulator of
-// a lane holds keys 4 g .. 4 g + 3 (+16) of one head, which is exactly its
-// P^T operand (k slot j of lane group g = key 4 g + j, or 16 + 4 g + j - 4),
-// so V^T is read with the same key order through transposed 16-bit LDS
-// reads. Invalid selections load a valid row of the same stage and are
-// masked to probability 0; stages without any valid selection are skipped.
+// kernel. The source slot of every selection is resolved first; stages of 64
+// selected rows then stream through a two-stage LDS ring (stage s + 1 is in
+// flight while stage s is used), staged like an extend page.
+// Per stage, wave w computes S^T = K . Q^T for keys 16 w .. 16 w + 15 and the
+// 16 heads (v_mfma_f32_16x16x32_bf16: M = keys, N = heads, K = 576); the
+// waves exchange their per-head maxima and bf16 P^T fragments through LDS;
+// then wave w computes O^T += V^T . P^T for value columns 128 w .. 128 w + 127
+// over all 64 keys, two 32-key steps whose k slots of lane group g are keys
+// 4 g .. 4 g + 3 of the first and of the second 16-key tile, the order in
+// which both the S^T accumulators (P^T) and the transposed V^T reads hold
+// them. Logits are kept in log2 units. Invalid selections load a valid row of
+// the same stage and are masked to probability 0; stages without any valid
+// selection load cache row 0 and skip the arithmetic.
 // ---------------------------------------------------------------------------
-constexpr int kDecRows = 32;                                  // selections per stage
-constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
+constexpr int kDecRows = 64;                                  // selections per stage
+constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 73728 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
-constexpr int kDecGll = kDecStage / 1024 / 4;                 // loads per wave per stage (9)
 constexpr int kDecMaxCH = 512;
 
-// This wave's kDecGll direct loads of one stage. Load I (= 9 wave + n) fills
-// LDS bytes [1024 I, 1024 I + 1024): loads 0..31 are nope rows, 32..35 hold
-// the rope parts of rows 8 (I - 32) .. 8 (I - 32) + 7.
-__device__ __forceinline__ void stage_rows(unsigned char* buf, const uint16_t* __restrict__ kv,
+// This wave's 18 direct loads of one stage: nope rows r = 4 n + wave
+// (n < 16) at LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows
+// 8 G .. 8 G + 7 for G = wave, wave + 4 at kDecRopeOff + 1024 G.
+__device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restrict__ kv,
                                            int row_stride, const int* s_src, int wave) {
   const int l = lane_id_volatile();
+  const uint32_t l16 = 16u * (uint32_t)l;
 #pragma unroll
-  for (int n = 0; n < kDecGll; ++n) {
-    const int I = kDecGll * wave + n;  // wave-uniform
-    int r, e;
-    if (I < kDecRows) {
-      r = I;
-      e = 8 * (l ^ nope_x(r));
-    } else {
-      r = ((I - kDecRows) << 3) + (l >> 3);
-      e = 512 + 8 * ((l & 7) ^ rope_x(r));
-    }
-    gll16(kv + (size_t)s_src[r] * row_stride + e, buf + I * 1024);
+  for (int n = 0; n < kDecRows / 4; ++n) {
+    const int r = 4 * n + wave;
+    const int src = __builtin_amdgcn_readfirstlane(s_src[r]);
+    gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), kv + (size_t)src * row_stride, buf + r * NOPE_B);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int G = wave + 4 * j;
+    const int r = 8 * G + (l >> 3);
+    gll16_a(kv + (size_t)s_src[r] * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
+            buf + kDecRopeOff + G * 1024);
   }
 }
 
 template <int dummy = 0>
-__global__ __launch_bounds__(256, 2) void mla_decode_partial(
+__global__ __launch_bounds__(256, 1) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int T, int S, int H, int k,
@@ -149,35 +150,39 @@ __global__ __launch_bounds__(256, 2) void mla_decode_partial(
     float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[2][kDecStage];
   __shared__ int s_src[kDecMaxCH];
-  __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
+  __shared__ uint64_t s_mask[kDecMaxCH / kDecRows];
+  __shared__ float s_mx[4][16];
+  __shared__ uint2 s_pf[4][64];
+  __shared__ float s_l[4][16];
 
   const int c = blockIdx.x / HB, hb = blockIdx.x - c * HB, t = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, l = lane_id();
+  const int tid = threadIdx.x, l = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = l >> 4, col = l & 15;
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int i_begin = c * CH, i_end = min(i_begin + CH, k);
   const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
+  const float scale2 = sm_scale * 1.44269504088896341f;
 
-  // ---- resolve sources and per-stage validity masks (64 entries per wave pass)
+  // ---- resolve sources and per-stage validity masks (one stage per wave pass)
   if (nst > 0) {
     const int32_t* sel = topk + (size_t)t * k;
     const int32_t* ptrow = pt + (size_t)ri.seq * MP;
     for (int i0 = wave * 64; i0 < nst * kDecRows; i0 += 256) {
       const int i = i0 + l, ii = i_begin + i;
       int src = -1;
-      if (i < nst * kDecRows && ii < i_end) {
+      if (ii < i_end) {
         const int j = sel[ii];
         if (j >= 0 && j < ri.kv && j <= ri.abs_q)
           src = clamp_page(ptrow[j / PS], num_pages) * PS + (j % PS);
       }
       const uint64_t m = __ballot(src >= 0);
-      const uint32_t m32 = (uint32_t)(m >> (l & 32));
-      const int first = m32 ? (l & 32) + __builtin_ctz(m32) : l;
+      const int first = m ? (int)__builtin_ctzll(m) : l;
       const int fsrc = __shfl(src, first, DSA_WAVE);
-      if (i < nst * kDecRows) {
-        s_src[i] = src >= 0 ? src : fsrc;
-        if ((l & 31) == 0) s_mask[i / kDecRows] = m32;
-      }
+      // a stage without any valid selection still stages cache row 0 (read,
+      // never used), so that every stage issues the same loads
+      s_src[i] = src >= 0 ? src : (m ? fsrc : 0);
+      if (l == 0) s_mask[i0 / kDecRows] = m;
     }
   }
   // ---- this lane's query fragments: head 16 hb + col, k values 32 i + 8 g ..
@@ -196,15 +201,16 @@ __global__ __launch_bounds__(256, 2) void mla_decode_partial(
   }
   __syncthreads();
 
-  // per-lane LDS offsets: S^T reads (key row col of a 16-key tile, chunk 4 i + g)
+  // per-lane LDS offsets. S^T reads: key row 16 wave + col, chunk 4 i + g.
   const int nx = nope_x(col), rx = rope_x(col);
   int soff[4], roff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) soff[j] = col * NOPE_B + 64 * (j ^ (nx >> 2)) + 16 * ((g ^ nx) & 3);
+  for (int j = 0; j < 4; ++j)
+    soff[j] = (16 * wave + col) * NOPE_B + 64 * (j ^ (nx >> 2)) + 16 * ((g ^ nx) & 3);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
-    roff[j] = kDecRopeOff + col * ROPE_B + 16 * ((4 * j + g) ^ rx);
-  // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
+    roff[j] = kDecRopeOff + (16 * wave + col) * ROPE_B + 16 * ((4 * j + g) ^ rx);
+  // V^T reads: key row 32 ks + 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
   const int vr = 4 * g + (col >> 2), vq = col & 3;
   const int vx = nope_x(vr);
   const int vbase = vr * NOPE_B + 256 * wave + 16 * ((vq >> 1) ^ (vx & 1)) + 8 * (vq & 1);
@@ -214,89 +220,87 @@ __global__ __launch_bounds__(256, 2) void mla_decode_partial(
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const uint32_t lds0 = lds_addr_of(ring[0]), lds1 = lds_addr_of(ring[1]);
 
-  if (nst > 0 && s_mask[0]) stage_rows(ring[0], kv, row_stride, s_src, wave);
-  if (nst > 1 && s_mask[1]) stage_rows(ring[1], kv, row_stride, s_src + kDecRows, wave);
+  if (nst > 0) stage_rows(lds0, kv, row_stride, s_src, wave);
   for (int st = 0; st < nst; ++st) {
-    const uint32_t mask = s_mask[st];
-    unsigned char* buf = ring[st & 1];
-    if (mask) {
-      if (st + 1 < nst && s_mask[st + 1]) wait_vmcnt<kDecGll>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      // S^T for keys 0..15 and 16..31
-      f32x4 s[2];
+    const uint64_t mask = s_mask[st];
+    const unsigned char* buf = ring[st & 1];
+    wait_vmcnt<0>();
+    lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
+    if (st + 1 < nst)
+      stage_rows((st & 1) ? lds0 : lds1, kv, row_stride, s_src + (st + 1) * kDecRows, wave);
+    if (mask == 0) continue;
+    // ---- S^T for this wave's 16 keys
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const unsigned char* kb = buf + tt * 16 * NOPE_B;
-        const unsigned char* rb = buf + tt * 16 * ROPE_B;
+    for (int i = 0; i < DK / 32; ++i) {
+      const int off = i < 16 ? soff[i & 3] + 256 * (i >> 2) : roff[i - 16];
+      sacc = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + off)), qf[i], sacc);
+    }
+    // ---- masked softmax over the stage's 64 keys (log2 units)
+    const uint32_t wm = (uint32_t)(mask >> (16 * wave + 4 * g));
+    float x[4];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < DK / 32; ++i) {
-          const int off = i < 16 ? soff[i & 3] + 256 * (i >> 2) : roff[i - 16];
-          const bf16x8 a =
-              as_bf16x8(*reinterpret_cast<const uint4*>((i < 16 ? kb : rb) + off));
-          s[tt] = mfma16(a, qf[i], s[tt]);
-        }
-      }
-      // masked online softmax over the head's 32 keys (4 lane groups x 8)
-      float x[8];
-      float mx = -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      x[r] = ((wm >> r) & 1u) ? sacc[r] * scale2 : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    if (g == 0) s_mx[wave][col] = mx;
+    lds_barrier();
+    const float m_new = fmaxf(m_run, fmaxf(fmaxf(s_mx[0][col], s_mx[1][col]),
+                                           fmaxf(s_mx[2][col], s_mx[3][col])));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+    float p[4];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_new);
+    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    m_run = m_new;
+    uint2 pk;
+    pk.x = pack_bf16x2(p[0], p[1]);
+    pk.y = pack_bf16x2(p[2], p[3]);
+    s_pf[wave][l] = pk;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = 16 * tt + 4 * g + r;
-          const float v = ((mask >> key) & 1u) ? s[tt][r] * sm_scale : -INFINITY;
-          x[4 * tt + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-      float p[8], ps = 0.f;
+    for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __expf(x[e] - m_new);
-        ps += p[e];
-      }
-      ps += shfl_xor_f(ps, 16);
-      ps += shfl_xor_f(ps, 32);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-      uint4 pk;
-      pk.x = pack_bf16x2(p[0], p[1]);
-      pk.y = pack_bf16x2(p[2], p[3]);
-      pk.z = pack_bf16x2(p[4], p[5]);
-      pk.w = pack_bf16x2(p[6], p[7]);
-      const bf16x8 pb = as_bf16x8(pk);
-      // O^T (value columns 128 wave + 16 ct + 4 g + r, head col) += V^T P^T
+      for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
+    lds_barrier();
+    // ---- O^T (value columns 128 wave + 16 ct + 4 g + r, head col) += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 pb4;
+      const uint2 lo = s_pf[2 * ks][l], hi = s_pf[2 * ks + 1][l];
+      pb4.x = lo.x;
+      pb4.y = lo.y;
+      pb4.z = hi.x;
+      pb4.w = hi.y;
+      const bf16x8 pb = as_bf16x8(pb4);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const int off = vbase + ((32 * ct) ^ vxor);
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
-        const v4s hi =
+        const int off = vbase + 32 * ks * NOPE_B + ((32 * ct) ^ vxor);
+        const v4s vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
+        const v4s vhi =
             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off + 16 * NOPE_B));
         bf16x8 va;
-        __builtin_memcpy(&va, &lo, 8);
-        __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &hi, 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
+        __builtin_memcpy(&va, &vlo, 8);
+        __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vhi, 8);
         o[ct] = mfma16(va, pb, o[ct]);
       }
     }
-    if (st + 2 < nst && s_mask[st + 2]) {
-      lds_barrier();  // every wave is done with this buffer
-      stage_rows(buf, kv, row_stride, s_src + (st + 2) * kDecRows, wave);
-    }
   }
-  // ---- partials: m, l per head; O rows as float4 (4 consecutive columns)
+  // ---- partials: m (natural-log units), l summed over lanes and waves, O
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  if (g == 0) s_l[wave][col] = l_run;
+  __syncthreads();
   const size_t base = ((size_t)t * nch + c) * H;
   if (head < H) {
     if (wave == 0 && g == 0) {
-      part_ml[(base + head) * 2 + 0] = m_run;
-      part_ml[(base + head) * 2 + 1] = l_run;
+      part_ml[(base + head) * 2 + 0] = m_run * 0.693147180559945309f;
+      part_ml[(base + head) * 2 + 1] = s_l[0][col] + s_l[1][col] + s_l[2][col] + s_l[3][col];
     }
     float* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
 #pragma unroll
@@ -376,12 +380,11 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
 }
 
 int mla_decode_chunk(int T, int k) {
-  // about two workgroups per compute unit, 2 .. 16 stages of kDecRows each:
-  // at least two stages so that a workgroup's loads overlap, at most 16 to
-  // bound the partial (m, l, O) traffic of the combine
+  // about one workgroup per compute unit, 1 .. 8 stages of kDecRows each
+  // (at most 8 to bound the partial (m, l, O) traffic of the combine)
   const long nsub = (k + kDecRows - 1) / kDecRows;
-  long per = ((long)T * nsub + 511) / 512;
-  if (per < 2) per = 2;
+  long per = ((long)T * nsub + 255) / 256;
+  if (per < 1) per = 1;
   if (per > kDecMaxCH / kDecRows) per = kDecMaxCH / kDecRows;
   return (int)per * kDecRows;
 }
