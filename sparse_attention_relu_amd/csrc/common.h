@@ -75,9 +75,10 @@ __device__ __forceinline__ RowInfo row_info_wave(const int32_t* __restrict__ cu,
     const int c = __popcll(done);
     const int last = (S - base < DSA_WAVE ? S - base : DSA_WAVE);
     if (c < last) {
-      const int s0 = __shfl(q0, c, DSA_WAVE);
-      const int s1 = __shfl(q1, c, DSA_WAVE);
-      const int sk = __shfl(kv, c, DSA_WAVE);
+      // the same value in every lane; readfirstlane tells the compiler so
+      const int s0 = __builtin_amdgcn_readfirstlane(__shfl(q0, c, DSA_WAVE));
+      const int s1 = __builtin_amdgcn_readfirstlane(__shfl(q1, c, DSA_WAVE));
+      const int sk = __builtin_amdgcn_readfirstlane(__shfl(kv, c, DSA_WAVE));
       if (t < s0) return r;  // before the owner's first row: no sequence
       r.seq = base + c;
       r.abs_q = sk - (s1 - s0) + (t - s0);

@@ -60,52 +60,89 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
 }
 
 // ---------------------------------------------------------------------------
-// Streaming per-row scorer (decode and any ragged layout). One wave scores
-// NSUB blocks of 64 consecutive positions of one row: the page of every key
-// it will touch is looked up first, then the keys of block s + 1 are loaded
-// straight into MFMA B-operand registers while block s is multiplied. The
-// query fragment and head weights stay in registers.
-// grid = (ceil(cap / (4 * 64 * NSUB)), T), block = 256.
+// Streaming scorer (decode and any ragged layout with short query runs). A
+// workgroup scores NSTG consecutive stages of 256 positions of one row: the
+// keys of stage s + 1 stream into a two-stage LDS ring by direct global->LDS
+// loads while stage s is multiplied, so every compute unit keeps a stage of
+// keys in flight. A load fills 1024 LDS bytes with 1024 / (2 D) consecutive
+// positions of one page (one page-table entry per load); the 16-byte chunk c
+// of key row r sits at slot c ^ (r % (D / 8)), so the 32 rows that a lane
+// group reads at one chunk hit distinct banks. Wave w multiplies positions
+// 64 w .. 64 w + 63 of each stage: A = query fragments (heads as M, resident),
+// B = keys from LDS (N = 32 positions). Positions past the row's valid range
+// load the sequence's first key and are never stored.
+// grid = (ceil(cap / (256 NSTG)), T), block = 256, static LDS 2 x 256 x 2D.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ void load_key_frags(const uint16_t* __restrict__ cache, int pg, int PS,
-                                               int j, int hf, bf16x8 (&b)[D / 16]) {
-  constexpr int HALF = D / 2;
-  const bool ok = pg >= 0;
-  const uint16_t* kp = cache + ((size_t)(ok ? pg : 0) * PS + (j % PS)) * D + hf * HALF;
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i)
-    b[i] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(kp + 8 * i) : zero_u4());
+constexpr int kStreamKeys = 256;  // positions per stage
+
+__device__ __forceinline__ void gll16_idx(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
 }
 
-template <int D, int HB, int NSUB>
-__global__ __launch_bounds__(256) void idx_score_rows(
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// This wave's direct loads of one stage: load I (= NL wave + n) covers stage
+// rows I * RPI + l / CPR; lane l fetches the chunk that belongs at its slot
+// l % CPR, i.e. chunk (l % CPR) ^ (row % CPR). Since I * RPI is a multiple of
+// RPI and l / CPR < RPI, row % CPR = (I * RPI) % CPR ^ (l / CPR) % CPR.
+template <int D>
+__device__ __forceinline__ void stream_stage(uint32_t buf, const uint16_t* __restrict__ cache,
+                                             const int32_t* __restrict__ ptrow, int num_pages,
+                                             int PS, int j_stage, int n_valid, int wave, int l) {
+  constexpr int RB = 2 * D;                  // bytes per key row
+  constexpr int RPI = 1024 / RB;             // rows per load
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int NL = kStreamKeys / RPI / 4;  // loads per wave per stage
+  const int lr = l / CPR, lc = l % CPR;
+  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    const int I = NL * wave + n;
+    int j0 = j_stage + I * RPI;  // first position of this load (one page)
+    if (j0 >= n_valid) j0 = 0;   // past the row: any valid row, never stored
+    const int page = clamp_page(ptrow[j0 / PS], num_pages);
+    gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
+              cache + ((size_t)page * PS + (j0 % PS)) * D, buf + I * 1024);
+  }
+}
+
+template <int D, int HB>
+__global__ __launch_bounds__(256, 1) void idx_score_stream(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
-    int PS, int MP, float* __restrict__ scores, long ld) {
+    int PS, int MP, int NSTG, float* __restrict__ scores, long ld) {
   constexpr int KS = D / 16;
   constexpr int HALF = D / 2;
-  constexpr int KPW = 64 * NSUB;
+  constexpr int RB = 2 * D;
+  constexpr int CPR = D / 8;
+  constexpr int STAGE = kStreamKeys * RB;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
   const int t = blockIdx.y;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
   const int m = l & 31, hf = l >> 5;
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
-  const int j_begin = (blockIdx.x * 4 + wave) * KPW;
-  if (ri.seq < 0 || j_begin >= ri.n_valid) return;
-  const int j_end = min(j_begin + KPW, ri.n_valid);
+  const int n = ri.n_valid;
+  const int j_begin = blockIdx.x * NSTG * kStreamKeys;
+  if (ri.seq < 0 || j_begin >= n) return;
+  const int nst = min(NSTG, (n - j_begin + kStreamKeys - 1) / kStreamKeys);
   const int32_t* ptrow = pt + (size_t)ri.seq * MP;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
+  const uint32_t lds1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[1];
 
-  // pages of every key of this wave (-1: past the row's end)
-  int pg[NSUB][2];
-#pragma unroll
-  for (int sb = 0; sb < NSUB; ++sb)
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int j = j_begin + 64 * sb + 32 * blk + m;
-      pg[sb][blk] = j < j_end ? clamp_page(ptrow[j / PS], num_pages) : -1;
-    }
+  stream_stage<D>(lds0, cache, ptrow, num_pages, PS, j_begin, n, wave, l);
   bf16x8 a[HB][KS];
   float wv[HB][16];
 #pragma unroll
@@ -114,34 +151,45 @@ __global__ __launch_bounds__(256) void idx_score_rows(
     load_q_frag<D>(q + ((size_t)t * H + (head < H ? head : 0)) * D + hf * HALF, head < H, a[hb]);
     load_head_weights(w + (size_t)t * H, H, hb, hf, wv[hb]);
   }
+  // complete these loads here, not at their first use inside the stage loop
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : : "v"(a[hb][i]));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) asm volatile("" : : "v"(wv[hb][r]));
+  }
   float* srow = scores + (size_t)t * ld;
-
-  bf16x8 b[2][2][KS];
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-    load_key_frags<D>(cache, pg[0][blk], PS, j_begin + 32 * blk + m, hf, b[0][blk]);
-#pragma unroll
-  for (int sb = 0; sb < NSUB; ++sb) {
-    if (sb + 1 < NSUB) {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        load_key_frags<D>(cache, pg[sb + 1][blk], PS, j_begin + 64 * (sb + 1) + 32 * blk + m, hf,
-                          b[(sb + 1) & 1][blk]);
-    }
+  for (int s2 = 0; s2 < nst; ++s2) {
+    const int j_stage = j_begin + s2 * kStreamKeys;
+    wait_vm<0>();
+    lds_sync();  // stage s2 has landed for every wave; stage s2 - 1 is consumed
+    if (s2 + 1 < nst)
+      stream_stage<D>((s2 & 1) ? lds0 : lds1, cache, ptrow, num_pages, PS,
+                      j_stage + kStreamKeys, n, wave, l);
+    const unsigned char* buf = ring[s2 & 1];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int j = j_begin + 64 * sb + 32 * blk + m;
+      const int kr = 64 * wave + 32 * blk + m;  // key row within the stage
+      const int j = j_stage + kr;
+      bf16x8 b[KS];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const int chunk = hf * HALF / 8 + i;  // dims hf * D / 2 + 8 i ..
+        b[i] = as_bf16x8(*reinterpret_cast<const uint4*>(buf + kr * RB +
+                                                          16 * (chunk ^ (kr % CPR))));
+      }
       float part = 0.0f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         f32x16 acc = {};
 #pragma unroll
         for (int i = 0; i < KS; ++i)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[sb & 1][blk][i], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], b[i], acc, 0, 0, 0);
         part += relu_weighted_sum(acc, wv[hb]);
       }
       part += shfl_xor_f(part, 32);
-      if (hf == 0 && j < j_end) srow[j] = part;
+      if (hf == 0 && j < n) srow[j] = part;
     }
   }
 }
@@ -833,24 +881,21 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-template <int D, int HB, int NSUB>
-static hipError_t launch_rows_n(const IndexerArgs& a, hipStream_t st) {
-  constexpr int KPW = 64 * NSUB;
-  const int cap = a.MP * a.PS;
-  dim3 grid((cap + 4 * KPW - 1) / (4 * KPW), a.T);
-  ProfScope prof("idx_score_rows", st);
-  hipLaunchKernelGGL((idx_score_rows<D, HB, NSUB>), grid, dim3(256), 0, st, a.q, a.w, a.cache,
-                     a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
-                     a.ld);
-  return hipGetLastError();
-}
-
-// One 64-key block per wave: the key loads of a wave then live in registers
-// only once, which keeps three waves per SIMD in flight (a software
-// pipelined multi-block wave holds fewer waves and moves fewer bytes).
+// Stages per workgroup: about four workgroups per compute unit over the
+// batch's upper bound T * cap, between 1 and 16 stages.
 template <int D, int HB>
 static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
-  return launch_rows_n<D, HB, 1>(a, st);
+  const long cap = (long)a.MP * a.PS;
+  long nstg = ((long)a.T * cap + 1024L * kStreamKeys - 1) / (1024L * kStreamKeys);
+  if (nstg < 1) nstg = 1;
+  if (nstg > 16) nstg = 16;
+  const long per = nstg * kStreamKeys;
+  dim3 grid((unsigned)((cap + per - 1) / per), a.T);
+  ProfScope prof("idx_score_stream", st);
+  hipLaunchKernelGGL((idx_score_stream<D, HB>), grid, dim3(256), 0, st, a.q, a.w, a.cache,
+                     a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, (int)nstg,
+                     a.scores, a.ld);
+  return hipGetLastError();
 }
 
 template <int D, int HB>
