@@ -61,19 +61,20 @@ __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const floa
 
 // ---------------------------------------------------------------------------
 // Streaming scorer (decode and any ragged layout with short query runs). A
-// workgroup scores NSTG consecutive stages of 256 positions of one row: the
-// keys of stage s + 1 stream into a two-stage LDS ring by direct global->LDS
-// loads while stage s is multiplied, so every compute unit keeps a stage of
-// keys in flight. A load fills 1024 LDS bytes with 1024 / (2 D) consecutive
+// workgroup scores NSTG consecutive stages of 128 positions of one row: the
+// keys of stages s + 1 .. s + 3 stream into a four-stage LDS ring by direct
+// global->LDS loads while stage s is multiplied, and each consumed stage is
+// refilled at once, so the loads in flight never drain. A load fills 1024 LDS bytes with 1024 / (2 D) consecutive
 // positions of one page (one page-table entry per load); the 16-byte chunk c
 // of key row r sits at slot c ^ (r % (D / 8)), so the 32 rows that a lane
 // group reads at one chunk hit distinct banks. Wave w multiplies positions
-// 64 w .. 64 w + 63 of each stage: A = query fragments (heads as M, resident),
+// 32 w .. 32 w + 31 of each stage: A = query fragments (heads as M, resident),
 // B = keys from LDS (N = 32 positions). Positions past the row's valid range
 // load the sequence's first key and are never stored.
-// grid = (ceil(cap / (256 NSTG)), T), block = 256, static LDS 2 x 256 x 2D.
+// grid = (ceil(cap / (128 NSTG)), T), block = 256, static LDS 4 x 128 x 2D.
 // ---------------------------------------------------------------------------
-constexpr int kStreamKeys = 256;  // positions per stage
+constexpr int kStreamKeys = 128;  // positions per stage
+constexpr int kStreamRing = 4;    // LDS stages: three in flight while one is used
 
 __device__ __forceinline__ void gll16_idx(uint32_t voff, const void* sbase, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void idx_score_stream(
   constexpr int RB = 2 * D;
   constexpr int CPR = D / 8;
   constexpr int STAGE = kStreamKeys * RB;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStreamRing][STAGE];
   const int t = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = lane_id();
@@ -139,10 +140,15 @@ __global__ __launch_bounds__(256, 1) void idx_score_stream(
   if (ri.seq < 0 || j_begin >= n) return;
   const int nst = min(NSTG, (n - j_begin + kStreamKeys - 1) / kStreamKeys);
   const int32_t* ptrow = pt + (size_t)ri.seq * MP;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
-  const uint32_t lds1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[1];
+  const uint32_t lds_ring =
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
+  constexpr int NL = kStreamKeys / (1024 / RB) / 4;  // loads per wave per stage
 
-  stream_stage<D>(lds0, cache, ptrow, num_pages, PS, j_begin, n, wave, l);
+#pragma unroll
+  for (int q2 = 0; q2 < kStreamRing - 1; ++q2)
+    if (q2 < nst)
+      stream_stage<D>(lds_ring + q2 * STAGE, cache, ptrow, num_pages, PS,
+                      j_begin + q2 * kStreamKeys, n, wave, l);
   bf16x8 a[HB][KS];
   float wv[HB][16];
 #pragma unroll
@@ -162,15 +168,19 @@ __global__ __launch_bounds__(256, 1) void idx_score_stream(
   float* srow = scores + (size_t)t * ld;
   for (int s2 = 0; s2 < nst; ++s2) {
     const int j_stage = j_begin + s2 * kStreamKeys;
-    wait_vm<0>();
+    // stages s2 + 1 .. s2 + kStreamRing - 2 were issued after this one
+    const int later = min(kStreamRing - 2, nst - 1 - s2);
+    if (later >= 2) wait_vm<2 * NL>();
+    else if (later == 1) wait_vm<NL>();
+    else wait_vm<0>();
     lds_sync();  // stage s2 has landed for every wave; stage s2 - 1 is consumed
-    if (s2 + 1 < nst)
-      stream_stage<D>((s2 & 1) ? lds0 : lds1, cache, ptrow, num_pages, PS,
-                      j_stage + kStreamKeys, n, wave, l);
-    const unsigned char* buf = ring[s2 & 1];
+    if (s2 + kStreamRing - 1 < nst)
+      stream_stage<D>(lds_ring + ((s2 + kStreamRing - 1) % kStreamRing) * STAGE, cache, ptrow,
+                      num_pages, PS, j_stage + (kStreamRing - 1) * kStreamKeys, n, wave, l);
+    const unsigned char* buf = ring[s2 % kStreamRing];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int kr = 64 * wave + 32 * blk + m;  // key row within the stage
+    for (int blk = 0; blk < 1; ++blk) {
+      const int kr = 32 * wave + m;  // key row within the stage
       const int j = j_stage + kr;
       bf16x8 b[KS];
 #pragma unroll
@@ -881,14 +891,17 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // Host-side launchers
 // ---------------------------------------------------------------------------
-// Stages per workgroup: about four workgroups per compute unit over the
-// batch's upper bound T * cap, between 1 and 16 stages.
+// Stages per workgroup, from the batch's upper bound of T * cap positions:
+// a small batch gets one round of workgroups (one per compute unit, the ring
+// fills the LDS), a large one about four per unit; 1 .. 32 stages each.
 template <int D, int HB>
 static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
   const long cap = (long)a.MP * a.PS;
-  long nstg = ((long)a.T * cap + 1024L * kStreamKeys - 1) / (1024L * kStreamKeys);
+  const long total = (long)a.T * ((cap + kStreamKeys - 1) / kStreamKeys);
+  const long target = total <= 2048 ? 256 : 1024;
+  long nstg = (total + target - 1) / target;
   if (nstg < 1) nstg = 1;
-  if (nstg > 16) nstg = 16;
+  if (nstg > 32) nstg = 32;
   const long per = nstg * kStreamKeys;
   dim3 grid((unsigned)((cap + per - 1) / per), a.T);
   ProfScope prof("idx_score_stream", st);
