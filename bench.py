@@ -134,7 +134,8 @@ def _roofline_entry(bound, work, ms, per_step_launches=1):
 
 # Sources whose text decides each kernel's machine code.
 KERNEL_SOURCES = {
-    "idx_score_stream": "indexer.hip", "idx_score_tiles": "indexer.hip",
+    "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
+    "idx_score_tiles": "indexer.hip",
     "topk_select": "indexer.hip", "mla_decode_partial": "mla.hip",
     "mla_decode_combine": "mla.hip", "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
@@ -207,9 +208,11 @@ def bench_decode(dsa, wl, args):
     sel = topk.cpu().numpy()
     n_sel = int((sel >= 0).sum())
     D, Hi, PS = wl.D_idx, wl.H_idx, wl.PS
+    score_bytes = (int(nval.sum()) * (D * 2 + 4) + T * Hi * (D * 2 + 4)
+                   + int(np.ceil(nval / PS).sum()) * 4)
     work = {
-        "idx_score_stream": ("hbm", int(nval.sum()) * (D * 2 + 4) + T * Hi * (D * 2 + 4)
-                           + int(np.ceil(nval / PS).sum()) * 4),
+        "idx_score_stream": ("hbm", score_bytes),
+        "idx_score_flat": ("hbm", score_bytes),
         "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
         "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
         "mla_decode_combine": ("hbm", T * H * DV * 2),
@@ -233,7 +236,7 @@ def bench_decode(dsa, wl, args):
 
     return dict(ms=ms, tok_s=T / (ms * 1e-3), kernels=kernels, roofline=roof,
                 selected=n_sel, keys=int(nval.sum()),
-                indexer_ms=round(part(("idx_score_stream", "topk_select")), 4),
+                indexer_ms=round(part(("idx_score_stream", "idx_score_flat", "topk_select")), 4),
                 attend_ms=round(part(("mla_decode_partial", "mla_decode_combine")), 4))
 
 

@@ -205,6 +205,259 @@ __global__ __launch_bounds__(256, 1) void idx_score_stream(
 }
 
 // ---------------------------------------------------------------------------
+// Balanced streaming scorer for ragged batches. The batch's work is the flat
+// list of (row, 128-position stage) pairs in row order; each of G persistent
+// workgroups (one per compute unit) takes an equal contiguous share of it, so
+// rows of any length mix without a tail of part-filled workgroups, and the
+// four-stage ring keeps streaming across row boundaries (one ring fill per
+// workgroup instead of one per row piece).
+//
+// Every workgroup first computes each row's valid length and the prefix of
+// stage counts (cu_q_lens and seq_lens staged in LDS, one binary search per
+// row). The query rows of 32 heads and their weights travel with the first
+// stage of each row through the same direct loads, into one of two LDS
+// slots (alternating by row); the issue cursor never runs more than one row
+// ahead of the compute cursor, so a slot is rewritten only after its row is
+// done. Stage waits count only key loads, so a query load or a score store
+// issued later can only make a wait longer, never too short.
+// grid = (number of compute units), block = 256.
+// ---------------------------------------------------------------------------
+constexpr int kFlatMaxT = 1024;
+
+template <int D>
+struct FlatShape {
+  static constexpr int RB = 2 * D;                   // bytes per key (and query) row
+  static constexpr int STAGE = kStreamKeys * RB;
+  static constexpr int QBYTES = 32 * RB;             // 32 head rows
+  static constexpr int QSLOT = QBYTES + 256;         // + 64 fp32 weights
+  // cu_q_lens and seq_lens are staged in the ring before it is used
+  static constexpr int MAX_S = (kStreamRing * STAGE / 4 - 1) / 2;
+};
+
+__device__ __forceinline__ void gll16_ptr(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void gll4_ptr(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// Query rows of row t (heads >= H repeat head H - 1; they get weight 0) in
+// the key layout, then the weights.
+template <int D>
+__device__ __forceinline__ void flat_issue_query(uint32_t slot, const uint16_t* __restrict__ q,
+                                                 const float* __restrict__ w, int t, int H,
+                                                 int wave, int l) {
+  constexpr int RB = 2 * D, CPR = D / 8, RPI = 1024 / RB, NQ = 32 / RPI;
+#pragma unroll
+  for (int I = wave; I < NQ; I += 4) {
+    const int h = I * RPI + l / CPR;
+    const int hs = h < H ? h : H - 1;
+    const int c = (l % CPR) ^ (h % CPR);
+    gll16_ptr(q + ((size_t)t * H + hs) * D + 8 * c,
+              __builtin_amdgcn_readfirstlane(slot + I * 1024));
+  }
+  if (wave == 3) gll4_ptr(w + (size_t)t * H + (l < H ? l : H - 1), slot + 32 * RB);
+}
+
+// Keys of one stage, the page-table entries of all of this wave's loads
+// fetched before the first load is issued.
+template <int D>
+__device__ __forceinline__ void flat_issue_keys(uint32_t buf, const uint16_t* __restrict__ cache,
+                                                const int32_t* __restrict__ ptrow, int num_pages,
+                                                int PS, int j_stage, int n_valid, int wave,
+                                                int l) {
+  constexpr int RB = 2 * D, RPI = 1024 / RB, CPR = D / 8, NL = kStreamKeys / RPI / 4;
+  const int lr = l / CPR, lc = l % CPR;
+  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+  int jj[NL], pg[NL];
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    int j0 = j_stage + (NL * wave + n) * RPI;
+    if (j0 >= n_valid) j0 = 0;  // past the row: any valid row, never stored
+    jj[n] = j0;
+    pg[n] = ptrow[j0 / PS];
+  }
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    const int I = NL * wave + n;
+    const uint64_t src = (uint64_t)(uintptr_t)(
+        cache + ((size_t)clamp_page(pg[n], num_pages) * PS + (jj[n] % PS)) * D);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
+    gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
+              (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+              __builtin_amdgcn_readfirstlane(buf + I * 1024));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void idx_score_flat(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
+    int PS, int MP, float* __restrict__ scores, long ld) {
+  using F = FlatShape<D>;
+  constexpr int KS = D / 16, HALF = D / 2, RB = F::RB, CPR = D / 8;
+  constexpr int NL = kStreamKeys / (1024 / RB) / 4;  // key loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kStreamRing][F::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char qbuf[2][F::QSLOT];
+  __shared__ int s_pre[kFlatMaxT + 1];
+  __shared__ int s_n[kFlatMaxT];
+  __shared__ int s_seq[kFlatMaxT];
+  __shared__ int s_scan[4];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane_id();
+  const int m = l & 31, hf = l >> 5;
+  const int cap = MP * PS;
+
+  // ---- valid length of every row and the prefix of its stage counts
+  int* s_cu = reinterpret_cast<int*>(ring[0]);
+  int* s_sl = s_cu + (S + 1);
+  for (int i = tid; i <= S; i += 256) s_cu[i] = cu[i];
+  for (int i = tid; i < S; i += 256) s_sl[i] = seq_lens[i];
+  __syncthreads();
+  const int R = (T + 255) / 256;  // rows per thread, consecutive
+  int cnt = 0;
+  for (int i = 0; i < R; ++i) {
+    const int t = R * tid + i;
+    if (t >= T) break;
+    int seq = -1, n = 0;
+    if (S > 0 && t >= s_cu[0] && t < s_cu[S]) {
+      int lo = 0, hi = S;  // first s with cu[s + 1] > t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_cu[mid + 1] > t) hi = mid; else lo = mid + 1;
+      }
+      if (lo < S) {
+        const int q0 = s_cu[lo], q1 = s_cu[lo + 1];
+        const int kv = s_sl[lo];
+        const int abs_q = kv - (q1 - q0) + (t - q0);
+        const int kc = kv < 0 ? 0 : (kv > cap ? cap : kv);
+        n = abs_q + 1 < kc ? abs_q + 1 : kc;
+        n = n < 0 ? 0 : n;
+        seq = lo;
+      }
+    }
+    s_n[t] = n;
+    s_seq[t] = seq;
+    cnt += (n + kStreamKeys - 1) / kStreamKeys;
+  }
+  int total;
+  int run = block_inclusive_scan<256>(cnt, s_scan, &total) - cnt;
+  for (int i = 0; i < R; ++i) {
+    const int t = R * tid + i;
+    if (t >= T) break;
+    s_pre[t] = run;
+    run += (s_n[t] + kStreamKeys - 1) / kStreamKeys;
+  }
+  if (tid == 0) s_pre[T] = total;
+  __syncthreads();  // also: the staging area is free for the ring
+
+  // ---- this workgroup's share [f_begin, f_end) of the flat stage list
+  const int G = gridDim.x;
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int f_begin = (int)((long)blockIdx.x * total / G);
+  const int f_end = (int)((long)(blockIdx.x + 1) * total / G);
+  if (f_begin >= f_end) return;
+  int r0 = 0;
+  {
+    int lo = 0, hi = T - 1;  // last row with s_pre[row] <= f_begin (it has stages)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= f_begin) lo = mid; else hi = mid - 1;
+    }
+    r0 = __builtin_amdgcn_readfirstlane(lo);
+  }
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
+  const uint32_t lds_q = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)qbuf[0];
+  auto pre = [&](int r) { return __builtin_amdgcn_readfirstlane(s_pre[r]); };
+
+  // issue cursor: next stage fi, its row ri and the row's ordinal ki
+  int fi = f_begin, ri = r0, ki = 0;
+  // compute cursor: row rc and ordinal kc of the stage being computed
+  int rc = r0, kc = 0;
+  auto issue = [&]() {
+    fi = __builtin_amdgcn_readfirstlane(fi);
+    ri = __builtin_amdgcn_readfirstlane(ri);
+    ki = __builtin_amdgcn_readfirstlane(ki);
+    const int base = pre(ri);
+    if (fi == f_begin || fi == base)
+      flat_issue_query<D>(lds_q + (ki & 1) * F::QSLOT, q, w, ri, H, wave, l);
+    const int seq = __builtin_amdgcn_readfirstlane(s_seq[ri]);
+    const int n = __builtin_amdgcn_readfirstlane(s_n[ri]);
+    flat_issue_keys<D>(lds_ring + (fi % kStreamRing) * F::STAGE, cache, pt + (size_t)seq * MP,
+                       num_pages, PS, (fi - base) * kStreamKeys, n, wave, l);
+    ++fi;
+    if (fi < f_end && fi >= pre(ri + 1)) {
+      do { ++ri; } while (pre(ri + 1) <= fi);
+      ++ki;
+    }
+  };
+  while (fi < f_end && fi < f_begin + kStreamRing - 1 && ki <= 1) issue();
+
+  bf16x8 a[KS];
+  float wv[16];
+  int n_c = 0, base_c = 0;
+  float* srow = scores;
+  for (int fc = f_begin; fc < f_end; ++fc) {
+    const int later = fi - fc - 1;  // stages issued after this one (0 .. 2)
+    if (later >= 2) wait_vm<2 * NL>();
+    else if (later == 1) wait_vm<NL>();
+    else wait_vm<0>();
+    lds_sync();  // stage fc (and its row's query) landed; stage fc - 1 is consumed
+    bool fresh = fc == f_begin;
+    if (fc >= pre(rc + 1)) {
+      do { ++rc; } while (pre(rc + 1) <= fc);
+      ++kc;
+      fresh = true;
+    }
+    while (fi < f_end && fi <= fc + kStreamRing - 1 && ki <= kc + 1) issue();
+    if (fresh) {
+      const unsigned char* qs = qbuf[kc & 1];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const int chunk = hf * HALF / 8 + i;
+        const uint4 v = *reinterpret_cast<const uint4*>(qs + m * RB + 16 * (chunk ^ (m % CPR)));
+        a[i] = as_bf16x8(m < H ? v : zero_u4());
+      }
+      const float* wl = reinterpret_cast<const float*>(qs + F::QBYTES);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = 8 * (r >> 2) + 4 * hf + (r & 3);
+        wv[r] = head < H ? wl[head] : 0.0f;
+      }
+      n_c = __builtin_amdgcn_readfirstlane(s_n[rc]);
+      base_c = pre(rc);
+      srow = scores + (size_t)rc * ld;
+    }
+    const unsigned char* buf = ring[fc % kStreamRing];
+    const int kr = 32 * wave + m;  // key row within the stage
+    const int j = (fc - base_c) * kStreamKeys + kr;
+    bf16x8 b[KS];
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int chunk = hf * HALF / 8 + i;
+      b[i] = as_bf16x8(*reinterpret_cast<const uint4*>(buf + kr * RB + 16 * (chunk ^ (kr % CPR))));
+    }
+    f32x16 acc = {};
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], acc, 0, 0, 0);
+    float part = relu_weighted_sum(acc, wv);
+    part += shfl_xor_f(part, 32);
+    if (hf == 0 && j < n_c) srow[j] = part;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled MFMA scorer for query chunks (extend). A workgroup owns TR = NW * QPW
 // consecutive packed rows and a range of RK key positions; every wave keeps
 // QPW query fragments in registers, and 64-key blocks of the owning
@@ -894,10 +1147,26 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 // Stages per workgroup, from the batch's upper bound of T * cap positions:
 // a small batch gets one round of workgroups (one per compute unit, the ring
 // fills the LDS), a large one about four per unit; 1 .. 32 stages each.
+static int compute_units() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n;
+}
+
 template <int D, int HB>
 static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
   const long cap = (long)a.MP * a.PS;
   const long total = (long)a.T * ((cap + kStreamKeys - 1) / kStreamKeys);
+  if (HB == 1 && total > 2048 && total < (1L << 30) && a.T <= kFlatMaxT &&
+      a.S <= FlatShape<D>::MAX_S) {
+    ProfScope prof("idx_score_flat", st);
+    hipLaunchKernelGGL((idx_score_flat<D>), dim3(compute_units()), dim3(256), 0, st, a.q, a.w,
+                       a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP,
+                       a.scores, a.ld);
+    return hipGetLastError();
+  }
   const long target = total <= 2048 ? 256 : 1024;
   long nstg = (total + target - 1) / target;
   if (nstg < 1) nstg = 1;

@@ -99,6 +99,42 @@ def test_indexer_edges(dsa, name, path):
     check_topk_rows_valid(got, wl.seq_lens, cu, k)
 
 
+# Ragged decode-style batches large enough (rows x 128-position stages above
+# 2048) for the balanced scorer: rows of very different lengths, empty
+# sequences, rows past the last sequence, H < 32, every D, and many short rows
+# so that one workgroup's share spans many rows.
+INDEXER_FLAT = {
+    # name: (S, kv range, q_len choices, PS, MP, H, D, k, extra_rows)
+    "d128_h32_mixed": (40, (0, 4000), (0, 1, 1, 2, 5), 64, 64, 32, 128, 256, 3),
+    "d64_h20_ps16": (100, (1, 3200), (1,), 16, 200, 20, 64, 100, 0),
+    "d32_many_short_rows": (1000, (1, 300), (1,), 16, 160, 32, 32, 64, 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(INDEXER_FLAT))
+def test_indexer_flat(dsa, name):
+    S, (lo, hi), qchoice, PS, MP, H, D, k, extra = INDEXER_FLAT[name]
+    rng = np.random.default_rng(4242)
+    ql = rng.choice(qchoice, size=S)
+    kv = np.maximum(rng.integers(lo, hi + 1, size=S), ql)
+    cu = np.concatenate([[0], np.cumsum(ql)]).tolist()
+    wl = W.build(name=name, seed=78, S=S, kv_lens=kv.tolist(), PS=PS, MP=MP, batches={"b": cu},
+                 H_idx=H, D_idx=D, k=k, with_mla=False, extra_pages=1)
+    b = wl.batches["b"]
+    q_idx, w = b.q_idx, b.w
+    if extra:
+        q_idx = np.concatenate([q_idx, q_idx[:1].repeat(extra, 0)])
+        w = np.concatenate([w, w[:1].repeat(extra, 0)])
+    T = q_idx.shape[0]
+    assert T * -(-(MP * PS) // 128) > 2048
+    log(f"indexer flat {name} T={T}")
+    d = Dev(wl)
+    got = _gpu_topk(dsa, d, q_idx, w, cu, k, 1)
+    exp = _oracle_topk(wl, b, k=k, q_idx=q_idx, w=w, cu=np.array(cu))
+    assert np.array_equal(got, exp)
+    check_topk_rows_valid(got, wl.seq_lens, cu, k)
+
+
 def test_indexer_ties_and_negative_zero(dsa):
     """All-zero queries (every score ties at 0) and negative weights (scores
     of -0.0 mixed with +0.0): order is by position."""
