@@ -100,28 +100,34 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // Decode: grid = (nch * HB, T), block = 256. Workgroup (c, hb, t) attends row
 // t over selections [c * CH, (c + 1) * CH) for heads 16 hb .. 16 hb + 15 and
 // leaves its partial (max m, sum l, unnormalised O) per head for the combine
-// kernel. The source slot of every selection is resolved first; stages of 64
-// selected rows then stream through a two-stage LDS ring (stage s + 1 is in
-// flight while stage s is used), staged like an extend page.
-// Per stage, wave w computes S^T = K . Q^T for keys 16 w .. 16 w + 15 and the
-// 16 heads (v_mfma_f32_16x16x32_bf16: M = keys, N = heads, K = 576); the
-// waves exchange their per-head maxima and bf16 P^T fragments through LDS;
-// then wave w computes O^T += V^T . P^T for value columns 128 w .. 128 w + 127
-// over all 64 keys, two 32-key steps whose k slots of lane group g are keys
-// 4 g .. 4 g + 3 of the first and of the second 16-key tile, the order in
-// which both the S^T accumulators (P^T) and the transposed V^T reads hold
-// them. Logits are kept in log2 units. Invalid selections load a valid row of
-// the same stage and are masked to probability 0; stages without any valid
-// selection load cache row 0 and skip the arithmetic.
+// kernel. The source slot of every selection is resolved first; stages of 32
+// selected rows then stream through a four-stage LDS ring (three stages in
+// flight while one is used, each refilled as soon as it is consumed), staged
+// like an extend page.
+// S^T = K . Q^T of a stage is two 16-key tiles for the 16 heads
+// (v_mfma_f32_16x16x32_bf16: M = keys, N = heads); the contraction over the
+// 576 latent columns is split between the waves (k steps 5, 5, 4, 4 of 32
+// columns), so each staged key is read from LDS once, and the four partial
+// tiles meet through LDS, summed in the same order by every wave. A lane then
+// holds keys 4 g .. 4 g + 3 of both tiles for head `col`, which is exactly
+// its P^T operand for one 32-key step, and its O^T accumulators belong to the
+// same head, so every wave runs the same online softmax on its own: wave w
+// computes O^T += V^T . P^T for value columns 128 w .. 128 w + 127, reading
+// V^T with transposed LDS reads in the same key order. Logits are kept
+// in log2 units. Invalid selections load a valid row of the same stage and
+// are masked to probability 0; stages without any valid selection load cache
+// row 0 and skip the arithmetic.
 // ---------------------------------------------------------------------------
-constexpr int kDecRows = 64;                                  // selections per stage
-constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 73728 bytes
+constexpr int kDecRows = 32;                                  // selections per stage
+constexpr int kDecRing = 4;                                   // LDS stages
+constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
+constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
 constexpr int kDecMaxCH = 512;
 
-// This wave's 18 direct loads of one stage: nope rows r = 4 n + wave
-// (n < 16) at LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows
-// 8 G .. 8 G + 7 for G = wave, wave + 4 at kDecRopeOff + 1024 G.
+// This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
+// LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
+// 8 wave + 7 at kDecRopeOff + 1024 wave.
 __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restrict__ kv,
                                            int row_stride, const int* s_src, int wave) {
   const int l = lane_id_volatile();
@@ -132,13 +138,9 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
     const int src = __builtin_amdgcn_readfirstlane(s_src[r]);
     gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), kv + (size_t)src * row_stride, buf + r * NOPE_B);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int G = wave + 4 * j;
-    const int r = 8 * G + (l >> 3);
-    gll16_a(kv + (size_t)s_src[r] * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
-            buf + kDecRopeOff + G * 1024);
-  }
+  const int r = 8 * wave + (l >> 3);
+  gll16_a(kv + (size_t)s_src[r] * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
+          buf + kDecRopeOff + wave * 1024);
 }
 
 template <int dummy = 0>
@@ -148,12 +150,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int T, int S, int H, int k,
     int PS, int MP, float sm_scale, int CH, int nch, int HB, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][kDecStage];
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
-  __shared__ uint64_t s_mask[kDecMaxCH / kDecRows];
-  __shared__ float s_mx[4][16];
-  __shared__ uint2 s_pf[4][64];
-  __shared__ float s_l[4][16];
+  __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
+  __shared__ f32x4 s_part[4][2][64];  // per wave: partial S^T of both tiles
 
   const int c = blockIdx.x / HB, hb = blockIdx.x - c * HB, t = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id();
@@ -164,53 +164,73 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
   const float scale2 = sm_scale * 1.44269504088896341f;
 
-  // ---- resolve sources and per-stage validity masks (one stage per wave pass)
-  if (nst > 0) {
-    const int32_t* sel = topk + (size_t)t * k;
-    const int32_t* ptrow = pt + (size_t)ri.seq * MP;
-    for (int i0 = wave * 64; i0 < nst * kDecRows; i0 += 256) {
-      const int i = i0 + l, ii = i_begin + i;
-      int src = -1;
-      if (ii < i_end) {
-        const int j = sel[ii];
-        if (j >= 0 && j < ri.kv && j <= ri.abs_q)
-          src = clamp_page(ptrow[j / PS], num_pages) * PS + (j % PS);
-      }
-      const uint64_t m = __ballot(src >= 0);
-      const int first = m ? (int)__builtin_ctzll(m) : l;
-      const int fsrc = __shfl(src, first, DSA_WAVE);
-      // a stage without any valid selection still stages cache row 0 (read,
-      // never used), so that every stage issues the same loads
-      s_src[i] = src >= 0 ? src : (m ? fsrc : 0);
-      if (l == 0) s_mask[i0 / kDecRows] = m;
-    }
-  }
-  // ---- this lane's query fragments: head 16 hb + col, k values 32 i + 8 g ..
+  // ---- this wave's k steps [kb, kb + nk) of 32 latent columns
+  const int kb = wave < 2 ? 5 * wave : 4 * wave + 2;
+  const int nk = wave < 2 ? 5 : 4;
+  // ---- this lane's query fragments: head 16 hb + col, k values 32 (kb + u) + 8 g ..
+  // (issued first, so that their latency overlaps the resolution below)
   const int head = 16 * hb + col;
-  bf16x8 qf[DK / 32];
+  bf16x8 qf[5];
   {
     const uint16_t* qrow = q + ((size_t)t * H + (head < H ? head : 0)) * DK + 8 * g;
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i)
-      qf[i] = as_bf16x8(head < H && nst > 0 ? *reinterpret_cast<const uint4*>(qrow + 32 * i)
-                                            : zero_u4());
-    // complete these loads here: a first use inside the stage loop would make
-    // the compiler wait for every outstanding load there, ring loads included
-#pragma unroll
-    for (int i = 0; i < DK / 32; ++i) asm volatile("" : : "v"(qf[i]));
+    for (int u = 0; u < 5; ++u)
+      qf[u] = as_bf16x8(head < H && nst > 0 && u < nk
+                            ? *reinterpret_cast<const uint4*>(qrow + 32 * (kb + u))
+                            : zero_u4());
   }
+  // ---- resolve sources and per-stage validity masks: entry i = 64 (4 p + wave) + l
+  // of pass p (two stages per wave and pass), all selection loads first
+  if (nst > 0) {
+    const int32_t* sel = topk + (size_t)t * k;
+    const int32_t* ptrow = pt + (size_t)ri.seq * MP;
+    constexpr int NP = kDecMaxCH / 256;
+    int j[NP];
+#pragma unroll
+    for (int p2 = 0; p2 < NP; ++p2) {
+      const int ii = i_begin + 256 * p2 + 64 * wave + l;
+      j[p2] = ii < i_end ? sel[ii] : -1;
+    }
+    int src[NP];
+#pragma unroll
+    for (int p2 = 0; p2 < NP; ++p2) {
+      const int jj = j[p2];
+      const bool ok = jj >= 0 && jj < ri.kv && jj <= ri.abs_q;
+      src[p2] = ok ? clamp_page(ptrow[jj / PS], num_pages) * PS + (jj % PS) : -1;
+    }
+#pragma unroll
+    for (int p2 = 0; p2 < NP; ++p2) {
+      const int i = 256 * p2 + 64 * wave + l;
+      if (i - l >= nst * kDecRows) break;  // wave-uniform
+      const uint64_t m = __ballot(src[p2] >= 0);
+      const uint32_t mh = (uint32_t)(l < 32 ? m : m >> 32);  // this lane's stage
+      const int first = mh ? (int)__builtin_ctz(mh) + (l & 32) : l;
+      const int fsrc = __shfl(src[p2], first, DSA_WAVE);
+      // a stage without any valid selection still stages cache row 0 (read,
+      // never used), so that every stage issues the same loads
+      s_src[i] = src[p2] >= 0 ? src[p2] : (mh ? fsrc : 0);
+      if ((l & 31) == 0 && i < nst * kDecRows) s_mask[i / kDecRows] = mh;
+    }
+  }
+  // complete the query loads here: a first use inside the stage loop would
+  // make the compiler wait for every outstanding load there, ring loads included
+#pragma unroll
+  for (int u = 0; u < 5; ++u) asm volatile("" : : "v"(qf[u]));
   __syncthreads();
 
-  // per-lane LDS offsets. S^T reads: key row 16 wave + col, chunk 4 i + g.
+  // per-lane LDS offsets. S^T reads: key row col (+16 for the second tile),
+  // chunk 4 i + g of k step i (nope_x and rope_x of row 16 + col equal those
+  // of col).
   const int nx = nope_x(col), rx = rope_x(col);
-  int soff[4], roff[2];
+  int koff[5], kstep[5];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    soff[j] = (16 * wave + col) * NOPE_B + 64 * (j ^ (nx >> 2)) + 16 * ((g ^ nx) & 3);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    roff[j] = kDecRopeOff + (16 * wave + col) * ROPE_B + 16 * ((4 * j + g) ^ rx);
-  // V^T reads: key row 32 ks + 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
+  for (int u = 0; u < 5; ++u) {
+    const int i = kb + u;
+    koff[u] = i < 16 ? col * NOPE_B + 16 * ((4 * i + g) ^ nx)
+                     : kDecRopeOff + col * ROPE_B + 16 * ((4 * (i - 16) + g) ^ rx);
+    kstep[u] = i < 16 ? 16 * NOPE_B : 16 * ROPE_B;
+  }
+  // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
   const int vr = 4 * g + (col >> 2), vq = col & 3;
   const int vx = nope_x(vr);
   const int vbase = vr * NOPE_B + 256 * wave + 16 * ((vq >> 1) ^ (vx & 1)) + 8 * (vq & 1);
@@ -220,87 +240,98 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) o[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const uint32_t lds0 = lds_addr_of(ring[0]), lds1 = lds_addr_of(ring[1]);
+  const uint32_t lds_ring = lds_addr_of(ring[0]);
 
-  if (nst > 0) stage_rows(lds0, kv, row_stride, s_src, wave);
-  for (int st = 0; st < nst; ++st) {
-    const uint64_t mask = s_mask[st];
-    const unsigned char* buf = ring[st & 1];
-    wait_vmcnt<0>();
-    lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
-    if (st + 1 < nst)
-      stage_rows((st & 1) ? lds0 : lds1, kv, row_stride, s_src + (st + 1) * kDecRows, wave);
-    if (mask == 0) continue;
-    // ---- S^T for this wave's 16 keys
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < DK / 32; ++i) {
-      const int off = i < 16 ? soff[i & 3] + 256 * (i >> 2) : roff[i - 16];
-      sacc = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + off)), qf[i], sacc);
+  for (int s = 0; s < kDecRing - 1; ++s)
+    if (s < nst) stage_rows(lds_ring + s * kDecStage, kv, row_stride, s_src + s * kDecRows, wave);
+  for (int st = 0; st < nst; ++st) {
+    // stages st + 1 .. st + 2 were issued after this one
+    const int later = min(kDecRing - 2, nst - 1 - st);
+    if (later >= 2) wait_vmcnt<2 * kDecLoads>();
+    else if (later == 1) wait_vmcnt<kDecLoads>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
+    if (st + kDecRing - 1 < nst)
+      stage_rows(lds_ring + ((st + kDecRing - 1) % kDecRing) * kDecStage, kv, row_stride,
+                 s_src + (st + kDecRing - 1) * kDecRows, wave);
+    const uint32_t mask = s_mask[st];
+    if (mask == 0) continue;
+    const unsigned char* buf = ring[st % kDecRing];
+    // ---- this wave's part of S^T for the stage's 32 keys (two tiles)
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      if (u < nk) {
+        s0 = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u])), qf[u], s0);
+        s1 = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u] + kstep[u])), qf[u],
+                    s1);
+      }
     }
-    // ---- masked softmax over the stage's 64 keys (log2 units)
-    const uint32_t wm = (uint32_t)(mask >> (16 * wave + 4 * g));
-    float x[4];
+    s_part[wave][0][l] = s0;
+    s_part[wave][1][l] = s1;
+    lds_barrier();
+    s0 = s_part[0][0][l];
+    s1 = s_part[0][1][l];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) {
+      s0 += s_part[w2][0][l];
+      s1 += s_part[w2][1][l];
+    }
+    // ---- masked online softmax over the stage's 32 keys (log2 units)
+    const uint32_t m0 = mask >> (4 * g), m1 = mask >> (16 + 4 * g);
+    float x0[4], x1[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = ((wm >> r) & 1u) ? sacc[r] * scale2 : -INFINITY;
-      mx = fmaxf(mx, x[r]);
+      x0[r] = ((m0 >> r) & 1u) ? s0[r] * scale2 : -INFINITY;
+      x1[r] = ((m1 >> r) & 1u) ? s1[r] * scale2 : -INFINITY;
+      mx = fmaxf(mx, fmaxf(x0[r], x1[r]));
     }
     mx = fmaxf(mx, shfl_xor_f(mx, 16));
     mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (g == 0) s_mx[wave][col] = mx;
-    lds_barrier();
-    const float m_new = fmaxf(m_run, fmaxf(fmaxf(s_mx[0][col], s_mx[1][col]),
-                                           fmaxf(s_mx[2][col], s_mx[3][col])));
+    const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
-    float p[4];
+    float p0[4], p1[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_new);
-    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    for (int r = 0; r < 4; ++r) {
+      p0[r] = __builtin_amdgcn_exp2f(x0[r] - m_new);
+      p1[r] = __builtin_amdgcn_exp2f(x1[r] - m_new);
+    }
+    l_run = l_run * alpha + ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
     m_run = m_new;
-    uint2 pk;
-    pk.x = pack_bf16x2(p[0], p[1]);
-    pk.y = pack_bf16x2(p[2], p[3]);
-    s_pf[wave][l] = pk;
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+      for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
-    lds_barrier();
+        for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
+    }
+    uint4 pb4;
+    pb4.x = pack_bf16x2(p0[0], p0[1]);
+    pb4.y = pack_bf16x2(p0[2], p0[3]);
+    pb4.z = pack_bf16x2(p1[0], p1[1]);
+    pb4.w = pack_bf16x2(p1[2], p1[3]);
+    const bf16x8 pb = as_bf16x8(pb4);
     // ---- O^T (value columns 128 wave + 16 ct + 4 g + r, head col) += V^T P^T
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 pb4;
-      const uint2 lo = s_pf[2 * ks][l], hi = s_pf[2 * ks + 1][l];
-      pb4.x = lo.x;
-      pb4.y = lo.y;
-      pb4.z = hi.x;
-      pb4.w = hi.y;
-      const bf16x8 pb = as_bf16x8(pb4);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const int off = vbase + 32 * ks * NOPE_B + ((32 * ct) ^ vxor);
-        const v4s vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
-        const v4s vhi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off + 16 * NOPE_B));
-        bf16x8 va;
-        __builtin_memcpy(&va, &vlo, 8);
-        __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vhi, 8);
-        o[ct] = mfma16(va, pb, o[ct]);
-      }
+    for (int ct = 0; ct < 8; ++ct) {
+      const int off = vbase + ((32 * ct) ^ vxor);
+      const v4s vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
+      const v4s vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off + 16 * NOPE_B));
+      bf16x8 va;
+      __builtin_memcpy(&va, &vlo, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vhi, 8);
+      o[ct] = mfma16(va, pb, o[ct]);
     }
   }
-  // ---- partials: m (natural-log units), l summed over lanes and waves, O
+  // ---- partials: m (natural-log units), l summed over the lane groups, O
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
-  if (g == 0) s_l[wave][col] = l_run;
-  __syncthreads();
   const size_t base = ((size_t)t * nch + c) * H;
   if (head < H) {
     if (wave == 0 && g == 0) {
       part_ml[(base + head) * 2 + 0] = m_run * 0.693147180559945309f;
-      part_ml[(base + head) * 2 + 1] = s_l[0][col] + s_l[1][col] + s_l[2][col] + s_l[3][col];
+      part_ml[(base + head) * 2 + 1] = l_run;
     }
     float* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
 #pragma unroll
@@ -380,13 +411,13 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
 }
 
 int mla_decode_chunk(int T, int k) {
-  // about one workgroup per compute unit, 1 .. 8 stages of kDecRows each
+  // about one workgroup per compute unit, 1 .. 8 blocks of 64 selections each
   // (at most 8 to bound the partial (m, l, O) traffic of the combine)
-  const long nsub = (k + kDecRows - 1) / kDecRows;
+  const long nsub = (k + 63) / 64;
   long per = ((long)T * nsub + 255) / 256;
   if (per < 1) per = 1;
-  if (per > kDecMaxCH / kDecRows) per = kDecMaxCH / kDecRows;
-  return (int)per * kDecRows;
+  if (per > kDecMaxCH / 64) per = kDecMaxCH / 64;
+  return (int)per * 64;
 }
 
 hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
