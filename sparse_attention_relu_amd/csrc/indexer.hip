@@ -458,38 +458,67 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 }
 
 // ---------------------------------------------------------------------------
-// Tiled MFMA scorer for query chunks (extend). A workgroup owns TR = NW * QPW
-// consecutive packed rows and a range of RK key positions; every wave keeps
-// QPW query fragments in registers, and 64-key blocks of the owning
-// sequence's keys are staged once per workgroup through a double-buffered
-// LDS ring and reused by all its rows. Rows of a tile may belong to several
-// sequences: the tile is walked one sequence segment at a time.
-// grid = (ceil(cap / RK), ceil(T / TR)), block = NW * 64.
+// Tiled MFMA scorer for query chunks (extend). A workgroup of 8 waves owns 8
+// consecutive packed rows (wave w: row t0 + w, its query fragments and head
+// weights in registers) and a range of up to kTileMaxRK key positions. The
+// keys stream through a four-stage LDS ring of 64-key blocks by direct
+// global->LDS loads (three blocks in flight while one is multiplied), in the
+// swizzled layout of the streaming scorer, and every staged block serves all
+// 8 rows. A wave stores its row's 64 scores of a block with one instruction
+// (lane l: key l), so the waits on the ring count every outstanding memory
+// operation exactly: the key loads of later blocks plus the stores of the
+// last three blocks. Rows of a tile may belong to several sequences: the
+// tile is walked one sequence segment at a time.
+// grid = (ceil(cap / kTileMaxRK), ceil(T / 8)), block = 512.
 // ---------------------------------------------------------------------------
-template <int D, int HB, int QPW, int NW>
-__global__ __launch_bounds__(NW * 64) void idx_score_tiles(
+constexpr int kTileMaxRK = 2048;  // key range of one tile workgroup
+constexpr int kTileRows = 8;      // rows per workgroup, one per wave
+constexpr int kTileKB = 64;       // keys per staged block
+constexpr int kTileRing = 4;
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in 0 .. 15
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    default: wait_vm<15>(); break;
+  }
+}
+
+template <int D, int HB>
+__global__ __launch_bounds__(512, 2) void idx_score_tiles(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
-    int PS, int MP, int RK, float* __restrict__ scores, long ld) {
-  constexpr int KS = D / 16;
-  constexpr int HALF = D / 2;
-  constexpr int TR = NW * QPW;
-  constexpr int KB = 64;             // keys per LDS block
-  constexpr int RS = D + 8;          // LDS row stride in bf16 (16 B pad)
-  constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int LOADS = (KB * CPR + NW * 64 - 1) / (NW * 64);
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][KB * RS];
-  __shared__ __attribute__((aligned(16))) float s_w[TR][HB * 32];
-  __shared__ int s_seq[TR], s_nv[TR];
+    int PS, int MP, float* __restrict__ scores, long ld) {
+  constexpr int KS = D / 16, HALF = D / 2, RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;
+  constexpr int BLK = kTileKB * RB;      // bytes per staged block
+  constexpr int NLB = BLK / 1024;        // direct loads per block (D / 8)
+  constexpr int NLW = (NLB + 7) / 8;     // at most this many per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kTileRing][BLK];
+  __shared__ int s_pg[kTileMaxRK / 16 + 1];  // page-table entries of the key range
+  __shared__ int s_seq[kTileRows], s_nv[kTileRows];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int m = l & 31, hf = l >> 5;
-  const int t0 = blockIdx.y * TR;
+  const int t0 = blockIdx.y * kTileRows;
   const int cap = MP * PS;
-  if (tid < TR) {
+  if (tid < kTileRows) {
     const int t = t0 + tid;
     RowInfo ri;
     ri.seq = -1;
@@ -498,117 +527,114 @@ __global__ __launch_bounds__(NW * 64) void idx_score_tiles(
     s_seq[tid] = ri.seq;
     s_nv[tid] = ri.n_valid;
   }
-  // head weights of the tile's rows (0 for padding heads and rows)
-  for (int i = tid; i < TR * HB * 32; i += NW * 64) {
-    const int r = i / (HB * 32), h = i % (HB * 32);
-    const int t = t0 + r;
-    s_w[r][h] = (t < T && h < H) ? w[(size_t)t * H + h] : 0.0f;
-  }
   __syncthreads();
-  const int r_lo = blockIdx.x * RK;
+  const int k0 = blockIdx.x * kTileMaxRK;
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
+  const int lr = l / CPR, lc = l % CPR;
+  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
 
   int seg = 0;
-  while (seg < TR) {
-    const int s = s_seq[seg];
+  while (seg < kTileRows) {
+    const int s = __builtin_amdgcn_readfirstlane(s_seq[seg]);
     int seg_end = seg + 1;
-    while (seg_end < TR && s_seq[seg_end] == s) ++seg_end;
-    const int n_hi = s >= 0 ? s_nv[seg_end - 1] : 0;
-    const int k0 = r_lo, k1 = min(r_lo + RK, n_hi);
+    while (seg_end < kTileRows && s_seq[seg_end] == s) ++seg_end;
+    seg_end = __builtin_amdgcn_readfirstlane(seg_end);
+    const int n_hi = s >= 0 ? __builtin_amdgcn_readfirstlane(s_nv[seg_end - 1]) : 0;
+    const int k1 = min(k0 + kTileMaxRK, n_hi);
     if (s >= 0 && k0 < k1) {
-      // this wave's query rows inside the segment
-      bf16x8 a[QPW][HB][KS];
-      bool act[QPW];
-      int nv[QPW];
-#pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        const int r = wave * QPW + qi;
-        nv[qi] = s_nv[r];
-        act[qi] = (r >= seg) && (r < seg_end) && (nv[qi] > k0);
-        const int t = t0 + r;
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          const int head = 32 * hb + m;
-          const bool okq = act[qi] && head < H;
-          load_q_frag<D>(q + ((size_t)(okq ? t : 0) * H + (head < H ? head : 0)) * D + hf * HALF,
-                         okq, a[qi][hb]);
-        }
-      }
       const int32_t* ptrow = pt + (size_t)s * MP;
-
-      // staged loads of one 64-key block into registers, then LDS
-      uint4 stage[LOADS];
-      auto fetch = [&](int kb) {
+      const int pg0 = k0 / PS;
+      for (int i = tid; i <= (k1 - 1) / PS - pg0; i += 512) s_pg[i] = ptrow[pg0 + i];
+      // this wave's row, if it belongs to the segment
+      const int r = wave;
+      const int nv = s_nv[r];
+      const bool act = r >= seg && r < seg_end && nv > k0;
+      const int t = t0 + r;
+      bf16x8 a[HB][KS];
+      float wv[HB][16];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int idx = tid + i * NW * 64;
-          const int row = idx / CPR, c = idx % CPR;
-          const int j = kb + row;
-          uint4 v = zero_u4();
-          if (idx < KB * CPR && j < k1) {
-            const int page = clamp_page(ptrow[j / PS], num_pages);
-            v = *reinterpret_cast<const uint4*>(cache + ((size_t)page * PS + (j % PS)) * D + 8 * c);
-          }
-          stage[i] = v;
-        }
-      };
-      auto commit = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int idx = tid + i * NW * 64;
-          if (idx < KB * CPR) {
-            const int row = idx / CPR, c = idx % CPR;
-            *reinterpret_cast<uint4*>(&kbuf[buf][row * RS + 8 * c]) = stage[i];
-          }
-        }
-      };
-
-      fetch(k0);
-      commit(0);
-      __syncthreads();
-      int buf = 0;
-      for (int kb = k0; kb < k1; kb += KB) {
-        const bool more = kb + KB < k1;
-        if (more) fetch(kb + KB);
-#pragma unroll 1
-        for (int sb = 0; sb < KB / 32; ++sb) {
-          const int jrow = sb * 32 + m;
-          bf16x8 b[KS];
-#pragma unroll
-          for (int i = 0; i < KS; ++i)
-            b[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&kbuf[buf][jrow * RS + hf * HALF + 8 * i]));
-          const int j = kb + jrow;
-#pragma unroll
-          for (int qi = 0; qi < QPW; ++qi) {
-            if (!act[qi]) continue;
-            float part = 0.0f;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-              f32x16 acc = {};
-#pragma unroll
-              for (int i = 0; i < KS; ++i)
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[qi][hb][i], b[i], acc, 0, 0, 0);
-              // weights of accumulator rows 8 c + 4 hf + (0..3), c = 0..3
-              const float* wr = &s_w[wave * QPW + qi][32 * hb + 4 * hf];
-              float wv[16];
-#pragma unroll
-              for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 v = *reinterpret_cast<const float4*>(wr + 8 * c4);
-                wv[4 * c4 + 0] = v.x;
-                wv[4 * c4 + 1] = v.y;
-                wv[4 * c4 + 2] = v.z;
-                wv[4 * c4 + 3] = v.w;
-              }
-              part += relu_weighted_sum(acc, wv);
-            }
-            part += shfl_xor_f(part, 32);
-            if (hf == 0 && j < nv[qi])
-              scores[(size_t)(t0 + wave * QPW + qi) * ld + j] = part;
-          }
-        }
-        if (more) commit(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
+      for (int hb = 0; hb < HB; ++hb) {
+        const int head = 32 * hb + m;
+        const bool okq = act && head < H;
+        load_q_frag<D>(q + ((size_t)(okq ? t : 0) * H + (head < H ? head : 0)) * D + hf * HALF,
+                       okq, a[hb]);
+        load_head_weights(w + (size_t)(act ? t : 0) * H, H, hb, hf, wv[hb]);
       }
+      // complete these loads before the ring loads are issued
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+        for (int i = 0; i < KS; ++i) asm volatile("" : : "v"(a[hb][i]));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) asm volatile("" : : "v"(wv[hb][i]));
+      }
+      __syncthreads();  // s_pg ready
+
+      const int nb = (k1 - k0 + kTileKB - 1) / kTileKB;
+      const int nlw = wave < NLB % 8 || NLB % 8 == 0 ? NLW : NLW - 1;  // this wave's loads per block
+      // direct loads of block b: load I = wave + 8 n covers rows I * RPI .. of the block
+      auto stage = [&](int b) {
+        const uint32_t buf = lds_ring + (b % kTileRing) * BLK;
+#pragma unroll
+        for (int n = 0; n < NLW; ++n) {
+          const int I = wave + 8 * n;
+          if (I < NLB) {
+            int j0 = k0 + b * kTileKB + I * RPI;
+            if (j0 >= k1) j0 = k0;  // past the range: any staged row, never stored
+            const int page = clamp_page(s_pg[j0 / PS - pg0], num_pages);
+            const uint64_t src =
+                (uint64_t)(uintptr_t)(cache + ((size_t)page * PS + (j0 % PS)) * D);
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
+            gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
+                      (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                      __builtin_amdgcn_readfirstlane(buf + I * 1024));
+          }
+        }
+      };
+#pragma unroll
+      for (int b = 0; b < kTileRing - 1; ++b)
+        if (b < nb) stage(b);
+      float* srow = scores + (size_t)(act ? t : 0) * ld;
+      int hist = 0;  // bit i: this wave stored a block i + 1 iterations ago
+      for (int b = 0; b < nb; ++b) {
+        // outstanding after block b's loads: the loads of the blocks issued
+        // after it and the stores of the last three iterations
+        const int later = min(kTileRing - 2, nb - 1 - b);
+        wait_vm_dyn(later * nlw + __popc(hist & 7));
+        lds_sync();  // block b has landed for every wave; block b - 1 is consumed
+        if (b + kTileRing - 1 < nb) stage(b + kTileRing - 1);
+        hist <<= 1;
+        if (!act || k0 + b * kTileKB >= nv) continue;  // wave-uniform
+        const unsigned char* buf = ring[b % kTileRing];
+        float sc[kTileKB / 32];
+#pragma unroll
+        for (int sb = 0; sb < kTileKB / 32; ++sb) {
+          const int kr = sb * 32 + m;
+          bf16x8 bk[KS];
+#pragma unroll
+          for (int i = 0; i < KS; ++i) {
+            const int chunk = hf * HALF / 8 + i;
+            bk[i] = as_bf16x8(
+                *reinterpret_cast<const uint4*>(buf + kr * RB + 16 * (chunk ^ (kr % CPR))));
+          }
+          float part = 0.0f;
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int i = 0; i < KS; ++i)
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], bk[i], acc, 0, 0, 0);
+            part += relu_weighted_sum(acc, wv[hb]);
+          }
+          sc[sb] = part + shfl_xor_f(part, 32);  // both lane halves hold key sb * 32 + m
+        }
+        // lane l stores key l of the block (j < nv holds for lane 0 here)
+        const int j = k0 + b * kTileKB + l;
+        if (j < nv) srow[j] = hf ? sc[1] : sc[0];
+        hist |= 1;
+      }
+      __syncthreads();  // the ring is free for the next segment
     }
     seg = seg_end;
   }
@@ -1182,14 +1208,12 @@ static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
 
 template <int D, int HB>
 static hipError_t launch_tiles(const IndexerArgs& a, hipStream_t st) {
-  constexpr int QPW = 4 / HB, NW = 8, TR = QPW * NW;
   const int cap = a.MP * a.PS;
-  const int RK = 2048;
-  dim3 grid((cap + RK - 1) / RK, (a.T + TR - 1) / TR);
+  dim3 grid((cap + kTileMaxRK - 1) / kTileMaxRK, (a.T + kTileRows - 1) / kTileRows);
   ProfScope prof("idx_score_tiles", st);
-  hipLaunchKernelGGL((idx_score_tiles<D, HB, QPW, NW>), grid, dim3(NW * 64), 0, st, a.q, a.w,
-                     a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, RK,
-                     a.scores, a.ld);
+  hipLaunchKernelGGL((idx_score_tiles<D, HB>), grid, dim3(512), 0, st, a.q, a.w, a.cache,
+                     a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
+                     a.ld);
   return hipGetLastError();
 }
 
