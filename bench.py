@@ -42,8 +42,10 @@ def parse_args(argv=None):
                    help="extend workload measured beside it (0 = none)")
     p.add_argument("--ragged-config", type=int, default=3, choices=[0, 3],
                    help="ragged decode workload reported beside it (0 = none)")
+    p.add_argument("--long-config", type=int, default=5, choices=[0, 5],
+                   help="long-context extend with IndexShare layers (0: skip)")
     p.add_argument("--qb", type=int, default=256, help="query block of the extend layer")
-    p.add_argument("--only", choices=["all", "decode", "ragged", "extend", "copy"],
+    p.add_argument("--only", choices=["all", "decode", "ragged", "extend", "long", "copy"],
                    default="all",
                    help="run one workload alone (for per-workload profiles); 'copy' times a "
                         "plain 256 MiB device copy, the scale of the HBM byte counters")
@@ -118,6 +120,27 @@ def _kernel_times(dsa, step, steps):
     torch.cuda.synchronize()
     prof = dsa.profile_read()
     dsa.profile_enable(False)
+    return {k: (n, tot / n) for k, (n, tot) in prof.items()}
+
+
+def _kernel_times_cold(dsa, step, steps):
+    """The same per-kernel durations with the caches cold: a 1 GiB buffer
+    (four times the 256 MB infinity cache) is read before every step, outside
+    the library's timed launches. Reading, not writing, leaves the caches
+    holding clean lines, so the next kernel pays no write-back of the flush."""
+    import torch
+
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    dsa.profile_enable(True)
+    for _ in range(steps):
+        torch.sum(flush, dim=0, out=sink)  # a torch kernel: not one of the library's timed launches
+        step()
+    torch.cuda.synchronize()
+    prof = dsa.profile_read()
+    dsa.profile_enable(False)
+    del flush
     return {k: (n, tot / n) for k, (n, tot) in prof.items()}
 
 
@@ -202,6 +225,7 @@ def bench_decode(dsa, wl, args):
 
     ms = _timed(step, args.steps, args.warmup)
     kt = _kernel_times(dsa, step, args.steps)
+    kt_cold = _kernel_times_cold(dsa, step, max(5, args.steps // 5))
 
     # algorithmic work per launch
     nval = _row_valid_counts(wl, b.cu_q_lens)
@@ -224,6 +248,11 @@ def bench_decode(dsa, wl, args):
         if w:
             e.update(_roofline_entry(bound, w, avg))
             e["work"] = w
+        if name in kt_cold:
+            c = {"avg_us": round(kt_cold[name][1] * 1e3, 2)}
+            if w:
+                c["frac"] = _roofline_entry(bound, w, kt_cold[name][1])["frac"]
+            e["cold"] = c
         kernels[name] = e
     dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
     bound, w = work[dom]
@@ -243,7 +272,7 @@ def bench_decode(dsa, wl, args):
 # ----------------------------------------------------------------------------
 # extend
 # ----------------------------------------------------------------------------
-def bench_extend(dsa, wl, args, QB):
+def bench_extend(dsa, wl, args, QB, steps=None):
     import numpy as np
     import torch
 
@@ -273,7 +302,7 @@ def bench_extend(dsa, wl, args, QB):
             dsa.sparse_mla_extend(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
                                   d["cu"], units, counts, member, QB, wl.sm_scale, out=outs[i])
 
-    steps = max(2, args.steps // 4)
+    steps = steps or max(2, args.steps // 4)
     ms = _timed(step, steps, min(args.warmup, 2))
     kt = _kernel_times(dsa, step, steps)
     cnt = counts.cpu().numpy()
@@ -417,8 +446,12 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.only == "copy":
         return copy_calibration()
-    if args.only in ("ragged", "extend"):  # one side workload alone, its own line
-        if args.only == "ragged":
+    if args.only in ("ragged", "extend", "long"):  # one side workload alone, its own line
+        if args.only == "long":
+            wll = W.config(args.long_config or 5)
+            line = bench_extend(dsa, wll, args, 256, steps=max(2, args.steps // 10))
+            line["workload"] = wll.name
+        elif args.only == "ragged":
             wlr = W.config(args.ragged_config or 3)
             rd = bench_decode(dsa, wlr, args)
             line = {"workload": wlr.name, "tok_s": round(rd["tok_s"], 1),
@@ -467,6 +500,11 @@ def main(argv=None):
         ext = bench_extend(dsa, wle, args, qb)
         ext["workload"] = wle.name
         result["extend"] = ext
+    if args.only == "all" and args.long_config:
+        wll = W.config(args.long_config)
+        lng = bench_extend(dsa, wll, args, 256, steps=max(2, args.steps // 10))
+        lng["workload"] = wll.name
+        result["long_extend"] = lng
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
