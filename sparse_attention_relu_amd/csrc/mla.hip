@@ -508,7 +508,7 @@ __device__ __forceinline__ PageMeta page_meta(const int32_t* __restrict__ units,
 // Metadata of a union slot as loaded (clamped key, its page-table entry and
 // its sequence length), fetched a step ahead of its use.
 struct SlotRaw {
-  int key, ptv, slv;
+  int key, sp, lp, ptv, slv;  // key = sp * MP + lp
 };
 
 __device__ __forceinline__ int clamp_key(int key, int S, int MP) {
@@ -520,16 +520,18 @@ __device__ __forceinline__ SlotRaw slot_raw(const int32_t* __restrict__ pt,
                                             int MP) {
   SlotRaw r;
   r.key = key;
+  r.sp = key / MP;
+  r.lp = key - r.sp * MP;
   r.ptv = pt[key];
-  r.slv = seq_lens[key / MP];
+  r.slv = seq_lens[r.sp];
   return r;
 }
 
 __device__ __forceinline__ PageMeta meta_from_raw(const SlotRaw& r, int MP, int cap,
                                                   int num_pages) {
   PageMeta pm;
-  pm.sp = r.key / MP;
-  pm.lp = r.key % MP;
+  pm.sp = r.sp;
+  pm.lp = r.lp;
   pm.kvp = r.slv < 0 ? 0 : (r.slv > cap ? cap : r.slv);
   pm.page = clamp_page(r.ptv, num_pages);
   return pm;
@@ -572,7 +574,7 @@ __device__ __forceinline__ void stage_page(uint32_t buf, const uint16_t* __restr
 // the matrix work of a step instead of stalling the wave in one burst.
 struct StageCtx {
   const unsigned char* pg;
-  size_t rs;
+  uint32_t rs;  // bytes per cache row; a page (PS <= 64 rows) spans far less than 4 GiB
   uint32_t buf;
   int valid_rows, wave;
 };
@@ -582,7 +584,7 @@ __device__ __forceinline__ StageCtx stage_ctx(uint32_t buf, const uint16_t* __re
                                               int wave) {
   StageCtx c;
   c.pg = reinterpret_cast<const unsigned char*>(kv + (size_t)pm.page * PS * row_stride);
-  c.rs = (size_t)row_stride * 2;
+  c.rs = (uint32_t)row_stride * 2u;
   c.buf = buf;
   c.valid_rows = min(PS, pm.kvp - pm.lp * PS);
   c.wave = wave;
@@ -592,14 +594,14 @@ __device__ __forceinline__ StageCtx stage_ctx(uint32_t buf, const uint16_t* __re
 __device__ __forceinline__ void stage_one(const StageCtx& c, int n, int l) {
   if (n < PROWS / XW) {
     const int r = XW * n + c.wave;
-    const int use = r < c.valid_rows ? r : 0;
+    const uint32_t use = r < c.valid_rows ? (uint32_t)r : 0u;
     gll16_s((16u * (uint32_t)l) ^ (16u * (uint32_t)nope_x(r)), c.pg + use * c.rs,
             c.buf + r * NOPE_B);
   } else {
     const int G = c.wave + XW * (n - PROWS / XW);
     const int r = 8 * G + (l >> 3);
     const int use = r < c.valid_rows ? r : 0;
-    gll16_s((uint32_t)(use * (int)c.rs) + 2 * DV + 16u * (uint32_t)((l & 7) ^ rope_x(r)), c.pg,
+    gll16_s((uint32_t)use * c.rs + 2 * DV + 16u * (uint32_t)((l & 7) ^ rope_x(r)), c.pg,
             c.buf + ROPE_OFF + G * 1024);
   }
 }
