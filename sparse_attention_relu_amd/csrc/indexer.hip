@@ -855,7 +855,9 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const f
     }
     if (tid == 0) bstart[4096] = total;
     __syncthreads();
-    if (big > 0) atomicMax(&s_flag[0], big);
+    // one flag store per wave that holds an oversized candidate bucket (a
+    // single-address atomic from every thread would serialise)
+    if (__ballot(big > kDirectBucketMax) != 0 && lane_id() == 0) s_flag[0] = 1;
     // the bucket holding place k - 1 ends the scattered range
     int r2 = run;
 #pragma unroll
@@ -865,7 +867,7 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const f
     }
     __syncthreads();
   }
-  if (s_flag[0] > kDirectBucketMax) return false;
+  if (s_flag[0] != 0) return false;
   const int lim = s_flag[1];
   for (int c0 = 0; c0 < n; c0 += kSelChunk) {
     uint32_t keys[kSelM];
@@ -1121,10 +1123,10 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       s_dig[0] = 0;
     }
     __syncthreads();
-    if (big > 0) atomicMax(&s_dig[0], big);
+    if (__ballot(big > kRankBucketMax) != 0 && lane_id() == 0) s_dig[0] = 1;
     __syncthreads();
   }
-  if (s_dig[0] <= kRankBucketMax) {
+  if (s_dig[0] == 0) {  // no bucket above kRankBucketMax
     for (int i = tid; i < count; i += NT) {
       const uint32_t key = list_key[i];
       const uint32_t slot = atomicAdd(&cursor[(kmax - key) >> sh], 1u);
