@@ -888,8 +888,12 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const f
     const uint64_t cm = scomp[sl];
     const int b = bucket((uint32_t)(cm >> 32));
     const int b0 = bstart[b], b1 = bstart[b + 1];
-    int r = 0;
-    for (int u = b0; u < b1; ++u) r += scomp[u] > cm;
+    int r = 0, u = b0;
+    for (; u + 4 <= b1; u += 4) {  // four independent reads in flight
+      const uint64_t c0 = scomp[u], c1 = scomp[u + 1], c2 = scomp[u + 2], c3 = scomp[u + 3];
+      r += (int)(c0 > cm) + (int)(c1 > cm) + (int)(c2 > cm) + (int)(c3 > cm);
+    }
+    for (; u < b1; ++u) r += scomp[u] > cm;
     if (b0 + r < k) orow[b0 + r] = (int)(~(uint32_t)cm);
   }
   for (int i = n + tid; i < k; i += NT) orow[i] = -1;
