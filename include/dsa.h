@@ -85,8 +85,8 @@ int dsa_abi_version(void);
  *   max_q_len  host upper bound on q_len(s) over the batch (a hint that picks
  *              the streaming per-row kernel when <= 1 and the MFMA tile
  *              kernel otherwise; any value gives the same result)
- * Supported: H in {1..64} with H % 32 == 0 or H <= 32, D % 32 == 0 and
- * D <= 256, PS % 16 == 0, 1 <= k <= 4096.
+ * Supported: 1 <= H <= 64, D in {32, 64, 128}, PS a multiple of 16,
+ * MP * PS <= 2^24, 1 <= k <= 4096; otherwise DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
                                   int max_q_len);
@@ -119,8 +119,8 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
  *   blk_units   int32 [nQB, u_max]       output
  *   blk_counts  int32 [nQB]              output
  *   blk_member  uint64 [nQB, u_max, QB]  output
- * Supported: PS in {16, 32, 48, 64}, S * MP <= 2^20, u_max <= 16384,
- * QB <= 1024.
+ * Supported: PS <= 64 (one 64-bit membership word per page), S * MP <= 2^18,
+ * 1 <= u_max <= 8192, 1 <= QB <= 1024; otherwise DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_block_union_workspace(int T, int S, int MP, int QB, int u_max);
 int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t* cu_q_lens,
@@ -147,7 +147,8 @@ int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t*
  *   kv_cache   bf16 [num_pages, PS, row_stride], row_stride >= 576
  *   topk       int32 [T, k]
  *   out        bf16 [T, H, 512]  output
- * Supported: H in {16, 32, 48, 64} or H <= 16, PS % 16 == 0, k <= 65536.
+ * Supported: 1 <= H <= 64, MP * PS <= 2^24, 1 <= k <= 65536; otherwise
+ * DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_sparse_mla_decode_workspace(int T, int H, int k);
 int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, int num_pages,
@@ -171,8 +172,8 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
  *   q, kv_cache, out   as in dsa_sparse_mla_decode
  *   blk_*              as produced by dsa_block_union with the same
  *                      (T, QB, u_max, PS, MP)
- * Supported: H == 16 or H == 32 ... (H % 16 == 0, H <= 64), PS in
- * {16, 32, 48, 64}, QB * H % 64 == 0 or QB * H <= 64.
+ * Supported: 1 <= H <= 64, PS <= 64, 1 <= QB <= 1024, S * MP <= 2^24;
+ * otherwise DSA_ERR_UNSUPPORTED.
  */
 size_t dsa_sparse_mla_extend_workspace(int T, int H, int QB, int u_max);
 int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, int num_pages,

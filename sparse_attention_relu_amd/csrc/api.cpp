@@ -93,6 +93,8 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
   if (D != 32 && D != 64 && D != 128)
     return fail(DSA_ERR_UNSUPPORTED, "indexer D=%d not in {32, 64, 128}", D);
   if (k < 1 || k > 4096) return fail(DSA_ERR_UNSUPPORTED, "k=%d not in [1, 4096]", k);
+  // one direct load stages up to 16 consecutive key rows of one page
+  if (PS % 16 != 0) return fail(DSA_ERR_UNSUPPORTED, "indexer PS=%d is not a multiple of 16", PS);
   if (T == 0) return ok();
   if (!q_idx || !w || !idx_cache || !page_table || !seq_lens || !cu_q_lens || !topk)
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");

@@ -48,6 +48,7 @@ def test_indexer_validation(lib):
     assert _idx_call(lib, k=0) == _lib.DSA_ERR_UNSUPPORTED
     assert _idx_call(lib, k=5000) == _lib.DSA_ERR_UNSUPPORTED
     assert _idx_call(lib, H=65) == _lib.DSA_ERR_UNSUPPORTED
+    assert _idx_call(lib, PS=24) == _lib.DSA_ERR_UNSUPPORTED  # a load stages 16 rows of one page
     assert _idx_call(lib, T=-1) == _lib.DSA_ERR_INVALID_ARG
     assert _idx_call(lib, q=None) == _lib.DSA_ERR_INVALID_ARG
     assert _idx_call(lib, q=(1 << 12) + 2) == _lib.DSA_ERR_INVALID_ARG  # misaligned
