@@ -341,71 +341,86 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
 }
 
 // grid = (T, H), block = 256: merge the nch partials of (t, h),
-//   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0.
-// Thread (g, d4) = (tid / 128, tid % 128) folds chunks g, g + 2, ... for value
-// columns 4 d4 .. 4 d4 + 3 with a running maximum, issuing all loads of a batch
-// of kCombU chunks at once; the two halves then merge through LDS.
-constexpr int kCombU = 16;
-
-__device__ __forceinline__ void merge_partial(float& M, float& L, float4& o, float m, float l,
-                                              const float4& v) {
-  if (!(l > 0.f)) return;
-  const float mn = fmaxf(M, m);
-  const float a = M == -INFINITY ? 0.f : __expf(M - mn);
-  const float b = __expf(m - mn);
-  L = L * a + l * b;
-  o.x = o.x * a + v.x * b;
-  o.y = o.y * a + v.y * b;
-  o.z = o.z * a + v.z * b;
-  o.w = o.w * a + v.w * b;
-  M = mn;
-}
+//   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0,
+// M = max m_c. The chunk weights e^(m_c - M) are computed once, in LDS; then
+// thread (g, d4) = (tid / 128, tid % 128) sums chunks g, g + 2, ... for
+// value columns 4 d4 .. 4 d4 + 3 with all its loads independent, and the two
+// halves meet through LDS.
+constexpr int kCombMaxCH = 1024;  // partials per (row, head) the combine handles
 
 __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int H, int nch,
                                                           uint16_t* __restrict__ out) {
+  __shared__ float s_w[kCombMaxCH];
   __shared__ float4 s_o[128];
-  __shared__ float s_ml[2];
+  __shared__ float s_red[8];
+  __shared__ float s_l;
   const int t = blockIdx.x, h = blockIdx.y;
-  const int g = threadIdx.x >> 7, d4 = threadIdx.x & 127;
+  const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
   const size_t base = (size_t)t * nch * H;
-  float M = -INFINITY, L = 0.f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = g; c0 < nch; c0 += 2 * kCombU) {
-    float m[kCombU], l[kCombU];
-    float4 v[kCombU];
+  // ---- M = max over live chunks (l_c > 0)
+  float mloc = -INFINITY;
+  for (int c = tid; c < nch; c += 256) {
+    const size_t r = base + (size_t)c * H + h;
+    const float m = part_ml[r * 2], lc = part_ml[r * 2 + 1];
+    const float mm = lc > 0.f ? m : -INFINITY;
+    s_w[c] = mm;
+    mloc = fmaxf(mloc, mm);
+  }
 #pragma unroll
-    for (int u = 0; u < kCombU; ++u) {
+  for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
+  if (l == 0) s_red[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  // ---- weights and L = sum_c w_c l_c
+  float lloc = 0.f;
+  for (int c = tid; c < nch; c += 256) {
+    const size_t r = base + (size_t)c * H + h;
+    const float w = s_w[c] == -INFINITY ? 0.f : __expf(s_w[c] - M);
+    s_w[c] = w;
+    lloc += w * part_ml[r * 2 + 1];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lloc += shfl_xor_f(lloc, o);
+  __syncthreads();  // every M is read; s_red is free
+  if (l == 0) s_red[4 + wave] = lloc;
+  __syncthreads();
+  if (tid == 0) s_l = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+  // ---- O: this thread's half of the chunks, independent loads
+  const int g = tid >> 7, d4 = tid & 127;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // (a chunk without live selections has w = 0 and a zero partial O)
+  for (int c0 = g; c0 < nch; c0 += 8) {
+    float w[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       const int c = c0 + 2 * u;
+      w[u] = 0.f;
+      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (c < nch) {
-        const size_t r = base + (size_t)c * H + h;
-        m[u] = part_ml[r * 2];
-        l[u] = part_ml[r * 2 + 1];
-        v[u] = *reinterpret_cast<const float4*>(part_o + r * DV + 4 * d4);
-      } else {
-        m[u] = -INFINITY;
-        l[u] = 0.f;
-        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        w[u] = s_w[c];
+        v[u] = *reinterpret_cast<const float4*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4);
       }
     }
 #pragma unroll
-    for (int u = 0; u < kCombU; ++u) merge_partial(M, L, o, m[u], l[u], v[u]);
-  }
-  if (g == 1) {
-    s_o[d4] = o;
-    if (d4 == 0) {
-      s_ml[0] = M;
-      s_ml[1] = L;
+    for (int u = 0; u < 4; ++u) {
+      acc.x = fmaf(w[u], v[u].x, acc.x);
+      acc.y = fmaf(w[u], v[u].y, acc.y);
+      acc.z = fmaf(w[u], v[u].z, acc.z);
+      acc.w = fmaf(w[u], v[u].w, acc.w);
     }
   }
+  if (g == 1) s_o[d4] = acc;
   __syncthreads();
   if (g == 0) {
-    merge_partial(M, L, o, s_ml[0], s_ml[1], s_o[d4]);
+    const float4 b = s_o[d4];
+    const float L = s_l;
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     uint2 packed;
-    packed.x = pack_bf16x2(o.x * inv, o.y * inv);
-    packed.y = pack_bf16x2(o.z * inv, o.w * inv);
+    packed.x = pack_bf16x2((acc.x + b.x) * inv, (acc.y + b.y) * inv);
+    packed.y = pack_bf16x2((acc.z + b.z) * inv, (acc.w + b.w) * inv);
     *reinterpret_cast<uint2*>(out + ((size_t)t * H + h) * DV + 4 * d4) = packed;
   }
 }
