@@ -278,6 +278,8 @@ MLA_CASES = {
     "h4_ps16": (2, [90, 333], 16, 24, [2, 5], 4, 40, 0, 64),
     "h32_ps32": (2, [500, 260], 32, 16, [4, 4], 32, 96, 1, 0),
     "h64_ps64": (1, [3000], 64, 50, [3], 64, 300, 0, 0),
+    # a partial second 16-head block, PS = 48, padded rows, a row past the end
+    "h20_ps48": (2, [777, 1300], 48, 30, [3, 2], 20, 260, 1, 8),
 }
 
 
@@ -329,6 +331,8 @@ EXTEND_CASES = {
     "h32_qb5_partial_tile": ("h32_ps32", 5, None),
     "h64_qb2": ("h64_ps64", 2, None),
     "h16_lossy_umax": ("h16_ps64_multi", 8, 5),
+    "h4_ps16_qb16": ("h4_ps16", 16, None),
+    "h20_ps48_qb3": ("h20_ps48", 3, None),
 }
 
 
