@@ -20,31 +20,55 @@ __global__ void union_clear(uint64_t* __restrict__ bits, long n) {
     bits[i] = 0ull;
 }
 
-// grid = (nQB, ceil(QB / RPW)), block = 256; LDS bitmap of NW words.
+// grid = (nQB, ceil(QB / RPW)), block = 256; LDS bitmap of NW words. The
+// sequences of the workgroup's rows are looked up in parallel first; then
+// one flat loop over (row, selection) pairs keeps many loads in flight.
+constexpr int kUnionRowsMax = 1024;  // rows of one workgroup (QB <= 1024)
+constexpr int kUnionWordsLds = 512;  // bitmap words staged in LDS by union_member
+
 __global__ __launch_bounds__(256) void union_mark(const int32_t* __restrict__ topk,
                                                   const int32_t* __restrict__ seq_lens,
                                                   const int32_t* __restrict__ cu, int T, int S,
                                                   int k, int PS, int MP, int QB, int RPW, int NW,
                                                   uint64_t* __restrict__ bits) {
   extern __shared__ uint64_t lbits[];
+  __shared__ int s_seq[kUnionRowsMax];
   const int b = blockIdx.x;
   const int r0 = blockIdx.y * RPW;
-  const int r1 = min(r0 + RPW, QB);
-  for (int i = threadIdx.x; i < NW; i += 256) lbits[i] = 0ull;
-  __syncthreads();
+  const int nr = max(0, min(min(r0 + RPW, QB), T - b * QB) - r0);  // live rows
   const int cap = MP * PS;
-  for (int r = r0; r < r1; ++r) {
-    const int t = b * QB + r;
-    if (t >= T) break;
-    const RowInfo ri = row_info(cu, seq_lens, S, t, cap);
-    if (ri.seq < 0) continue;
-    const int32_t* sel = topk + (size_t)t * k;
-    for (int i = threadIdx.x; i < k; i += 256) {
-      const int j = sel[i];
-      if (j < 0 || j >= cap) continue;
-      const int key = ri.seq * MP + j / PS;
-      atomicOr(reinterpret_cast<unsigned long long*>(&lbits[key >> 6]), 1ull << (key & 63));
+  for (int i = threadIdx.x; i < NW; i += 256) lbits[i] = 0ull;
+  for (int r = threadIdx.x; r < nr; r += 256)
+    s_seq[r] = row_info(cu, seq_lens, S, b * QB + r0 + r, cap).seq;
+  __syncthreads();
+  const int32_t* sel = topk + ((size_t)b * QB + r0) * k;
+  auto mark = [&](int idx, int j) {
+    const int seq = s_seq[idx / k];
+    if (seq < 0 || j < 0 || j >= cap) return;
+    const int key = seq * MP + j / PS;
+    atomicOr(reinterpret_cast<unsigned long long*>(&lbits[key >> 6]), 1ull << (key & 63));
+  };
+  const int n = nr * k;
+  if ((k & 3) == 0 && ((uintptr_t)topk & 15) == 0) {  // 16-byte loads, issued first
+    constexpr int U = 4;
+    for (int i0 = 4 * threadIdx.x; i0 < n; i0 += 4 * 256 * U) {
+      int4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 4 * 256 * u;
+        v[u] = i < n ? *reinterpret_cast<const int4*>(sel + i) : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 4 * 256 * u;
+        mark(i, v[u].x);
+        mark(i + 1, v[u].y);
+        mark(i + 2, v[u].z);
+        mark(i + 3, v[u].w);
+      }
     }
+  } else {
+    for (int idx = threadIdx.x; idx < n; idx += 256) mark(idx, sel[idx]);
   }
   __syncthreads();
   uint64_t* gb = bits + (size_t)b * NW;
@@ -86,38 +110,70 @@ __global__ __launch_bounds__(256) void union_compact(const uint64_t* __restrict_
 }
 
 // grid = (nQB, ceil(QB / QPW)), block = 256; LDS tile [u_max][QPW] uint64.
+// As in union_mark, the rows' sequences are looked up in parallel and one
+// flat loop covers every (query, selection) pair.
 __global__ __launch_bounds__(256) void union_member(
     const int32_t* __restrict__ topk, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, int T, int S, int k, int PS, int MP, int QB, int u_max,
     int QPW, int NW, const uint64_t* __restrict__ bits, const int32_t* __restrict__ prefix,
     const int32_t* __restrict__ counts, uint64_t* __restrict__ member) {
   extern __shared__ uint64_t tile[];
+  __shared__ int s_seq[kUnionRowsMax];
+  __shared__ uint64_t s_bits[kUnionWordsLds];
+  __shared__ int32_t s_pre[kUnionWordsLds];
   const int b = blockIdx.x;
   const int q0 = blockIdx.y * QPW;
   const int nq = min(QPW, QB - q0);
+  const int nlive = max(0, min(nq, T - b * QB - q0));  // queries that are rows of the batch
   const int u_lim = min(counts[b], u_max);
-  for (int i = threadIdx.x; i < u_lim * QPW; i += 256) tile[i] = 0ull;
-  __syncthreads();
   const int cap = MP * PS;
-  const uint64_t* gb = bits + (size_t)b * NW;
-  const int32_t* gp = prefix + (size_t)b * NW;
-  for (int qi = 0; qi < nq; ++qi) {
-    const int t = b * QB + q0 + qi;
-    if (t >= T) break;
-    const RowInfo ri = row_info(cu, seq_lens, S, t, cap);
-    if (ri.seq < 0) continue;
-    const int32_t* sel = topk + (size_t)t * k;
-    for (int i = threadIdx.x; i < k; i += 256) {
-      const int j = sel[i];
-      if (j < 0 || j >= cap) continue;
-      const int key = ri.seq * MP + j / PS;
-      const int wd = key >> 6, bit = key & 63;
-      const uint64_t below = bit ? (gb[wd] & (~0ull >> (64 - bit))) : 0ull;
-      const int slot = gp[wd] + __popcll(below);
-      if (slot < u_lim)
-        atomicOr(reinterpret_cast<unsigned long long*>(&tile[slot * QPW + qi]),
-                 1ull << (j % PS));
+  for (int i = threadIdx.x; i < u_lim * QPW; i += 256) tile[i] = 0ull;
+  for (int qi = threadIdx.x; qi < nlive; qi += 256)
+    s_seq[qi] = row_info(cu, seq_lens, S, b * QB + q0 + qi, cap).seq;
+  __syncthreads();
+  // the block's bitmap words and their rank prefixes, from LDS when they fit
+  const bool in_lds = NW <= kUnionWordsLds;
+  if (in_lds)
+    for (int i = threadIdx.x; i < NW; i += 256) {
+      s_bits[i] = bits[(size_t)b * NW + i];
+      s_pre[i] = prefix[(size_t)b * NW + i];
     }
+  __syncthreads();
+  const uint64_t* gb = in_lds ? s_bits : bits + (size_t)b * NW;
+  const int32_t* gp = in_lds ? s_pre : prefix + (size_t)b * NW;
+  const int32_t* sel = topk + ((size_t)b * QB + q0) * k;
+  auto add = [&](int idx, int j) {
+    const int qi = idx / k;
+    const int seq = s_seq[qi];
+    if (seq < 0 || j < 0 || j >= cap) return;
+    const int key = seq * MP + j / PS;
+    const int wd = key >> 6, bit = key & 63;
+    const uint64_t below = bit ? (gb[wd] & (~0ull >> (64 - bit))) : 0ull;
+    const int slot = gp[wd] + __popcll(below);
+    if (slot < u_lim)
+      atomicOr(reinterpret_cast<unsigned long long*>(&tile[slot * QPW + qi]), 1ull << (j % PS));
+  };
+  const int n = nlive * k;
+  if ((k & 3) == 0 && ((uintptr_t)topk & 15) == 0) {  // 16-byte loads, issued first
+    constexpr int U = 4;
+    for (int i0 = 4 * threadIdx.x; i0 < n; i0 += 4 * 256 * U) {
+      int4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 4 * 256 * u;
+        v[u] = i < n ? *reinterpret_cast<const int4*>(sel + i) : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + 4 * 256 * u;
+        add(i, v[u].x);
+        add(i + 1, v[u].y);
+        add(i + 2, v[u].z);
+        add(i + 3, v[u].w);
+      }
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < n; idx += 256) add(idx, sel[idx]);
   }
   __syncthreads();
   uint64_t* mb = member + (size_t)b * u_max * QB;
@@ -149,7 +205,7 @@ hipError_t block_union(const UnionArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int RPW = 16;
+  const int RPW = 4;
   {
     ProfScope prof("union_mark", st);
     hipLaunchKernelGGL(union_mark, dim3(nqb, (a.QB + RPW - 1) / RPW), dim3(256),
