@@ -657,14 +657,13 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
 // a stable block radix sort over the bits in which the keys differ orders the
 // list instead.
 //
-// Each thread owns kSelM consecutive positions of a chunk; the first chunk
-// (the whole row when it has at most kSelNT * kSelM positions) is read once
-// and kept in registers for every pass.
+// Each thread owns M consecutive positions of a chunk (M = 8 when a score
+// row holds at most 8192 positions, else 16); the first chunk (the whole row
+// when it has at most kSelNT * M positions) is read once, before the row's
+// bounds are known, and kept in registers for every pass.
 // grid = T, block = 1024, dynamic LDS = select_lds_bytes(k).
 // ---------------------------------------------------------------------------
 constexpr int kSelNT = 1024;
-constexpr int kSelM = 16;  // consecutive positions per thread in a chunk
-constexpr int kSelChunk = kSelNT * kSelM;
 
 // Bin d of an nb-bin histogram holding the need-th largest key (counting
 // from the top bin down); writes (d, count above d) to out[0..1].
@@ -699,13 +698,13 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nb, int nee
   __syncthreads();
 }
 
-// Keys of positions c0 + kSelM * tid + e (e < kSelM); positions >= n get 0.
-__device__ __forceinline__ void load_keys(const float* row, int n, int c0,
-                                          uint32_t (&keys)[kSelM]) {
-  const int j0 = c0 + threadIdx.x * kSelM;
-  if (j0 + kSelM <= n) {
+// Keys of positions c0 + M * tid + e (e < M); positions >= n get 0.
+template <int M>
+__device__ __forceinline__ void load_keys(const float* row, int n, int c0, uint32_t (&keys)[M]) {
+  const int j0 = c0 + threadIdx.x * M;
+  if (j0 + M <= n) {
 #pragma unroll
-    for (int e = 0; e < kSelM; e += 4) {
+    for (int e = 0; e < M; e += 4) {
       const float4 v = *reinterpret_cast<const float4*>(row + j0 + e);
       keys[e] = score_order_bits(v.x);
       keys[e + 1] = score_order_bits(v.y);
@@ -714,14 +713,36 @@ __device__ __forceinline__ void load_keys(const float* row, int n, int c0,
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < kSelM; ++e) keys[e] = (j0 + e < n) ? score_order_bits(row[j0 + e]) : 0u;
+    for (int e = 0; e < M; ++e) keys[e] = (j0 + e < n) ? score_order_bits(row[j0 + e]) : 0u;
+  }
+}
+
+// Keys of the first chunk, read before the row's length is known: every
+// position below `lim` (the workspace row length capped at the chunk, a
+// multiple of M) is loaded. Keys at positions >= n hold whatever the
+// workspace holds there; every later use of them is guarded by j < n.
+template <int M>
+__device__ __forceinline__ void load_keys_ahead(const float* row, int lim, uint32_t (&keys)[M]) {
+  const int j0 = threadIdx.x * M;
+  if (j0 < lim) {
+#pragma unroll
+    for (int e = 0; e < M; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + j0 + e);
+      keys[e] = score_order_bits(v.x);
+      keys[e + 1] = score_order_bits(v.y);
+      keys[e + 2] = score_order_bits(v.z);
+      keys[e + 3] = score_order_bits(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < M; ++e) keys[e] = 0u;
   }
 }
 
 template <int IPT>
 struct SelectCfg {
   static constexpr int CAP = kSelNT * IPT;  // list capacity
-  static_assert(CAP <= kSelChunk, "the short-row path keeps the row in one chunk");
+  static_assert(CAP <= kSelNT * 8, "the short-row path keeps the row in one chunk");
   using Sorter = rocprim::block_radix_sort<uint32_t, kSelNT, IPT, int>;
   // LDS: list key/pos [CAP] | hist/cursor [4096] | bucket start [4096 + 64]
   //      | bucket-ordered key [CAP] | bucket-ordered list index (u16) [CAP]
@@ -756,41 +777,58 @@ __device__ __forceinline__ float order_key_value(uint32_t key) {
 }
 
 // Direct rank of a row of n <= kDirectMaxN positions. Thread tid owns
-// positions c0 + kSelM * tid + e of every chunk c0; the first chunk's keys
-// are in registers, later chunks are read again from the row. Scores are
-// bucketed by value, b = (vmax - v) * 4095.5 / (vmax - vmin) (monotone, so
-// equal scores share a bucket and a larger score never lands in a later
-// bucket). Only positions whose bucket starts below k can be in the answer;
-// each one's place is its bucket's start plus the number of bucket members
-// ahead of it (larger key, or equal key and smaller position: one comparison
-// of the composite key << 32 | ~position). Returns false, having written
+// positions c0 + M * tid + e of every chunk c0; the first chunk's keys are in
+// registers, later chunks are read again from the row. Scores are bucketed
+// by value, b = (vmax - v) * 4095.5 / (vmax - vmin) (monotone, so equal
+// scores share a bucket and a larger score never lands in a later bucket).
+// Only positions whose bucket starts below k can be in the answer; each
+// one's place is its bucket's start plus the number of bucket members ahead
+// of it (larger key, or equal key and smaller position: one comparison of
+// the composite key << 32 | ~position). Returns false, having written
 // nothing, when the spread is degenerate or a candidate bucket holds more
-// than kDirectBucketMax positions.
+// than kDirectBucketMax positions. Five block barriers. When the row fits one
+// chunk, the histogram's atomic returns each key's offset inside its bucket,
+// so the candidates are placed without a second round of atomics.
 constexpr int kDirectMaxN = 1 << 17;
 
-template <int NT>
-__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const float* row, int n,
+struct DirectShared {
+  uint32_t red[2][kSelNT / 64];  // per-wave key minimum / maximum
+  int wsum[kSelNT / 64];         // per-wave bucket-count sums
+  int wbig[kSelNT / 64];         // per-wave "oversized candidate bucket" flags
+  int lim;                       // end of the bucket holding place k - 1
+  int blast;                     // that bucket (candidates are the buckets up to it)
+};
+
+template <int NT, int M>
+__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float* row, int n,
                                             int k, uint32_t* lds, size_t cur_off,
-                                            size_t start_off, size_t key_off, int* s_scan,
-                                            uint32_t (*s_red)[NT / 64], int* s_flag,
+                                            size_t start_off, size_t key_off, DirectShared& sh,
                                             int32_t* __restrict__ orow) {
-  const int tid = threadIdx.x;
+  constexpr int C = NT * M;
+  constexpr int BPT = 4096 / NT;
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid >> 6;
+  uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + cur_off);
+  int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + start_off);
+  uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
   // keys of chunk c0 (the first one from registers)
-  auto chunk_keys = [&](int c0, uint32_t (&keys)[kSelM]) {
+  auto chunk_keys = [&](int c0, uint32_t (&keys)[M]) {
     if (c0 == 0) {
 #pragma unroll
-      for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
+      for (int e = 0; e < M; ++e) keys[e] = k0[e];
     } else {
-      load_keys(row, n, c0, keys);
+      load_keys<M>(row, n, c0, keys);
     }
   };
-  uint32_t kmin = ~0u, kmax = 0u;
-  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
-    uint32_t keys[kSelM];
-    chunk_keys(c0, keys);
-    const int j0 = c0 + tid * kSelM;
+  // ---- phase 1: clear the bucket counters; key minimum and maximum
 #pragma unroll
-    for (int e = 0; e < kSelM; ++e)
+  for (int u = 0; u < BPT; ++u) cursor[tid * BPT + u] = 0u;
+  uint32_t kmin = ~0u, kmax = 0u;
+  for (int c0 = 0; c0 < n; c0 += C) {
+    uint32_t keys[M];
+    chunk_keys(c0, keys);
+    const int j0 = c0 + tid * M;
+#pragma unroll
+    for (int e = 0; e < M; ++e)
       if (j0 + e < n) {
         kmin = min(kmin, keys[e]);
         kmax = max(kmax, keys[e]);
@@ -801,15 +839,16 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const f
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, DSA_WAVE));
     kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, DSA_WAVE));
   }
-  if (lane_id() == 0) {
-    s_red[0][tid >> 6] = kmin;
-    s_red[1][tid >> 6] = kmax;
+  if (lane == 0) {
+    sh.red[0][wv] = kmin;
+    sh.red[1][wv] = kmax;
   }
   __syncthreads();
+  // ---- phase 2: bucket histogram
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
-    kmin = min(kmin, s_red[0][i]);
-    kmax = max(kmax, s_red[1][i]);
+    kmin = min(kmin, sh.red[0][i]);
+    kmax = max(kmax, sh.red[1][i]);
   }
   const float vmax = order_key_value(kmax), vmin = order_key_value(kmin);
   const float scale = 4095.5f / (vmax - vmin);
@@ -818,95 +857,145 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[kSelM], const f
     const float b = (vmax - order_key_value(key)) * scale;
     return min(4095, (int)b);
   };
-  uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + cur_off);
-  int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + start_off);
-  uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
-  for (int b = tid; b < 4096; b += NT) cursor[b] = 0u;
-  __syncthreads();
-  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
-    uint32_t keys[kSelM];
-    chunk_keys(c0, keys);
-    const int j0 = c0 + tid * kSelM;
+  // a row of one chunk keeps each key's bucket and its arrival rank inside
+  // the bucket (the counter's old value, its offset in the bucket-grouped
+  // list) as bucket << 16 | rank; invalid positions get bucket 4096. (With 16
+  // positions per thread the extra registers would spill: atomics instead.)
+  const bool one_chunk = M <= 8 && n <= C;
+  uint32_t rk0[M];
+  if (one_chunk) {
+    const int j0 = tid * M;
 #pragma unroll
-    for (int e = 0; e < kSelM; ++e)
-      if (j0 + e < n) atomicAdd(&cursor[bucket(keys[e])], 1u);
+    for (int e = 0; e < M; ++e) {
+      const uint32_t b = j0 + e < n ? (uint32_t)bucket(k0[e]) : 4096u;
+      rk0[e] = b < 4096u ? (b << 16) | atomicAdd(&cursor[b], 1u) : (4096u << 16);
+    }
+  } else {
+    for (int c0 = 0; c0 < n; c0 += C) {
+      uint32_t keys[M];
+      chunk_keys(c0, keys);
+      const int j0 = c0 + tid * M;
+#pragma unroll
+      for (int e = 0; e < M; ++e)
+        if (j0 + e < n) atomicAdd(&cursor[bucket(keys[e])], 1u);
+    }
   }
   __syncthreads();
-  {
-    constexpr int BPT = 4096 / NT;
-    int c[BPT], local = 0, big = 0;
+  // ---- phase 3: exclusive prefix of the counts (wave scan, then wave sums)
+  int c[BPT], local = 0;
 #pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-      c[u] = (int)cursor[tid * BPT + u];
-      local += c[u];
+  for (int u = 0; u < BPT; ++u) {
+    c[u] = (int)cursor[tid * BPT + u];
+    local += c[u];
+  }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, DSA_WAVE);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) sh.wsum[wv] = incl;
+  __syncthreads();
+  // ---- phase 4: bucket starts and cursors; the bucket holding place k - 1
+  // (exactly one when n > k) records where the candidate range ends
+  {
+    int run = incl - local, total = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      const int x = sh.wsum[i];
+      run += i < wv ? x : 0;
+      total += x;
     }
-    int total;
-    int run = block_inclusive_scan<NT>(local, s_scan, &total) - local;
-    if (tid == 0) {
-      s_flag[0] = 0;
-      s_flag[1] = min(n, k);  // end of the positions that are scattered
-    }
+    int big = 0;
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       bstart[tid * BPT + u] = run;
-      cursor[tid * BPT + u] = (uint32_t)run;
+      if (!one_chunk) cursor[tid * BPT + u] = (uint32_t)run;
       if (run < k) big = max(big, c[u]);
+      if (run < k && run + c[u] >= k) {
+        sh.lim = run + c[u];
+        sh.blast = tid * BPT + u;
+      }
       run += c[u];
     }
-    if (tid == 0) bstart[4096] = total;
-    __syncthreads();
-    // one flag store per wave that holds an oversized candidate bucket (a
-    // single-address atomic from every thread would serialise)
-    if (__ballot(big > kDirectBucketMax) != 0 && lane_id() == 0) s_flag[0] = 1;
-    // the bucket holding place k - 1 ends the scattered range
-    int r2 = run;
-#pragma unroll
-    for (int u = BPT - 1; u >= 0; --u) {
-      r2 -= c[u];
-      if (r2 < k && r2 + c[u] >= k) s_flag[1] = r2 + c[u];
-    }
-    __syncthreads();
-  }
-  if (s_flag[0] != 0) return false;
-  const int lim = s_flag[1];
-  for (int c0 = 0; c0 < n; c0 += kSelChunk) {
-    uint32_t keys[kSelM];
-    chunk_keys(c0, keys);
-    const int j0 = c0 + tid * kSelM;
-#pragma unroll
-    for (int e = 0; e < kSelM; ++e)
-      if (j0 + e < n) {
-        const int b = bucket(keys[e]);
-        if (bstart[b] < k) {
-          const uint32_t slot = atomicAdd(&cursor[b], 1u);
-          scomp[slot] = ((uint64_t)keys[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
-        }
-      }
+    if (tid == NT - 1) bstart[4096] = total;
+    const bool wbig = __ballot(big > kDirectBucketMax) != 0;
+    if (lane == 0) sh.wbig[wv] = wbig ? 1 : 0;
   }
   __syncthreads();
-  for (int sl = tid; sl < lim; sl += NT) {
-    const uint64_t cm = scomp[sl];
-    const int b = bucket((uint32_t)(cm >> 32));
-    const int b0 = bstart[b], b1 = bstart[b + 1];
-    int r = 0, u = b0;
-    for (; u + 4 <= b1; u += 4) {  // four independent reads in flight
-      const uint64_t c0 = scomp[u], c1 = scomp[u + 1], c2 = scomp[u + 2], c3 = scomp[u + 3];
-      r += (int)(c0 > cm) + (int)(c1 > cm) + (int)(c2 > cm) + (int)(c3 > cm);
+  {
+    int anybig = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) anybig |= sh.wbig[i];
+    if (anybig) return false;
+  }
+  // bucket starts grow with the bucket, so "start below k" is "bucket <= blast"
+  const int lim = n <= k ? n : sh.lim;
+  const int blast = n <= k ? 4095 : sh.blast;
+  // ---- phase 5: scatter the candidates (bucket start below k) by bucket
+  if (one_chunk) {
+    const int j0 = tid * M;
+    int bs[M];
+#pragma unroll
+    for (int e = 0; e < M; ++e) bs[e] = (int)(rk0[e] >> 16) <= blast ? bstart[rk0[e] >> 16] : 0;
+#pragma unroll
+    for (int e = 0; e < M; ++e)
+      if ((int)(rk0[e] >> 16) <= blast)
+        scomp[bs[e] + (int)(rk0[e] & 0xffffu)] =
+            ((uint64_t)k0[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
+  } else {
+    for (int c0 = 0; c0 < n; c0 += C) {
+      uint32_t keys[M];
+      chunk_keys(c0, keys);
+      const int j0 = c0 + tid * M;
+#pragma unroll
+      for (int e = 0; e < M; ++e)
+        if (j0 + e < n) {
+          const int b = bucket(keys[e]);
+          if (b <= blast) {
+            const uint32_t slot = atomicAdd(&cursor[b], 1u);
+            scomp[slot] = ((uint64_t)keys[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
+          }
+        }
     }
-    for (; u < b1; ++u) r += scomp[u] > cm;
-    if (b0 + r < k) orow[b0 + r] = (int)(~(uint32_t)cm);
+  }
+  __syncthreads();
+  // ---- phase 6: place of every candidate; a thread's (up to) four entries
+  // have their reads issued together
+  for (int s0 = tid; s0 < lim; s0 += 4 * NT) {
+    uint64_t cm[4];
+    int b0[4], b1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cm[r] = s0 + r * NT < lim ? scomp[s0 + r * NT] : 0ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int b = s0 + r * NT < lim ? bucket((uint32_t)(cm[r] >> 32)) : 0;
+      b0[r] = s0 + r * NT < lim ? bstart[b] : 0;
+      b1[r] = s0 + r * NT < lim ? bstart[b + 1] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int rk = 0, u = b0[r];
+      for (; u + 4 <= b1[r]; u += 4) {  // four independent reads in flight
+        const uint64_t x0 = scomp[u], x1 = scomp[u + 1], x2 = scomp[u + 2], x3 = scomp[u + 3];
+        rk += (int)(x0 > cm[r]) + (int)(x1 > cm[r]) + (int)(x2 > cm[r]) + (int)(x3 > cm[r]);
+      }
+      for (; u < b1[r]; ++u) rk += scomp[u] > cm[r];
+      if (b0[r] < b1[r] && b0[r] + rk < k) orow[b0[r] + rk] = (int)(~(uint32_t)cm[r]);
+    }
   }
   for (int i = n + tid; i < k; i += NT) orow[i] = -1;
   return true;
 }
 
-template <int IPT>
+template <int IPT, int M>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ seq_lens,
                                                       int S, int cap, int k,
                                                       int32_t* __restrict__ topk) {
   constexpr int NT = kSelNT;
+  constexpr int CHUNK = NT * M;
   using Cfg = SelectCfg<IPT>;
   constexpr int CAP = Cfg::CAP;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
@@ -918,23 +1007,24 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   __shared__ int s_scan[NT / 64];
   __shared__ int s_dig[2];
   __shared__ uint32_t s_bits[4][NT / 64];
+  __shared__ DirectShared s_direct;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
+  const float* row = scores + (size_t)t * ld;
+  // chunk 0, resident for all passes; its loads overlap the row lookup
+  uint32_t k0[M];
+  load_keys_ahead<M>(row, ld < (long)CHUNK ? (int)ld : CHUNK, k0);
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
   const int n = ri.n_valid;
-  const float* row = scores + (size_t)t * ld;
   int32_t* orow = topk + (size_t)t * k;
   if (n == 0) {
     for (int i = tid; i < k; i += NT) orow[i] = -1;
     return;
   }
-
-  uint32_t k0[kSelM];  // chunk 0, resident for all passes
-  load_keys(row, n, 0, k0);
   if (n <= kDirectMaxN &&
-      topk_direct<NT>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
-                      s_scan, s_bits, s_dig, orow))
+      topk_direct<NT, M>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
+                         s_direct, orow))
     return;
   __syncthreads();  // the select path reuses the LDS
   // OR / AND / min / max of the keys this thread lists
@@ -942,9 +1032,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
 
   int count;
   if (n <= CAP) {  // everything fits the sort: no selection needed
-    const int j0 = tid * kSelM;
+    const int j0 = tid * M;
 #pragma unroll
-    for (int e = 0; e < kSelM; ++e) {
+    for (int e = 0; e < M; ++e) {
       const int j = j0 + e;
       if (j < n) {
         list_key[j] = k0[e];
@@ -968,17 +1058,17 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       for (int i = tid; i < nb; i += NT) hist[i] = 0;
       __syncthreads();
       const int shift = 32 - pbits - w;
-      for (int c0 = 0; c0 < n; c0 += kSelChunk) {
-        uint32_t keys[kSelM];
+      for (int c0 = 0; c0 < n; c0 += CHUNK) {
+        uint32_t keys[M];
         if (c0 == 0) {
 #pragma unroll
-          for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
+          for (int e = 0; e < M; ++e) keys[e] = k0[e];
         } else {
-          load_keys(row, n, c0, keys);
+          load_keys<M>(row, n, c0, keys);
         }
-        const int j0 = c0 + tid * kSelM;
+        const int j0 = c0 + tid * M;
 #pragma unroll
-        for (int e = 0; e < kSelM; ++e) {
+        for (int e = 0; e < M; ++e) {
           const uint32_t key = keys[e];
           if (j0 + e < n && (pbits == 0 || (key >> (32 - pbits)) == prefix))
             atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
@@ -997,18 +1087,18 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     const int above = k - need;
     // ---- collect in position order: above -> [0, above), bin -> [above, ...)
     int nabove = 0, nbnd = 0;
-    for (int c0 = 0; c0 < n; c0 += kSelChunk) {
-      uint32_t keys[kSelM];
+    for (int c0 = 0; c0 < n; c0 += CHUNK) {
+      uint32_t keys[M];
       if (c0 == 0) {
 #pragma unroll
-        for (int e = 0; e < kSelM; ++e) keys[e] = k0[e];
+        for (int e = 0; e < M; ++e) keys[e] = k0[e];
       } else {
-        load_keys(row, n, c0, keys);
+        load_keys<M>(row, n, c0, keys);
       }
-      const int j0 = c0 + tid * kSelM;
+      const int j0 = c0 + tid * M;
       int fa = 0, fb = 0;
 #pragma unroll
-      for (int e = 0; e < kSelM; ++e) {
+      for (int e = 0; e < M; ++e) {
         const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
         const bool ok = j0 + e < n;
         fa += ok && v > prefix;
@@ -1020,7 +1110,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       int ia = nabove + (excl & 0xffff);
       int ib = nbnd + (excl >> 16);
 #pragma unroll
-      for (int e = 0; e < kSelM; ++e) {
+      for (int e = 0; e < M; ++e) {
         const int j = j0 + e;
         const uint32_t v = exact ? keys[e] : (keys[e] >> (32 - pbits));
         if (j < n && v > prefix) {
@@ -1250,7 +1340,7 @@ size_t topk_select_lds_bytes(int k) {
   }
 }
 
-template <int IPT>
+template <int IPT, int M>
 static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
   const size_t lds = SelectCfg<IPT>::BYTES;
   // raise the dynamic-LDS limit once per device
@@ -1260,22 +1350,28 @@ static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<IPT>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<IPT, M>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit);
   }
   ProfScope prof("topk_select", st);
-  hipLaunchKernelGGL((topk_select<IPT>), dim3(a.T), dim3(kSelNT), lds, st, a.scores, a.ld, a.cu,
-                     a.seq_lens, a.S, a.MP * a.PS, a.k, a.topk);
+  hipLaunchKernelGGL((topk_select<IPT, M>), dim3(a.T), dim3(kSelNT), lds, st, a.scores, a.ld,
+                     a.cu, a.seq_lens, a.S, a.MP * a.PS, a.k, a.topk);
   return hipGetLastError();
+}
+
+// positions per thread: 8 when a whole score row fits one chunk of 8192
+template <int IPT>
+static hipError_t launch_select_m(const IndexerArgs& a, hipStream_t st) {
+  return a.ld <= (long)kSelNT * 8 ? launch_select<IPT, 8>(a, st) : launch_select<IPT, 16>(a, st);
 }
 
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
   switch (select_ipt(a.k)) {
-    case 2: return launch_select<2>(a, st);
-    case 4: return launch_select<4>(a, st);
-    default: return launch_select<8>(a, st);
+    case 2: return launch_select_m<2>(a, st);
+    case 4: return launch_select_m<4>(a, st);
+    default: return launch_select_m<8>(a, st);
   }
 }
 
