@@ -159,38 +159,40 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   const int tid = threadIdx.x, l = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = l >> 4, col = l & 15;
-  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int i_begin = c * CH, i_end = min(i_begin + CH, k);
-  const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
   const float scale2 = sm_scale * 1.44269504088896341f;
 
   // ---- this wave's k steps [kb, kb + nk) of 32 latent columns
   const int kb = wave < 2 ? 5 * wave : 4 * wave + 2;
   const int nk = wave < 2 ? 5 : 4;
-  // ---- this lane's query fragments: head 16 hb + col, k values 32 (kb + u) + 8 g ..
-  // (issued first, so that their latency overlaps the resolution below)
+  // ---- the selection entries of this chunk (entry i = 64 (4 p + wave) + l
+  // of pass p, two stages per wave and pass) and this lane's query fragments
+  // (head 16 hb + col, k values 32 (kb + u) + 8 g ..) depend only on the row
+  // index, so they are loaded together with the row's sequence bounds
+  constexpr int NP = kDecMaxCH / 256;
+  int j[NP];
+  {
+    const int32_t* sel = topk + (size_t)t * k;
+#pragma unroll
+    for (int p2 = 0; p2 < NP; ++p2) {
+      const int ii = i_begin + 256 * p2 + 64 * wave + l;
+      j[p2] = ii < i_end ? sel[ii] : -1;
+    }
+  }
   const int head = 16 * hb + col;
   bf16x8 qf[5];
   {
     const uint16_t* qrow = q + ((size_t)t * H + (head < H ? head : 0)) * DK + 8 * g;
 #pragma unroll
     for (int u = 0; u < 5; ++u)
-      qf[u] = as_bf16x8(head < H && nst > 0 && u < nk
-                            ? *reinterpret_cast<const uint4*>(qrow + 32 * (kb + u))
-                            : zero_u4());
+      qf[u] = as_bf16x8(head < H && u < nk ? *reinterpret_cast<const uint4*>(qrow + 32 * (kb + u))
+                                           : zero_u4());
   }
-  // ---- resolve sources and per-stage validity masks: entry i = 64 (4 p + wave) + l
-  // of pass p (two stages per wave and pass), all selection loads first
+  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
+  const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
+  // ---- resolve sources and per-stage validity masks
   if (nst > 0) {
-    const int32_t* sel = topk + (size_t)t * k;
     const int32_t* ptrow = pt + (size_t)ri.seq * MP;
-    constexpr int NP = kDecMaxCH / 256;
-    int j[NP];
-#pragma unroll
-    for (int p2 = 0; p2 < NP; ++p2) {
-      const int ii = i_begin + 256 * p2 + 64 * wave + l;
-      j[p2] = ii < i_end ? sel[ii] : -1;
-    }
     int src[NP];
 #pragma unroll
     for (int p2 = 0; p2 < NP; ++p2) {
@@ -342,11 +344,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
 
 // grid = (T, H), block = 256: merge the nch partials of (t, h),
 //   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0,
-// M = max m_c. The chunk weights e^(m_c - M) are computed once, in LDS; then
-// thread (g, d4) = (tid / 128, tid % 128) sums chunks g, g + 2, ... for
-// value columns 4 d4 .. 4 d4 + 3 with all its loads independent, and the two
-// halves meet through LDS.
+// M = max m_c. Thread (g, d4) = (tid / 128, tid % 128) sums chunks g, g + 2,
+// ... for value columns 4 d4 .. 4 d4 + 3. The (m, l) pairs and the first
+// kCombAhead of this thread's O partials are all loaded at once; the chunk
+// weights e^(m_c - M) are then computed once, in LDS, and the two halves of
+// the sum meet through LDS.
 constexpr int kCombMaxCH = 1024;  // partials per (row, head) the combine handles
+constexpr int kCombAhead = 16;    // O partials per thread loaded with the (m, l) pairs
 
 __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
@@ -355,11 +359,11 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
   __shared__ float s_w[kCombMaxCH];
   __shared__ float4 s_o[128];
   __shared__ float s_red[8];
-  __shared__ float s_l;
   const int t = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
+  const int g = tid >> 7, d4 = tid & 127;
   const size_t base = (size_t)t * nch * H;
-  // ---- M = max over live chunks (l_c > 0)
+  // ---- (m, l) of the chunks, then this thread's first O partials
   float mloc = -INFINITY;
   for (int c = tid; c < nch; c += 256) {
     const size_t r = base + (size_t)c * H + h;
@@ -368,6 +372,14 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
     s_w[c] = mm;
     mloc = fmaxf(mloc, mm);
   }
+  float4 va[kCombAhead];
+#pragma unroll
+  for (int u = 0; u < kCombAhead; ++u) {
+    const int c = g + 2 * u;
+    va[u] = c < nch ? *reinterpret_cast<const float4*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // ---- M = max over live chunks (l_c > 0)
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mloc = fmaxf(mloc, shfl_xor_f(mloc, o));
   if (l == 0) s_red[wave] = mloc;
@@ -383,15 +395,21 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) lloc += shfl_xor_f(lloc, o);
-  __syncthreads();  // every M is read; s_red is free
+  __syncthreads();  // every M is read and every weight written; s_red is free
   if (l == 0) s_red[4 + wave] = lloc;
-  __syncthreads();
-  if (tid == 0) s_l = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-  // ---- O: this thread's half of the chunks, independent loads
-  const int g = tid >> 7, d4 = tid & 127;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  // ---- O: this thread's half of the chunks
   // (a chunk without live selections has w = 0 and a zero partial O)
-  for (int c0 = g; c0 < nch; c0 += 8) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < kCombAhead; ++u) {
+    const int c = g + 2 * u;
+    const float w = c < nch ? s_w[c] : 0.f;
+    acc.x = fmaf(w, va[u].x, acc.x);
+    acc.y = fmaf(w, va[u].y, acc.y);
+    acc.z = fmaf(w, va[u].z, acc.z);
+    acc.w = fmaf(w, va[u].w, acc.w);
+  }
+  for (int c0 = g + 2 * kCombAhead; c0 < nch; c0 += 8) {
     float w[4];
     float4 v[4];
 #pragma unroll
@@ -416,7 +434,7 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
   __syncthreads();
   if (g == 0) {
     const float4 b = s_o[d4];
-    const float L = s_l;
+    const float L = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     uint2 packed;
     packed.x = pack_bf16x2((acc.x + b.x) * inv, (acc.y + b.y) * inv);
