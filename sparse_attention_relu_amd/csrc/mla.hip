@@ -19,11 +19,17 @@ namespace dsa {
 // Staged latent rows. A staged row keeps its 512 "nope" columns (1024 bytes)
 // and its 64 rope columns (128 bytes) in two separate regions, so that 16-byte
 // chunk c of a row sits at a power-of-two stride and can be XOR-swizzled:
-// nope row r keeps chunk c (0..63) at slot c ^ nope_x(r),
-// nope_x(r) = 2 (r & 7) + ((r >> 3) & 1), so any 16 consecutive rows read at
-// one chunk hit 16 distinct bank groups, and the 4 consecutive rows x 2
-// adjacent chunks of one transposed read hit 8; rope row r keeps chunk c
-// (0..7) at c ^ ((r >> 1) & 7). Rows are filled by direct global->LDS 16-byte
+// nope row r keeps chunk c (0..63) at slot c ^ nope_x(r), with
+// nope_x(r) = 4 (r & 3) + 2 ((r >> 2) & 1) + ((r >> 3) & 1). Slot s of any row
+// lies in bank group s mod 16 (16 groups of four 4-byte banks), so:
+//   - 16 consecutive rows (from a multiple of 16) read at one chunk hit all
+//     16 groups (nope_x is a bijection there);
+//   - 4 consecutive rows (from a multiple of 4) x 4 aligned chunks, the half
+//     wave of an extend transposed read, hit all 16 (bits 2..3 of nope_x
+//     differ between the 4 rows, and the chunks fill bits 0..1);
+//   - 8 consecutive rows (from a multiple of 8) x 2 aligned chunks, the half
+//     wave of a decode transposed read, hit all 16 (nope_x >> 1 differs).
+// Rope row r keeps chunk c (0..7) at c ^ ((r >> 1) & 7). Rows are filled by direct global->LDS 16-byte
 // loads (global_load_lds_dwordx4): one wave instruction writes 1024
 // consecutive LDS bytes, 16 per lane, so a lane simply fetches the chunk that
 // belongs at its slot.
@@ -37,7 +43,9 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int nope_x(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int nope_x(int r) {
+  return ((r & 3) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
+}
 __device__ __forceinline__ int rope_x(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -232,11 +240,14 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
                      : kDecRopeOff + col * ROPE_B + 16 * ((4 * (i - 16) + g) ^ rx);
     kstep[u] = i < 16 ? 16 * NOPE_B : 16 * ROPE_B;
   }
-  // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3)
+  // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3),
+  // i.e. 16-byte chunk 16 wave + 2 ct + (col & 3) / 2, byte 8 (col & 1)
   const int vr = 4 * g + (col >> 2), vq = col & 3;
   const int vx = nope_x(vr);
-  const int vbase = vr * NOPE_B + 256 * wave + 16 * ((vq >> 1) ^ (vx & 1)) + 8 * (vq & 1);
-  const int vxor = 32 * (vx >> 1);
+  int voff[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+    voff[ct] = vr * NOPE_B + 256 * wave + 16 * ((2 * ct + (vq >> 1)) ^ vx) + 8 * (vq & 1);
 
   f32x4 o[8];
 #pragma unroll
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     // ---- O^T (value columns 128 wave + 16 ct + 4 g + r, head col) += V^T P^T
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const int off = vbase + ((32 * ct) ^ vxor);
+      const int off = voff[ct];
       const v4s vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off));
       const v4s vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(buf + off + 16 * NOPE_B));
       bf16x8 va;
@@ -640,6 +651,10 @@ __device__ __forceinline__ void stage_one(const StageCtx& c, int n, int l) {
 }
 
 constexpr int kStageLoads = PROWS / XW + 2;  // 18 direct loads per wave per page
+#ifndef DSA_S_AHEAD
+#define DSA_S_AHEAD 6
+#endif
+constexpr int kSAhead = DSA_S_AHEAD;  // S^T operand reads in flight per wave
 
 struct ExtArgs {
   const uint16_t* __restrict__ kv;
@@ -687,8 +702,11 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
   lds_barrier();
   const PageMeta pm = P.cur;
   const PageMeta pn = meta_from_raw(P.next, A.MP, A.cap, A.num_pages);
-  // the next page's loads are issued during this page's S^T products
-  const bool do_stage = slot + 1 < A.u_lim;
+  // the next page's loads are issued during this page's S^T products. The
+  // last step stages the slot it already holds in P.next (a clamped, valid
+  // key) into the buffer nobody reads again: unconditional loads keep the
+  // matrix loop free of branches.
+  const bool do_stage = true;
   const StageCtx sc = stage_ctx(nxt, A.kv, A.row_stride, pn, A.PS, X.wave);
   // metadata for the coming steps
   uint64_t mem_n = 0;
@@ -719,35 +737,43 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
     // ---- S^T tile: keys 32 role + m (A from LDS), rows m (B = resident q);
     // step i reads chunk 2 i + g of key row 32 role + m
     auto s_off = [&](int i) { return i < 32 ? X.soff[i & 7] + 256 * (i >> 3) : X.soff[8 + (i - 32)]; };
-    // operands are read two steps ahead of the MFMA that consumes them
-    bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(0)));
-    bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(1)));
+    // operands are read kSAhead steps ahead of the MFMA that consumes them,
+    // so that several LDS reads per wave are in flight
+    bf16x8 aq[kSAhead];
+#pragma unroll
+    for (int i = 0; i < kSAhead; ++i)
+      aq[i] = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(i)));
 #pragma unroll
     for (int i = 0; i < DK / 16; ++i) {
-      bf16x8 a2 = a1;
-      if (i + 2 < DK / 16) a2 = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(i + 2)));
-      sacc = mfma32(a0, X.qb[i], sacc);
+      const bf16x8 a = aq[i % kSAhead];
+      if (i + kSAhead < DK / 16)
+        aq[i % kSAhead] = as_bf16x8(*reinterpret_cast<const uint4*>(cur + s_off(i + kSAhead)));
+      sacc = mfma32(a, X.qb[i], sacc);
       if (do_stage && (i & 1) == 0 && (i >> 1) < kStageLoads) stage_one(sc, i >> 1, l);
-      a0 = a1;
-      a1 = a2;
     }
     // accumulator r of this lane holds key 8 (r / 4) + 4 g + (r % 4) of the
-    // half; logits are kept in log2 units (sm_scale * log2 e folded in)
+    // half; logits are kept in log2 units (sm_scale * log2 e folded in). A
+    // masked key becomes -inf by a bit select on the sign-extended mask bit.
     const uint32_t hg = hm >> (4 * g);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 8 * (r >> 2) + (r & 3);
-      sacc[r] = ((hg >> key) & 1u) ? sacc[r] * A.scale2 : -INFINITY;
+      const uint32_t sel = (uint32_t)((int)(hg << (31 - key)) >> 31);
+      const uint32_t v = __float_as_uint(sacc[r] * A.scale2);
+      sacc[r] = __uint_as_float((v & sel) | (0xff800000u & ~sel));
       mx = fmaxf(mx, sacc[r]);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    if (g == 0) smax[(pr * 2 + role) * 32 + m] = mx;
+    // each half-wave publishes its own maximum; the row's four partial
+    // maxima (two halves, two roles) are combined after the barrier
+    smax[((pr * 2 + role) * 2 + g) * 32 + m] = mx;
   }
   lds_barrier();
   bf16x8 pb[2];
   float alpha = 1.f;
   if (pair_any) {
-    mx = fmaxf(mx, smax[(pr * 2 + (role ^ 1)) * 32 + m]);
+    mx = fmaxf(fmaxf(mx, smax[((pr * 2 + role) * 2 + (g ^ 1)) * 32 + m]),
+               fmaxf(smax[((pr * 2 + (role ^ 1)) * 2) * 32 + m],
+                     smax[((pr * 2 + (role ^ 1)) * 2 + 1) * 32 + m]));
     if (mx > X.m_used + kLazyMax2) {
       alpha = __builtin_amdgcn_exp2f(X.m_used - mx);  // 0 while nothing was accumulated
       X.m_used = mx;
@@ -823,10 +849,9 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
 // V^T reads: the lane supplies row key0 = 32 kh + 16 st + 4 g + kq (read 0)
 // or key0 + 8 (read 1), 16-byte chunk 16 wave + 4 ct + c0 and byte boff,
 // with kq = (l & 15) >> 2, c0 = 2 ((l >> 4) & 1) + ((l & 3) >> 1), boff =
-// 8 (l & 1). Since nope_x(key) = 8 g + 2 kq + e, its slot is 16 wave +
-// 4 (ct ^ z) + (c0 ^ w_e) with z = 2 g + (kq >> 1), w_e = 2 (kq & 1) + e,
-// so 4 per-lane values per read plus the constants 1024 (32 kh + 16 st) and
-// 256 wave.
+// 8 (l & 1). nope_x depends on the row modulo 16 only, so the slot is
+// 16 wave + ((4 ct + c0) ^ nope_x(4 g + kq + 8 e)): 4 per-lane values per
+// read plus the constants 1024 (32 kh + 16 st) and 256 wave.
 __device__ __forceinline__ void ext_offsets(ExtLane& X) {
   const int kr = 32 * X.role + X.m;
   const int y = X.g ^ nope_x(kr);
@@ -838,13 +863,12 @@ __device__ __forceinline__ void ext_offsets(ExtLane& X) {
   const int kq = (l & 15) >> 2, qq = l & 3;
   const int c0 = 2 * ((l >> 4) & 1) + (qq >> 1);
   const int boff = 8 * (qq & 1);
-  const int z = 2 * X.g + (kq >> 1);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int key = 4 * X.g + kq + 8 * e;
-    const int w = c0 ^ (2 * (kq & 1) + e);
+    const int x = nope_x(key);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) X.toff[e][j] = key * NOPE_B + 64 * (j ^ z) + 16 * w + boff;
+    for (int j = 0; j < 4; ++j) X.toff[e][j] = key * NOPE_B + 16 * ((4 * j + c0) ^ x) + boff;
   }
 }
 
@@ -860,7 +884,7 @@ void mla_extend_qblock(
   __shared__ __attribute__((aligned(1024))) unsigned char page0[PAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) unsigned char page1[PAGE_BYTES];
   __shared__ bf16x8 pfrag[2 * 2 * 2 * 64];  // P^T fragments [pair][role][step][lane]
-  __shared__ float s_max[2 * 2 * 32];        // row maxima [pair][role][row]
+  __shared__ float s_max[2 * 2 * 2 * 32];    // row maxima [pair][role][half][row]
   __shared__ float s_alpha[2 * 32];          // offset rescale factors [pair][row]
   const int TPB = (QB * H + XROWS - 1) / XROWS;
   const int nqb = (T + QB - 1) / QB;
@@ -939,6 +963,7 @@ void mla_extend_qblock(
     const unsigned char* cur = (slot & 1) ? page1 : page0;
     ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max, s_alpha);
   }
+  wait_vmcnt<0>();  // the last step's staging loads land before the workgroup ends
   // ---- row sums over both key halves, then normalise and store this
   // wave's value columns 128 wave + 32 ct + 8 (r / 4) + 4 g + (r % 4) of the
   // rows m of both pairs
