@@ -651,10 +651,7 @@ __device__ __forceinline__ void stage_one(const StageCtx& c, int n, int l) {
 }
 
 constexpr int kStageLoads = PROWS / XW + 2;  // 18 direct loads per wave per page
-#ifndef DSA_S_AHEAD
-#define DSA_S_AHEAD 6
-#endif
-constexpr int kSAhead = DSA_S_AHEAD;  // S^T operand reads in flight per wave
+constexpr int kSAhead = 6;  // S^T operand reads in flight per wave
 
 struct ExtArgs {
   const uint16_t* __restrict__ kv;
@@ -673,7 +670,8 @@ struct ExtLane {
   RowInfo ri;
   bf16x8 qb[DK / 16];
   f32x16 o[2][4];  // O^T tiles: [pair of the rows][32-column block of this wave]
-  float m_used, l_part;
+  float m_used[2];  // softmax offsets of rows m of pair 0 and pair 1 (log2 units)
+  float l_part;
 };
 
 // Metadata carried from step to step: slot s's page (complete), slot s + 1's
@@ -692,8 +690,7 @@ struct ExtPipe {
 // step's wait, so no load latency is exposed inside a step.
 __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& P, int slot,
                                          const unsigned char* __restrict__ cur, uint32_t nxt,
-                                         bf16x8* __restrict__ pf, float* __restrict__ smax,
-                                         float* __restrict__ salpha) {
+                                         bf16x8* __restrict__ pf, float* __restrict__ smax) {
   const int l = X.l, g = X.g, m = X.m, pr = X.pr, role = X.role;
   // this wave's loads of page `slot` (issued one step earlier) and the
   // metadata loads of the previous step have landed; after the barrier
@@ -763,25 +760,34 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
       sacc[r] = __uint_as_float((v & sel) | (0xff800000u & ~sel));
       mx = fmaxf(mx, sacc[r]);
     }
-    // each half-wave publishes its own maximum; the row's four partial
-    // maxima (two halves, two roles) are combined after the barrier
-    smax[((pr * 2 + role) * 2 + g) * 32 + m] = mx;
   }
+  // every half-wave publishes its own maximum (-inf without selections); the
+  // four partial maxima of a row (two halves, two roles) meet after the
+  // barrier, and every wave combines them for the rows of BOTH pairs: the
+  // lazy offset update is deterministic, so each wave tracks the offsets of
+  // both pairs' rows itself and rescales its accumulators without a second
+  // exchange
+  smax[((pr * 2 + role) * 2 + g) * 32 + m] = mx;
   lds_barrier();
-  bf16x8 pb[2];
-  float alpha = 1.f;
-  if (pair_any) {
-    mx = fmaxf(fmaxf(mx, smax[((pr * 2 + role) * 2 + (g ^ 1)) * 32 + m]),
-               fmaxf(smax[((pr * 2 + (role ^ 1)) * 2) * 32 + m],
-                     smax[((pr * 2 + (role ^ 1)) * 2 + 1) * 32 + m]));
-    if (mx > X.m_used + kLazyMax2) {
-      alpha = __builtin_amdgcn_exp2f(X.m_used - mx);  // 0 while nothing was accumulated
-      X.m_used = mx;
-      X.l_part *= alpha;
+  float al[2];
+#pragma unroll
+  for (int p2 = 0; p2 < 2; ++p2) {
+    const float* sm = smax + p2 * 4 * 32 + m;
+    const float rm = fmaxf(fmaxf(sm[0], sm[32]), fmaxf(sm[64], sm[96]));
+    al[p2] = 1.f;
+    if (rm > X.m_used[p2] + kLazyMax2) {
+      al[p2] = __builtin_amdgcn_exp2f(X.m_used[p2] - rm);  // 0 while nothing was accumulated
+      X.m_used[p2] = rm;
     }
+  }
+  const float alpha = pr ? al[1] : al[0];
+  const float m_own = pr ? X.m_used[1] : X.m_used[0];
+  X.l_part *= alpha;
+  bf16x8 pb[2];
+  if (pair_any) {
     // exp2(-inf) is 0, so masked keys need no test; a row with no offset
     // yet has only masked keys and subtracts 0 instead of -inf
-    const float off = X.m_used == -INFINITY ? 0.f : X.m_used;
+    const float off = m_own == -INFINITY ? 0.f : m_own;
     uint32_t w[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -798,19 +804,17 @@ __device__ __forceinline__ void ext_step(const ExtArgs& A, ExtLane& X, ExtPipe& 
   }
   pf[((pr * 2 + role) * 2 + 0) * 64 + l] = pb[0];
   pf[((pr * 2 + role) * 2 + 1) * 64 + l] = pb[1];
-  if (role == 0 && g == 0) salpha[pr * 32 + m] = alpha;
-  lds_barrier();
   // ---- rescale the O rows whose softmax offset moved (rows m of both pairs)
-  const float a0 = salpha[m], a1 = salpha[32 + m];
-  if (__ballot(a0 != 1.f || a1 != 1.f) != 0) {
+  if (__ballot(al[0] != 1.f || al[1] != 1.f) != 0) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        X.o[0][ct][r] *= a0;
-        X.o[1][ct][r] *= a1;
+        X.o[0][ct][r] *= al[0];
+        X.o[1][ct][r] *= al[1];
       }
   }
+  lds_barrier();
   // ---- O^T += V^T P^T for value columns 128 wave + 32 ct + ..., all 64 rows:
   // four 16-key steps; each V^T fragment feeds the MFMAs of both pairs
   auto vfrag = [&](int j) {  // j = (kh * 2 + st) * 4 + ct
@@ -885,7 +889,6 @@ void mla_extend_qblock(
   __shared__ __attribute__((aligned(1024))) unsigned char page1[PAGE_BYTES];
   __shared__ bf16x8 pfrag[2 * 2 * 2 * 64];  // P^T fragments [pair][role][step][lane]
   __shared__ float s_max[2 * 2 * 2 * 32];    // row maxima [pair][role][half][row]
-  __shared__ float s_alpha[2 * 32];          // offset rescale factors [pair][row]
   const int TPB = (QB * H + XROWS - 1) / XROWS;
   const int nqb = (T + QB - 1) / QB;
   // the TPB workgroups of a block get ids of one residue mod 8, i.e. one XCD
@@ -926,7 +929,8 @@ void mla_extend_qblock(
   for (int p2 = 0; p2 < 2; ++p2)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) X.o[p2][ct] = f32x16{};
-  X.m_used = -INFINITY;
+  X.m_used[0] = -INFINITY;
+  X.m_used[1] = -INFINITY;
   X.l_part = 0.f;
 
   ExtArgs A;
@@ -961,7 +965,7 @@ void mla_extend_qblock(
   const uint32_t lds0 = lds_addr_of(page0), lds1 = lds_addr_of(page1);
   for (int slot = 0; slot < A.u_lim; ++slot) {
     const unsigned char* cur = (slot & 1) ? page1 : page0;
-    ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max, s_alpha);
+    ext_step(A, X, P, slot, cur, (slot & 1) ? lds0 : lds1, pfrag, s_max);
   }
   wait_vmcnt<0>();  // the last step's staging loads land before the workgroup ends
   // ---- row sums over both key halves, then normalise and store this
