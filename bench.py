@@ -351,7 +351,43 @@ def bench_extend(dsa, wl, args, QB, steps=None):
         roof.update({"kernel": dom, "traffic": measured_traffic(dom, wl.name),
                      "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
         res["roofline"] = roof
+    res["per_query"] = _per_query_attend(dsa, wl, d, topk, outs, steps, kt)
     return res
+
+
+def _per_query_attend(dsa, wl, d, topk, outs, steps, kt_qblock):
+    """The same layers attended per query: each packed row gathers its own
+    selected latent rows (the decode kernels run on the extend batch), with no
+    block union. Reported beside the query-block kernel; its outputs are
+    compared with the query-block outputs of the same selections."""
+    import torch
+
+    layers = len(outs)
+    T, k, H = topk.shape[0], topk.shape[1], outs[0].shape[1]
+    ws_d = torch.empty(max(1, dsa.sparse_mla_decode_workspace(T, H, k)), dtype=torch.uint8,
+                       device="cuda")
+    outs_pq = [torch.empty_like(o) for o in outs]
+
+    def step():
+        for i in range(layers):
+            dsa.sparse_mla_decode(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
+                                  d["cu"], topk, wl.sm_scale, out=outs_pq[i], workspace=ws_d)
+
+    ms = _timed(step, steps, 1)
+    kt = _kernel_times(dsa, step, steps)
+    torch.cuda.synchronize()
+    diff = max(float((a.float() - b.float()).abs().max()) for a, b in zip(outs, outs_pq))
+    n_sel = int((topk >= 0).sum())
+    gather = n_sel * DK * 2 + T * k * 4 + T * H * DK * 2
+    part = kt["mla_decode_partial"][1]
+    e = {"ms_per_layer": round(ms / layers, 4),
+         "partial_us": round(part * 1e3, 2),
+         "combine_us": round(kt["mla_decode_combine"][1] * 1e3, 2),
+         "partial_roofline": _roofline_entry("hbm", gather, part),
+         "gathered_bytes_per_layer": gather,
+         "speedup_vs_qblock": round(kt_qblock["mla_extend_qblock"][1] / (ms / layers), 2),
+         "max_abs_diff_vs_qblock": round(diff, 5)}
+    return e
 
 
 def _rows_seq(wl, cu):

@@ -145,6 +145,16 @@ def _extend_config(dsa, cid, QB, n_random, n_blocks):
         ref = _oracle_rows_mla(wl, b, tk, rows, layer=layer)
         check_attention(got, ref, rows=rows, what=f"config {cid} QB={QB} layer {layer}")
 
+    if QB == 256:
+        # per-query attend of the same packed batch: every row gathers its own
+        # selected rows (the decode kernels), no union
+        log(f"config {cid}: per-query attend (indexer selection)")
+        out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"],
+                                    tk_t, wl.sm_scale)
+        torch.cuda.synchronize()
+        ref = _oracle_rows_mla(wl, b, tk, rows)
+        check_attention(to_np(out), ref, rows=rows, what=f"config {cid} per-query")
+
     log(f"config {cid}: extend attend with the locality selection")
     loc = W.locality_selection(wl.seq_lens, cu, wl.k, 100 + cid)
     lt = i32(loc, "cuda")
