@@ -352,6 +352,8 @@ def bench_extend(dsa, wl, args, QB, steps=None):
                      "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
         res["roofline"] = roof
     res["per_query"] = _per_query_attend(dsa, wl, d, topk, outs, steps, kt)
+    # the library's own choice between the two paths for these unions
+    res["attend_path_chosen"] = dsa.extend_attend_path(cnt, T, H, k, wl.PS, QB, u_max)
     return res
 
 

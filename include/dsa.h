@@ -184,6 +184,33 @@ int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, i
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_extend_attend_path — which of the two token-exact extend attention
+ * paths to run for a packed batch whose block unions are built: the query
+ * block (dsa_sparse_mla_extend, one page fetch per block, MFMA work growing
+ * with the union sizes) or per query (dsa_sparse_mla_decode on the packed
+ * batch: every row gathers its own selected rows, HBM work growing with
+ * T * k). Both give the same result per query; the choice only decides the
+ * time. The query-block kernel page ("sparse_mla_prefill_qblock.py", module
+ * docstring) sets the two designs against each other: one re-fetches every
+ * page per query, the other walks each block's page union once.
+ *
+ * The estimate is each path's work at the rate this library measures on
+ * MI355X: executed query-block flops sum_b min(blk_counts[b], u_max) *
+ * QB * H * PS * (576 + 512) * 2 at 1.0e15 flop/s, against the per-query
+ * bytes (selected latent rows of 1152 bytes, selection entries, queries and
+ * fp32 partials) at 5.7e12 B/s.
+ *
+ *   blk_counts_host  HOST int32 [nQB], the blk_counts of dsa_block_union
+ *                    copied to the host; read only, not kept
+ *   nQB = ceil(T / QB); T, H, k, PS, QB, u_max as in the other calls
+ * Returns 0 (query block), 1 (per query), or DSA_ERR_INVALID_ARG (as a
+ * negative number) for a null pointer, a non-positive size or nQB that does
+ * not match T and QB. Touches no GPU state.
+ */
+int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
+                           int QB, int u_max);
+
+/*
  * Kernel timing (diagnostics). dsa_profile_enable(1) clears earlier records
  * and makes every subsequent kernel launch of the entry points above record
  * a pair of HIP events on its own stream; dsa_profile_enable(0) stops it.

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     DsaError,
     block_union,
     block_union_workspace,
+    extend_attend_path,
     header_functions,
     indexer_topk,
     indexer_topk_workspace,

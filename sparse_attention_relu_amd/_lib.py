@@ -40,6 +40,7 @@ SIGNATURES = {
     "dsa_sparse_mla_decode": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
                               + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_sparse_mla_extend_workspace": (_c_size, [_c_int] * 4),
+    "dsa_extend_attend_path": (_c_int, [_vp] + [_c_int] * 7),
     "dsa_profile_enable": (_c_int, [_c_int]),
     "dsa_profile_read": (_c_int, [_c_int, ctypes.c_char_p, _c_int, _vp, _vp, _vp]),
     "dsa_sparse_mla_extend": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -248,6 +249,22 @@ def _mla_common(q, kv_cache, page_table, seq_lens, cu_q_lens):
         raise ValueError(f"q last dim must be 576, got {Dk}")
     P, PS, row_stride = kv_cache.shape
     return dev, S, MP, T, H, P, PS, row_stride
+
+
+def extend_attend_path(blk_counts, T: int, H: int, k: int, PS: int, QB: int,
+                       u_max: int) -> str:
+    """"qblock" or "per_query": the faster token-exact extend attention for
+    a batch whose block unions are built (blk_counts: the union sizes, any
+    array or tensor; a device tensor is copied to the host)."""
+    import numpy as np
+
+    if hasattr(blk_counts, "detach"):
+        blk_counts = blk_counts.detach().cpu().numpy()
+    c = np.ascontiguousarray(blk_counts, dtype=np.int32)
+    r = load().dsa_extend_attend_path(c.ctypes.data, int(c.size), T, H, k, PS, QB, u_max)
+    if r < 0:
+        raise DsaError("dsa_extend_attend_path", -r, last_error())
+    return "per_query" if r == 1 else "qblock"
 
 
 def sparse_mla_decode_workspace(T, H, k) -> int:

@@ -221,6 +221,31 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
+int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
+                           int QB, int u_max) {
+  if (!blk_counts_host || T <= 0 || H <= 0 || k <= 0 || PS <= 0 || QB <= 0 || u_max <= 0)
+    return -fail(DSA_ERR_INVALID_ARG, "extend path: null counts or a non-positive size");
+  if ((long)nQB != ((long)T + QB - 1) / QB)
+    return -fail(DSA_ERR_INVALID_ARG, "extend path: nQB=%d does not match T=%d, QB=%d", nQB, T,
+                 QB);
+  // measured on MI355X: executed MFMA rate of the query-block kernel and the
+  // HBM rate of the per-query gather
+  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.7e12;
+  double pages = 0.0;
+  for (int b = 0; b < nQB; ++b) {
+    const int c = blk_counts_host[b];
+    pages += c < 0 ? 0.0 : (c < u_max ? c : u_max);
+  }
+  const double t_qblock = pages * QB * H * PS * (576.0 + 512.0) * 2.0 / kQblockFlops;
+  const int CH = dsa::mla_decode_chunk(T, k);
+  const double nch = (double)((k + CH - 1) / CH);
+  const double bytes = (double)T * k * (1152.0 + 4.0) + (double)T * H * 1152.0 +
+                       (double)T * nch * H * (512.0 + 2.0) * 4.0 * 2.0;
+  const double t_query = bytes / kGatherBytes;
+  ok();
+  return t_query < t_qblock ? 1 : 0;
+}
+
 size_t dsa_sparse_mla_extend_workspace(int T, int H, int QB, int u_max) {
   (void)T; (void)H; (void)QB; (void)u_max;
   return 0;

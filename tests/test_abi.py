@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -110,3 +110,27 @@ def test_decode_workspace_formula(lib):
     ws = dsa.sparse_mla_decode_workspace(8, 16, 2048)
     assert ws > 0 and ws % 256 == 0
     assert dsa.sparse_mla_decode_workspace(0, 16, 2048) == 0
+
+
+def test_extend_attend_path(lib):
+    """Host-side choice between the query-block and per-query extend paths:
+    the chunked-extend shape (4 x 1024 queries, unions of about 200 of 208
+    pages) keeps the query block; the long-context shape (8192 queries,
+    unions of about 2000 of 2048 pages, 62x the useful MFMA work) goes per
+    query; tiny unions always keep the query block."""
+    import numpy as np
+
+    assert dsa.extend_attend_path(np.full(16, 202), 4096, 16, 2048, 64, 256, 832) == "qblock"
+    assert dsa.extend_attend_path(np.full(32, 1986), 8192, 16, 2048, 64, 256, 2048) == \
+        "per_query"
+    assert dsa.extend_attend_path(np.full(64, 4), 4096, 16, 2048, 64, 64, 832) == "qblock"
+    # counts beyond u_max are capped (the kernel walks at most u_max slots)
+    a = dsa.extend_attend_path(np.full(16, 10 ** 6), 4096, 16, 2048, 64, 256, 208)
+    assert a == dsa.extend_attend_path(np.full(16, 208), 4096, 16, 2048, 64, 256, 208)
+    c = np.zeros(3, dtype=np.int32)
+    assert lib.dsa_extend_attend_path(c.ctypes.data, 3, 100, 16, 2048, 64, 64, 8) == \
+        -_lib.DSA_ERR_INVALID_ARG  # nQB != ceil(T / QB)
+    assert lib.dsa_extend_attend_path(None, 2, 100, 16, 2048, 64, 64, 8) == \
+        -_lib.DSA_ERR_INVALID_ARG
+    with pytest.raises(dsa.DsaError):
+        dsa.extend_attend_path(np.zeros(2), 100, 16, 0, 64, 64, 8)
