@@ -198,7 +198,7 @@ int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, i
  * MI355X: executed query-block flops sum_b min(blk_counts[b], u_max) *
  * QB * H * PS * (576 + 512) * 2 at 1.0e15 flop/s, against the per-query
  * bytes (selected latent rows of 1152 bytes, selection entries, queries and
- * fp32 partials) at 5.7e12 B/s.
+ * the per-chunk partial results, written and read back) at 5.3e12 B/s.
  *
  *   blk_counts_host  HOST int32 [nQB], the blk_counts of dsa_block_union
  *                    copied to the host; read only, not kept

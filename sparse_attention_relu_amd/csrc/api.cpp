@@ -52,7 +52,7 @@ int check_ragged(int T, int S, int PS, int MP, int num_pages) {
 size_t decode_ws(int T, int H, int k) {
   const int ch = dsa::mla_decode_chunk(T, k);
   const size_t nch = (size_t)((k + ch - 1) / ch);
-  return align256((size_t)T * nch * H * 512 * 4) + align256((size_t)T * nch * H * 2 * 4);
+  return align256((size_t)T * nch * H * 512 * 2) + align256((size_t)T * nch * H * 2 * 4);
 }
 
 }  // namespace
@@ -215,9 +215,9 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = static_cast<float*>(workspace);
+  a.part_o = static_cast<uint16_t*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256((size_t)T * nch * H * 512 * 4));
+                                       align256((size_t)T * nch * H * 512 * 2));
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
@@ -228,9 +228,10 @@ int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H
   if ((long)nQB != ((long)T + QB - 1) / QB)
     return -fail(DSA_ERR_INVALID_ARG, "extend path: nQB=%d does not match T=%d, QB=%d", nQB, T,
                  QB);
-  // measured on MI355X: executed MFMA rate of the query-block kernel and the
-  // HBM rate of the per-query gather
-  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.7e12;
+  // measured on MI355X, end to end per layer: executed MFMA rate of the
+  // query-block kernel, and the byte rate of the per-query path (partial
+  // kernel plus combine)
+  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.3e12;
   double pages = 0.0;
   for (int b = 0; b < nQB; ++b) {
     const int c = blk_counts_host[b];
@@ -240,7 +241,7 @@ int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H
   const int CH = dsa::mla_decode_chunk(T, k);
   const double nch = (double)((k + CH - 1) / CH);
   const double bytes = (double)T * k * (1152.0 + 4.0) + (double)T * H * 1152.0 +
-                       (double)T * nch * H * (512.0 + 2.0) * 4.0 * 2.0;
+                       (double)T * nch * H * (512.0 * 2.0 + 2.0 * 4.0) * 2.0;
   const double t_query = bytes / kGatherBytes;
   ok();
   return t_query < t_qblock ? 1 : 0;

@@ -57,7 +57,7 @@ struct MlaArgs {
   int T, S, H, k, PS, MP, QB, u_max;
   float sm_scale;
   uint16_t* out;
-  float* part_o;   // decode workspace
+  uint16_t* part_o;  // decode workspace: unnormalised partial O, bf16
   float* part_ml;
 };
 

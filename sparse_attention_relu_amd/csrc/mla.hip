@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int T, int S, int H, int k,
-    int PS, int MP, float sm_scale, int CH, int nch, int HB, float* __restrict__ part_o,
+    int PS, int MP, float sm_scale, int CH, int nch, int HB, uint16_t* __restrict__ part_o,
     float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
@@ -346,24 +346,39 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
       part_ml[(base + head) * 2 + 0] = m_run * 0.693147180559945309f;
       part_ml[(base + head) * 2 + 1] = l_run;
     }
-    float* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
+    // the unnormalised O goes out in bf16: the combine forms a convex
+    // combination of the chunks, so each value's rounding (2^-9 relative)
+    // stays that small in the result, and the partial traffic halves
+    uint16_t* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-      *reinterpret_cast<float4*>(orow + 16 * ct) = make_float4(o[ct][0], o[ct][1], o[ct][2], o[ct][3]);
+    for (int ct = 0; ct < 8; ++ct) {
+      uint2 v;
+      v.x = pack_bf16x2(o[ct][0], o[ct][1]);
+      v.y = pack_bf16x2(o[ct][2], o[ct][3]);
+      *reinterpret_cast<uint2*>(orow + 16 * ct) = v;
+    }
   }
 }
 
 // grid = (T, H), block = 256: merge the nch partials of (t, h),
 //   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0,
 // M = max m_c. Thread (g, d4) = (tid / 128, tid % 128) sums chunks g, g + 2,
-// ... for value columns 4 d4 .. 4 d4 + 3. The (m, l) pairs and the first
-// kCombAhead of this thread's O partials are all loaded at once; the chunk
-// weights e^(m_c - M) are then computed once, in LDS, and the two halves of
-// the sum meet through LDS.
+// ... for value columns 4 d4 .. 4 d4 + 3. The first kCombAhead of this
+// thread's O partials (bf16) and the (m, l) pairs are all loaded at once; the
+// chunk weights e^(m_c - M) are then computed once, in LDS, and the two
+// halves of the sum meet through LDS.
 constexpr int kCombMaxCH = 1024;  // partials per (row, head) the combine handles
 constexpr int kCombAhead = 16;    // O partials per thread loaded with the (m, l) pairs
 
-__global__ __launch_bounds__(256) void mla_decode_combine(const float* __restrict__ part_o,
+// acc += w * (four bf16 partial values packed in v)
+__device__ __forceinline__ void fma_bf16x4(float4& acc, float w, uint2 v) {
+  acc.x = fmaf(w, __uint_as_float(v.x << 16), acc.x);
+  acc.y = fmaf(w, __uint_as_float(v.x & 0xffff0000u), acc.y);
+  acc.z = fmaf(w, __uint_as_float(v.y << 16), acc.z);
+  acc.w = fmaf(w, __uint_as_float(v.y & 0xffff0000u), acc.w);
+}
+
+__global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int H, int nch,
                                                           uint16_t* __restrict__ out) {
@@ -374,7 +389,15 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
   const int tid = threadIdx.x, l = lane_id(), wave = tid >> 6;
   const int g = tid >> 7, d4 = tid & 127;
   const size_t base = (size_t)t * nch * H;
-  // ---- (m, l) of the chunks, then this thread's first O partials
+  // ---- this thread's first O partials, then the (m, l) pairs: all in
+  // flight together. The O loads are unconditional (a chunk past nch reads
+  // the last chunk and gets weight 0), so that none of them waits for another
+  uint2 va[kCombAhead];
+#pragma unroll
+  for (int u = 0; u < kCombAhead; ++u) {
+    const int c = min(g + 2 * u, nch - 1);
+    va[u] = *reinterpret_cast<const uint2*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4);
+  }
   float mloc = -INFINITY;
   for (int c = tid; c < nch; c += 256) {
     const size_t r = base + (size_t)c * H + h;
@@ -382,13 +405,6 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
     const float mm = lc > 0.f ? m : -INFINITY;
     s_w[c] = mm;
     mloc = fmaxf(mloc, mm);
-  }
-  float4 va[kCombAhead];
-#pragma unroll
-  for (int u = 0; u < kCombAhead; ++u) {
-    const int c = g + 2 * u;
-    va[u] = c < nch ? *reinterpret_cast<const float4*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // ---- M = max over live chunks (l_c > 0)
 #pragma unroll
@@ -414,31 +430,19 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const float* __restric
 #pragma unroll
   for (int u = 0; u < kCombAhead; ++u) {
     const int c = g + 2 * u;
-    const float w = c < nch ? s_w[c] : 0.f;
-    acc.x = fmaf(w, va[u].x, acc.x);
-    acc.y = fmaf(w, va[u].y, acc.y);
-    acc.z = fmaf(w, va[u].z, acc.z);
-    acc.w = fmaf(w, va[u].w, acc.w);
+    fma_bf16x4(acc, c < nch ? s_w[c] : 0.f, va[u]);
   }
   for (int c0 = g + 2 * kCombAhead; c0 < nch; c0 += 8) {
-    float w[4];
-    float4 v[4];
+    uint2 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = c0 + 2 * u;
-      w[u] = 0.f;
-      v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < nch) {
-        w[u] = s_w[c];
-        v[u] = *reinterpret_cast<const float4*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4);
-      }
+      const int c = min(c0 + 2 * u, nch - 1);
+      v[u] = *reinterpret_cast<const uint2*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc.x = fmaf(w[u], v[u].x, acc.x);
-      acc.y = fmaf(w[u], v[u].y, acc.y);
-      acc.z = fmaf(w[u], v[u].z, acc.z);
-      acc.w = fmaf(w[u], v[u].w, acc.w);
+      const int c = c0 + 2 * u;
+      fma_bf16x4(acc, c < nch ? s_w[c] : 0.f, v[u]);
     }
   }
   if (g == 1) s_o[d4] = acc;
