@@ -13,7 +13,9 @@ from .dsa import (  # noqa: F401
     head_mix,
     indexer_score_row,
     indexer_scores,
+    indexer_page_topk,
     indexer_topk,
+    page_tokens,
     member_bit,
     n_valid_keys,
     query_rows,

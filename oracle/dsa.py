@@ -24,6 +24,9 @@ function on it):
   to global keys by the request's page-table base, blocks packed over the
   ragged token axis and allowed to straddle requests.
 
+* "ref.py" page, ``streamindex_page_topk_ref``: the page-level indexer,
+  token scores max-pooled per page and the top ``k_pages`` pages.
+
 Readings taken where the pages leave a step open (each is a row of the
 design notes' list of readings):
 
@@ -157,6 +160,68 @@ def indexer_score_row(q, w, idx_cache, page_table, seq_lens, cu_q_lens, t):
     n = n_valid_keys(seq_lens[s], pos[t])
     keys = np.asarray(gather_rows(idx_cache, page_table, s, np.arange(n)), dtype=np.float64)
     return indexer_scores(np.asarray(q[t], np.float64), np.asarray(w[t], np.float64), keys)
+
+
+def page_pool(scores, PS):
+    """Page scores of a row whose valid positions are 0 .. n-1: page p is the
+    maximum over its valid positions p*PS .. min((p+1)*PS, n) - 1 ("ref.py",
+    ``streamindex_page_topk_ref``: masked positions at -inf, then a max over
+    the page axis). Only pages holding a valid position are returned."""
+    n = scores.shape[0]
+    n_pages = -(-n // PS)
+    padded = np.full(n_pages * PS, -np.inf)
+    padded[:n] = scores
+    return padded.reshape(n_pages, PS).max(axis=1)
+
+
+def indexer_page_topk(q, w, idx_cache, page_table, seq_lens, cu_q_lens, k_pages, rows=None):
+    """Exact page-level top-k of the lightning indexer.
+
+    "ref.py" page, ``streamindex_page_topk_ref``: the token scores of
+    ``streamindex_topk_ref`` with every masked position (j >= kv_len or
+    j > abs_q) at -inf, max-pooled over the PS positions of each seq-local
+    page; the top ``k_pages`` pages of that page score, -1 where the score is
+    -inf (a page with no valid position) and past the last page.
+
+    Read exactly (like the token top-k): pages in the canonical order, page
+    score descending, ties to the lower page id. A page is valid iff it holds
+    a valid position, i.e. the first ceil(n_valid / PS) pages of the row.
+
+    Returns int32 [T, k_pages] of seq-local page ids.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    PS = idx_cache.shape[1]
+    T = q.shape[0]
+    seq, pos = query_rows(seq_lens, cu_q_lens, T)
+    out = np.full((T, k_pages), -1, dtype=np.int32)
+    for t in range(T) if rows is None else rows:
+        s = int(seq[t])
+        if s < 0:
+            continue
+        n = n_valid_keys(seq_lens[s], pos[t])
+        if n == 0:
+            continue
+        keys = np.asarray(gather_rows(idx_cache, page_table, s, np.arange(n)), dtype=np.float64)
+        page_scores = page_pool(indexer_scores(q[t], w[t], keys), PS)
+        order = canonical_order(page_scores)[: min(k_pages, page_scores.size)]
+        out[t, : order.size] = order
+    return out
+
+
+def page_tokens(pages, PS):
+    """Positions of the selected pages: row t lists, for each slot i of
+    ``pages[t]``, the positions ``pages[t, i] * PS + r`` for r < PS (-1 for
+    a -1 slot). The attention over them masks j >= kv_len and j > abs_q
+    itself, so a page that runs past the sequence end only contributes its
+    valid positions ("ref.py", ``sparse_mla_ref`` masks; the page-budget
+    decode of the backend page attends all valid tokens of its pages)."""
+    pages = np.asarray(pages, dtype=np.int64)
+    T, kp = pages.shape
+    r = np.arange(PS, dtype=np.int64)
+    tok = pages[:, :, None] * PS + r[None, None, :]
+    tok = np.where(pages[:, :, None] >= 0, tok, -1)
+    return tok.reshape(T, kp * PS).astype(np.int32)
 
 
 # ----------------------------------------------------------------------------

@@ -414,7 +414,98 @@ def pin_mla_softmax_rows_sum_to_one():
         assert np.allclose(p.sum(-1), 1.0, atol=1e-12) and (p >= 0).all()
 
 
+def py_scores(q, w, cache, pt, s, t, n):
+    """Pure-Python scores of row t against positions 0 .. n-1 of sequence s."""
+    sc = []
+    for j in range(n):
+        kj = py_key(cache, pt, s, j)
+        tot = 0.0
+        for h in range(len(q[t])):
+            d = sum(q[t][h][x] * kj[x] for x in range(len(kj)))
+            tot += w[t][h] * (d if d > 0 else 0.0)
+        sc.append(tot)
+    return sc
+
+
+def brute_page_topk(q, w, cache, pt, seq_lens, cu, k_pages):
+    """Pure-Python page top-k: explicit page maxima, rank counting."""
+    PS = len(cache[0])
+    T = len(q)
+    out = [[-1] * k_pages for _ in range(T)]
+    for t, info in enumerate(py_abs_positions(seq_lens, cu, T)):
+        if info is None:
+            continue
+        s, a = info
+        n = max(0, min(int(seq_lens[s]), a + 1))
+        sc = py_scores(q, w, cache, pt, s, t, n)
+        npg = (n + PS - 1) // PS
+        ps = [max(sc[p * PS: min((p + 1) * PS, n)]) for p in range(npg)]
+        for p in range(npg):
+            rank = sum(1 for i in range(npg) if ps[i] > ps[p] or (ps[i] == ps[p] and i < p))
+            if rank < k_pages:
+                out[t][rank] = p
+    return out
+
+
+def pin_page_topk_bruteforce():
+    """Micro workloads with partial last pages, positive head weights and
+    mixed-sign ones (negative scores: a masked position must never count
+    as 0 in a page's maximum)."""
+    for seed in range(6):
+        wl = micro(seed)
+        q, w, cache, pt, sl, cu = _indexer_inputs(wl, "b")
+        for sign in (np.ones(w.shape[1]), np.array([-1.0, 1.0, -1.0])):
+            ws = w * sign[None, :]
+            for kp in (1, 2, 7):
+                got = oracle.indexer_page_topk(q, ws, cache, pt, sl, cu, kp)
+                exp = brute_page_topk(q.tolist(), ws.tolist(), cache.tolist(), pt.tolist(),
+                                      sl.tolist(), cu.tolist(), kp)
+                assert got.tolist() == exp, (seed, kp)
+
+
+def pin_page_topk_unit_pages_is_token_topk():
+    """With one position per page the page top-k is the token top-k."""
+    for seed in range(3):
+        wl = micro(100 + seed, PS=1, MP=20)
+        q, w, cache, pt, sl, cu = _indexer_inputs(wl, "b")
+        got = oracle.indexer_page_topk(q, w, cache, pt, sl, cu, wl.k)
+        assert np.array_equal(got, oracle.indexer_topk(q, w, cache, pt, sl, cu, wl.k)), seed
+
+
+def pin_page_topk_invariants_tiny():
+    """Tiny workload (PS 16): padding count, valid pages only, page scores
+    non-increasing, and the best token's page first."""
+    wl = W.config(1, with_mla=False)
+    for bname in ("decode", "extend"):
+        q, w, cache, pt, sl, cu = _indexer_inputs(wl, bname)
+        T = q.shape[0]
+        kp = 3
+        got = oracle.indexer_page_topk(q, w, cache, pt, sl, cu, kp)
+        seq, pos = oracle.query_rows(sl, cu, T)
+        for t in range(T):
+            if seq[t] < 0:
+                assert (got[t] == -1).all()
+                continue
+            n = oracle.n_valid_keys(sl[seq[t]], pos[t])
+            npg = -(-n // wl.PS)
+            row = got[t]
+            assert (row[min(kp, npg):] == -1).all() and (row[:min(kp, npg)] >= 0).all()
+            assert (row[:min(kp, npg)] < npg).all() and len(set(row[:min(kp, npg)])) == min(kp, npg)
+            sc = oracle.indexer_score_row(q, w, cache, pt, sl, cu, t)
+            pmax = [sc[p * wl.PS:(p + 1) * wl.PS].max() for p in row[:min(kp, npg)]]
+            assert all(pmax[i] >= pmax[i + 1] for i in range(len(pmax) - 1))
+            assert row[0] == int(np.argmax(sc)) // wl.PS or pmax[0] == sc.max()
+
+
+def pin_page_tokens():
+    pages = np.array([[2, 0, -1], [-1, -1, -1]])
+    exp = [[8, 9, 10, 11, 0, 1, 2, 3, -1, -1, -1, -1], [-1] * 12]
+    assert oracle.page_tokens(pages, 4).tolist() == exp
+
+
 PINS = [
+    pin_page_topk_bruteforce, pin_page_topk_unit_pages_is_token_topk,
+    pin_page_topk_invariants_tiny, pin_page_tokens,
     pin_indexer_golden, pin_indexer_bruteforce, pin_indexer_tiny_bruteforce,
     pin_indexer_zero_query, pin_indexer_single_head, pin_indexer_k_covers_all,
     pin_indexer_invariants_tiny, pin_indexer_page_permutation, pin_indexer_weight_scaling,
@@ -500,6 +591,20 @@ def _m_softmax_wrong_axis(logits):
     return e / e.sum(axis=0, keepdims=True)
 
 
+def _m_page_pool_mean(scores, PS):
+    n = scores.shape[0]
+    npg = -(-n // PS)
+    return np.array([scores[p * PS:(p + 1) * PS].mean() for p in range(npg)])
+
+
+def _m_page_pool_masked_zero(scores, PS):
+    n = scores.shape[0]
+    npg = -(-n // PS)
+    padded = np.zeros(npg * PS)
+    padded[:n] = scores
+    return padded.reshape(npg, PS).max(axis=1)
+
+
 def _m_query_rows_shift(seq_lens, cu_q_lens, T):
     seq, pos = _ORIG["query_rows"](seq_lens, cu_q_lens, T)
     return seq, np.where(pos >= 0, pos - 1, pos)
@@ -526,6 +631,8 @@ MUTANTS = {
     "attend_drops_rope": ("attend", _m_attend_nope_only),
     "softmax_axis": ("softmax", _m_softmax_wrong_axis),
     "abs_position_shift": ("query_rows", _m_query_rows_shift),
+    "page_pool_mean": ("page_pool", _m_page_pool_mean),
+    "page_pool_masked_as_zero": ("page_pool", _m_page_pool_masked_zero),
 }
 
 
