@@ -97,6 +97,49 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
                      size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_indexer_page_topk — lightning-indexer exact top-k over pages.
+ * "ref.py", streamindex_page_topk_ref.
+ *
+ * The scores of dsa_indexer_topk, with every position that is not valid for
+ * the row (j >= seq_lens[s] or j > abs_q) at -inf, max-pooled over the PS
+ * positions of each seq-local page p (positions p*PS .. p*PS + PS - 1). The
+ * pages that hold a valid position are the first ceil(n_valid / PS) of the
+ * row; pages[t, :] receives the first min(k_pages, that many) of them by
+ * page score descending, equal scores by page id ascending, then -1 up to
+ * k_pages. Rows outside every sequence are all -1; pages is fully written.
+ *
+ *   q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, max_q_len
+ *              as in dsa_indexer_topk
+ *   pages      int32 [T, k_pages]  output, seq-local page ids
+ * Supported: as dsa_indexer_topk, with PS a multiple of 16 up to 64 and
+ * 1 <= k_pages <= 4096; otherwise DSA_ERR_UNSUPPORTED.
+ */
+size_t dsa_indexer_page_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k_pages,
+                                       int max_q_len);
+int dsa_indexer_page_topk(const void* q_idx, const float* w, const void* idx_cache,
+                          int num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                          int k_pages, int max_q_len, int32_t* pages, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_page_tokens — the positions of selected pages, for the token-exact
+ * attention entry points: tokens[t, i] = pages[t, i / PS] * PS + i % PS, or
+ * -1 where pages[t, i / PS] is -1. Attending these with
+ * dsa_sparse_mla_decode (or through dsa_block_union and
+ * dsa_sparse_mla_extend) attends every valid position of the selected pages
+ * (the attention masks j >= seq_lens and j > abs_q itself): the page-budget
+ * decode of "dsa_sparse_backend.py" (the page-scoring indexer path).
+ *
+ *   pages   int32 [T, k_pages]
+ *   tokens  int32 [T, k_pages * PS]  output
+ * Returns DSA_ERR_INVALID_ARG for T < 0, k_pages < 1, PS < 1 or
+ * k_pages * PS > 65536.
+ */
+int dsa_page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* tokens,
+                    void* stream);
+
+/*
  * dsa_block_union — per query-block union of selected pages and per-token
  * membership. "sparse_mla_prefill_qblock.py", build_block_unit_tables, with
  * the ragged lifting of sparse_mla_attention_qblock.

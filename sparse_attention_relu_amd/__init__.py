@@ -11,10 +11,13 @@ from ._lib import (  # noqa: F401
     block_union_workspace,
     extend_attend_path,
     header_functions,
+    indexer_page_topk,
+    indexer_page_topk_workspace,
     indexer_topk,
     indexer_topk_workspace,
     last_error,
     load,
+    page_tokens,
     profile_enable,
     profile_read,
     sparse_mla_decode,

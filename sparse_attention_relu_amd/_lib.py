@@ -41,6 +41,10 @@ SIGNATURES = {
                               + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_sparse_mla_extend_workspace": (_c_size, [_c_int] * 4),
     "dsa_extend_attend_path": (_c_int, [_vp] + [_c_int] * 7),
+    "dsa_indexer_page_topk_workspace": (_c_size, [_c_int] * 8),
+    "dsa_indexer_page_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
+                              + [_vp, _vp, _c_size, _vp]),
+    "dsa_page_tokens": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dsa_profile_enable": (_c_int, [_c_int]),
     "dsa_profile_read": (_c_int, [_c_int, ctypes.c_char_p, _c_int, _vp, _vp, _vp]),
     "dsa_sparse_mla_extend": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -205,6 +209,51 @@ def indexer_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int,
                                  _ptr(seq_lens), _ptr(cu_q_lens), T, S, H, D, PS, MP, k,
                                  max_q_len, _ptr(out), _ptr(ws), nbytes, _stream(stream))
     _check("dsa_indexer_topk", st)
+    return out
+
+
+def indexer_page_topk_workspace(T, S, H, D, PS, MP, k_pages, max_q_len) -> int:
+    return load().dsa_indexer_page_topk_workspace(T, S, H, D, PS, MP, k_pages, max_q_len)
+
+
+def indexer_page_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k_pages: int,
+                      max_q_len: int, out=None, workspace=None, stream=None):
+    """Exact page-level indexer top-k -> int32 [T, k_pages] seq-local page
+    ids (dsa_indexer_page_topk)."""
+    torch = _torch()
+    dev = q_idx.device
+    _need(q_idx, "q_idx", torch.bfloat16, 3, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    _need(idx_cache, "idx_cache", torch.bfloat16, 3, dev)
+    S, MP = _ragged(page_table, seq_lens, cu_q_lens, dev)
+    T, H, D = q_idx.shape
+    P, PS, Dc = idx_cache.shape
+    if Dc != D or tuple(w.shape) != (T, H):
+        raise ValueError("q_idx [T,H,D], w [T,H], idx_cache [P,PS,D] disagree")
+    if out is None:
+        out = torch.empty((T, k_pages), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, 2, dev)
+    nbytes = indexer_page_topk_workspace(T, S, H, D, PS, MP, k_pages, max_q_len)
+    ws = _workspace(nbytes, dev, workspace)
+    st = load().dsa_indexer_page_topk(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P,
+                                      _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S,
+                                      H, D, PS, MP, k_pages, max_q_len, _ptr(out), _ptr(ws),
+                                      nbytes, _stream(stream))
+    _check("dsa_indexer_page_topk", st)
+    return out
+
+
+def page_tokens(pages, PS: int, out=None, stream=None):
+    """Positions of selected pages -> int32 [T, k_pages * PS] (dsa_page_tokens)."""
+    torch = _torch()
+    dev = pages.device
+    _need(pages, "pages", torch.int32, 2, dev)
+    T, kp = pages.shape
+    if out is None:
+        out = torch.empty((T, kp * PS), dtype=torch.int32, device=dev)
+    _need(out, "out", torch.int32, 2, dev)
+    st = load().dsa_page_tokens(_ptr(pages), T, kp, PS, _ptr(out), _stream(stream))
+    _check("dsa_page_tokens", st)
     return out
 
 

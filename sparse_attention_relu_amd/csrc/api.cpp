@@ -38,6 +38,8 @@ constexpr int kMaxCap = 1 << 24;  // positions per sequence (MP * PS)
 
 long scores_ld(int MP, int PS) { return (((long)MP * PS) + 63) / 64 * 64; }
 
+long pages_ld(int MP) { return ((long)MP + 63) / 64 * 64; }
+
 int check_ragged(int T, int S, int PS, int MP, int num_pages) {
   if (T < 0) return fail(DSA_ERR_INVALID_ARG, "T=%d must be >= 0", T);
   if (S < 0) return fail(DSA_ERR_INVALID_ARG, "S=%d must be >= 0", S);
@@ -120,6 +122,73 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
   hipError_t e = dsa::indexer_score(a, s);
   if (e != hipSuccess) return hip_status(e, "indexer score launch");
   return hip_status(dsa::indexer_select(a, s), "indexer top-k launch");
+}
+
+// ---------------------------------------------------------------------------
+size_t dsa_indexer_page_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k_pages,
+                                       int max_q_len) {
+  (void)S; (void)H; (void)D; (void)k_pages; (void)max_q_len;
+  if (T <= 0 || PS <= 0 || MP <= 0) return 0;
+  return align256((size_t)T * scores_ld(MP, PS) * 4) + align256((size_t)T * pages_ld(MP) * 4);
+}
+
+int dsa_indexer_page_topk(const void* q_idx, const float* w, const void* idx_cache,
+                          int num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                          int k_pages, int max_q_len, int32_t* pages, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (H < 1 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "indexer H=%d not in [1, 64]", H);
+  if (D != 32 && D != 64 && D != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer D=%d not in {32, 64, 128}", D);
+  if (k_pages < 1 || k_pages > 4096)
+    return fail(DSA_ERR_UNSUPPORTED, "k_pages=%d not in [1, 4096]", k_pages);
+  if (PS % 16 != 0 || PS > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "page top-k PS=%d is not a multiple of 16 up to 64", PS);
+  if (T == 0) return ok();
+  if (!q_idx || !w || !idx_cache || !page_table || !seq_lens || !cu_q_lens || !pages)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(q_idx) || !aligned16(idx_cache))
+    return fail(DSA_ERR_INVALID_ARG, "q_idx and idx_cache must be 16-byte aligned");
+  const size_t need = dsa_indexer_page_topk_workspace(T, S, H, D, PS, MP, k_pages, max_q_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "page top-k workspace %zu < %zu bytes", workspace_bytes,
+                need);
+  dsa::IndexerArgs a;
+  a.q = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.cache = static_cast<const uint16_t*>(idx_cache);
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.T = T; a.S = S; a.H = H; a.D = D; a.PS = PS; a.MP = MP; a.k = k_pages;
+  a.max_q_len = max_q_len;
+  a.scores = static_cast<float*>(workspace);
+  a.ld = scores_ld(MP, PS);
+  a.page_scores = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                           align256((size_t)T * a.ld * 4));
+  a.ldp = pages_ld(MP);
+  a.topk = pages;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::indexer_score(a, s);
+  if (e != hipSuccess) return hip_status(e, "indexer score launch");
+  e = dsa::indexer_page_pool(a, s);
+  if (e != hipSuccess) return hip_status(e, "page pool launch");
+  return hip_status(dsa::indexer_page_select(a, s), "page top-k launch");
+}
+
+int dsa_page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* tokens,
+                    void* stream) {
+  if (T < 0 || k_pages < 1 || PS < 1 || (long)k_pages * PS > 65536)
+    return fail(DSA_ERR_INVALID_ARG, "page tokens: T=%d, k_pages=%d, PS=%d (need T >= 0 and "
+                "1 <= k_pages * PS <= 65536)", T, k_pages, PS);
+  if (T == 0) return ok();
+  if (!pages || !tokens) return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  return hip_status(dsa::page_tokens(pages, T, k_pages, PS, tokens,
+                                     static_cast<hipStream_t>(stream)),
+                    "page tokens launch");
 }
 
 // ---------------------------------------------------------------------------

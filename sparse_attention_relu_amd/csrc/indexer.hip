@@ -992,7 +992,7 @@ template <int IPT, int M>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ seq_lens,
-                                                      int S, int cap, int k,
+                                                      int S, int cap, int unit, int k,
                                                       int32_t* __restrict__ topk) {
   constexpr int NT = kSelNT;
   constexpr int CHUNK = NT * M;
@@ -1016,7 +1016,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   uint32_t k0[M];
   load_keys_ahead<M>(row, ld < (long)CHUNK ? (int)ld : CHUNK, k0);
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
-  const int n = ri.n_valid;
+  // positions of the row: its valid tokens, or (unit = PS) the pages that
+  // hold one
+  const int n = (ri.n_valid + unit - 1) / unit;
   int32_t* orow = topk + (size_t)t * k;
   if (n == 0) {
     for (int i = tid; i < k; i += NT) orow[i] = -1;
@@ -1340,8 +1342,17 @@ size_t topk_select_lds_bytes(int k) {
   }
 }
 
+// One select launch: rows of `ld` scores, n = ceil(n_valid / unit) of them
+// valid, k kept.
+struct SelectJob {
+  const float* scores;
+  long ld;
+  int unit, k;
+  int32_t* out;
+};
+
 template <int IPT, int M>
-static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
+static hipError_t launch_select(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
   const size_t lds = SelectCfg<IPT>::BYTES;
   // raise the dynamic-LDS limit once per device
   static std::atomic<uint64_t> attr_done{0};
@@ -1356,23 +1367,101 @@ static hipError_t launch_select(const IndexerArgs& a, hipStream_t st) {
     attr_done.fetch_or(bit);
   }
   ProfScope prof("topk_select", st);
-  hipLaunchKernelGGL((topk_select<IPT, M>), dim3(a.T), dim3(kSelNT), lds, st, a.scores, a.ld,
-                     a.cu, a.seq_lens, a.S, a.MP * a.PS, a.k, a.topk);
+  hipLaunchKernelGGL((topk_select<IPT, M>), dim3(a.T), dim3(kSelNT), lds, st, j.scores, j.ld,
+                     a.cu, a.seq_lens, a.S, a.MP * a.PS, j.unit, j.k, j.out);
   return hipGetLastError();
 }
 
 // positions per thread: 8 when a whole score row fits one chunk of 8192
 template <int IPT>
-static hipError_t launch_select_m(const IndexerArgs& a, hipStream_t st) {
-  return a.ld <= (long)kSelNT * 8 ? launch_select<IPT, 8>(a, st) : launch_select<IPT, 16>(a, st);
+static hipError_t launch_select_m(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
+  return j.ld <= (long)kSelNT * 8 ? launch_select<IPT, 8>(a, j, st)
+                                  : launch_select<IPT, 16>(a, j, st);
+}
+
+static hipError_t select_job(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
+  switch (select_ipt(j.k)) {
+    case 2: return launch_select_m<2>(a, j, st);
+    case 4: return launch_select_m<4>(a, j, st);
+    default: return launch_select_m<8>(a, j, st);
+  }
 }
 
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
-  switch (select_ipt(a.k)) {
-    case 2: return launch_select_m<2>(a, st);
-    case 4: return launch_select_m<4>(a, st);
-    default: return launch_select_m<8>(a, st);
+  return select_job(a, SelectJob{a.scores, a.ld, 1, a.k, a.topk}, st);
+}
+
+hipError_t indexer_page_select(const IndexerArgs& a, hipStream_t st) {
+  return select_job(a, SelectJob{a.page_scores, a.ldp, a.PS, a.k, a.topk}, st);
+}
+
+// ---------------------------------------------------------------------------
+// Page scores ("ref.py", streamindex_page_topk_ref: masked positions at
+// -inf, then the maximum over each page). grid = T, block = 256. A
+// 16-lane group covers one page (PS <= 64: four scores per lane); a wave
+// does four pages per step. Pages at or past ceil(n_valid / PS) are not
+// written: the select never reads them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void page_pool(const float* __restrict__ scores, long ld,
+                                                 const int32_t* __restrict__ cu,
+                                                 const int32_t* __restrict__ seq_lens, int S,
+                                                 int cap, int PS, float* __restrict__ pscores,
+                                                 long ldp) {
+  const int t = blockIdx.x;
+  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
+  const int n = ri.n_valid;
+  const int npg = (n + PS - 1) / PS;
+  const int l = lane_id(), grp = l >> 4, i = l & 15;
+  const float* row = scores + (size_t)t * ld;
+  float* prow = pscores + (size_t)t * ldp;
+  for (int p0 = 4 * (threadIdx.x >> 6); p0 < npg; p0 += 16) {
+    const int p = p0 + grp;
+    float m = -INFINITY;
+    if (p < npg && 4 * i < PS) {
+      const int j = p * PS + 4 * i;
+      if (j + 4 <= n) {
+        const float4 v = *reinterpret_cast<const float4*>(row + j);
+        m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+      } else {
+        for (int e = 0; e < 4; ++e)
+          if (j + e < n) m = fmaxf(m, row[j + e]);
+      }
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
+    if (p < npg && i == 0) prow[p] = m;
   }
+}
+
+hipError_t indexer_page_pool(const IndexerArgs& a, hipStream_t st) {
+  ProfScope prof("page_pool", st);
+  hipLaunchKernelGGL(page_pool, dim3(a.T), dim3(256), 0, st, a.scores, a.ld, a.cu, a.seq_lens,
+                     a.S, a.MP * a.PS, a.PS, a.page_scores, a.ldp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Positions of selected pages: tokens[t, i] = pages[t, i / PS] * PS + i % PS,
+// or -1 for a -1 page slot. grid = (T, ceil(k_pages * PS / 256)).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void page_token_list(const int32_t* __restrict__ pages,
+                                                       int k_pages, int PS,
+                                                       int32_t* __restrict__ tokens) {
+  const int t = blockIdx.x;
+  const int n = k_pages * PS;
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int p = pages[(size_t)t * k_pages + i / PS];
+  tokens[(size_t)t * n + i] = p >= 0 ? p * PS + i % PS : -1;
+}
+
+hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* tokens,
+                       hipStream_t st) {
+  const int n = k_pages * PS;
+  ProfScope prof("page_token_list", st);
+  hipLaunchKernelGGL(page_token_list, dim3(T, (n + 255) / 256), dim3(256), 0, st, pages,
+                     k_pages, PS, tokens);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -21,10 +21,18 @@ struct IndexerArgs {
   float* scores;  // workspace [T, ld]
   long ld;
   int32_t* topk;
+  // page-level selection: page scores [T, ldp] (max over each page's valid
+  // positions); the select then ranks pages, ceil(n_valid / PS) per row
+  float* page_scores;
+  long ldp;
 };
 
 hipError_t indexer_score(const IndexerArgs& a, hipStream_t st);
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st);
+hipError_t indexer_page_pool(const IndexerArgs& a, hipStream_t st);
+hipError_t indexer_page_select(const IndexerArgs& a, hipStream_t st);
+hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* tokens,
+                       hipStream_t st);
 size_t topk_select_lds_bytes(int k);
 
 struct UnionArgs {

@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -135,3 +135,25 @@ def test_extend_attend_path(lib):
         -_lib.DSA_ERR_INVALID_ARG
     with pytest.raises(dsa.DsaError):
         dsa.extend_attend_path(np.zeros(2), 100, 16, 0, 64, 64, 8)
+
+
+def test_page_entry_validation(lib):
+    def call(**kw):
+        a = dict(T=2, S=1, H=32, D=128, PS=64, MP=4, kp=4, ws=None, wsb=0)
+        a.update(kw)
+        return lib.dsa_indexer_page_topk(1 << 12, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12, 1 << 12,
+                                         a["T"], a["S"], a["H"], a["D"], a["PS"], a["MP"],
+                                         a["kp"], 1, 1 << 12, a["ws"], a["wsb"], None)
+
+    assert call(kp=0) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(kp=5000) == _lib.DSA_ERR_UNSUPPORTED
+    assert call(PS=128, MP=2) == _lib.DSA_ERR_UNSUPPORTED  # one 16-lane group pools a page
+    assert call(PS=24) == _lib.DSA_ERR_UNSUPPORTED
+    assert call() == _lib.DSA_ERR_WORKSPACE
+    assert call(T=0) == _lib.DSA_OK
+    need = dsa.indexer_page_topk_workspace(2, 1, 32, 128, 64, 4, 4, 1)
+    assert need >= dsa.indexer_topk_workspace(2, 1, 32, 128, 64, 4, 4, 1) + 2 * 4 * 4
+    assert lib.dsa_page_tokens(1 << 12, 2, 0, 64, 1 << 12, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_page_tokens(1 << 12, 2, 2048, 64, 1 << 12, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_page_tokens(None, 2, 4, 64, 1 << 12, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_page_tokens(1 << 12, 0, 4, 64, 1 << 12, None) == _lib.DSA_OK

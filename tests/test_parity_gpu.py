@@ -384,3 +384,97 @@ def test_repeat_determinism(dsa):
     o1, _, _ = _gpu_extend(dsa, d, q, d.kv_cache[0], b.cu_q_lens, tk1, wl.sm_scale, 16, 32)
     o2, _, _ = _gpu_extend(dsa, d, q, d.kv_cache[0], b.cu_q_lens, tk1, wl.sm_scale, 16, 32)
     assert np.array_equal(o1, o2)
+
+
+# ----------------------------------------------------------------------------
+# Page-level selection: page top-k, page positions, attention over the pages
+# ----------------------------------------------------------------------------
+def _oracle_page_topk(wl, q_idx, w, cu, k_pages):
+    return oracle.indexer_page_topk(bf16_to_f64(q_idx), w.astype(np.float64),
+                                    bf16_to_f64(wl.idx_cache), wl.page_table, wl.seq_lens,
+                                    np.asarray(cu), k_pages)
+
+
+def _gpu_page_topk(dsa, d, q_idx, w, cu, k_pages, max_q_len):
+    torch = torch_mod()
+    out = dsa.indexer_page_topk(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache, d.page_table,
+                                d.seq_lens, i32(cu, "cuda"), k_pages, max_q_len)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("bname", ["decode", "extend"])
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+def test_page_topk_tiny(dsa, bname, path):
+    wl = W.config(1)
+    b = wl.batches[bname]
+    d = Dev(wl)
+    mql = 1 if path == "rows" else max(2, _max_q_len(b.cu_q_lens))
+    for kp in (1, 3, 16):
+        log(f"page top-k tiny {bname} path={path} k_pages={kp}")
+        got = _gpu_page_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, kp, mql)
+        assert np.array_equal(got, _oracle_page_topk(wl, b.q_idx, b.w, b.cu_q_lens, kp))
+
+
+PAGE_EDGE = {
+    # name: (S, kv_lens, PS, MP, q_lens, H, D, k_pages, negative weights)
+    "ps16_mixed_empty_seq": (3, [37, 200, 64], 16, 16, [1, 5, 0], 4, 32, 4, False),
+    "ps32_negative_weights": (2, [77, 300], 32, 10, [3, 7], 8, 64, 3, True),
+    "ps48_partial_pages": (2, [100, 1000], 48, 24, [2, 9], 32, 128, 5, True),
+    "ps64_k_covers_all": (2, [1000, 4097], 64, 80, [4, 3], 32, 128, 100, False),
+    "ps16_rows_above_8192_pages": (1, [132000], 16, 8256, [2], 4, 32, 64, True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGE_EDGE))
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+def test_page_topk_edges(dsa, name, path):
+    S, kv, PS, MP, ql, H, D, kp, neg = PAGE_EDGE[name]
+    cu = np.concatenate([[0], np.cumsum(ql)]).tolist()
+    wl = W.build(name=name, seed=91, S=S, kv_lens=kv, PS=PS, MP=MP, batches={"b": cu}, H_idx=H,
+                 D_idx=D, k=kp, with_mla=False, extra_pages=1)
+    b = wl.batches["b"]
+    w = b.w.copy()
+    if neg:  # negative head weights: page maxima below 0, masked slots must not count
+        w[:, ::2] *= -1.0
+    log(f"page top-k edge {name} path={path}")
+    d = Dev(wl)
+    mql = 1 if path == "rows" else max(2, max(ql))
+    got = _gpu_page_topk(dsa, d, b.q_idx, w, cu, kp, mql)
+    assert np.array_equal(got, _oracle_page_topk(wl, b.q_idx, w, cu, kp))
+
+
+def test_page_tokens_and_attention_tiny(dsa):
+    """Page top-k -> page positions -> attention (decode kernels, and the
+    query-block path through the union) against the oracle's attention
+    over the oracle's page positions."""
+    torch = torch_mod()
+    wl = W.config(1)
+    d = Dev(wl)
+    kp = 3
+    for bname in ("decode", "extend"):
+        b = wl.batches[bname]
+        bt = d.batch(bname)
+        mql = max(1, _max_q_len(b.cu_q_lens))
+        pages = dsa.indexer_page_topk(bt["q_idx"], bt["w"], d.idx_cache, d.page_table,
+                                      d.seq_lens, bt["cu"], kp, mql)
+        tok = dsa.page_tokens(pages, wl.PS)
+        torch.cuda.synchronize()
+        exp_pages = _oracle_page_topk(wl, b.q_idx, b.w, b.cu_q_lens, kp)
+        exp_tok = oracle.page_tokens(exp_pages, wl.PS)
+        assert np.array_equal(pages.cpu().numpy(), exp_pages)
+        assert np.array_equal(tok.cpu().numpy(), exp_tok)
+        ref = oracle.sparse_mla(bf16_to_f64(b.q_mla[0]), bf16_to_f64(wl.kv_cache[0]),
+                                wl.page_table, wl.seq_lens, b.cu_q_lens, exp_tok, wl.sm_scale,
+                                wl.Dv)
+        out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"],
+                                    tok, wl.sm_scale)
+        torch.cuda.synchronize()
+        check_attention(to_np(out), ref, what=f"page attend {bname} (per query)")
+        if bname == "extend":
+            for QB in wl.QB:
+                u, c, m = dsa.block_union(tok, d.seq_lens, bt["cu"], wl.PS, wl.MP, QB, wl.u_max)
+                out = dsa.sparse_mla_extend(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens,
+                                            bt["cu"], u, c, m, QB, wl.sm_scale)
+                torch.cuda.synchronize()
+                check_attention(to_np(out), ref, what=f"page attend extend QB={QB}")
