@@ -269,6 +269,39 @@ def bench_decode(dsa, wl, args):
                 attend_ms=round(part(("mla_decode_partial", "mla_decode_combine")), 4))
 
 
+def bench_page_decode(dsa, wl, args):
+    """The same decode layer with page-level selection: the page top-k
+    (k_pages = k / PS pages, max-pooled page scores), the selected pages'
+    positions, then sparse MLA over every valid position of those pages."""
+    import torch
+
+    d = _dev_inputs(wl, "decode")
+    b = wl.batches["decode"]
+    T, H, PS = b.T, wl.H_mla, wl.PS
+    kp = max(1, wl.k // PS)
+    pages = torch.empty((T, kp), dtype=torch.int32, device="cuda")
+    tok = torch.empty((T, kp * PS), dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
+    ws_i = torch.empty(max(1, dsa.indexer_page_topk_workspace(T, wl.S, wl.H_idx, wl.D_idx, PS,
+                                                              wl.MP, kp, 1)),
+                       dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(max(1, dsa.sparse_mla_decode_workspace(T, H, kp * PS)),
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.indexer_page_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
+                              d["seq_lens"], d["cu"], kp, 1, out=pages, workspace=ws_i)
+        dsa.page_tokens(pages, PS, out=tok)
+        dsa.sparse_mla_decode(d["q"][0], d["kv_cache"][0], d["page_table"], d["seq_lens"],
+                              d["cu"], tok, wl.sm_scale, out=out, workspace=ws_d)
+
+    steps = max(5, args.steps // 2)
+    ms = _timed(step, steps, min(args.warmup, 3))
+    kt = _kernel_times(dsa, step, steps)
+    return {"k_pages": kp, "ms_per_step": round(ms, 5), "tok_s": round(T / (ms * 1e-3), 1),
+            "kernels_us": {nm: round(avg * 1e3, 2) for nm, (n, avg) in kt.items()}}
+
+
 # ----------------------------------------------------------------------------
 # extend
 # ----------------------------------------------------------------------------
@@ -494,7 +527,7 @@ def main(argv=None):
             rd = bench_decode(dsa, wlr, args)
             line = {"workload": wlr.name, "tok_s": round(rd["tok_s"], 1),
                     "ms_per_step": round(rd["ms"], 5), "roofline": rd["roofline"],
-                    "kernels": rd["kernels"]}
+                    "kernels": rd["kernels"], "page_decode": bench_page_decode(dsa, wlr, args)}
         else:
             wle = W.config(args.extend_config or 4)
             qb = args.qb if args.qb in wle.QB else wle.QB[0]
@@ -523,6 +556,7 @@ def main(argv=None):
                    "step": "one DSA decode layer: indexer top-k + sparse MLA"},
         "roofline": dec["roofline"],
         "kernels": dec["kernels"],
+        "page_decode": bench_page_decode(dsa, wl, args),
     }
     if args.only == "all" and args.ragged_config and args.ragged_config != args.config:
         wlr = W.config(args.ragged_config)
@@ -531,7 +565,8 @@ def main(argv=None):
             "workload": wlr.name, "seqs": wlr.S, "tokens": int(wlr.seq_lens.sum()),
             "tok_s": round(rd["tok_s"], 1), "ms_per_step": round(rd["ms"], 5),
             "indexer_ms": rd["indexer_ms"], "attend_ms": rd["attend_ms"],
-            "roofline": rd["roofline"], "kernels": rd["kernels"]}
+            "roofline": rd["roofline"], "kernels": rd["kernels"],
+            "page_decode": bench_page_decode(dsa, wlr, args)}
     if args.only == "all" and args.extend_config:
         wle = W.config(args.extend_config)
         qb = args.qb if args.qb in wle.QB else wle.QB[0]

@@ -80,6 +80,34 @@ def test_config2_decode_batch(dsa):
     _decode_config(dsa, 2)
 
 
+def test_config2_page_level_decode(dsa):
+    """Page-level selection at the decode-batch size (k / PS = 32 pages of
+    64 positions): page top-k on every row, then attention over the pages."""
+    torch = torch_mod()
+    wl = W.config(2)
+    b = wl.batches["decode"]
+    d = Dev(wl)
+    bt = d.batch("decode")
+    kp = wl.k // wl.PS
+    log(f"config 2: page top-k, k_pages={kp}")
+    pages = dsa.indexer_page_topk(bt["q_idx"], bt["w"], d.idx_cache, d.page_table, d.seq_lens,
+                                  bt["cu"], kp, 1)
+    tok = dsa.page_tokens(pages, wl.PS)
+    torch.cuda.synchronize()
+    exp = oracle.indexer_page_topk(bf16_to_f64(b.q_idx), b.w.astype(np.float64),
+                                   wl.idx_cache.f64_view(), wl.page_table, wl.seq_lens,
+                                   b.cu_q_lens, kp)
+    assert np.array_equal(pages.cpu().numpy(), exp), "page top-k differs from the oracle"
+    exp_tok = oracle.page_tokens(exp, wl.PS)
+    assert np.array_equal(tok.cpu().numpy(), exp_tok)
+    log("config 2: attention over the selected pages")
+    out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"], tok,
+                                wl.sm_scale)
+    torch.cuda.synchronize()
+    check_attention(to_np(out), _oracle_rows_mla(wl, b, exp_tok, list(range(b.T))),
+                    what="config 2 page-level decode")
+
+
 @pytest.mark.timeout(600)
 def test_config3_ragged_decode(dsa):
     _decode_config(dsa, 3)
