@@ -271,8 +271,8 @@ def bench_decode(dsa, wl, args):
 
 def bench_page_decode(dsa, wl, args):
     """The same decode layer with page-level selection: the page top-k
-    (k_pages = k / PS pages, max-pooled page scores), the selected pages'
-    positions, then sparse MLA over every valid position of those pages."""
+    (k_pages = k / PS pages, max-pooled page scores), then sparse MLA over
+    every valid position of those pages (page lists read directly)."""
     import torch
 
     d = _dev_inputs(wl, "decode")
@@ -280,7 +280,6 @@ def bench_page_decode(dsa, wl, args):
     T, H, PS = b.T, wl.H_mla, wl.PS
     kp = max(1, wl.k // PS)
     pages = torch.empty((T, kp), dtype=torch.int32, device="cuda")
-    tok = torch.empty((T, kp * PS), dtype=torch.int32, device="cuda")
     out = torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda")
     ws_i = torch.empty(max(1, dsa.indexer_page_topk_workspace(T, wl.S, wl.H_idx, wl.D_idx, PS,
                                                               wl.MP, kp, 1)),
@@ -291,9 +290,9 @@ def bench_page_decode(dsa, wl, args):
     def step():
         dsa.indexer_page_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
                               d["seq_lens"], d["cu"], kp, 1, out=pages, workspace=ws_i)
-        dsa.page_tokens(pages, PS, out=tok)
-        dsa.sparse_mla_decode(d["q"][0], d["kv_cache"][0], d["page_table"], d["seq_lens"],
-                              d["cu"], tok, wl.sm_scale, out=out, workspace=ws_d)
+        dsa.sparse_mla_decode_pages(d["q"][0], d["kv_cache"][0], d["page_table"],
+                                    d["seq_lens"], d["cu"], pages, wl.sm_scale, out=out,
+                                    workspace=ws_d)
 
     steps = max(5, args.steps // 2)
     ms = _timed(step, steps, min(args.warmup, 3))

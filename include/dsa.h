@@ -201,6 +201,28 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
                           size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_sparse_mla_decode_pages — sparse absorbed-MLA attention over every
+ * valid position of each row's selected pages: the page-budget decode of
+ * "dsa_sparse_backend.py" (the page-scoring indexer path, whose pages come
+ * from dsa_indexer_page_topk). The result equals dsa_sparse_mla_decode on
+ * the positions dsa_page_tokens would list for the same pages (the masks
+ * j < seq_lens and j <= abs_q drop the positions past the sequence end),
+ * without materialising them.
+ *
+ *   pages   int32 [T, k_pages] seq-local page ids, -1 for none; duplicates
+ *           count twice, as repeated positions do in dsa_sparse_mla_decode
+ *   other arguments as in dsa_sparse_mla_decode; the workspace is
+ *   dsa_sparse_mla_decode_workspace(T, H, k_pages * PS)
+ * Supported: as dsa_sparse_mla_decode, with 1 <= k_pages * PS <= 65536.
+ */
+int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_stride,
+                                int num_pages, const int32_t* page_table,
+                                const int32_t* seq_lens, const int32_t* cu_q_lens,
+                                const int32_t* pages, int T, int S, int H, int k_pages, int PS,
+                                int MP, float sm_scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
  * dsa_sparse_mla_extend — query-block sparse absorbed-MLA attention.
  * "sparse_mla_prefill_qblock.py", _qblock_kernel / sparse_mla_attention_qblock.
  *

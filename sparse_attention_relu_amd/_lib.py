@@ -45,6 +45,8 @@ SIGNATURES = {
     "dsa_indexer_page_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                               + [_vp, _vp, _c_size, _vp]),
     "dsa_page_tokens": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "dsa_sparse_mla_decode_pages": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
+                                    + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_profile_enable": (_c_int, [_c_int]),
     "dsa_profile_read": (_c_int, [_c_int, ctypes.c_char_p, _c_int, _vp, _vp, _vp]),
     "dsa_sparse_mla_extend": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -338,6 +340,28 @@ def sparse_mla_decode(q, kv_cache, page_table, seq_lens, cu_q_lens, topk, sm_sca
                                       PS, MP, float(sm_scale), _ptr(out), _ptr(ws), nbytes,
                                       _stream(stream))
     _check("dsa_sparse_mla_decode", st)
+    return out
+
+
+def sparse_mla_decode_pages(q, kv_cache, page_table, seq_lens, cu_q_lens, pages,
+                            sm_scale: float, out=None, workspace=None, stream=None):
+    """Sparse absorbed MLA over every valid position of each row's selected
+    pages -> bf16 [T, H, 512] (dsa_sparse_mla_decode_pages)."""
+    torch = _torch()
+    dev, S, MP, T, H, P, PS, rs = _mla_common(q, kv_cache, page_table, seq_lens, cu_q_lens)
+    _need(pages, "pages", torch.int32, 2, dev)
+    if pages.shape[0] != T:
+        raise ValueError("pages rows must match q rows")
+    kp = pages.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    nbytes = sparse_mla_decode_workspace(T, H, kp * PS)
+    ws = _workspace(nbytes, dev, workspace)
+    st = load().dsa_sparse_mla_decode_pages(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
+                                            _ptr(seq_lens), _ptr(cu_q_lens), _ptr(pages), T, S,
+                                            H, kp, PS, MP, float(sm_scale), _ptr(out), _ptr(ws),
+                                            nbytes, _stream(stream))
+    _check("dsa_sparse_mla_decode_pages", st)
     return out
 
 

@@ -290,6 +290,47 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
+int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_stride,
+                                int num_pages, const int32_t* page_table,
+                                const int32_t* seq_lens, const int32_t* cu_q_lens,
+                                const int32_t* pages, int T, int S, int H, int k_pages, int PS,
+                                int MP, float sm_scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (k_pages < 1 || (long)k_pages * PS > 65536)
+    return fail(DSA_ERR_UNSUPPORTED, "k_pages=%d with PS=%d: need 1 <= k_pages * PS <= 65536",
+                k_pages, PS);
+  if (T == 0) return ok();
+  st = check_mla_common(q, kv_cache, row_stride, H, PS, out);
+  if (st) return st;
+  if (!page_table || !seq_lens || !cu_q_lens || !pages)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const int k = k_pages * PS;
+  const size_t need = dsa_sparse_mla_decode_workspace(T, H, k);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", workspace_bytes, need);
+  const int ch = dsa::mla_decode_chunk(T, k);
+  const size_t nch = (size_t)((k + ch - 1) / ch);
+  dsa::MlaArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv_cache);
+  a.row_stride = row_stride;
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.topk = pages;
+  a.sel_pages = true;
+  a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = static_cast<uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256((size_t)T * nch * H * 512 * 2));
+  return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
 int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
                            int QB, int u_max) {
   if (!blk_counts_host || T <= 0 || H <= 0 || k <= 0 || PS <= 0 || QB <= 0 || u_max <= 0)

@@ -1397,10 +1397,12 @@ hipError_t indexer_page_select(const IndexerArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Page scores ("ref.py", streamindex_page_topk_ref: masked positions at
-// -inf, then the maximum over each page). grid = T, block = 256. A
-// 16-lane group covers one page (PS <= 64: four scores per lane); a wave
-// does four pages per step. Pages at or past ceil(n_valid / PS) are not
-// written: the select never reads them.
+// -inf, then the maximum over each page). grid = (T, ceil(MP / 64)), block =
+// 256: workgroup (t, c) pools pages 64 c .. 64 c + 63 of row t. A 16-lane
+// group covers one page (PS <= 64: four scores per lane); wave w takes pages
+// 64 c + 16 w + 4 it + group (it < 4) with all its loads issued before any
+// reduction. Pages at or past ceil(n_valid / PS) are not written: the select
+// never reads them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void page_pool(const float* __restrict__ scores, long ld,
                                                  const int32_t* __restrict__ cu,
@@ -1408,35 +1410,45 @@ __global__ __launch_bounds__(256) void page_pool(const float* __restrict__ score
                                                  int cap, int PS, float* __restrict__ pscores,
                                                  long ldp) {
   const int t = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
   const int n = ri.n_valid;
   const int npg = (n + PS - 1) / PS;
+  const int p_base = 64 * (int)blockIdx.y + 16 * wave;
+  if (p_base >= npg) return;  // wave-uniform; no block barrier follows
   const int l = lane_id(), grp = l >> 4, i = l & 15;
   const float* row = scores + (size_t)t * ld;
-  float* prow = pscores + (size_t)t * ldp;
-  for (int p0 = 4 * (threadIdx.x >> 6); p0 < npg; p0 += 16) {
-    const int p = p0 + grp;
-    float m = -INFINITY;
+  float m[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int p = p_base + 4 * it + grp;
+    m[it] = -INFINITY;
     if (p < npg && 4 * i < PS) {
       const int j = p * PS + 4 * i;
       if (j + 4 <= n) {
         const float4 v = *reinterpret_cast<const float4*>(row + j);
-        m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+        m[it] = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
       } else {
         for (int e = 0; e < 4; ++e)
-          if (j + e < n) m = fmaxf(m, row[j + e]);
+          if (j + e < n) m[it] = fmaxf(m[it], row[j + e]);
       }
     }
+  }
+  float* prow = pscores + (size_t)t * ldp;
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, shfl_xor_f(m, o));
-    if (p < npg && i == 0) prow[p] = m;
+  for (int it = 0; it < 4; ++it) {
+    float v = m[it];
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+    const int p = p_base + 4 * it + grp;
+    if (p < npg && i == 0) prow[p] = v;
   }
 }
 
 hipError_t indexer_page_pool(const IndexerArgs& a, hipStream_t st) {
   ProfScope prof("page_pool", st);
-  hipLaunchKernelGGL(page_pool, dim3(a.T), dim3(256), 0, st, a.scores, a.ld, a.cu, a.seq_lens,
-                     a.S, a.MP * a.PS, a.PS, a.page_scores, a.ldp);
+  hipLaunchKernelGGL(page_pool, dim3(a.T, (a.MP + 63) / 64), dim3(256), 0, st, a.scores, a.ld,
+                     a.cu, a.seq_lens, a.S, a.MP * a.PS, a.PS, a.page_scores, a.ldp);
   return hipGetLastError();
 }
 

@@ -58,7 +58,8 @@ struct MlaArgs {
   const int32_t* pt;
   const int32_t* seq_lens;
   const int32_t* cu;
-  const int32_t* topk;  // decode
+  const int32_t* topk;  // decode: positions [T, k], or pages [T, k / PS]
+  bool sel_pages;       // decode: topk holds pages (k = k_pages * PS)
   const int32_t* units;  // extend
   const int32_t* counts;
   const uint64_t* member;

@@ -151,13 +151,16 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
           buf + kDecRopeOff + wave * 1024);
 }
 
-template <int dummy = 0>
+// PAGED = 1: the selection of a row is a list of sel_ld seq-local pages, and
+// entry i of the row (k = sel_ld * PS entries) is position
+// page[i / PS] * PS + i % PS, or none for a -1 page.
+template <int PAGED>
 __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int T, int S, int H, int k,
-    int PS, int MP, float sm_scale, int CH, int nch, int HB, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int sel_ld, int T, int S,
+    int H, int k, int PS, int MP, float sm_scale, int CH, int nch, int HB,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
   __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
@@ -180,11 +183,17 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   constexpr int NP = kDecMaxCH / 256;
   int j[NP];
   {
-    const int32_t* sel = topk + (size_t)t * k;
+    const int32_t* sel = topk + (size_t)t * sel_ld;
 #pragma unroll
     for (int p2 = 0; p2 < NP; ++p2) {
       const int ii = i_begin + 256 * p2 + 64 * wave + l;
-      j[p2] = ii < i_end ? sel[ii] : -1;
+      if (PAGED) {
+        const int pi = ii / PS;
+        const int pg = ii < i_end ? sel[pi] : -1;
+        j[p2] = pg >= 0 ? pg * PS + (ii - pi * PS) : -1;
+      } else {
+        j[p2] = ii < i_end ? sel[ii] : -1;
+      }
     }
   }
   const int head = 16 * hb + col;
@@ -475,9 +484,16 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
   const int HB = (a.H + 15) / 16;
   {
     ProfScope prof("mla_decode_partial", st);
-    hipLaunchKernelGGL((mla_decode_partial<0>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q, a.kv,
-                       a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk, a.T, a.S, a.H,
-                       a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB, a.part_o, a.part_ml);
+    if (a.sel_pages)
+      hipLaunchKernelGGL((mla_decode_partial<1>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q,
+                         a.kv, a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk,
+                         a.k / a.PS, a.T, a.S, a.H, a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB,
+                         a.part_o, a.part_ml);
+    else
+      hipLaunchKernelGGL((mla_decode_partial<0>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q,
+                         a.kv, a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk, a.k,
+                         a.T, a.S, a.H, a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB, a.part_o,
+                         a.part_ml);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

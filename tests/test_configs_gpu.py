@@ -104,8 +104,12 @@ def test_config2_page_level_decode(dsa):
     out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, bt["cu"], tok,
                                 wl.sm_scale)
     torch.cuda.synchronize()
-    check_attention(to_np(out), _oracle_rows_mla(wl, b, exp_tok, list(range(b.T))),
-                    what="config 2 page-level decode")
+    ref = _oracle_rows_mla(wl, b, exp_tok, list(range(b.T)))
+    check_attention(to_np(out), ref, what="config 2 page-level decode")
+    out = dsa.sparse_mla_decode_pages(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens,
+                                      bt["cu"], pages, wl.sm_scale)
+    torch.cuda.synchronize()
+    check_attention(to_np(out), ref, what="config 2 page-level decode (page lists)")
 
 
 @pytest.mark.timeout(600)

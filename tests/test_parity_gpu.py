@@ -471,6 +471,10 @@ def test_page_tokens_and_attention_tiny(dsa):
                                     tok, wl.sm_scale)
         torch.cuda.synchronize()
         check_attention(to_np(out), ref, what=f"page attend {bname} (per query)")
+        out = dsa.sparse_mla_decode_pages(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens,
+                                          bt["cu"], pages, wl.sm_scale)
+        torch.cuda.synchronize()
+        check_attention(to_np(out), ref, what=f"page attend {bname} (page lists)")
         if bname == "extend":
             for QB in wl.QB:
                 u, c, m = dsa.block_union(tok, d.seq_lens, bt["cu"], wl.PS, wl.MP, QB, wl.u_max)
