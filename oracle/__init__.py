@@ -16,6 +16,7 @@ from .dsa import (  # noqa: F401
     indexer_page_topk,
     indexer_topk,
     page_tokens,
+    paged_write,
     member_bit,
     n_valid_keys,
     query_rows,

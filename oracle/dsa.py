@@ -26,6 +26,9 @@ function on it):
 
 * "ref.py" page, ``streamindex_page_topk_ref``: the page-level indexer,
   token scores max-pooled per page and the top ``k_pages`` pages.
+* "dsa_sparse_backend.py" page, ``_scatter_paged``, and
+  "sparse_mla_prefill_qblock.py" page, ``paged_write_back``: the paged
+  cache self-write of the new tokens ahead of the attention.
 
 Readings taken where the pages leave a step open (each is a row of the
 design notes' list of readings):
@@ -222,6 +225,37 @@ def page_tokens(pages, PS):
     tok = pages[:, :, None] * PS + r[None, None, :]
     tok = np.where(pages[:, :, None] >= 0, tok, -1)
     return tok.reshape(T, kp * PS).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Paged cache writes
+# ----------------------------------------------------------------------------
+def paged_write(cache, rows, col0, page_table, seq_lens, cu_q_lens):
+    """The cache after the new rows are written ("dsa_sparse_backend.py",
+    ``_scatter_paged``; "sparse_mla_prefill_qblock.py", ``paged_write_back``):
+    packed row t of sequence s goes to seq-local position
+    ``a = seq_lens[s] - q_len(s) + (t - q_start)``, i.e. physical page
+    ``page_table[s, a // PS]`` at offset ``a % PS``, columns
+    ``col0 .. col0 + cols - 1``; the other columns and slots are unchanged.
+
+    Reading taken: rows outside every sequence, and positions outside
+    ``0 <= a < min(seq_lens[s], MP * PS)``, are dropped (the pages route them
+    to a reserved page of their allocator instead).
+
+    cache [P, PS, C], rows [T, cols]; returns a new array.
+    """
+    out = np.array(cache, copy=True)
+    rows = np.asarray(rows)
+    T, cols = rows.shape
+    PS = cache.shape[1]
+    MP = page_table.shape[1]
+    seq, pos = query_rows(seq_lens, cu_q_lens, T)
+    for t in range(T):
+        s, a = int(seq[t]), int(pos[t])
+        if s < 0 or a < 0 or a >= min(int(seq_lens[s]), MP * PS):
+            continue
+        out[page_table[s, a // PS], a % PS, col0:col0 + cols] = rows[t]
+    return out
 
 
 # ----------------------------------------------------------------------------

@@ -503,7 +503,38 @@ def pin_page_tokens():
     assert oracle.page_tokens(pages, 4).tolist() == exp
 
 
+def pin_paged_write_bruteforce():
+    """Plain-Python slot arithmetic on micro workloads (with rows past the
+    last sequence); everything not written stays as it was, and reading the
+    written positions back through the page table gives the new rows."""
+    for seed in range(4):
+        wl = micro(200 + seed, q_lens=(3, 0, 2), S=3)
+        b = wl.batches["b"]
+        cache = bf16_to_f64(wl.idx_cache)
+        T = int(b.cu_q_lens[-1]) + 2  # two rows in no sequence
+        rows = np.arange(T * 2, dtype=np.float64).reshape(T, 2) + 1000.0
+        got = oracle.paged_write(cache, rows, 1, wl.page_table, wl.seq_lens, b.cu_q_lens)
+        exp = cache.copy()
+        cu = [int(x) for x in b.cu_q_lens]
+        PS = cache.shape[1]
+        for s in range(wl.S):
+            q0, q1 = cu[s], cu[s + 1]
+            for t in range(q0, q1):
+                a = int(wl.seq_lens[s]) - (q1 - q0) + (t - q0)
+                if 0 <= a < int(wl.seq_lens[s]):
+                    pg = int(wl.page_table[s][a // PS])
+                    exp[pg, a % PS, 1] = rows[t, 0]
+                    exp[pg, a % PS, 2] = rows[t, 1]
+        assert np.array_equal(np.nan_to_num(got, nan=-7.0), np.nan_to_num(exp, nan=-7.0)), seed
+        seq, pos = oracle.query_rows(wl.seq_lens, b.cu_q_lens, T)
+        for t in range(T):
+            if seq[t] >= 0:
+                back = oracle.gather_rows(got, wl.page_table, int(seq[t]), [int(pos[t])])[0]
+                assert np.array_equal(back[1:3], rows[t])
+
+
 PINS = [
+    pin_paged_write_bruteforce,
     pin_page_topk_bruteforce, pin_page_topk_unit_pages_is_token_topk,
     pin_page_topk_invariants_tiny, pin_page_tokens,
     pin_indexer_golden, pin_indexer_bruteforce, pin_indexer_tiny_bruteforce,
