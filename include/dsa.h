@@ -140,6 +140,32 @@ int dsa_page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* t
                     void* stream);
 
 /*
+ * dsa_paged_write — the paged cache self-write of the new tokens, ahead of
+ * the indexer and the attention: "dsa_sparse_backend.py", _scatter_paged
+ * (indexer keys) and "sparse_mla_prefill_qblock.py", paged_write_back
+ * (latent rows [c_kv | k_rope]).
+ *
+ * Packed row t of sequence s (q_start <= t < q_end) lands at its seq-local
+ * position a = seq_lens[s] - (q_end - q_start) + (t - q_start):
+ *     cache[page_table[s, a / PS], a % PS, col0 + c] = src[t, c],  c < cols.
+ * Rows outside every sequence, and positions outside
+ * 0 <= a < min(seq_lens[s], MP * PS), are dropped. Other columns and slots
+ * are left untouched, so the latent row is written by two calls (c_kv at
+ * col0 = 0 with cols = 512, k_rope at col0 = 512 with cols = 64) and the
+ * indexer key by one (cols = D). Rows of one call must name distinct slots.
+ *
+ *   src    bf16 [T, src_stride], the first cols columns are written
+ *   cache  bf16 [num_pages, PS, row_stride], written in place
+ * Returns DSA_ERR_INVALID_ARG unless cols, col0, row_stride and src_stride
+ * are multiples of 8 with col0 + cols <= row_stride and cols <= src_stride,
+ * and src and cache are 16-byte aligned.
+ */
+int dsa_paged_write(const void* src, int src_stride, int cols, int col0, void* cache,
+                    int row_stride, int num_pages, const int32_t* page_table,
+                    const int32_t* seq_lens, const int32_t* cu_q_lens, int T, int S, int PS,
+                    int MP, void* stream);
+
+/*
  * dsa_block_union — per query-block union of selected pages and per-token
  * membership. "sparse_mla_prefill_qblock.py", build_block_unit_tables, with
  * the ragged lifting of sparse_mla_attention_qblock.

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     last_error,
     load,
     page_tokens,
+    paged_write,
     profile_enable,
     profile_read,
     sparse_mla_decode,

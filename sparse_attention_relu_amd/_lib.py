@@ -45,6 +45,8 @@ SIGNATURES = {
     "dsa_indexer_page_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                               + [_vp, _vp, _c_size, _vp]),
     "dsa_page_tokens": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
+    "dsa_paged_write": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp]
+                        + [_c_int] * 4 + [_vp]),
     "dsa_sparse_mla_decode_pages": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
                                     + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_profile_enable": (_c_int, [_c_int]),
@@ -257,6 +259,28 @@ def page_tokens(pages, PS: int, out=None, stream=None):
     st = load().dsa_page_tokens(_ptr(pages), T, kp, PS, _ptr(out), _stream(stream))
     _check("dsa_page_tokens", st)
     return out
+
+
+def paged_write(src, cache, page_table, seq_lens, cu_q_lens, col0: int = 0, stream=None):
+    """Write row t of src (bf16 [T, cols], unit column stride) into the cache
+    slot of its sequence position, columns col0 .. col0 + cols - 1
+    (dsa_paged_write). The cache tensor is updated in place and returned."""
+    torch = _torch()
+    dev = cache.device
+    _need(cache, "cache", torch.bfloat16, 3, dev)
+    if src.dtype != torch.bfloat16 or src.dim() != 2 or src.device != dev or src.stride(1) != 1:
+        raise ValueError("src must be a bf16 [T, cols] tensor with unit column stride on "
+                         "the cache's device")
+    if not cache.is_contiguous():
+        raise ValueError("cache must be contiguous")
+    S, MP = _ragged(page_table, seq_lens, cu_q_lens, dev)
+    T, cols = src.shape
+    P, PS, rs = cache.shape
+    st = load().dsa_paged_write(_ptr(src), src.stride(0), cols, col0, _ptr(cache), rs, P,
+                                _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S, PS, MP,
+                                _stream(stream))
+    _check("dsa_paged_write", st)
+    return cache
 
 
 def block_union_workspace(T, S, MP, QB, u_max) -> int:

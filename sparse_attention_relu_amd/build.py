@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "profile.cpp", "indexer.hip", "union.hip", "mla.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "indexer.hip", "union.hip", "mla.hip",
+           "cache_write.hip"]
 HEADERS = ["common.h", "kernels.h", "profile.h"]
 
 COMMON_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

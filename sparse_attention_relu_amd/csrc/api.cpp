@@ -191,6 +191,37 @@ int dsa_page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* t
                     "page tokens launch");
 }
 
+int dsa_paged_write(const void* src, int src_stride, int cols, int col0, void* cache,
+                    int row_stride, int num_pages, const int32_t* page_table,
+                    const int32_t* seq_lens, const int32_t* cu_q_lens, int T, int S, int PS,
+                    int MP, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (cols < 8 || cols % 8 || col0 < 0 || col0 % 8 || row_stride % 8 ||
+      (long)col0 + cols > row_stride || src_stride < cols || src_stride % 8)
+    return fail(DSA_ERR_INVALID_ARG,
+                "paged write: cols=%d, col0=%d, row_stride=%d, src_stride=%d (need multiples "
+                "of 8 with col0 + cols <= row_stride and cols <= src_stride)",
+                cols, col0, row_stride, src_stride);
+  if (T == 0) return ok();
+  if (!src || !cache || !page_table || !seq_lens || !cu_q_lens)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if (!aligned16(src) || !aligned16(cache))
+    return fail(DSA_ERR_INVALID_ARG, "src and cache must be 16-byte aligned");
+  dsa::CacheWriteArgs a;
+  a.src = static_cast<const uint16_t*>(src);
+  a.src_stride = src_stride;
+  a.cols = cols;
+  a.col0 = col0;
+  a.cache = static_cast<uint16_t*>(cache);
+  a.row_stride = row_stride;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.T = T; a.S = S; a.PS = PS; a.MP = MP; a.num_pages = num_pages;
+  return hip_status(dsa::paged_write(a, static_cast<hipStream_t>(stream)), "paged write launch");
+}
+
 // ---------------------------------------------------------------------------
 size_t dsa_block_union_workspace(int T, int S, int MP, int QB, int u_max) {
   (void)u_max;

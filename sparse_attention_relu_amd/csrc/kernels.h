@@ -70,6 +70,19 @@ struct MlaArgs {
   float* part_ml;
 };
 
+struct CacheWriteArgs {
+  const uint16_t* src;  // bf16 [T, src_stride]
+  int src_stride, cols, col0;
+  uint16_t* cache;      // bf16 [num_pages, PS, row_stride]
+  int row_stride;
+  const int32_t* pt;
+  const int32_t* seq_lens;
+  const int32_t* cu;
+  int T, S, PS, MP, num_pages;
+};
+
+hipError_t paged_write(const CacheWriteArgs& a, hipStream_t st);
+
 int mla_decode_chunk(int T, int k);
 hipError_t mla_decode(const MlaArgs& a, hipStream_t st);
 hipError_t mla_extend(const MlaArgs& a, hipStream_t st);

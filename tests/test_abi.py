@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 19
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -157,3 +157,20 @@ def test_page_entry_validation(lib):
     assert lib.dsa_page_tokens(1 << 12, 2, 2048, 64, 1 << 12, None) == _lib.DSA_ERR_INVALID_ARG
     assert lib.dsa_page_tokens(None, 2, 4, 64, 1 << 12, None) == _lib.DSA_ERR_INVALID_ARG
     assert lib.dsa_page_tokens(1 << 12, 0, 4, 64, 1 << 12, None) == _lib.DSA_OK
+
+
+def test_paged_write_validation(lib):
+    def call(**kw):
+        a = dict(ss=576, cols=512, col0=0, rs=576, T=2, S=1, PS=64, MP=4, src=1 << 12)
+        a.update(kw)
+        return lib.dsa_paged_write(a["src"], a["ss"], a["cols"], a["col0"], 1 << 12, a["rs"], 4,
+                                   1 << 12, 1 << 12, 1 << 12, a["T"], a["S"], a["PS"], a["MP"],
+                                   None)
+
+    assert call(cols=12) == _lib.DSA_ERR_INVALID_ARG
+    assert call(col0=4) == _lib.DSA_ERR_INVALID_ARG
+    assert call(col0=512, cols=128) == _lib.DSA_ERR_INVALID_ARG  # past the row
+    assert call(ss=256) == _lib.DSA_ERR_INVALID_ARG  # src rows shorter than cols
+    assert call(src=(1 << 12) + 2) == _lib.DSA_ERR_INVALID_ARG  # misaligned
+    assert call(src=None) == _lib.DSA_ERR_INVALID_ARG
+    assert call(T=0) == _lib.DSA_OK

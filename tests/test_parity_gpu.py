@@ -482,3 +482,53 @@ def test_page_tokens_and_attention_tiny(dsa):
                                             bt["cu"], u, c, m, QB, wl.sm_scale)
                 torch.cuda.synchronize()
                 check_attention(to_np(out), ref, what=f"page attend extend QB={QB}")
+
+
+# ----------------------------------------------------------------------------
+# Paged cache self-write
+# ----------------------------------------------------------------------------
+def _same_bits(a, b):
+    return np.array_equal(np.nan_to_num(a, nan=-12345.0), np.nan_to_num(b, nan=-12345.0))
+
+
+@pytest.mark.parametrize("bname", ["decode", "extend"])
+def test_paged_write_tiny(dsa, bname):
+    """New indexer keys (one call) and new latent rows (c_kv, then k_rope)
+    written into the caches, compared slot by slot with the oracle; two
+    extra rows past the last sequence are dropped. Then the attention over
+    the updated latent cache matches the oracle's (write, then attend)."""
+    torch = torch_mod()
+    wl = W.config(1)
+    b = wl.batches[bname]
+    d = Dev(wl)
+    bt = d.batch(bname)
+    T = b.T + 2
+    cu_t = bt["cu"]
+    rng = np.random.default_rng(5)
+    keys = rng.integers(-2, 3, size=(T, wl.D_idx)).astype(np.float32)
+    lat = rng.standard_normal((T, 576)).astype(np.float32)
+    keys_t = torch.from_numpy(keys).to("cuda").to(torch.bfloat16)
+    lat_t = torch.from_numpy(lat).to("cuda").to(torch.bfloat16)
+    idx0 = to_np(d.idx_cache)
+    kv0 = to_np(d.kv_cache[0])
+    dsa.paged_write(keys_t, d.idx_cache, d.page_table, d.seq_lens, cu_t)
+    dsa.paged_write(lat_t[:, :512], d.kv_cache[0], d.page_table, d.seq_lens, cu_t, col0=0)
+    dsa.paged_write(lat_t[:, 512:], d.kv_cache[0], d.page_table, d.seq_lens, cu_t, col0=512)
+    torch.cuda.synchronize()
+    exp_idx = oracle.paged_write(idx0, to_np(keys_t), 0, wl.page_table, wl.seq_lens, b.cu_q_lens)
+    exp_kv = oracle.paged_write(kv0, to_np(lat_t), 0, wl.page_table, wl.seq_lens, b.cu_q_lens)
+    assert _same_bits(to_np(d.idx_cache), exp_idx), "indexer cache after the write"
+    assert _same_bits(to_np(d.kv_cache[0]), exp_kv), "latent cache after the write"
+    # write, then attend: every causal position of each row, over the new cache
+    seq, pos = oracle.query_rows(wl.seq_lens, b.cu_q_lens, b.T)
+    sel = np.full((b.T, 256), -1, dtype=np.int32)
+    for t in range(b.T):
+        if seq[t] >= 0:
+            n = oracle.n_valid_keys(wl.seq_lens[seq[t]], pos[t])
+            sel[t, :min(n, 256)] = np.arange(min(n, 256))
+    out = dsa.sparse_mla_decode(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens, cu_t,
+                                i32(sel, "cuda"), wl.sm_scale)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_mla(bf16_to_f64(b.q_mla[0]), exp_kv, wl.page_table, wl.seq_lens,
+                            b.cu_q_lens, sel, wl.sm_scale, wl.Dv)
+    check_attention(to_np(out), ref, what=f"write then attend ({bname})")
