@@ -162,7 +162,8 @@ KERNEL_SOURCES = {
     "topk_select": "indexer.hip", "mla_decode_partial": "mla.hip",
     "mla_decode_combine": "mla.hip", "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
-    "union_member": "union.hip",
+    "union_member": "union.hip", "page_pool": "indexer.hip", "page_token_list": "indexer.hip",
+    "paged_write_rows": "cache_write.hip",
 }
 
 
@@ -386,7 +387,34 @@ def bench_extend(dsa, wl, args, QB, steps=None):
     res["per_query"] = _per_query_attend(dsa, wl, d, topk, outs, steps, kt)
     # the library's own choice between the two paths for these unions
     res["attend_path_chosen"] = dsa.extend_attend_path(cnt, T, H, k, wl.PS, QB, u_max)
+    res["cache_write"] = _cache_write(dsa, wl, d, steps)
     return res
+
+
+def _cache_write(dsa, wl, d, steps):
+    """The self-write of the chunk's new tokens ahead of the layer: indexer
+    keys (one call) and latent rows (c_kv, k_rope). Timed last: it rewrites
+    the chunk's own cache slots."""
+    import torch
+
+    T = int(d["cu"][-1].item())
+    g = torch.Generator(device="cuda").manual_seed(11)
+    keys = torch.randint(-2, 3, (T, wl.D_idx), generator=g, device="cuda").to(torch.bfloat16)
+    lat = torch.randn((T, DK), generator=g, device="cuda").to(torch.bfloat16)
+
+    def step():
+        dsa.paged_write(keys, d["idx_cache"], d["page_table"], d["seq_lens"], d["cu"])
+        dsa.paged_write(lat[:, :DV], d["kv_cache"][0], d["page_table"], d["seq_lens"], d["cu"])
+        dsa.paged_write(lat[:, DV:], d["kv_cache"][0], d["page_table"], d["seq_lens"], d["cu"],
+                        col0=DV)
+
+    step()
+    kt = _kernel_times(dsa, step, steps)
+    n, avg = kt["paged_write_rows"]
+    ms = avg * n / steps  # device time of the three writes (the host calls take longer)
+    moved = T * (wl.D_idx + DK) * 2 * 2  # read and written once
+    return {"tokens": T, "launches": n // steps, "us_per_layer": round(ms * 1e3, 2),
+            "roofline": _roofline_entry("hbm", moved, ms)}
 
 
 def _per_query_attend(dsa, wl, d, topk, outs, steps, kt_qblock):

@@ -12,31 +12,79 @@
 
 namespace dsa {
 
-// grid = (T, ceil(cols / 8 / 256)), block = 256: thread i copies the 16-byte
-// chunk i (8 bf16 values) of its row.
+constexpr int kWriteRowsPerWave = 4;
+
+// grid = ceil(T / (4 * kWriteRowsPerWave)), block = 256: wave w of block b
+// writes rows (4 b + w) * kWriteRowsPerWave + r, lane l copying 16-byte
+// chunks l, l + 64, ... (8 bf16 values each) of a row. The owner of each row
+// is found from one pass over the sequence bounds per wave. Rows up to 512
+// columns (one chunk per lane) load all of the wave's rows before the first
+// store, from clamped in-bounds addresses, so that no load waits for another.
 __global__ __launch_bounds__(256) void paged_write_rows(
     const uint16_t* __restrict__ src, long src_stride, int cols, int col0,
     uint16_t* __restrict__ cache, long row_stride, const int32_t* __restrict__ pt,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int S, int PS, int MP,
-    int num_pages) {
-  const int t = blockIdx.x;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int PS,
+    int MP, int num_pages) {
+  const int l = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int t0 = (4 * (int)blockIdx.x + wave) * kWriteRowsPerWave;
+  if (t0 >= T) return;
   const int cap = MP * PS;
-  const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
-  // ri.kv is seq_len clamped to [0, MP * PS]
-  if (ri.seq < 0 || ri.abs_q < 0 || ri.abs_q >= ri.kv || c >= cols) return;
-  const int a = ri.abs_q;
-  const long slot = (long)clamp_page(pt[(size_t)ri.seq * MP + a / PS], num_pages) * PS + a % PS;
-  const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)t * src_stride + c);
-  *reinterpret_cast<uint4*>(cache + slot * row_stride + col0 + c) = v;
+  int slot[kWriteRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kWriteRowsPerWave; ++r) slot[r] = -1;
+  // owners: sequences in groups of 64 lanes (one load round for S <= 64)
+  for (int base = 0; base < S; base += DSA_WAVE) {
+    const int i = base + l;
+    const bool in = i < S;
+    const int q0 = in ? cu[i] : 0, q1 = in ? cu[i + 1] : 0, kv = in ? seq_lens[i] : 0;
+#pragma unroll
+    for (int r = 0; r < kWriteRowsPerWave; ++r) {
+      const int t = t0 + r;
+      const uint64_t own = __ballot(in && q0 <= t && t < q1);
+      if (own != 0ull) {  // at most one sequence owns a row (cu is non-decreasing)
+        const int src_l = (int)__builtin_ctzll(own);
+        const int s = base + src_l;
+        const int a0 = __shfl(q0, src_l, DSA_WAVE), a1 = __shfl(q1, src_l, DSA_WAVE);
+        const int sk = __shfl(kv, src_l, DSA_WAVE);
+        const int a = sk - (a1 - a0) + (t - a0);
+        const int lim = sk < cap ? sk : cap;
+        if (t < T && a >= 0 && a < lim)
+          slot[r] = clamp_page(pt[(size_t)s * MP + a / PS], num_pages) * PS + a % PS;
+      }
+    }
+  }
+  if (cols <= 8 * DSA_WAVE) {
+    const int c = 8 * l < cols ? 8 * l : 0;
+    uint4 v[kWriteRowsPerWave];
+#pragma unroll
+    for (int r = 0; r < kWriteRowsPerWave; ++r) {
+      const int t = slot[r] >= 0 ? t0 + r : t0;  // t0 < T is a valid row
+      v[r] = *reinterpret_cast<const uint4*>(src + (size_t)t * src_stride + c);
+    }
+#pragma unroll
+    for (int r = 0; r < kWriteRowsPerWave; ++r)
+      if (slot[r] >= 0 && 8 * l < cols)
+        *reinterpret_cast<uint4*>(cache + (size_t)slot[r] * row_stride + col0 + c) = v[r];
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < kWriteRowsPerWave; ++r) {
+    if (slot[r] < 0) continue;  // wave-uniform
+    const uint16_t* srow = src + (size_t)(t0 + r) * src_stride;
+    uint16_t* drow = cache + (size_t)slot[r] * row_stride + col0;
+    for (int c = 8 * l; c < cols; c += 8 * DSA_WAVE)
+      *reinterpret_cast<uint4*>(drow + c) = *reinterpret_cast<const uint4*>(srow + c);
+  }
 }
 
 hipError_t paged_write(const CacheWriteArgs& a, hipStream_t st) {
-  const int chunks = (a.cols / 8 + 255) / 256;
+  const int rows_per_block = 4 * kWriteRowsPerWave;
   ProfScope prof("paged_write_rows", st);
-  hipLaunchKernelGGL(paged_write_rows, dim3(a.T, chunks), dim3(256), 0, st, a.src,
-                     (long)a.src_stride, a.cols, a.col0, a.cache, (long)a.row_stride, a.pt,
-                     a.seq_lens, a.cu, a.S, a.PS, a.MP, a.num_pages);
+  hipLaunchKernelGGL(paged_write_rows, dim3((a.T + rows_per_block - 1) / rows_per_block),
+                     dim3(256), 0, st, a.src, (long)a.src_stride, a.cols, a.col0, a.cache,
+                     (long)a.row_stride, a.pt, a.seq_lens, a.cu, a.T, a.S, a.PS, a.MP,
+                     a.num_pages);
   return hipGetLastError();
 }
 
