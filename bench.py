@@ -326,12 +326,19 @@ def bench_extend(dsa, wl, args, QB, steps=None):
     ws_u = torch.empty(max(1, dsa.block_union_workspace(T, wl.S, wl.MP, QB, u_max)),
                        dtype=torch.uint8, device="cuda")
 
+    # IndexShare: the first layer is full (indexer + union), the others are
+    # shared and attend with its tables (one slot)
+    full_slot, src_slot, n_full = dsa.index_share_map(["full"] + ["shared"] * (layers - 1))
+    assert n_full == 1
+
     def step():
-        dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"], d["seq_lens"],
-                         d["cu"], k, d["max_q_len"], out=topk, workspace=ws_i)
-        dsa.block_union(topk, d["seq_lens"], d["cu"], wl.PS, wl.MP, QB, u_max,
-                        out=(units, counts, member), workspace=ws_u)
-        for i in range(layers):  # the full layer, then IndexShare layers reuse the tables
+        for i in range(layers):
+            if i in full_slot:
+                dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
+                                 d["seq_lens"], d["cu"], k, d["max_q_len"], out=topk,
+                                 workspace=ws_i)
+                dsa.block_union(topk, d["seq_lens"], d["cu"], wl.PS, wl.MP, QB, u_max,
+                                out=(units, counts, member), workspace=ws_u)
             dsa.sparse_mla_extend(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
                                   d["cu"], units, counts, member, QB, wl.sm_scale, out=outs[i])
 

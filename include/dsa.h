@@ -275,6 +275,25 @@ int dsa_sparse_mla_extend(const void* q, const void* kv_cache, int row_stride, i
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_index_share_map — the static IndexShare layer mapping ("ref.py",
+ * build_index_share_map; "dsa_sparse_backend.py", module docstring: shared
+ * layers reuse the top-k of the last full layer). Host logic only.
+ *
+ *   layer_full  HOST int32 [num_layers]: 1 = full layer (runs the indexer,
+ *               owns an indexer-key cache and a top-k slot), 0 = shared
+ *   full_slot   HOST int32 [num_layers] output: the slot a full layer owns,
+ *               slots numbered 0, 1, ... in layer order; -1 for shared layers
+ *   src_slot    HOST int32 [num_layers] output: the slot whose top-k the
+ *               layer attends with (its own if full, else the nearest
+ *               preceding full layer's)
+ * Returns the number of full layers (of slots), or DSA_ERR_INVALID_ARG as a
+ * negative number when a shared layer has no full layer before it, a kind
+ * is neither 0 nor 1, or an array is null.
+ */
+int dsa_index_share_map(const int32_t* layer_full, int num_layers, int32_t* full_slot,
+                        int32_t* src_slot);
+
+/*
  * dsa_extend_attend_path — which of the two token-exact extend attention
  * paths to run for a packed batch whose block unions are built: the query
  * block (dsa_sparse_mla_extend, one page fetch per block, MFMA work growing

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     block_union_workspace,
     extend_attend_path,
     header_functions,
+    index_share_map,
     indexer_page_topk,
     indexer_page_topk_workspace,
     indexer_topk,

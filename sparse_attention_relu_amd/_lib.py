@@ -41,6 +41,7 @@ SIGNATURES = {
                               + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_sparse_mla_extend_workspace": (_c_size, [_c_int] * 4),
     "dsa_extend_attend_path": (_c_int, [_vp] + [_c_int] * 7),
+    "dsa_index_share_map": (_c_int, [_vp, _c_int, _vp, _vp]),
     "dsa_indexer_page_topk_workspace": (_c_size, [_c_int] * 8),
     "dsa_indexer_page_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                               + [_vp, _vp, _c_size, _vp]),
@@ -340,6 +341,30 @@ def extend_attend_path(blk_counts, T: int, H: int, k: int, PS: int, QB: int,
     if r < 0:
         raise DsaError("dsa_extend_attend_path", -r, last_error())
     return "per_query" if r == 1 else "qblock"
+
+
+def index_share_map(indexer_types):
+    """IndexShare layer mapping (dsa_index_share_map). indexer_types lists
+    "full" or "shared" per layer. Returns (full_slot, src_slot, num_full):
+    full_slot maps each full layer to the slot it owns, src_slot maps every
+    layer to the slot whose top-k it attends with."""
+    import numpy as np
+
+    kinds = []
+    for i, kind in enumerate(indexer_types):
+        if kind not in ("full", "shared"):
+            raise ValueError(f"unknown indexer type {kind!r} at layer {i}")
+        kinds.append(1 if kind == "full" else 0)
+    n = len(kinds)
+    lf = np.asarray(kinds, dtype=np.int32)
+    fs = np.empty(max(n, 1), dtype=np.int32)
+    ss = np.empty(max(n, 1), dtype=np.int32)
+    r = load().dsa_index_share_map(lf.ctypes.data, n, fs.ctypes.data, ss.ctypes.data)
+    if r < 0:
+        raise DsaError("dsa_index_share_map", -r, last_error())
+    full_slot = {i: int(fs[i]) for i in range(n) if kinds[i] == 1}
+    src_slot = {i: int(ss[i]) for i in range(n)}
+    return full_slot, src_slot, int(r)
 
 
 def sparse_mla_decode_workspace(T, H, k) -> int:

@@ -362,6 +362,30 @@ int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_str
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
+int dsa_index_share_map(const int32_t* layer_full, int num_layers, int32_t* full_slot,
+                        int32_t* src_slot) {
+  if (!layer_full || !full_slot || !src_slot || num_layers < 0)
+    return -fail(DSA_ERR_INVALID_ARG, "index share map: null array or negative layer count");
+  int last = -1, nfull = 0;
+  for (int i = 0; i < num_layers; ++i) {
+    if (layer_full[i] != 0 && layer_full[i] != 1)
+      return -fail(DSA_ERR_INVALID_ARG, "index share map: layer %d kind %d is neither 0 nor 1",
+                   i, layer_full[i]);
+    if (layer_full[i] == 1) {
+      last = nfull++;
+      full_slot[i] = last;
+    } else {
+      if (last < 0)
+        return -fail(DSA_ERR_INVALID_ARG, "index share map: layer %d is shared but no full "
+                     "layer precedes it", i);
+      full_slot[i] = -1;
+    }
+    src_slot[i] = last;
+  }
+  ok();
+  return nfull;
+}
+
 int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
                            int QB, int u_max) {
   if (!blk_counts_host || T <= 0 || H <= 0 || k <= 0 || PS <= 0 || QB <= 0 || u_max <= 0)

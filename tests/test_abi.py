@@ -21,7 +21,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 19
+    assert len(declared) == 20
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -174,3 +174,18 @@ def test_paged_write_validation(lib):
     assert call(src=(1 << 12) + 2) == _lib.DSA_ERR_INVALID_ARG  # misaligned
     assert call(src=None) == _lib.DSA_ERR_INVALID_ARG
     assert call(T=0) == _lib.DSA_OK
+
+
+def test_index_share_map(lib):
+    """Full layers own consecutive slots; a shared layer uses the nearest
+    preceding full layer's slot; a leading shared layer is an error."""
+    full, src, n = dsa.index_share_map(["full", "shared", "shared", "full", "shared"])
+    assert n == 2 and full == {0: 0, 3: 1}
+    assert src == {0: 0, 1: 0, 2: 0, 3: 1, 4: 1}
+    full, src, n = dsa.index_share_map(["full"] * 3)
+    assert n == 3 and full == {0: 0, 1: 1, 2: 2} and src == {0: 0, 1: 1, 2: 2}
+    assert dsa.index_share_map([]) == ({}, {}, 0)
+    with pytest.raises(dsa.DsaError):
+        dsa.index_share_map(["shared", "full"])
+    with pytest.raises(ValueError):
+        dsa.index_share_map(["full", "dense"])
