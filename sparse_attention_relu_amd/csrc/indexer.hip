@@ -97,6 +97,33 @@ __device__ __forceinline__ void lds_sync() {
 // rows I * RPI + l / CPR; lane l fetches the chunk that belongs at its slot
 // l % CPR, i.e. chunk (l % CPR) ^ (row % CPR). Since I * RPI is a multiple of
 // RPI and l / CPR < RPI, row % CPR = (I * RPI) % CPR ^ (l / CPR) % CPR.
+// Physical cache rows of one wave's NL loads of a stage (RPI rows each):
+// load n starts at position j = j_stage + RPI (NL wave + n). The wave's
+// positions span NL * RPI = 32 consecutive positions from a multiple of 32,
+// and PS is a multiple of 16, so they touch at most two pages: two
+// divisions and three page-table reads (wave-uniform, scalar) instead of a
+// division and a read per load. A load past the row's valid positions reads
+// position 0 (any valid row; its scores are never stored).
+template <int NL, int RPI>
+__device__ __forceinline__ void wave_stage_rows(const int32_t* __restrict__ ptrow, int num_pages,
+                                                int PS, int j_stage, int n_valid, int wave,
+                                                long (&row)[NL]) {
+  static_assert(NL * RPI == 32, "a wave's loads of a stage cover 32 positions");
+  const int jb = j_stage + NL * RPI * wave;
+  const int p_lo = jb / PS;
+  const int p_hi = (jb + NL * RPI - 1) / PS;  // p_lo or p_lo + 1
+  const int q_lo = jb < n_valid ? p_lo : 0;
+  const int q_hi = p_hi * PS < n_valid ? p_hi : q_lo;
+  const long pg_lo = (long)clamp_page(ptrow[q_lo], num_pages) * PS;
+  const long pg_hi = (long)clamp_page(ptrow[q_hi], num_pages) * PS;
+  const long pg_0 = (long)clamp_page(ptrow[0], num_pages) * PS;
+#pragma unroll
+  for (int n = 0; n < NL; ++n) {
+    const int j = jb + RPI * n;
+    row[n] = j >= n_valid ? pg_0 : (j < p_hi * PS ? pg_lo + (j - p_lo * PS) : pg_hi + (j - p_hi * PS));
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void stream_stage(uint32_t buf, const uint16_t* __restrict__ cache,
                                              const int32_t* __restrict__ ptrow, int num_pages,
@@ -107,14 +134,13 @@ __device__ __forceinline__ void stream_stage(uint32_t buf, const uint16_t* __res
   constexpr int NL = kStreamKeys / RPI / 4;  // loads per wave per stage
   const int lr = l / CPR, lc = l % CPR;
   const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+  long row[NL];
+  wave_stage_rows<NL, RPI>(ptrow, num_pages, PS, j_stage, n_valid, wave, row);
 #pragma unroll
   for (int n = 0; n < NL; ++n) {
     const int I = NL * wave + n;
-    int j0 = j_stage + I * RPI;  // first position of this load (one page)
-    if (j0 >= n_valid) j0 = 0;   // past the row: any valid row, never stored
-    const int page = clamp_page(ptrow[j0 / PS], num_pages);
-    gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
-              cache + ((size_t)page * PS + (j0 % PS)) * D, buf + I * 1024);
+    gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)), cache + (size_t)row[n] * D,
+              buf + I * 1024);
   }
 }
 
@@ -276,19 +302,12 @@ __device__ __forceinline__ void flat_issue_keys(uint32_t buf, const uint16_t* __
   constexpr int RB = 2 * D, RPI = 1024 / RB, CPR = D / 8, NL = kStreamKeys / RPI / 4;
   const int lr = l / CPR, lc = l % CPR;
   const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
-  int jj[NL], pg[NL];
-#pragma unroll
-  for (int n = 0; n < NL; ++n) {
-    int j0 = j_stage + (NL * wave + n) * RPI;
-    if (j0 >= n_valid) j0 = 0;  // past the row: any valid row, never stored
-    jj[n] = j0;
-    pg[n] = ptrow[j0 / PS];
-  }
+  long row[NL];
+  wave_stage_rows<NL, RPI>(ptrow, num_pages, PS, j_stage, n_valid, wave, row);
 #pragma unroll
   for (int n = 0; n < NL; ++n) {
     const int I = NL * wave + n;
-    const uint64_t src = (uint64_t)(uintptr_t)(
-        cache + ((size_t)clamp_page(pg[n], num_pages) * PS + (jj[n] % PS)) * D);
+    const uint64_t src = (uint64_t)(uintptr_t)(cache + (size_t)row[n] * D);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
     gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
