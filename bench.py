@@ -392,8 +392,13 @@ def bench_extend(dsa, wl, args, QB, steps=None):
                      "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
         res["roofline"] = roof
     res["per_query"] = _per_query_attend(dsa, wl, d, topk, outs, steps, kt)
-    # the library's own choice between the two paths for these unions
+    # the library's own choice between the two paths for these unions, and
+    # the step with the chosen path for every layer (indexer and union once)
     res["attend_path_chosen"] = dsa.extend_attend_path(cnt, T, H, k, wl.PS, QB, u_max)
+    per_layer = (res["per_query"]["ms_per_layer"] if res["attend_path_chosen"] == "per_query"
+                 else kt["mla_extend_qblock"][1])
+    res["ms_per_step_chosen_path"] = round(ms - layers * kt["mla_extend_qblock"][1]
+                                           + layers * per_layer, 4)
     res["cache_write"] = _cache_write(dsa, wl, d, steps)
     return res
 
