@@ -160,7 +160,8 @@ KERNEL_SOURCES = {
     "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
     "idx_score_tiles": "indexer.hip",
     "topk_select": "indexer.hip", "mla_decode_partial": "mla.hip",
-    "mla_decode_combine": "mla.hip", "mla_extend_qblock": "mla.hip",
+    "mla_decode_combine": "mla.hip", "mla_decode_combine_wide": "mla.hip",
+    "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
     "union_member": "union.hip", "page_pool": "indexer.hip", "page_token_list": "indexer.hip",
     "paged_write_rows": "cache_write.hip",

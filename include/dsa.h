@@ -308,7 +308,7 @@ int dsa_index_share_map(const int32_t* layer_full, int num_layers, int32_t* full
  * MI355X: executed query-block flops sum_b min(blk_counts[b], u_max) *
  * QB * H * PS * (576 + 512) * 2 at 1.0e15 flop/s, against the per-query
  * bytes (selected latent rows of 1152 bytes, selection entries, queries and
- * the per-chunk partial results, written and read back) at 5.3e12 B/s.
+ * the per-chunk partial results, written and read back) at 5.7e12 B/s.
  *
  *   blk_counts_host  HOST int32 [nQB], the blk_counts of dsa_block_union
  *                    copied to the host; read only, not kept

@@ -396,7 +396,7 @@ int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H
   // measured on MI355X, end to end per layer: executed MFMA rate of the
   // query-block kernel, and the byte rate of the per-query path (partial
   // kernel plus combine)
-  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.3e12;
+  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.7e12;
   double pages = 0.0;
   for (int b = 0; b < nQB; ++b) {
     const int c = blk_counts_host[b];

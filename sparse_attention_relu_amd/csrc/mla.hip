@@ -131,7 +131,7 @@ constexpr int kDecRing = 4;                                   // LDS stages
 constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
 constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
-constexpr int kDecMaxCH = 512;
+constexpr int kDecMaxCH = 1024;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
 // LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
@@ -369,15 +369,100 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   }
 }
 
-// grid = (T, H), block = 256: merge the nch partials of (t, h),
+// grid = (T, ceil(H / 4)), block = 256: wave w merges the nch partials of
+// (t, h = 4 blockIdx.y + w),
+//   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0,
+// M = max m_c. Lane c holds chunk c's (m, l) (chunks in groups of 64); the
+// maximum and the normaliser are wave reductions, and chunk c's weight
+// reaches the other lanes by a shuffle. Lane l sums value columns
+// 8 l .. 8 l + 7 (one 16-byte bf16 load per chunk), the first kCombAhead
+// chunks' loads issued unconditionally before the (m, l) loads (a chunk past
+// nch reads the last one and gets weight 0). No block barrier.
+constexpr int kCombAhead = 16;  // O partials per lane loaded with the (m, l) pairs
+
+// acc[0..7] += w * (eight bf16 values packed in v)
+__device__ __forceinline__ void fma_bf16x8(float (&acc)[8], float w, uint4 v) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] = fmaf(w, __uint_as_float(u[i] << 16), acc[2 * i]);
+    acc[2 * i + 1] = fmaf(w, __uint_as_float(u[i] & 0xffff0000u), acc[2 * i + 1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml,
+                                                          int H, int nch,
+                                                          uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  if (h >= H) return;  // wave-uniform
+  const int l = lane_id();
+  const size_t base = (size_t)t * nch * H;
+  auto orow = [&](int c) { return part_o + (base + (size_t)c * H + h) * DV + 8 * l; };
+  uint4 va[kCombAhead];
+#pragma unroll
+  for (int u = 0; u < kCombAhead; ++u)
+    va[u] = *reinterpret_cast<const uint4*>(orow(min(u, nch - 1)));
+  // ---- M and L over the live chunks (l_c > 0), 64 chunks per pass
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + l;
+    const size_t r = base + (size_t)min(c, nch - 1) * H + h;
+    const float m = part_ml[r * 2], lc = part_ml[r * 2 + 1];
+    M = fmaxf(M, c < nch && lc > 0.f ? m : -INFINITY);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + l;
+    const size_t r = base + (size_t)min(c, nch - 1) * H + h;
+    const float m = part_ml[r * 2], lc = part_ml[r * 2 + 1];
+    const float wl = c < nch && lc > 0.f ? __expf(m - M) : 0.f;  // this lane's chunk weight
+    L += wl * (c < nch ? lc : 0.f);
+    const int n = min(64, nch - c0);
+    int u0 = 0;
+    if (c0 == 0) {
+#pragma unroll
+      for (int u = 0; u < kCombAhead; ++u)
+        fma_bf16x8(acc, u < n ? __shfl(wl, u, DSA_WAVE) : 0.f, va[u]);
+      u0 = kCombAhead;
+    }
+    // the rest in batches of eight loads issued together (clamped, weight 0
+    // past the last chunk)
+    for (; u0 < n; u0 += 8) {
+      uint4 vb[8];
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        vb[v] = *reinterpret_cast<const uint4*>(orow(c0 + min(u0 + v, n - 1)));
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        fma_bf16x8(acc, u0 + v < n ? __shfl(wl, (u0 + v) & 63, DSA_WAVE) : 0.f, vb[v]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += shfl_xor_f(L, o);
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  uint4 packed;
+  packed.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  packed.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  packed.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  packed.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(out + ((size_t)t * H + h) * DV + 8 * l) = packed;
+}
+
+// Many chunks (nch > kCombAhead). grid = (T, H), block = 256: merge the nch
+// partials of (t, h),
 //   out = sum_c e^(m_c - M) O_c / sum_c e^(m_c - M) l_c  over chunks with l_c > 0,
 // M = max m_c. Thread (g, d4) = (tid / 128, tid % 128) sums chunks g, g + 2,
-// ... for value columns 4 d4 .. 4 d4 + 3. The first kCombAhead of this
+// ... for value columns 4 d4 .. 4 d4 + 3. The first kWideAhead of this
 // thread's O partials (bf16) and the (m, l) pairs are all loaded at once; the
 // chunk weights e^(m_c - M) are then computed once, in LDS, and the two
 // halves of the sum meet through LDS.
-constexpr int kCombMaxCH = 1024;  // partials per (row, head) the combine handles
-constexpr int kCombAhead = 16;    // O partials per thread loaded with the (m, l) pairs
+constexpr int kCombMaxCH = 1024;  // partials per (row, head) the wide combine handles
+constexpr int kWideAhead = 16;    // O partials per thread loaded with the (m, l) pairs
 
 // acc += w * (four bf16 partial values packed in v)
 __device__ __forceinline__ void fma_bf16x4(float4& acc, float w, uint2 v) {
@@ -387,7 +472,7 @@ __device__ __forceinline__ void fma_bf16x4(float4& acc, float w, uint2 v) {
   acc.w = fmaf(w, __uint_as_float(v.y & 0xffff0000u), acc.w);
 }
 
-__global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __restrict__ part_o,
+__global__ __launch_bounds__(256) void mla_decode_combine_wide(const uint16_t* __restrict__ part_o,
                                                           const float* __restrict__ part_ml,
                                                           int H, int nch,
                                                           uint16_t* __restrict__ out) {
@@ -401,9 +486,9 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __rest
   // ---- this thread's first O partials, then the (m, l) pairs: all in
   // flight together. The O loads are unconditional (a chunk past nch reads
   // the last chunk and gets weight 0), so that none of them waits for another
-  uint2 va[kCombAhead];
+  uint2 va[kWideAhead];
 #pragma unroll
-  for (int u = 0; u < kCombAhead; ++u) {
+  for (int u = 0; u < kWideAhead; ++u) {
     const int c = min(g + 2 * u, nch - 1);
     va[u] = *reinterpret_cast<const uint2*>(part_o + (base + (size_t)c * H + h) * DV + 4 * d4);
   }
@@ -437,11 +522,11 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __rest
   // (a chunk without live selections has w = 0 and a zero partial O)
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int u = 0; u < kCombAhead; ++u) {
+  for (int u = 0; u < kWideAhead; ++u) {
     const int c = g + 2 * u;
     fma_bf16x4(acc, c < nch ? s_w[c] : 0.f, va[u]);
   }
-  for (int c0 = g + 2 * kCombAhead; c0 < nch; c0 += 8) {
+  for (int c0 = g + 2 * kWideAhead; c0 < nch; c0 += 8) {
     uint2 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -468,8 +553,10 @@ __global__ __launch_bounds__(256) void mla_decode_combine(const uint16_t* __rest
 }
 
 int mla_decode_chunk(int T, int k) {
-  // about one workgroup per compute unit, 1 .. 8 blocks of 64 selections each
-  // (at most 8 to bound the partial (m, l, O) traffic of the combine)
+  // about one workgroup per compute unit, 1 .. 16 blocks of 64 selections
+  // each: a large batch gets long chunks, which halves both the one-time
+  // prologues (one workgroup per compute unit runs at a time) and the
+  // partials the combine reads
   const long nsub = (k + 63) / 64;
   long per = ((long)T * nsub + 255) / 256;
   if (per < 1) per = 1;
@@ -498,8 +585,12 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ProfScope prof("mla_decode_combine", st);
-  hipLaunchKernelGGL(mla_decode_combine, dim3(a.T, a.H), dim3(256), 0, st, a.part_o, a.part_ml,
-                     a.H, nch, a.out);
+  if (nch > kCombAhead)  // many chunks: two thread groups per (row, head) share them
+    hipLaunchKernelGGL(mla_decode_combine_wide, dim3(a.T, a.H), dim3(256), 0, st, a.part_o,
+                       a.part_ml, a.H, nch, a.out);
+  else
+    hipLaunchKernelGGL(mla_decode_combine, dim3(a.T, (a.H + 3) / 4), dim3(256), 0, st, a.part_o,
+                       a.part_ml, a.H, nch, a.out);
   return hipGetLastError();
 }
 
