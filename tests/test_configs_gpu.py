@@ -117,6 +117,37 @@ def test_config3_ragged_decode(dsa):
     _decode_config(dsa, 3)
 
 
+@pytest.mark.timeout(600)
+def test_config3_page_level_decode(dsa):
+    """Page-level selection on the ragged decode (rows of 4K..32K positions,
+    k / PS = 32 pages): page top-k of every row checked for its padding and
+    range, eight sampled rows against the oracle, then the page-list
+    attention of those rows."""
+    torch = torch_mod()
+    wl = W.config(3)
+    b = wl.batches["decode"]
+    d = Dev(wl)
+    bt = d.batch("decode")
+    kp = wl.k // wl.PS
+    pages = dsa.indexer_page_topk(bt["q_idx"], bt["w"], d.idx_cache, d.page_table, d.seq_lens,
+                                  bt["cu"], kp, 1)
+    out = dsa.sparse_mla_decode_pages(bt["q"], d.kv_cache[0], d.page_table, d.seq_lens,
+                                      bt["cu"], pages, wl.sm_scale)
+    torch.cuda.synchronize()
+    got = pages.cpu().numpy()
+    npg = -(-wl.seq_lens // wl.PS)  # decode rows: every position of the sequence is valid
+    assert ((got >= 0) == (np.arange(kp)[None, :] < np.minimum(kp, npg)[:, None])).all()
+    assert (got < npg[:, None]).all()
+    rows = sorted({0, b.T - 1} | set(np.random.default_rng(3).choice(b.T, 6, replace=False).tolist()))
+    log(f"config 3: page top-k oracle on rows {rows}")
+    exp = oracle.indexer_page_topk(bf16_to_f64(b.q_idx), b.w.astype(np.float64),
+                                   wl.idx_cache.f64_view(), wl.page_table, wl.seq_lens,
+                                   b.cu_q_lens, kp, rows=rows)
+    assert np.array_equal(got[rows], exp[rows]), "page top-k differs from the oracle"
+    ref = _oracle_rows_mla(wl, b, oracle.page_tokens(exp, wl.PS), rows)
+    check_attention(to_np(out), ref, rows=rows, what="config 3 page-level decode")
+
+
 def _check_union_all_blocks(units, counts, member, topk, QB, u_max):
     """Properties of every block: sorted unique units, -1 tail, and per query
     popcount = number of selections (lossless caps)."""
