@@ -85,6 +85,9 @@ int dsa_abi_version(void);
  *   max_q_len  host upper bound on q_len(s) over the batch (a hint that picks
  *              the streaming per-row kernel when <= 1 and the MFMA tile
  *              kernel otherwise; any value gives the same result)
+ *   workspace  device scratch of at least dsa_indexer_topk_workspace(...)
+ *              bytes for the same arguments: the fp32 score rows and, for
+ *              the tile kernel, each row's extreme scores per 2048 positions
  * Supported: 1 <= H <= 64, D in {32, 64, 128}, PS a multiple of 16,
  * MP * PS <= 2^24, 1 <= k <= 4096; otherwise DSA_ERR_UNSUPPORTED.
  */

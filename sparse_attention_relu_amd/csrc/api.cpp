@@ -79,9 +79,10 @@ int dsa_abi_version(void) { return 1; }
 // ---------------------------------------------------------------------------
 size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
                                   int max_q_len) {
-  (void)S; (void)H; (void)D; (void)k; (void)max_q_len;
+  (void)S; (void)H; (void)D; (void)k;
   if (T <= 0 || PS <= 0 || MP <= 0) return 0;
-  return align256((size_t)T * scores_ld(MP, PS) * 4);
+  return align256((size_t)T * scores_ld(MP, PS) * 4) +
+         align256((size_t)T * dsa::score_ext_ld(max_q_len, MP * PS) * 8);
 }
 
 int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
@@ -117,6 +118,10 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
   a.max_q_len = max_q_len;
   a.scores = static_cast<float*>(workspace);
   a.ld = scores_ld(MP, PS);
+  a.ext_ld = dsa::score_ext_ld(max_q_len, MP * PS);
+  if (a.ext_ld > 0)
+    a.ext = reinterpret_cast<uint2*>(static_cast<char*>(workspace) +
+                                     align256((size_t)T * a.ld * 4));
   a.topk = topk;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dsa::indexer_score(a, s);

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
-    int PS, int MP, float* __restrict__ scores, long ld) {
+    int PS, int MP, float* __restrict__ scores, long ld, uint2* __restrict__ ext, int ext_ld) {
   constexpr int KS = D / 16, HALF = D / 2, RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;
   constexpr int BLK = kTileKB * RB;      // bytes per staged block
   constexpr int NLB = BLK / 1024;        // direct loads per block (D / 8)
@@ -616,6 +616,7 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
         if (b < nb) stage(b);
       float* srow = scores + (size_t)(act ? t : 0) * ld;
       int hist = 0;  // bit i: this wave stored a block i + 1 iterations ago
+      uint32_t kmn = ~0u, kmx = 0u;  // order keys of this lane's stored scores
       for (int b = 0; b < nb; ++b) {
         // outstanding after block b's loads: the loads of the blocks issued
         // after it and the stores of the last three iterations
@@ -650,8 +651,24 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
         }
         // lane l stores key l of the block (j < nv holds for lane 0 here)
         const int j = k0 + b * kTileKB + l;
-        if (j < nv) srow[j] = hf ? sc[1] : sc[0];
+        if (j < nv) {
+          const float v = hf ? sc[1] : sc[0];
+          srow[j] = v;
+          const uint32_t key = score_order_bits(v);
+          kmn = min(kmn, key);
+          kmx = max(kmx, key);
+        }
         hist |= 1;
+      }
+      // the row's extreme order keys over this tile (at least position k0 is
+      // valid when the wave is active), for the select's bucket range
+      if (ext != nullptr && act) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, DSA_WAVE));
+          kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, DSA_WAVE));
+        }
+        if (l == 0) ext[(size_t)t * ext_ld + blockIdx.x] = make_uint2(kmn, kmx);
       }
       __syncthreads();  // the ring is free for the next segment
     }
@@ -822,6 +839,7 @@ template <int NT, int M>
 __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float* row, int n,
                                             int k, uint32_t* lds, size_t cur_off,
                                             size_t start_off, size_t key_off, DirectShared& sh,
+                                            const uint2* __restrict__ ext_row,
                                             int32_t* __restrict__ orow) {
   constexpr int C = NT * M;
   constexpr int BPT = 4096 / NT;
@@ -842,16 +860,26 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
 #pragma unroll
   for (int u = 0; u < BPT; ++u) cursor[tid * BPT + u] = 0u;
   uint32_t kmin = ~0u, kmax = 0u;
-  for (int c0 = 0; c0 < n; c0 += C) {
-    uint32_t keys[M];
-    chunk_keys(c0, keys);
-    const int j0 = c0 + tid * M;
+  if (ext_row != nullptr && n > C) {
+    // a row of several chunks: the scorer's per-tile extremes instead of a
+    // pass over the later chunks
+    for (int i = tid; i < (n + kTileMaxRK - 1) / kTileMaxRK; i += NT) {
+      const uint2 e = ext_row[i];
+      kmin = min(kmin, e.x);
+      kmax = max(kmax, e.y);
+    }
+  } else {
+    for (int c0 = 0; c0 < n; c0 += C) {
+      uint32_t keys[M];
+      chunk_keys(c0, keys);
+      const int j0 = c0 + tid * M;
 #pragma unroll
-    for (int e = 0; e < M; ++e)
-      if (j0 + e < n) {
-        kmin = min(kmin, keys[e]);
-        kmax = max(kmax, keys[e]);
-      }
+      for (int e = 0; e < M; ++e)
+        if (j0 + e < n) {
+          kmin = min(kmin, keys[e]);
+          kmax = max(kmax, keys[e]);
+        }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -1012,6 +1040,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ seq_lens,
                                                       int S, int cap, int unit, int k,
+                                                      const uint2* __restrict__ ext, int ext_ld,
                                                       int32_t* __restrict__ topk) {
   constexpr int NT = kSelNT;
   constexpr int CHUNK = NT * M;
@@ -1045,7 +1074,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   }
   if (n <= kDirectMaxN &&
       topk_direct<NT, M>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
-                         s_direct, orow))
+                         s_direct, ext != nullptr ? ext + (size_t)t * ext_ld : nullptr, orow))
     return;
   __syncthreads();  // the select path reuses the LDS
   // OR / AND / min / max of the keys this thread lists
@@ -1330,13 +1359,17 @@ static hipError_t launch_tiles(const IndexerArgs& a, hipStream_t st) {
   ProfScope prof("idx_score_tiles", st);
   hipLaunchKernelGGL((idx_score_tiles<D, HB>), grid, dim3(512), 0, st, a.q, a.w, a.cache,
                      a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
-                     a.ld);
+                     a.ld, a.ext, a.ext_ld);
   return hipGetLastError();
 }
 
 template <int D, int HB>
 static hipError_t launch_score(const IndexerArgs& a, hipStream_t st) {
   return a.max_q_len <= 1 ? launch_rows<D, HB>(a, st) : launch_tiles<D, HB>(a, st);
+}
+
+int score_ext_ld(int max_q_len, int cap) {
+  return max_q_len <= 1 ? 0 : (cap + kTileMaxRK - 1) / kTileMaxRK;
 }
 
 hipError_t indexer_score(const IndexerArgs& a, hipStream_t st) {
@@ -1368,6 +1401,8 @@ struct SelectJob {
   long ld;
   int unit, k;
   int32_t* out;
+  const uint2* ext;  // per-tile extreme keys of the rows, or nullptr
+  int ext_ld;
 };
 
 template <int IPT, int M>
@@ -1387,7 +1422,7 @@ static hipError_t launch_select(const IndexerArgs& a, const SelectJob& j, hipStr
   }
   ProfScope prof("topk_select", st);
   hipLaunchKernelGGL((topk_select<IPT, M>), dim3(a.T), dim3(kSelNT), lds, st, j.scores, j.ld,
-                     a.cu, a.seq_lens, a.S, a.MP * a.PS, j.unit, j.k, j.out);
+                     a.cu, a.seq_lens, a.S, a.MP * a.PS, j.unit, j.k, j.ext, j.ext_ld, j.out);
   return hipGetLastError();
 }
 
@@ -1407,11 +1442,11 @@ static hipError_t select_job(const IndexerArgs& a, const SelectJob& j, hipStream
 }
 
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st) {
-  return select_job(a, SelectJob{a.scores, a.ld, 1, a.k, a.topk}, st);
+  return select_job(a, SelectJob{a.scores, a.ld, 1, a.k, a.topk, a.ext, a.ext_ld}, st);
 }
 
 hipError_t indexer_page_select(const IndexerArgs& a, hipStream_t st) {
-  return select_job(a, SelectJob{a.page_scores, a.ldp, a.PS, a.k, a.topk}, st);
+  return select_job(a, SelectJob{a.page_scores, a.ldp, a.PS, a.k, a.topk, nullptr, 0}, st);
 }
 
 // ---------------------------------------------------------------------------

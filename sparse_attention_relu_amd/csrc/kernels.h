@@ -25,8 +25,15 @@ struct IndexerArgs {
   // positions); the select then ranks pages, ceil(n_valid / PS) per row
   float* page_scores;
   long ldp;
+  // tile scorer only: per (row, 2048-position tile) minimum and maximum order
+  // key of the stored scores [T, ext_ld] (nullptr: not produced)
+  uint2* ext = nullptr;
+  int ext_ld = 0;
 };
 
+// Tiles per row of the per-tile extreme keys the scorer writes for rows of
+// at most `cap` positions (0 when the chosen scorer writes none).
+int score_ext_ld(int max_q_len, int cap);
 hipError_t indexer_score(const IndexerArgs& a, hipStream_t st);
 hipError_t indexer_select(const IndexerArgs& a, hipStream_t st);
 hipError_t indexer_page_pool(const IndexerArgs& a, hipStream_t st);
