@@ -487,7 +487,11 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 // (lane l: key l), so the waits on the ring count every outstanding memory
 // operation exactly: the key loads of later blocks plus the stores of the
 // last three blocks. Rows of a tile may belong to several sequences: the
-// tile is walked one sequence segment at a time.
+// tile is walked one sequence segment at a time. With EXT each active wave
+// also writes its row's smallest and largest order key over the tile to
+// ext[t, tile] (the full key range when a score is NaN); the top-k of rows
+// longer than one select chunk takes its bucket range from these instead of
+// reading the scores an extra time.
 // grid = (ceil(cap / kTileMaxRK), ceil(T / 8)), block = 512.
 // ---------------------------------------------------------------------------
 constexpr int kTileMaxRK = 2048;  // key range of one tile workgroup
@@ -517,7 +521,7 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
   }
 }
 
-template <int D, int HB>
+template <int D, int HB, bool EXT>
 __global__ __launch_bounds__(512, 2) void idx_score_tiles(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
@@ -616,7 +620,9 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
         if (b < nb) stage(b);
       float* srow = scores + (size_t)(act ? t : 0) * ld;
       int hist = 0;  // bit i: this wave stored a block i + 1 iterations ago
-      uint32_t kmn = ~0u, kmx = 0u;  // order keys of this lane's stored scores
+      // extremes of this lane's stored scores (a NaN widens the range to all keys)
+      float fmn = __builtin_inff(), fmx = -__builtin_inff();
+      int nan = 0;
       for (int b = 0; b < nb; ++b) {
         // outstanding after block b's loads: the loads of the blocks issued
         // after it and the stores of the last three iterations
@@ -654,21 +660,27 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
         if (j < nv) {
           const float v = hf ? sc[1] : sc[0];
           srow[j] = v;
-          const uint32_t key = score_order_bits(v);
-          kmn = min(kmn, key);
-          kmx = max(kmx, key);
+          if (EXT) {
+            fmn = fminf(fmn, v);
+            fmx = fmaxf(fmx, v);
+            nan |= v != v;
+          }
         }
         hist |= 1;
       }
       // the row's extreme order keys over this tile (at least position k0 is
-      // valid when the wave is active), for the select's bucket range
-      if (ext != nullptr && act) {
+      // valid when the wave is active), for the select's bucket range; the
+      // order key is monotone in the score, so it is taken of the extremes
+      if (EXT && act) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
-          kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, DSA_WAVE));
-          kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, DSA_WAVE));
+          fmn = fminf(fmn, __shfl_xor(fmn, o, DSA_WAVE));
+          fmx = fmaxf(fmx, __shfl_xor(fmx, o, DSA_WAVE));
+          nan |= __shfl_xor(nan, o, DSA_WAVE);
         }
-        if (l == 0) ext[(size_t)t * ext_ld + blockIdx.x] = make_uint2(kmn, kmx);
+        if (l == 0)
+          ext[(size_t)t * ext_ld + blockIdx.x] =
+              nan ? make_uint2(0u, ~0u) : make_uint2(score_order_bits(fmn), score_order_bits(fmx));
       }
       __syncthreads();  // the ring is free for the next segment
     }
@@ -1357,9 +1369,14 @@ static hipError_t launch_tiles(const IndexerArgs& a, hipStream_t st) {
   const int cap = a.MP * a.PS;
   dim3 grid((cap + kTileMaxRK - 1) / kTileMaxRK, (a.T + kTileRows - 1) / kTileRows);
   ProfScope prof("idx_score_tiles", st);
-  hipLaunchKernelGGL((idx_score_tiles<D, HB>), grid, dim3(512), 0, st, a.q, a.w, a.cache,
-                     a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP, a.scores,
-                     a.ld, a.ext, a.ext_ld);
+  if (a.ext != nullptr)
+    hipLaunchKernelGGL((idx_score_tiles<D, HB, true>), grid, dim3(512), 0, st, a.q, a.w,
+                       a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP,
+                       a.scores, a.ld, a.ext, a.ext_ld);
+  else
+    hipLaunchKernelGGL((idx_score_tiles<D, HB, false>), grid, dim3(512), 0, st, a.q, a.w,
+                       a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP,
+                       a.scores, a.ld, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1368,8 +1385,9 @@ static hipError_t launch_score(const IndexerArgs& a, hipStream_t st) {
   return a.max_q_len <= 1 ? launch_rows<D, HB>(a, st) : launch_tiles<D, HB>(a, st);
 }
 
+// only rows longer than one select chunk (kSelNT x 16 positions) use them
 int score_ext_ld(int max_q_len, int cap) {
-  return max_q_len <= 1 ? 0 : (cap + kTileMaxRK - 1) / kTileMaxRK;
+  return max_q_len <= 1 || cap <= kSelNT * 16 ? 0 : (cap + kTileMaxRK - 1) / kTileMaxRK;
 }
 
 hipError_t indexer_score(const IndexerArgs& a, hipStream_t st) {

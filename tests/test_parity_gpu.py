@@ -75,6 +75,11 @@ INDEXER_EDGE = {
     "k4096_short_rows": (2, [100, 2500], 64, 40, [1, 2], 32, 128, 4096, 0),
     "k4096_long_rows": (1, [10000], 64, 160, [3], 32, 128, 4096, 0),
     "h32_d128_chunk_straddle": (4, [700, 64, 1500, 33], 64, 24, [33, 64, 47, 33], 32, 128, 128, 2),
+    # rows above 16384 positions (the select's key range then comes from the
+    # tile scorer's per-2048-position extremes) sharing 8-row tiles with short
+    # rows; 18433 positions leave a last tile of one position
+    "h32_d128_long_rows_tile_extremes": (3, [40000, 300, 18433], 64, 640, [5, 2, 4], 32, 128,
+                                         512, 1),
 }
 
 
@@ -153,13 +158,15 @@ def test_indexer_ties_and_negative_zero(dsa):
         assert np.array_equal(got, exp)
 
 
-@pytest.mark.parametrize("k", [200, 512])
-def test_indexer_crowded_ties(dsa, k):
-    """About 2980 keys share one vector (exactly equal scores) and 20 keys are
-    its double: the top-k is the 20 large scores, then the tied positions in
-    ascending order. With k=200 the ties fill one bucket of the select's rank
-    phase; with k=512 that bucket overflows and the list is sorted instead."""
-    wl = W.build(name="crowded", seed=11, S=1, kv_lens=[3000], PS=64, MP=48,
+@pytest.mark.parametrize("k,kv", [(200, 3000), (512, 3000), (512, 20000)])
+def test_indexer_crowded_ties(dsa, k, kv):
+    """All but 20 keys share one vector (exactly equal scores) and those 20
+    are its double: the top-k is the 20 large scores, then the tied positions
+    in ascending order. With k=200 the ties fill one bucket of the select's
+    rank phase; with k=512 that bucket overflows and the list is sorted
+    instead. At 20000 positions a row spans several select chunks and most
+    2048-position tiles hold a single score value."""
+    wl = W.build(name="crowded", seed=11, S=1, kv_lens=[kv], PS=64, MP=-(-kv // 64),
                  batches={"b": [0, 3]}, H_idx=8, D_idx=64, k=k, with_mla=False)
     b = wl.batches["b"]
     rows = wl.idx_cache.rows
@@ -170,7 +177,7 @@ def test_indexer_crowded_ties(dsa, k):
     d = Dev(wl)
     exp = _oracle_topk(wl, b, k=k)
     for mql in (1, 3):
-        log(f"indexer crowded ties k={k} mql={mql}")
+        log(f"indexer crowded ties k={k} kv={kv} mql={mql}")
         got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, k, mql)
         assert np.array_equal(got, exp)
 
