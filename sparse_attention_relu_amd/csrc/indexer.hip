@@ -809,8 +809,10 @@ struct SelectCfg {
   static constexpr size_t D_CUR_OFF = 0;
   static constexpr size_t D_START_OFF = 4096 * 4;
   static constexpr size_t D_KEY_OFF = D_START_OFF + (4096 + 64) * 4;
-  static constexpr size_t D_POS_OFF = 0;  // unused
-  static constexpr size_t DIRECT_BYTES = D_KEY_OFF + ((size_t)CAP + 64) * 8;
+  // | speculative candidates of a row of several chunks (composites) [SPEC]
+  static constexpr int SPEC = IPT == 8 ? 6144 : CAP;
+  static constexpr size_t D_SPEC_OFF = D_KEY_OFF + ((size_t)CAP + 64) * 8;
+  static constexpr size_t DIRECT_BYTES = D_SPEC_OFF + (size_t)SPEC * 8;
   static constexpr size_t BYTES = SEL_BYTES > DIRECT_BYTES ? SEL_BYTES : DIRECT_BYTES;
 };
 
@@ -845,12 +847,15 @@ struct DirectShared {
   int wbig[kSelNT / 64];         // per-wave "oversized candidate bucket" flags
   int lim;                       // end of the bucket holding place k - 1
   int blast;                     // that bucket (candidates are the buckets up to it)
+  int spec_n;                    // speculative candidates listed (may exceed the list)
+  int spec_b;                    // their last bucket
 };
 
 template <int NT, int M>
 __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float* row, int n,
                                             int k, uint32_t* lds, size_t cur_off,
-                                            size_t start_off, size_t key_off, DirectShared& sh,
+                                            size_t start_off, size_t key_off, size_t spec_off,
+                                            int spec_cap, DirectShared& sh,
                                             const uint2* __restrict__ ext_row,
                                             int32_t* __restrict__ orow) {
   constexpr int C = NT * M;
@@ -859,6 +864,7 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
   uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + cur_off);
   int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + start_off);
   uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
+  uint64_t* spec = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + spec_off);
   // keys of chunk c0 (the first one from registers)
   auto chunk_keys = [&](int c0, uint32_t (&keys)[M]) {
     if (c0 == 0) {
@@ -871,6 +877,10 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
   // ---- phase 1: clear the bucket counters; key minimum and maximum
 #pragma unroll
   for (int u = 0; u < BPT; ++u) cursor[tid * BPT + u] = 0u;
+  if (tid == 0) {
+    sh.spec_n = 0;
+    sh.spec_b = -1;
+  }
   uint32_t kmin = ~0u, kmax = 0u;
   if (ext_row != nullptr && n > C) {
     // a row of several chunks: the scorer's per-tile extremes instead of a
@@ -929,14 +939,87 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
       const uint32_t b = j0 + e < n ? (uint32_t)bucket(k0[e]) : 4096u;
       rk0[e] = b < 4096u ? (b << 16) | atomicAdd(&cursor[b], 1u) : (4096u << 16);
     }
+  } else if (n <= C) {
+    const int j0 = tid * M;
+#pragma unroll
+    for (int e = 0; e < M; ++e)
+      if (j0 + e < n) atomicAdd(&cursor[bucket(k0[e])], 1u);
   } else {
-    for (int c0 = 0; c0 < n; c0 += C) {
-      uint32_t keys[M];
-      chunk_keys(c0, keys);
-      const int j0 = c0 + tid * M;
+    // A row of several chunks. The first chunk (all valid) is counted alone;
+    // the bucket at which its count reaches 1.3 k C / n + 16 estimates where
+    // the row's candidates end. Every key up to that bucket is listed as
+    // counted, so that the candidates are taken from the list instead of a
+    // second pass over the row whenever the estimate covers them and the
+    // list did not overflow (checked once the row's counts are known).
+#pragma unroll
+    for (int e = 0; e < M; ++e) atomicAdd(&cursor[bucket(k0[e])], 1u);
+    __syncthreads();
+    {
+      int c[BPT], local = 0;
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        c[u] = (int)cursor[tid * BPT + u];
+        local += c[u];
+      }
+      int incl = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, DSA_WAVE);
+        if (lane >= off) incl += v;
+      }
+      if (lane == 63) sh.wsum[wv] = incl;
+      __syncthreads();
+      int run = incl - local;
+#pragma unroll
+      for (int i = 0; i < NT / 64; ++i) run += i < wv ? sh.wsum[i] : 0;
+      const int target = (int)(1.3f * (float)k * (float)C / (float)n) + 16;  // < C
+#pragma unroll
+      for (int u = 0; u < BPT; ++u) {
+        if (run < target && run + c[u] >= target) sh.spec_b = tid * BPT + u;
+        run += c[u];
+      }
+    }
+    __syncthreads();
+    const int gb = sh.spec_b;
+    // list the keys of buckets up to gb (bit e of `take`: key e of the
+    // thread's M), one LDS atomic per wave and chunk
+    auto spec_list = [&](const uint32_t (&keys)[M], uint32_t take, int j0) {
+      const int cnt = __popc(take);
+      int incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, DSA_WAVE);
+        if (lane >= off) incl += v;
+      }
+      int base = 0;
+      if (lane == 63) base = atomicAdd(&sh.spec_n, incl);
+      int slot = __shfl(base, 63, DSA_WAVE) + incl - cnt;
 #pragma unroll
       for (int e = 0; e < M; ++e)
-        if (j0 + e < n) atomicAdd(&cursor[bucket(keys[e])], 1u);
+        if ((take >> e) & 1u) {
+          if (slot < spec_cap) spec[slot] = ((uint64_t)keys[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
+          ++slot;
+        }
+    };
+    {
+      uint32_t take = 0;
+#pragma unroll
+      for (int e = 0; e < M; ++e) take |= (uint32_t)(bucket(k0[e]) <= gb) << e;
+      spec_list(k0, take, tid * M);
+    }
+    for (int c0 = C; c0 < n; c0 += C) {
+      uint32_t keys[M];
+      load_keys<M>(row, n, c0, keys);
+      const int j0 = c0 + tid * M;
+      uint32_t take = 0;
+#pragma unroll
+      for (int e = 0; e < M; ++e)
+        if (j0 + e < n) {
+          const int b = bucket(keys[e]);
+          atomicAdd(&cursor[b], 1u);
+          take |= (uint32_t)(b <= gb) << e;
+        }
+      spec_list(keys, take, j0);
     }
   }
   __syncthreads();
@@ -1002,6 +1085,14 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
       if ((int)(rk0[e] >> 16) <= blast)
         scomp[bs[e] + (int)(rk0[e] & 0xffffu)] =
             ((uint64_t)k0[e] << 32) | (uint64_t)(~(uint32_t)(j0 + e));
+  } else if (n > C && blast <= sh.spec_b && sh.spec_n <= spec_cap) {
+    // the listed keys hold every candidate
+    const int ns = sh.spec_n;
+    for (int i = tid; i < ns; i += NT) {
+      const uint64_t cm = spec[i];
+      const int b = bucket((uint32_t)(cm >> 32));
+      if (b <= blast) scomp[atomicAdd(&cursor[b], 1u)] = cm;
+    }
   } else {
     for (int c0 = 0; c0 < n; c0 += C) {
       uint32_t keys[M];
@@ -1086,7 +1177,8 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   }
   if (n <= kDirectMaxN &&
       topk_direct<NT, M>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
-                         s_direct, ext != nullptr ? ext + (size_t)t * ext_ld : nullptr, orow))
+                         Cfg::D_SPEC_OFF, Cfg::SPEC, s_direct,
+                         ext != nullptr ? ext + (size_t)t * ext_ld : nullptr, orow))
     return;
   __syncthreads();  // the select path reuses the LDS
   // OR / AND / min / max of the keys this thread lists
