@@ -838,7 +838,12 @@ __device__ __forceinline__ float order_key_value(uint32_t key) {
 // nothing, when the spread is degenerate or a candidate bucket holds more
 // than kDirectBucketMax positions. Five block barriers. When the row fits one
 // chunk, the histogram's atomic returns each key's offset inside its bucket,
-// so the candidates are placed without a second round of atomics.
+// so the candidates are placed without a second round of atomics. A row of
+// several chunks counts its first chunk alone (three more barriers), takes
+// from that count a bucket beyond which the candidates most likely do not
+// reach, and lists every key up to it during the histogram pass; when the
+// row's last candidate bucket is within that bound and the list did not
+// overflow, the candidates come from the list, else from a second pass.
 constexpr int kDirectMaxN = 1 << 17;
 
 struct DirectShared {
