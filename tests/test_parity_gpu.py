@@ -182,6 +182,33 @@ def test_indexer_crowded_ties(dsa, k, kv):
         assert np.array_equal(got, exp)
 
 
+@pytest.mark.parametrize("skew", ["early", "late"])
+def test_indexer_long_rows_skewed(dsa, skew):
+    """Rows of 40000 positions whose first 16384 keys (one select chunk) are
+    doubled ("early": the top-k crowds into them) or whose later keys are
+    ("late": far more large scores after the first chunk than it suggests).
+    Doubling a key doubles every head's dot product, so the positions keep
+    their order within each part; the select's estimate taken from the
+    first chunk misses in both directions and the exact answer must hold."""
+    kv = 40000
+    wl = W.build(name="skewed", seed=21, S=1, kv_lens=[kv], PS=64, MP=-(-kv // 64),
+                 batches={"b": [0, 3]}, H_idx=32, D_idx=128, k=2048, with_mla=False)
+    b = wl.batches["b"]
+    cache = wl.idx_cache
+    pos = np.arange(16384) if skew == "early" else np.arange(16384, kv)
+    phys = wl.page_table[0][pos // wl.PS].astype(np.int64) * wl.PS + pos % wl.PS
+    at = np.searchsorted(cache.slots, phys)
+    assert np.array_equal(cache.slots[at], phys)
+    cache.rows[at] = W.f32_to_bf16(2.0 * W.bf16_to_f32(cache.rows[at]))
+    d = Dev(wl)
+    exp = _oracle_topk(wl, b, k=2048)
+    for mql in (1, 3):
+        log(f"indexer long rows skew={skew} mql={mql}")
+        got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, 2048, mql)
+        assert np.array_equal(got, exp)
+    check_topk_rows_valid(got, wl.seq_lens, b.cu_q_lens, 2048)
+
+
 def test_indexer_zero_rows(dsa):
     """T > 0 with no sequence rows at all (cu_q_lens = 0...): all -1."""
     wl = W.build(name="none", seed=6, S=2, kv_lens=[50, 60], PS=16, MP=4,
