@@ -80,6 +80,11 @@ INDEXER_EDGE = {
     # rows; 18433 positions leave a last tile of one position
     "h32_d128_long_rows_tile_extremes": (3, [40000, 300, 18433], 64, 640, [5, 2, 4], 32, 128,
                                          512, 1),
+    # rows of several select chunks at the other list capacities (k up to
+    # 1024, and k above 2048 where the candidate list is the shortest
+    # relative to k)
+    "h32_d128_long_rows_k1000": (2, [40000, 20000], 64, 640, [3, 2], 32, 128, 1000, 0),
+    "h32_d128_long_rows_k4096": (2, [40000, 33000], 64, 640, [3, 2], 32, 128, 4096, 0),
 }
 
 
