@@ -230,6 +230,33 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
                           size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_sparse_mla_decode_static — dsa_sparse_mla_decode without a workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * result is the dsa_sparse_mla_decode result for the same arguments (the
+ * same kernels and the same split of each selection list).
+ *
+ * The split-list partials live in a static device array of the library,
+ * 32 MiB per GPU (zero-filled at load, held until the process ends); the
+ * call allocates nothing and frees nothing. Its address on a GPU is taken
+ * once, on the first call with that GPU current. Calls that need more than
+ * dsa_sparse_mla_decode_workspace(T, H, k) > 32 MiB return
+ * DSA_ERR_UNSUPPORTED (the workspace entry point has no such limit).
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there: calls that overlap on one GPU (concurrent streams, or threads)
+ * race and must be serialised by the caller. `stream` must belong to the
+ * current device (DSA_ERR_INVALID_ARG otherwise); GPUs beyond the 64th are
+ * not supported (DSA_ERR_HIP).
+ *
+ *   arguments as in dsa_sparse_mla_decode, without workspace and its size
+ */
+int dsa_sparse_mla_decode_static(const void* q, const void* kv_cache, int row_stride,
+                                 int num_pages, const int32_t* page_table,
+                                 const int32_t* seq_lens, const int32_t* cu_q_lens,
+                                 const int32_t* topk, int T, int S, int H, int k, int PS, int MP,
+                                 float sm_scale, void* out, void* stream);
+
+/*
  * dsa_sparse_mla_decode_pages — sparse absorbed-MLA attention over every
  * valid position of each row's selected pages: the page-budget decode of
  * "dsa_sparse_backend.py" (the page-scoring indexer path, whose pages come

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     profile_read,
     sparse_mla_decode,
     sparse_mla_decode_pages,
+    sparse_mla_decode_static,
     sparse_mla_decode_workspace,
     sparse_mla_extend,
     sparse_mla_extend_workspace,

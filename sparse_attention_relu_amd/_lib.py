@@ -48,6 +48,8 @@ SIGNATURES = {
     "dsa_page_tokens": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dsa_paged_write": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp]
                         + [_c_int] * 4 + [_vp]),
+    "dsa_sparse_mla_decode_static": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
+                                     + [_c_int] * 6 + [_c_float, _vp, _vp]),
     "dsa_sparse_mla_decode_pages": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
                                     + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_profile_enable": (_c_int, [_c_int]),
@@ -389,6 +391,28 @@ def sparse_mla_decode(q, kv_cache, page_table, seq_lens, cu_q_lens, topk, sm_sca
                                       PS, MP, float(sm_scale), _ptr(out), _ptr(ws), nbytes,
                                       _stream(stream))
     _check("dsa_sparse_mla_decode", st)
+    return out
+
+
+def sparse_mla_decode_static(q, kv_cache, page_table, seq_lens, cu_q_lens, topk,
+                             sm_scale: float, out=None, stream=None):
+    """sparse_mla_decode with the library's static per-GPU scratch instead of
+    a workspace (dsa_sparse_mla_decode_static): nothing is allocated for the
+    call apart from `out` when it is not given."""
+    torch = _torch()
+    dev, S, MP, T, H, P, PS, rs = _mla_common(q, kv_cache, page_table, seq_lens, cu_q_lens)
+    _need(topk, "topk", torch.int32, 2, dev)
+    if topk.shape[0] != T:
+        raise ValueError("topk rows must match q rows")
+    k = topk.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 3, dev)
+    st = load().dsa_sparse_mla_decode_static(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
+                                             _ptr(seq_lens), _ptr(cu_q_lens), _ptr(topk), T, S,
+                                             H, k, PS, MP, float(sm_scale), _ptr(out),
+                                             _stream(stream))
+    _check("dsa_sparse_mla_decode_static", st)
     return out
 
 

@@ -326,6 +326,60 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
+int dsa_sparse_mla_decode_static(const void* q, const void* kv_cache, int row_stride,
+                                 int num_pages, const int32_t* page_table,
+                                 const int32_t* seq_lens, const int32_t* cu_q_lens,
+                                 const int32_t* topk, int T, int S, int H, int k, int PS, int MP,
+                                 float sm_scale, void* out, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (k < 1 || k > 65536) return fail(DSA_ERR_UNSUPPORTED, "k=%d not in [1, 65536]", k);
+  if (T == 0) return ok();
+  st = check_mla_common(q, kv_cache, row_stride, H, PS, out);
+  if (st) return st;
+  if (!page_table || !seq_lens || !cu_q_lens || !topk)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  const size_t need = decode_ws(T, H, k);
+  if (need > dsa::kStaticScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "static decode: T=%d, H=%d, k=%d needs %zu bytes of scratch, the static "
+                "scratch holds %zu (use dsa_sparse_mla_decode with a workspace)",
+                T, H, k, need, dsa::kStaticScratchBytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (s != nullptr) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if ((int)sdev != dev)
+      return fail(DSA_ERR_INVALID_ARG, "static decode: the stream belongs to device %d, the "
+                  "current device is %d", (int)sdev, dev);
+  }
+  void* ws = nullptr;
+  e = dsa::static_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "static scratch address");
+  const int ch = dsa::mla_decode_chunk(T, k);
+  const size_t nch = (size_t)((k + ch - 1) / ch);
+  dsa::MlaArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = static_cast<const uint16_t*>(kv_cache);
+  a.row_stride = row_stride;
+  a.num_pages = num_pages;
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.topk = topk;
+  a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
+  a.sm_scale = sm_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = static_cast<uint16_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                       align256((size_t)T * nch * H * 512 * 2));
+  return hip_status(dsa::mla_decode(a, s), "static decode launch");
+}
+
 int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_stride,
                                 int num_pages, const int32_t* page_table,
                                 const int32_t* seq_lens, const int32_t* cu_q_lens,

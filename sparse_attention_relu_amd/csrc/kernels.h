@@ -91,6 +91,11 @@ struct CacheWriteArgs {
 hipError_t paged_write(const CacheWriteArgs& a, hipStream_t st);
 
 int mla_decode_chunk(int T, int k);
+// Size of the per-GPU static scratch of the allocation-free decode entry point,
+// and its device address on the current device (taken once per device).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxScratchDevices = 64;
+hipError_t static_scratch(void** ptr);
 hipError_t mla_decode(const MlaArgs& a, hipStream_t st);
 hipError_t mla_extend(const MlaArgs& a, hipStream_t st);
 

@@ -8,6 +8,7 @@
 // union page for all QB * H rows of a block, per-row validity = membership
 // bit AND causal AND kv_len, flash-style online softmax.
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -1117,6 +1118,36 @@ hipError_t mla_extend(const MlaArgs& a, hipStream_t st) {
                      a.num_pages, a.pt, a.seq_lens, a.cu, a.units, a.counts, a.member, a.T, a.S,
                      a.H, a.PS, a.MP, a.QB, a.u_max, a.sm_scale, a.out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident scratch of the allocation-free decode entry point: the
+// split-list partials (unnormalised O and (m, l)) live in this array instead
+// of a caller workspace. Each GPU the library runs on holds its own copy,
+// zero-filled when the code object loads and kept until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_dev[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    per_dev[dev] = p;
+  }
+  *ptr = per_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace dsa

@@ -21,7 +21,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 20
+    assert len(declared) == 21
+    assert "dsa_sparse_mla_decode_static" in declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -189,3 +190,15 @@ def test_index_share_map(lib):
         dsa.index_share_map(["shared", "full"])
     with pytest.raises(ValueError):
         dsa.index_share_map(["full", "dense"])
+
+
+def test_static_decode_host_checks(lib):
+    """The allocation-free decode refuses, on the host and before any HIP
+    call, an unsupported head count and a batch whose partials exceed its
+    32 MiB static scratch."""
+    p = 1 << 12
+    args = lambda T, H, k: (p, p, 576, 4, p, p, p, p, T, 1, H, k, 64, 4, 0.1, p, None)
+    assert lib.dsa_sparse_mla_decode_static(*args(2, 0, 16)) == 2
+    assert lib.dsa_sparse_mla_decode_static(*args(64, 64, 65536)) == 2
+    assert "static scratch" in dsa.last_error()
+    assert lib.dsa_sparse_mla_decode_static(*args(0, 16, 16)) == 0  # empty batch: nothing to do
