@@ -238,8 +238,10 @@ def paged_write(cache, rows, col0, page_table, seq_lens, cu_q_lens):
     ``page_table[s, a // PS]`` at offset ``a % PS``, columns
     ``col0 .. col0 + cols - 1``; the other columns and slots are unchanged.
 
-    Reading taken: rows outside every sequence, and positions outside
-    ``0 <= a < min(seq_lens[s], MP * PS)``, are dropped (the pages route them
+    Reading taken: rows outside every sequence, positions outside
+    ``0 <= a < min(seq_lens[s], MP * PS)``, and positions whose page-table
+    entry is not a page of the cache (outside ``[0, P)``, e.g. -1 for an
+    unassigned page) have no slot and are dropped (the pages route such rows
     to a reserved page of their allocator instead).
 
     cache [P, PS, C], rows [T, cols]; returns a new array.
@@ -247,14 +249,17 @@ def paged_write(cache, rows, col0, page_table, seq_lens, cu_q_lens):
     out = np.array(cache, copy=True)
     rows = np.asarray(rows)
     T, cols = rows.shape
-    PS = cache.shape[1]
+    P, PS = cache.shape[0], cache.shape[1]
     MP = page_table.shape[1]
     seq, pos = query_rows(seq_lens, cu_q_lens, T)
     for t in range(T):
         s, a = int(seq[t]), int(pos[t])
         if s < 0 or a < 0 or a >= min(int(seq_lens[s]), MP * PS):
             continue
-        out[page_table[s, a // PS], a % PS, col0:col0 + cols] = rows[t]
+        page = int(page_table[s, a // PS])
+        if page < 0 or page >= P:
+            continue
+        out[page, a % PS, col0:col0 + cols] = rows[t]
     return out
 
 

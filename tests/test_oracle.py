@@ -531,6 +531,31 @@ def pin_paged_write_bruteforce():
             if seq[t] >= 0:
                 back = oracle.gather_rows(got, wl.page_table, int(seq[t]), [int(pos[t])])[0]
                 assert np.array_equal(back[1:3], rows[t])
+    # page-table entries that name no page of the cache (-1, or past the
+    # pool) give those positions no slot: nothing at all is written for them
+    wl = micro(210, q_lens=(3, 0, 2), S=3)
+    b = wl.batches["b"]
+    cache = bf16_to_f64(wl.idx_cache)
+    P, PS = cache.shape[0], cache.shape[1]
+    T = int(b.cu_q_lens[-1])
+    rows = np.arange(T * 2, dtype=np.float64).reshape(T, 2) + 500.0
+    seq, pos = oracle.query_rows(wl.seq_lens, b.cu_q_lens, T)
+    pt = np.array(wl.page_table, copy=True)
+    t_bad, t_far = int(b.cu_q_lens[0]), int(b.cu_q_lens[2])  # first rows of sequences 0 and 2
+    pt[int(seq[t_bad]), int(pos[t_bad]) // PS] = -1
+    pt[int(seq[t_far]), int(pos[t_far]) // PS] = P + 3
+    got = oracle.paged_write(cache, rows, 1, pt, wl.seq_lens, b.cu_q_lens)
+    exp = cache.copy()
+    for t in range(T):
+        s, a = int(seq[t]), int(pos[t])
+        if s < 0 or not (0 <= a < int(wl.seq_lens[s])):
+            continue
+        pg = int(pt[s][a // PS])
+        if 0 <= pg < P:
+            exp[pg, a % PS, 1:3] = rows[t]
+    assert np.array_equal(np.nan_to_num(got, nan=-7.0), np.nan_to_num(exp, nan=-7.0))
+    # the -1 entry must not reach the last page (a negative index would)
+    assert np.array_equal(np.nan_to_num(got[P - 1], nan=-7.0), np.nan_to_num(exp[P - 1], nan=-7.0))
 
 
 PINS = [
