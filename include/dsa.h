@@ -151,11 +151,13 @@ int dsa_page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t* t
  * Packed row t of sequence s (q_start <= t < q_end) lands at its seq-local
  * position a = seq_lens[s] - (q_end - q_start) + (t - q_start):
  *     cache[page_table[s, a / PS], a % PS, col0 + c] = src[t, c],  c < cols.
- * Rows outside every sequence, and positions outside
- * 0 <= a < min(seq_lens[s], MP * PS), are dropped. Other columns and slots
- * are left untouched, so the latent row is written by two calls (c_kv at
- * col0 = 0 with cols = 512, k_rope at col0 = 512 with cols = 64) and the
- * indexer key by one (cols = D). Rows of one call must name distinct slots.
+ * Rows outside every sequence, positions outside
+ * 0 <= a < min(seq_lens[s], MP * PS), and positions whose page-table entry is
+ * not in [0, num_pages) (e.g. -1 for an unassigned page) are dropped. Other
+ * columns and slots are left untouched, so a latent row can be written whole
+ * (cols = 576) or by parts (c_kv at col0 = 0 with cols = 512, k_rope at
+ * col0 = 512 with cols = 64), the indexer key by one call (cols = D). Rows of
+ * one call must name distinct slots.
  *
  *   src    bf16 [T, src_stride], the first cols columns are written
  *   cache  bf16 [num_pages, PS, row_stride], written in place
@@ -167,6 +169,30 @@ int dsa_paged_write(const void* src, int src_stride, int cols, int col0, void* c
                     int row_stride, int num_pages, const int32_t* page_table,
                     const int32_t* seq_lens, const int32_t* cu_q_lens, int T, int S, int PS,
                     int MP, void* stream);
+
+/*
+ * dsa_paged_write_layer — one launch that writes a layer's new tokens into
+ * both of its caches ahead of its indexer and attention: the indexer keys
+ * ("dsa_sparse_backend.py", _scatter_paged) and the latent rows
+ * ("sparse_mla_prefill_qblock.py", paged_write_back, the self-write of
+ * prefill_write_and_attend_ragged_qblock). Each written row follows the
+ * dsa_paged_write rule (same slots, same dropped rows), with
+ *   idx_cache[page, a % PS, 0:D]      = idx_src[t, 0:D]
+ *   kv_cache[page, a % PS, 0:kv_cols] = kv_src[t, 0:kv_cols]
+ * Either source may be NULL to skip that cache (a layer that shares another
+ * layer's indexer has no keys of its own to write).
+ *
+ *   idx_src    bf16 [T, D] dense,       idx_cache bf16 [num_pages, PS, D]
+ *   kv_src     bf16 [T, kv_cols] dense, kv_cache  bf16 [num_pages, PS, row_stride]
+ *              (kv_cols = 576 writes the whole [c_kv | k_rope] row)
+ * Returns DSA_ERR_INVALID_ARG when both sources are NULL, when D, kv_cols or
+ * row_stride is not a positive multiple of 8 or kv_cols > row_stride, when a
+ * given source has no cache, or when a pointer is not 16-byte aligned.
+ */
+int dsa_paged_write_layer(const void* idx_src, int D, void* idx_cache, const void* kv_src,
+                          int kv_cols, void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, int T, int S, int PS, int MP, void* stream);
 
 /*
  * dsa_block_union — per query-block union of selected pages and per-token
@@ -349,6 +375,25 @@ int dsa_index_share_map(const int32_t* layer_full, int num_layers, int32_t* full
  */
 int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
                            int QB, int u_max);
+
+/*
+ * dsa_extend_attend_plan — the extend attention to run for a packed batch,
+ * chosen among the per-query path and query blocks of several sizes QB
+ * (the QB sweep of "dsa_sparse_backend.py", DSA_PREFILL_QBLOCK_QB), from
+ * each candidate's union sizes. The cost of each is the estimate of
+ * dsa_extend_attend_path; ties keep the per-query path, then the earlier
+ * candidate. Host logic only.
+ *
+ *   n_qb         number of query-block candidates (0: per query)
+ *   qb_host      HOST int32 [n_qb], the candidates' QB
+ *   counts_host  HOST [n_qb] pointers: candidate i's blk_counts from
+ *                dsa_block_union at QB = qb_host[i] (ceil(T / QB) entries)
+ *   T, H, k, PS, u_max  as in the other calls (u_max: the union tables' slots)
+ * Returns the chosen QB, 0 for the per-query path, or DSA_ERR_INVALID_ARG
+ * (as a negative number) for a null array, a non-positive QB or size.
+ */
+int dsa_extend_attend_plan(int n_qb, const int32_t* qb_host, const int32_t* const* counts_host,
+                           int T, int H, int k, int PS, int u_max);
 
 /*
  * Kernel timing (diagnostics). dsa_profile_enable(1) clears earlier records

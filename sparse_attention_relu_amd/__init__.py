@@ -10,6 +10,8 @@ from ._lib import (  # noqa: F401
     block_union,
     block_union_workspace,
     extend_attend_path,
+    extend_attend_plan,
+    extend_layers,
     header_functions,
     index_share_map,
     indexer_page_topk,
@@ -20,6 +22,7 @@ from ._lib import (  # noqa: F401
     load,
     page_tokens,
     paged_write,
+    paged_write_layer,
     profile_enable,
     profile_read,
     sparse_mla_decode,

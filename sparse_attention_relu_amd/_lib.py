@@ -41,6 +41,7 @@ SIGNATURES = {
                               + [_c_int] * 6 + [_c_float, _vp, _vp, _c_size, _vp]),
     "dsa_sparse_mla_extend_workspace": (_c_size, [_c_int] * 4),
     "dsa_extend_attend_path": (_c_int, [_vp] + [_c_int] * 7),
+    "dsa_extend_attend_plan": (_c_int, [_c_int, _vp, _vp] + [_c_int] * 5),
     "dsa_index_share_map": (_c_int, [_vp, _c_int, _vp, _vp]),
     "dsa_indexer_page_topk_workspace": (_c_size, [_c_int] * 8),
     "dsa_indexer_page_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
@@ -48,6 +49,8 @@ SIGNATURES = {
     "dsa_page_tokens": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _vp]),
     "dsa_paged_write": (_c_int, [_vp, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp]
                         + [_c_int] * 4 + [_vp]),
+    "dsa_paged_write_layer": (_c_int, [_vp, _c_int, _vp, _vp, _c_int, _vp, _c_int, _c_int,
+                                       _vp, _vp, _vp] + [_c_int] * 4 + [_vp]),
     "dsa_sparse_mla_decode_static": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
                                      + [_c_int] * 6 + [_c_float, _vp, _vp]),
     "dsa_sparse_mla_decode_pages": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp]
@@ -139,7 +142,27 @@ def _need(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _workspace(nbytes: int, device, workspace=None):
+def _alloc_stream(stream):
+    """The stream a tensor the binding allocates must belong to: memory
+    from torch's caching allocator is tied to the stream it is allocated on,
+    so a buffer that the library uses on another stream is allocated on that
+    stream (its memory is then not reused before that stream's work)."""
+    torch = _torch()
+    if stream is None or stream == torch.cuda.current_stream():
+        return None
+    return stream
+
+
+def _empty(shape, dtype, device, stream=None):
+    torch = _torch()
+    s = _alloc_stream(stream)
+    if s is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(s):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device, workspace=None, stream=None):
     torch = _torch()
     if nbytes == 0:
         return None
@@ -147,7 +170,7 @@ def _workspace(nbytes: int, device, workspace=None):
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
         return workspace
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty(nbytes, torch.uint8, device, stream)
 
 
 def _ragged(page_table, seq_lens, cu_q_lens, device):
@@ -208,10 +231,10 @@ def indexer_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int,
     if Dc != D or tuple(w.shape) != (T, H):
         raise ValueError("q_idx [T,H,D], w [T,H], idx_cache [P,PS,D] disagree")
     if out is None:
-        out = torch.empty((T, k), dtype=torch.int32, device=dev)
+        out = _empty((T, k), torch.int32, dev, stream)
     _need(out, "out", torch.int32, 2, dev)
     nbytes = indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_indexer_topk(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P, _ptr(page_table),
                                  _ptr(seq_lens), _ptr(cu_q_lens), T, S, H, D, PS, MP, k,
                                  max_q_len, _ptr(out), _ptr(ws), nbytes, _stream(stream))
@@ -238,10 +261,10 @@ def indexer_page_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k_pa
     if Dc != D or tuple(w.shape) != (T, H):
         raise ValueError("q_idx [T,H,D], w [T,H], idx_cache [P,PS,D] disagree")
     if out is None:
-        out = torch.empty((T, k_pages), dtype=torch.int32, device=dev)
+        out = _empty((T, k_pages), torch.int32, dev, stream)
     _need(out, "out", torch.int32, 2, dev)
     nbytes = indexer_page_topk_workspace(T, S, H, D, PS, MP, k_pages, max_q_len)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_indexer_page_topk(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P,
                                       _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S,
                                       H, D, PS, MP, k_pages, max_q_len, _ptr(out), _ptr(ws),
@@ -257,7 +280,7 @@ def page_tokens(pages, PS: int, out=None, stream=None):
     _need(pages, "pages", torch.int32, 2, dev)
     T, kp = pages.shape
     if out is None:
-        out = torch.empty((T, kp * PS), dtype=torch.int32, device=dev)
+        out = _empty((T, kp * PS), torch.int32, dev, stream)
     _need(out, "out", torch.int32, 2, dev)
     st = load().dsa_page_tokens(_ptr(pages), T, kp, PS, _ptr(out), _stream(stream))
     _check("dsa_page_tokens", st)
@@ -286,6 +309,44 @@ def paged_write(src, cache, page_table, seq_lens, cu_q_lens, col0: int = 0, stre
     return cache
 
 
+def paged_write_layer(idx_src, idx_cache, kv_src, kv_cache, page_table, seq_lens, cu_q_lens,
+                      stream=None):
+    """Write a layer's new tokens into its indexer-key cache and its latent
+    cache with one launch (dsa_paged_write_layer). idx_src bf16 [T, D] and
+    kv_src bf16 [T, cols] are dense; either (with its cache) may be None. The
+    caches are updated in place."""
+    torch = _torch()
+    if idx_src is None and kv_src is None:
+        raise ValueError("nothing to write: idx_src and kv_src are both None")
+    ref = idx_cache if idx_src is not None else kv_cache
+    dev = ref.device
+    S, MP = _ragged(page_table, seq_lens, cu_q_lens, dev)
+    T = (idx_src if idx_src is not None else kv_src).shape[0]
+    D, P, PS, cols, rs = 0, None, None, 0, 0
+    if idx_src is not None:
+        _need(idx_src, "idx_src", torch.bfloat16, 2, dev)
+        _need(idx_cache, "idx_cache", torch.bfloat16, 3, dev)
+        P, PS, D = idx_cache.shape
+        if idx_src.shape[1] != D:
+            raise ValueError("idx_src [T, D] and idx_cache [P, PS, D] disagree on D")
+    if kv_src is not None:
+        _need(kv_src, "kv_src", torch.bfloat16, 2, dev)
+        _need(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+        P2, PS2, rs = kv_cache.shape
+        if P is not None and (P2, PS2) != (P, PS):
+            raise ValueError("the two caches must have the same pages")
+        P, PS = P2, PS2
+        cols = kv_src.shape[1]
+        if kv_src.shape[0] != T:
+            raise ValueError("idx_src and kv_src disagree on T")
+    st = load().dsa_paged_write_layer(_ptr(idx_src), D, _ptr(idx_cache) if idx_src is not None
+                                      else None, _ptr(kv_src), cols,
+                                      _ptr(kv_cache) if kv_src is not None else None, rs, P,
+                                      _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S, PS,
+                                      MP, _stream(stream))
+    _check("dsa_paged_write_layer", st)
+
+
 def block_union_workspace(T, S, MP, QB, u_max) -> int:
     return load().dsa_block_union_workspace(T, S, MP, QB, u_max)
 
@@ -303,12 +364,12 @@ def block_union(topk, seq_lens, cu_q_lens, PS: int, MP: int, QB: int, u_max: int
     S = seq_lens.shape[0]
     nqb = (T + QB - 1) // QB
     if out is None:
-        out = (torch.empty((nqb, u_max), dtype=torch.int32, device=dev),
-               torch.empty((nqb,), dtype=torch.int32, device=dev),
-               torch.empty((nqb, u_max, QB), dtype=torch.uint64, device=dev))
+        out = (_empty((nqb, u_max), torch.int32, dev, stream),
+               _empty((nqb,), torch.int32, dev, stream),
+               _empty((nqb, u_max, QB), torch.uint64, dev, stream))
     units, counts, member = out
     nbytes = block_union_workspace(T, S, MP, QB, u_max)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_block_union(_ptr(topk), _ptr(seq_lens), _ptr(cu_q_lens), T, S, k, PS, MP, QB,
                                 u_max, _ptr(units), _ptr(counts), _ptr(member), _ptr(ws), nbytes,
                                 _stream(stream))
@@ -343,6 +404,29 @@ def extend_attend_path(blk_counts, T: int, H: int, k: int, PS: int, QB: int,
     if r < 0:
         raise DsaError("dsa_extend_attend_path", -r, last_error())
     return "per_query" if r == 1 else "qblock"
+
+
+def extend_attend_plan(counts_by_qb, T: int, H: int, k: int, PS: int, u_max: int) -> int:
+    """The extend attention to run (dsa_extend_attend_plan): the chosen QB
+    among the candidates, or 0 for the per-query path. counts_by_qb maps
+    each candidate QB to its blk_counts (any array or tensor; a device
+    tensor is copied to the host)."""
+    import numpy as np
+
+    qbs = [int(q) for q in counts_by_qb]
+    arrs = []
+    for q in qbs:
+        c = counts_by_qb[q]
+        if hasattr(c, "detach"):
+            c = c.detach().cpu().numpy()
+        arrs.append(np.ascontiguousarray(c, dtype=np.int32))
+    qb_arr = np.asarray(qbs if qbs else [0], dtype=np.int32)
+    ptrs = (ctypes.c_void_p * max(1, len(arrs)))(*[a.ctypes.data for a in arrs])
+    r = load().dsa_extend_attend_plan(len(qbs), qb_arr.ctypes.data, ctypes.addressof(ptrs), T, H,
+                                      k, PS, u_max)
+    if r < 0:
+        raise DsaError("dsa_extend_attend_plan", -r, last_error())
+    return int(r)
 
 
 def index_share_map(indexer_types):
@@ -383,9 +467,9 @@ def sparse_mla_decode(q, kv_cache, page_table, seq_lens, cu_q_lens, topk, sm_sca
         raise ValueError("topk rows must match q rows")
     k = topk.shape[1]
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        out = _empty((T, H, 512), torch.bfloat16, dev, stream)
     nbytes = sparse_mla_decode_workspace(T, H, k)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_sparse_mla_decode(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
                                       _ptr(seq_lens), _ptr(cu_q_lens), _ptr(topk), T, S, H, k,
                                       PS, MP, float(sm_scale), _ptr(out), _ptr(ws), nbytes,
@@ -406,7 +490,7 @@ def sparse_mla_decode_static(q, kv_cache, page_table, seq_lens, cu_q_lens, topk,
         raise ValueError("topk rows must match q rows")
     k = topk.shape[1]
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        out = _empty((T, H, 512), torch.bfloat16, dev, stream)
     _need(out, "out", torch.bfloat16, 3, dev)
     st = load().dsa_sparse_mla_decode_static(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
                                              _ptr(seq_lens), _ptr(cu_q_lens), _ptr(topk), T, S,
@@ -427,9 +511,9 @@ def sparse_mla_decode_pages(q, kv_cache, page_table, seq_lens, cu_q_lens, pages,
         raise ValueError("pages rows must match q rows")
     kp = pages.shape[1]
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        out = _empty((T, H, 512), torch.bfloat16, dev, stream)
     nbytes = sparse_mla_decode_workspace(T, H, kp * PS)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_sparse_mla_decode_pages(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
                                             _ptr(seq_lens), _ptr(cu_q_lens), _ptr(pages), T, S,
                                             H, kp, PS, MP, float(sm_scale), _ptr(out), _ptr(ws),
@@ -454,9 +538,9 @@ def sparse_mla_extend(q, kv_cache, page_table, seq_lens, cu_q_lens, units, count
     if nqb != (T + QB - 1) // QB or tuple(member.shape) != (nqb, u_max, QB):
         raise ValueError("union tables do not match (T, QB)")
     if out is None:
-        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        out = _empty((T, H, 512), torch.bfloat16, dev, stream)
     nbytes = sparse_mla_extend_workspace(T, H, QB, u_max)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_sparse_mla_extend(_ptr(q), _ptr(kv_cache), rs, P, _ptr(page_table),
                                       _ptr(seq_lens), _ptr(cu_q_lens), _ptr(units),
                                       _ptr(counts), _ptr(member), T, S, H, PS, MP, QB, u_max,
@@ -464,3 +548,94 @@ def sparse_mla_extend(q, kv_cache, page_table, seq_lens, cu_q_lens, units, count
                                       else None, nbytes, _stream(stream))
     _check("dsa_sparse_mla_extend", st)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Layer runner (model-loop glue)
+# ----------------------------------------------------------------------------
+def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max_q_len: int,
+                  sm_scale: float, q_idx, w, idx_cache, q, kv_cache, new_idx=None, new_kv=None,
+                  qb_candidates=(64, 256), u_max=None, path=None, outs=None, stream=None):
+    """Run a stack of DSA layers over one packed batch with IndexShare
+    ("ref.py", build_index_share_map; "dsa_sparse_backend.py", __call__:
+    a shared layer attends with the top-k of the nearest preceding full
+    layer). Only library calls, in this order per layer i:
+
+    1. the self-write of the batch's new tokens (dsa_paged_write_layer, one
+       launch): new_kv[i] into kv_cache[i] and, on a full layer, its
+       new_idx[slot] into idx_cache[slot] (skipped when new_kv is None);
+    2. on a full layer: the indexer top-k (dsa_indexer_topk) into the
+       layer's slot, then the block unions at each QB of qb_candidates
+       (dsa_block_union), whose sizes choose the attention
+       (dsa_extend_attend_plan: a QB or the per-query path; this reads the
+       union sizes on the host, a synchronisation of `stream`);
+    3. the attention of every layer with its source slot's selection:
+       dsa_sparse_mla_extend at the chosen QB, or dsa_sparse_mla_decode
+       (per query) on the packed batch.
+
+    indexer_types lists "full" / "shared" per layer; q_idx, w, idx_cache
+    (and new_idx) are lists indexed by slot (full layers in order); q,
+    kv_cache, new_kv are lists indexed by layer. path forces "per_query" or
+    a QB for every slot. Returns (outs, info): outs[i] bf16 [T, H, 512];
+    info["topk"][slot], info["choice"][slot] (0 = per query, else the QB),
+    info["counts"][slot] (QB -> blk_counts).
+    """
+    full_slot, src_slot, n_full = index_share_map(indexer_types)
+    n_layers = len(indexer_types)
+    torch = _torch()
+    dev = q[0].device
+    S, MP = _ragged(page_table, seq_lens, cu_q_lens, dev)
+    T, H, _ = q[0].shape
+    PS = kv_cache[0].shape[1]
+    if len(q_idx) != n_full or len(w) != n_full or len(idx_cache) != n_full:
+        raise ValueError(f"{n_full} full layers need {n_full} q_idx, w and idx_cache entries")
+    if len(q) != n_layers or len(kv_cache) != n_layers:
+        raise ValueError(f"{n_layers} layers need {n_layers} q and kv_cache entries")
+    if new_kv is not None and (len(new_kv) != n_layers or new_idx is None
+                               or len(new_idx) != n_full):
+        raise ValueError("new_kv needs one entry per layer and new_idx one per full layer")
+    qbs = [int(x) for x in qb_candidates]
+    topk = [None] * n_full
+    tables = [None] * n_full
+    choice = [None] * n_full
+    counts = [None] * n_full
+    if outs is None:
+        outs = [None] * n_layers
+    for i in range(n_layers):
+        slot = src_slot[i]
+        own = full_slot.get(i)
+        if new_kv is not None:
+            paged_write_layer(new_idx[own] if own is not None else None,
+                              idx_cache[own] if own is not None else None,
+                              new_kv[i], kv_cache[i], page_table, seq_lens, cu_q_lens,
+                              stream=stream)
+        if own is not None:
+            tk = indexer_topk(q_idx[own], w[own], idx_cache[own], page_table, seq_lens,
+                              cu_q_lens, k, max_q_len, stream=stream)
+            topk[own] = tk
+            tabs, cnts = {}, {}
+            for qb in qbs:
+                um = u_max if u_max is not None else min(qb * k, S * MP)
+                tabs[qb] = (block_union(tk, seq_lens, cu_q_lens, PS, MP, qb, um, stream=stream),
+                            um)
+                cnts[qb] = tabs[qb][0][1]
+            if path is None:
+                um0 = min(t[1] for t in tabs.values()) if tabs else (u_max or S * MP)
+                choice[own] = extend_attend_plan(cnts, T, H, k, PS, um0)
+            else:
+                choice[own] = 0 if path == "per_query" else int(path)
+                if choice[own] and choice[own] not in tabs:
+                    raise ValueError(f"forced QB {path} is not among qb_candidates")
+            tables[own] = tabs
+            counts[own] = cnts
+        c = choice[slot]
+        if c == 0:
+            outs[i] = sparse_mla_decode(q[i], kv_cache[i], page_table, seq_lens, cu_q_lens,
+                                        topk[slot], sm_scale, out=outs[i], stream=stream)
+        else:
+            (units, cnt, member), _um = tables[slot][c]
+            outs[i] = sparse_mla_extend(q[i], kv_cache[i], page_table, seq_lens, cu_q_lens,
+                                        units, cnt, member, c, sm_scale, out=outs[i],
+                                        stream=stream)
+    return outs, {"topk": topk, "choice": choice, "counts": counts,
+                  "src_slot": src_slot, "full_slot": full_slot}

@@ -213,18 +213,69 @@ int dsa_paged_write(const void* src, int src_stride, int cols, int col0, void* c
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(src) || !aligned16(cache))
     return fail(DSA_ERR_INVALID_ARG, "src and cache must be 16-byte aligned");
-  dsa::CacheWriteArgs a;
-  a.src = static_cast<const uint16_t*>(src);
-  a.src_stride = src_stride;
-  a.cols = cols;
-  a.col0 = col0;
-  a.cache = static_cast<uint16_t*>(cache);
-  a.row_stride = row_stride;
+  dsa::CacheWriteArgs a = {};
+  a.job[0].src = static_cast<const uint16_t*>(src);
+  a.job[0].src_stride = src_stride;
+  a.job[0].cols = cols;
+  a.job[0].col0 = col0;
+  a.job[0].cache = static_cast<uint16_t*>(cache);
+  a.job[0].row_stride = row_stride;
+  a.job[0].num_pages = num_pages;
+  a.njobs = 1;
   a.pt = page_table;
   a.seq_lens = seq_lens;
   a.cu = cu_q_lens;
-  a.T = T; a.S = S; a.PS = PS; a.MP = MP; a.num_pages = num_pages;
+  a.T = T; a.S = S; a.PS = PS; a.MP = MP;
   return hip_status(dsa::paged_write(a, static_cast<hipStream_t>(stream)), "paged write launch");
+}
+
+int dsa_paged_write_layer(const void* idx_src, int D, void* idx_cache, const void* kv_src,
+                          int kv_cols, void* kv_cache, int row_stride, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens,
+                          const int32_t* cu_q_lens, int T, int S, int PS, int MP, void* stream) {
+  int st = check_ragged(T, S, PS, MP, num_pages);
+  if (st) return st;
+  if (!idx_src && !kv_src)
+    return fail(DSA_ERR_INVALID_ARG, "layer write: neither indexer keys nor latent rows given");
+  if (idx_src && (D < 8 || D % 8 || !idx_cache))
+    return fail(DSA_ERR_INVALID_ARG, "layer write: D=%d must be a positive multiple of 8 with "
+                "an indexer cache", D);
+  if (kv_src && (kv_cols < 8 || kv_cols % 8 || row_stride % 8 || kv_cols > row_stride ||
+                 !kv_cache))
+    return fail(DSA_ERR_INVALID_ARG, "layer write: kv_cols=%d, row_stride=%d (need multiples "
+                "of 8 with kv_cols <= row_stride) and a latent cache", kv_cols, row_stride);
+  if (T == 0) return ok();
+  if (!page_table || !seq_lens || !cu_q_lens)
+    return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  if ((idx_src && (!aligned16(idx_src) || !aligned16(idx_cache))) ||
+      (kv_src && (!aligned16(kv_src) || !aligned16(kv_cache))))
+    return fail(DSA_ERR_INVALID_ARG, "sources and caches must be 16-byte aligned");
+  dsa::CacheWriteArgs a = {};
+  if (idx_src) {
+    dsa::CacheWriteJob& j = a.job[a.njobs++];
+    j.src = static_cast<const uint16_t*>(idx_src);
+    j.src_stride = D;
+    j.cols = D;
+    j.col0 = 0;
+    j.cache = static_cast<uint16_t*>(idx_cache);
+    j.row_stride = D;
+    j.num_pages = num_pages;
+  }
+  if (kv_src) {
+    dsa::CacheWriteJob& j = a.job[a.njobs++];
+    j.src = static_cast<const uint16_t*>(kv_src);
+    j.src_stride = kv_cols;
+    j.cols = kv_cols;
+    j.col0 = 0;
+    j.cache = static_cast<uint16_t*>(kv_cache);
+    j.row_stride = row_stride;
+    j.num_pages = num_pages;
+  }
+  a.pt = page_table;
+  a.seq_lens = seq_lens;
+  a.cu = cu_q_lens;
+  a.T = T; a.S = S; a.PS = PS; a.MP = MP;
+  return hip_status(dsa::paged_write(a, static_cast<hipStream_t>(stream)), "layer write launch");
 }
 
 // ---------------------------------------------------------------------------
@@ -445,6 +496,30 @@ int dsa_index_share_map(const int32_t* layer_full, int num_layers, int32_t* full
   return nfull;
 }
 
+namespace {
+// measured on MI355X, end to end per layer: executed MFMA rate of the
+// query-block kernel, and the byte rate of the per-query path (partial
+// kernel plus combine)
+constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.7e12;
+
+double qblock_seconds(const int32_t* counts, int nQB, int QB, int H, int PS, int u_max) {
+  double pages = 0.0;
+  for (int b = 0; b < nQB; ++b) {
+    const int c = counts[b];
+    pages += c < 0 ? 0.0 : (c < u_max ? c : u_max);
+  }
+  return pages * QB * H * PS * (576.0 + 512.0) * 2.0 / kQblockFlops;
+}
+
+double per_query_seconds(int T, int H, int k) {
+  const int CH = dsa::mla_decode_chunk(T, k);
+  const double nch = (double)((k + CH - 1) / CH);
+  const double bytes = (double)T * k * (1152.0 + 4.0) + (double)T * H * 1152.0 +
+                       (double)T * nch * H * (512.0 * 2.0 + 2.0 * 4.0) * 2.0;
+  return bytes / kGatherBytes;
+}
+}  // namespace
+
 int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H, int k, int PS,
                            int QB, int u_max) {
   if (!blk_counts_host || T <= 0 || H <= 0 || k <= 0 || PS <= 0 || QB <= 0 || u_max <= 0)
@@ -452,23 +527,33 @@ int dsa_extend_attend_path(const int32_t* blk_counts_host, int nQB, int T, int H
   if ((long)nQB != ((long)T + QB - 1) / QB)
     return -fail(DSA_ERR_INVALID_ARG, "extend path: nQB=%d does not match T=%d, QB=%d", nQB, T,
                  QB);
-  // measured on MI355X, end to end per layer: executed MFMA rate of the
-  // query-block kernel, and the byte rate of the per-query path (partial
-  // kernel plus combine)
-  constexpr double kQblockFlops = 1.0e15, kGatherBytes = 5.7e12;
-  double pages = 0.0;
-  for (int b = 0; b < nQB; ++b) {
-    const int c = blk_counts_host[b];
-    pages += c < 0 ? 0.0 : (c < u_max ? c : u_max);
-  }
-  const double t_qblock = pages * QB * H * PS * (576.0 + 512.0) * 2.0 / kQblockFlops;
-  const int CH = dsa::mla_decode_chunk(T, k);
-  const double nch = (double)((k + CH - 1) / CH);
-  const double bytes = (double)T * k * (1152.0 + 4.0) + (double)T * H * 1152.0 +
-                       (double)T * nch * H * (512.0 * 2.0 + 2.0 * 4.0) * 2.0;
-  const double t_query = bytes / kGatherBytes;
+  const double t_qblock = qblock_seconds(blk_counts_host, nQB, QB, H, PS, u_max);
+  const double t_query = per_query_seconds(T, H, k);
   ok();
   return t_query < t_qblock ? 1 : 0;
+}
+
+int dsa_extend_attend_plan(int n_qb, const int32_t* qb_host, const int32_t* const* counts_host,
+                           int T, int H, int k, int PS, int u_max) {
+  if (n_qb < 0 || (n_qb > 0 && (!qb_host || !counts_host)) || T <= 0 || H <= 0 || k <= 0 ||
+      PS <= 0 || u_max <= 0)
+    return -fail(DSA_ERR_INVALID_ARG, "extend plan: null candidate arrays or a non-positive size");
+  double best = per_query_seconds(T, H, k);
+  int choice = 0;
+  for (int i = 0; i < n_qb; ++i) {
+    const int QB = qb_host[i];
+    if (QB <= 0 || !counts_host[i])
+      return -fail(DSA_ERR_INVALID_ARG, "extend plan: candidate %d has QB=%d or no counts", i,
+                   QB);
+    const double t = qblock_seconds(counts_host[i], (int)(((long)T + QB - 1) / QB), QB, H, PS,
+                                    u_max);
+    if (t < best) {
+      best = t;
+      choice = QB;
+    }
+  }
+  ok();
+  return choice;
 }
 
 size_t dsa_sparse_mla_extend_workspace(int T, int H, int QB, int u_max) {

@@ -77,15 +77,22 @@ struct MlaArgs {
   float* part_ml;
 };
 
-struct CacheWriteArgs {
-  const uint16_t* src;  // bf16 [T, src_stride]
+// One cache of a paged write: src bf16 [T, src_stride] (first cols columns)
+// into cache bf16 [num_pages, PS, row_stride] at columns col0 ...
+struct CacheWriteJob {
+  const uint16_t* src;
   int src_stride, cols, col0;
-  uint16_t* cache;      // bf16 [num_pages, PS, row_stride]
-  int row_stride;
+  uint16_t* cache;
+  int row_stride, num_pages;
+};
+
+struct CacheWriteArgs {
+  CacheWriteJob job[2];  // the caches written by one launch
+  int njobs;             // 1 or 2
   const int32_t* pt;
   const int32_t* seq_lens;
   const int32_t* cu;
-  int T, S, PS, MP, num_pages;
+  int T, S, PS, MP;
 };
 
 hipError_t paged_write(const CacheWriteArgs& a, hipStream_t st);

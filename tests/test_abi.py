@@ -4,6 +4,8 @@ is made here)."""
 import ctypes
 import os
 
+import numpy as np
+
 import pytest
 
 import sparse_attention_relu_amd as dsa
@@ -21,7 +23,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 21
+    assert len(declared) == 23
     assert "dsa_sparse_mla_decode_static" in declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -202,3 +204,19 @@ def test_static_decode_host_checks(lib):
     assert lib.dsa_sparse_mla_decode_static(*args(64, 64, 65536)) == 2
     assert "static scratch" in dsa.last_error()
     assert lib.dsa_sparse_mla_decode_static(*args(0, 16, 16)) == 0  # empty batch: nothing to do
+
+
+def test_extend_attend_plan_picks_cheapest(lib):
+    """Host logic: the per-query path for saturated unions at the chunked
+    size; a query block when unions are small, the larger block when its
+    union is smaller per row."""
+    T, H, k, PS = 4096, 16, 2048, 64
+    sat = {64: np.full(64, 208), 256: np.full(16, 208)}
+    assert dsa.extend_attend_plan(sat, T, H, k, PS, 832) == 0
+    small = {64: np.full(64, 4), 256: np.full(16, 4)}
+    assert dsa.extend_attend_plan(small, T, H, k, PS, 832) == 64  # a tie keeps the first
+    small[256] = np.full(16, 3)
+    assert dsa.extend_attend_plan(small, T, H, k, PS, 832) == 256
+    assert dsa.extend_attend_plan({}, T, H, k, PS, 832) == 0
+    with pytest.raises(dsa.DsaError):
+        dsa.extend_attend_plan({0: np.zeros(1)}, T, H, k, PS, 832)
