@@ -1,17 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the DeepSeek-Sparse-Attention hot path on one MI355X.
 
-One step = one DSA layer of the workload:
-  decode  (default, 8 sequences x 8192 tokens): exact indexer top-k, then
-          sparse absorbed-MLA decode over the selected positions;
-  ragged decode (64 sequences, 4K..32K tokens, reported beside it);
-  extend  (4 requests x (12288 + 1024), reported beside it): indexer top-k,
-          query-block union tables, query-block sparse MLA.
-Inputs are seeded synthetic tensors already resident in HBM when the timed
-region starts. Prints ONE JSON line (rank 0).
+Headline (the JSON line's `value`): extend ms per layer on the long-context
+IndexShare workload (one request, 131072-token context, its final
+8192-token chunk, page size 64; indexer 32 heads x 128, k = 2048; four
+layers of sparse MLA with 16 heads, the first full, three sharing its
+top-k). One step is the four layers in order, each timed end to end:
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 2]
-                  [--ragged-config 3|0] [--extend-config 4|5|0] [--no-cpu-baseline]
+  full layer    the self-write of the chunk's indexer keys and latent rows
+                (one launch), the indexer top-k, the query-block union of
+                the attend's selection, and the sparse MLA attention;
+  shared layer  the self-write of its latent rows and the attention with the
+                full layer's selection and union.
+
+The attention runs on the path the library's plan picks from the union
+sizes (per query, or query blocks of 64 / 256). As the workload prescribes
+for timing, union and attention take the seeded locality selection (first 64
+positions, last 1024, uniform rest); the same step with the indexer's own
+selection is reported beside it. value = step ms / 4 layers.
+
+Beside it, in the same line: the decode batch (8 x 8192) and the ragged
+decode (64 x [4K, 32K]) in tokens/s, the chunked extend (4 x (12288 + 1024))
+at QB 64 and 256 and per query, per-kernel durations warm and with cold
+caches (median, p10, p90), the copy-kernel bandwidth, and the CPU oracle's
+per-stage time on the host cores.
+
+Inputs are seeded synthetic tensors already resident in HBM when a timed
+region starts. Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+                  [--only all|long|decode|ragged|extend|copy]
 """
 from __future__ import annotations
 
@@ -29,71 +47,102 @@ METRIC = "decode tok/s & extend ms/layer (indexer top-k + sparse MLA), % of roof
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 DK, DV = 576, 512
+FLUSH_BYTES = 1 << 30           # four times the 256 MB infinity cache
 
 
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--config", type=int, default=2, choices=[1, 2, 3],
-                   help="decode workload (1 tiny, 2 8x8192, 3 ragged 64x[4K,32K])")
-    p.add_argument("--extend-config", type=int, default=4, choices=[0, 1, 4, 5],
-                   help="extend workload measured beside it (0 = none)")
-    p.add_argument("--ragged-config", type=int, default=3, choices=[0, 3],
-                   help="ragged decode workload reported beside it (0 = none)")
-    p.add_argument("--long-config", type=int, default=5, choices=[0, 5],
-                   help="long-context extend with IndexShare layers (0: skip)")
-    p.add_argument("--qb", type=int, default=256, help="query block of the extend layer")
-    p.add_argument("--only", choices=["all", "decode", "ragged", "extend", "long", "copy"],
+    p.add_argument("--steps", type=int, default=10,
+                   help="timed steps of the headline (long-context) step")
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--only", choices=["all", "long", "decode", "ragged", "extend", "copy"],
                    default="all",
                    help="run one workload alone (for per-workload profiles); 'copy' times a "
-                        "plain 256 MiB device copy, the scale of the HBM byte counters")
+                        "plain device copy, the scale of the HBM byte counters")
+    p.add_argument("--cold-reps", type=int, default=0,
+                   help="repetitions of the cold/warm per-kernel statistics (0: per workload "
+                        "default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time of the oracle baseline sample")
     return p.parse_args(argv)
 
 
 # ----------------------------------------------------------------------------
-# helpers
+# device inputs
 # ----------------------------------------------------------------------------
+def _i32(a):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _bf16(a):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
 def _dev_inputs(wl, bname, layers=1):
     import numpy as np
     import torch
 
-    def i32(a):
-        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-
     b = wl.batches[bname]
     return dict(
-        page_table=i32(wl.page_table), seq_lens=i32(wl.seq_lens), cu=i32(b.cu_q_lens),
+        page_table=_i32(wl.page_table), seq_lens=_i32(wl.seq_lens), cu=_i32(b.cu_q_lens),
         idx_cache=wl.idx_cache.to_torch("cuda"),
         kv_cache=[wl.kv_cache[i].to_torch("cuda") for i in range(layers)],
-        q_idx=bf16(b.q_idx), w=torch.from_numpy(b.w).cuda(),
-        q=[bf16(b.q_mla[i]) for i in range(layers)],
+        q_idx=_bf16(b.q_idx), w=torch.from_numpy(b.w).cuda(),
+        q=[_bf16(b.q_mla[i]) for i in range(layers)],
         max_q_len=int(np.diff(b.cu_q_lens).max()),
     )
+
+
+def _rows_seq(wl, cu):
+    import numpy as np
+
+    T = int(cu[-1])
+    seq = np.full(T, -1, dtype=np.int64)
+    pos = np.full(T, -1, dtype=np.int64)
+    for s in range(wl.S):
+        q0, q1 = int(cu[s]), int(cu[s + 1])
+        seq[q0:q1] = s
+        pos[q0:q1] = int(wl.seq_lens[s]) - (q1 - q0) + np.arange(q1 - q0)
+    return seq, pos
+
+
+def _chunk_rows(cache, wl, cu):
+    """bf16 device tensor [T, D]: the workload cache's row at each packed
+    row's own position, i.e. the new tokens the layer's self-write puts into
+    the cache (writing them back leaves the workload unchanged)."""
+    import numpy as np
+
+    seq, pos = _rows_seq(wl, cu)
+    flat = wl.page_table[seq, pos // wl.PS].astype(np.int64) * wl.PS + pos % wl.PS
+    idx = np.searchsorted(cache.slots, flat)
+    assert (cache.slots[idx] == flat).all()
+    return _bf16(cache.rows[idx])
 
 
 def _row_valid_counts(wl, cu):
     """n_valid per packed row (positions j < kv and j <= abs_q)."""
     import numpy as np
 
-    T = int(cu[-1])
-    n = np.zeros(T, dtype=np.int64)
-    for s in range(wl.S):
-        q0, q1 = int(cu[s]), int(cu[s + 1])
-        a = int(wl.seq_lens[s]) - (q1 - q0) + np.arange(q1 - q0)
-        n[q0:q1] = np.clip(np.minimum(a + 1, int(wl.seq_lens[s])), 0, None)
-    return n
+    seq, pos = _rows_seq(wl, cu)
+    kv = np.where(seq >= 0, wl.seq_lens[np.maximum(seq, 0)], 0)
+    return np.clip(np.minimum(pos + 1, kv), 0, None)
 
 
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
 def _timed(step, steps, warmup):
-    """Average ms per step over `steps` calls, events on the current stream."""
+    """ms per step over exactly `steps` calls after `warmup` untimed ones,
+    bracketed by device synchronisation; events on the current stream (the
+    stream every library call here is launched on)."""
     import torch
 
     for _ in range(warmup):
@@ -110,7 +159,9 @@ def _timed(step, steps, warmup):
 
 
 def _kernel_times(dsa, step, steps):
-    """Per-kernel average launch duration (ms) from the library's event timer."""
+    """{kernel: (launches per step, average ms per launch)} over `steps`
+    steps, from the library's per-launch HIP events (recorded on the launch
+    stream of each kernel)."""
     import torch
 
     torch.cuda.synchronize()
@@ -120,31 +171,46 @@ def _kernel_times(dsa, step, steps):
     torch.cuda.synchronize()
     prof = dsa.profile_read()
     dsa.profile_enable(False)
-    return {k: (n, tot / n) for k, (n, tot) in prof.items()}
+    return {k: (n // steps, tot / n) for k, (n, tot) in prof.items()}
 
 
-def _kernel_times_cold(dsa, step, steps):
-    """The same per-kernel durations with the caches cold: a 1 GiB buffer
-    (four times the 256 MB infinity cache) is read before every step, outside
-    the library's timed launches. Reading, not writing, leaves the caches
-    holding clean lines, so the next kernel pays no write-back of the flush."""
+def _kernel_stats(dsa, step, reps, cold):
+    """Per-kernel launch duration statistics over `reps` steps, one step per
+    record: {kernel: [average ms per launch in each rep]}. With `cold`, a
+    1 GiB buffer (four times the 256 MB infinity cache) is read before every
+    step, outside the library's timed launches: a read leaves clean lines,
+    so the next kernel pays no write-back of the flush."""
     import torch
 
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if cold else None
     sink = torch.empty((), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
-    dsa.profile_enable(True)
-    for _ in range(steps):
-        torch.sum(flush, dim=0, out=sink)  # a torch kernel: not one of the library's timed launches
+    per = {}
+    step()
+    for _ in range(reps):
+        if cold:
+            torch.sum(flush, dim=0, out=sink)
+        torch.cuda.synchronize()
+        dsa.profile_enable(True)
         step()
-    torch.cuda.synchronize()
-    prof = dsa.profile_read()
-    dsa.profile_enable(False)
+        torch.cuda.synchronize()
+        prof = dsa.profile_read()
+        dsa.profile_enable(False)
+        for k, (n, tot) in prof.items():
+            per.setdefault(k, []).append(tot / n)
     del flush
-    return {k: (n, tot / n) for k, (n, tot) in prof.items()}
+    return per
 
 
-def _roofline_entry(bound, work, ms, per_step_launches=1):
+def _pct(xs):
+    import numpy as np
+
+    a = np.asarray(xs, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(a)), 2),
+            "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "reps": int(a.size)}
+
+
+def _roofline_entry(bound, work, ms):
     """work = algorithmic bytes (hbm) or flops (mfma) of ONE launch."""
     if bound == "hbm":
         achieved = work / (ms * 1e-3) / 1e9
@@ -155,13 +221,35 @@ def _roofline_entry(bound, work, ms, per_step_launches=1):
             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def _kernel_table(kt, warm, cold, work):
+    """One entry per kernel: the timed pass's average launch, warm and cold
+    statistics, and for kernels with algorithmic work its roofline fraction
+    (cold median first: the primary HBM measure; then warm and average)."""
+    out = {}
+    for name, (n, avg) in kt.items():
+        e = {"launches_per_step": n, "avg_us": round(avg * 1e3, 2)}
+        if name in warm:
+            e["warm"] = _pct(warm[name])
+        if name in cold:
+            e["cold"] = _pct(cold[name])
+        if name in work:
+            bound, w = work[name]
+            e["bound"], e["work_per_launch"] = bound, int(w)
+            if name in cold:
+                e["frac_cold_median"] = _roofline_entry(bound, w, e["cold"]["median_us"] / 1e3)["frac"]
+            if name in warm:
+                e["frac_warm_median"] = _roofline_entry(bound, w, e["warm"]["median_us"] / 1e3)["frac"]
+            e["frac_avg"] = _roofline_entry(bound, w, avg)["frac"]
+        out[name] = e
+    return out
+
+
 # Sources whose text decides each kernel's machine code.
 KERNEL_SOURCES = {
     "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
-    "idx_score_tiles": "indexer.hip",
-    "topk_select": "indexer.hip", "mla_decode_partial": "mla.hip",
-    "mla_decode_combine": "mla.hip", "mla_decode_combine_wide": "mla.hip",
-    "mla_extend_qblock": "mla.hip",
+    "idx_score_tiles": "indexer.hip", "topk_select": "indexer.hip",
+    "mla_decode_partial": "mla.hip", "mla_decode_combine": "mla.hip",
+    "mla_decode_combine_wide": "mla.hip", "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
     "union_member": "union.hip", "page_pool": "indexer.hip", "page_token_list": "indexer.hip",
     "paged_write_rows": "cache_write.hip",
@@ -174,7 +262,7 @@ def kernel_source_hash(kernel):
 
     csrc = os.path.join(ROOT, "sparse_attention_relu_amd", "csrc")
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCES[kernel], "common.h"):
+    for name in (KERNEL_SOURCES.get(kernel, "indexer.hip"), "common.h"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -201,10 +289,31 @@ def measured_traffic(kernel, workload):
         return None
 
 
+def _dominant(kt):
+    return max(kt, key=lambda nm: kt[nm][0] * kt[nm][1])
+
+
+def _headline_roofline(kt, kernels, work, workload):
+    dom = _dominant({k: v for k, v in kt.items() if k in work})
+    bound, w = work[dom]
+    n, avg = kt[dom]
+    roof = _roofline_entry(bound, w, avg)
+    roof.update({"traffic": measured_traffic(dom, workload), "kernel": dom,
+                 "work_per_launch": int(w), "avg_launch_us": round(avg * 1e3, 2),
+                 "launches_per_step": n, "measured_over": "the timed steps (library events)"})
+    e = kernels.get(dom, {})
+    if "cold" in e:
+        roof["cold"] = dict(e["cold"], frac=e.get("frac_cold_median"))
+    if "warm" in e:
+        roof["warm"] = dict(e["warm"], frac=e.get("frac_warm_median"))
+    return roof
+
+
 # ----------------------------------------------------------------------------
 # decode
 # ----------------------------------------------------------------------------
-def bench_decode(dsa, wl, args):
+def bench_decode(dsa, wl, steps, warmup, reps):
+    """One DSA decode layer: indexer top-k, then sparse MLA decode."""
     import numpy as np
     import torch
 
@@ -225,14 +334,13 @@ def bench_decode(dsa, wl, args):
         dsa.sparse_mla_decode(d["q"][0], d["kv_cache"][0], d["page_table"], d["seq_lens"],
                               d["cu"], topk, wl.sm_scale, out=out, workspace=ws_d)
 
-    ms = _timed(step, args.steps, args.warmup)
-    kt = _kernel_times(dsa, step, args.steps)
-    kt_cold = _kernel_times_cold(dsa, step, max(5, args.steps // 5))
+    ms = _timed(step, steps, warmup)
+    kt = _kernel_times(dsa, step, steps)
+    warm = _kernel_stats(dsa, step, reps, cold=False)
+    cold = _kernel_stats(dsa, step, reps, cold=True)
 
-    # algorithmic work per launch
     nval = _row_valid_counts(wl, b.cu_q_lens)
-    sel = topk.cpu().numpy()
-    n_sel = int((sel >= 0).sum())
+    n_sel = int((topk >= 0).sum())
     D, Hi, PS = wl.D_idx, wl.H_idx, wl.PS
     score_bytes = (int(nval.sum()) * (D * 2 + 4) + T * Hi * (D * 2 + 4)
                    + int(np.ceil(nval / PS).sum()) * 4)
@@ -241,43 +349,30 @@ def bench_decode(dsa, wl, args):
         "idx_score_flat": ("hbm", score_bytes),
         "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
         "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
-        "mla_decode_combine": ("hbm", T * H * DV * 2),
     }
-    kernels = {}
-    for name, (n, avg) in kt.items():
-        bound, w = work.get(name, ("hbm", 0))
-        e = {"avg_us": round(avg * 1e3, 2), "launches_per_step": n // args.steps}
-        if w:
-            e.update(_roofline_entry(bound, w, avg))
-            e["work"] = w
-        if name in kt_cold:
-            c = {"avg_us": round(kt_cold[name][1] * 1e3, 2)}
-            if w:
-                c["frac"] = _roofline_entry(bound, w, kt_cold[name][1])["frac"]
-            e["cold"] = c
-        kernels[name] = e
-    dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
-    bound, w = work[dom]
-    roof = _roofline_entry(bound, w, kt[dom][1])
-    roof.update({"kernel": dom, "traffic": measured_traffic(dom, wl.name),
-                 "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
+    kernels = _kernel_table(kt, warm, cold, work)
 
     def part(names):
-        return sum(kt[nm][1] * kt[nm][0] for nm in names if nm in kt) / args.steps
+        return sum(kt[nm][0] * kt[nm][1] for nm in names if nm in kt)
 
-    return dict(ms=ms, tok_s=T / (ms * 1e-3), kernels=kernels, roofline=roof,
-                selected=n_sel, keys=int(nval.sum()),
-                indexer_ms=round(part(("idx_score_stream", "idx_score_flat", "topk_select")), 4),
-                attend_ms=round(part(("mla_decode_partial", "mla_decode_combine")), 4))
+    cold_step = [sum(v[i] * kt[k_][0] for k_, v in cold.items() if k_ in kt)
+                 for i in range(reps)]
+    return {"workload": wl.name, "seqs": wl.S, "tokens": int(wl.seq_lens.sum()),
+            "tok_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "indexer_ms": round(part(("idx_score_stream", "idx_score_flat", "topk_select")), 5),
+            "attend_ms": round(part(("mla_decode_partial", "mla_decode_combine",
+                                     "mla_decode_combine_wide")), 5),
+            "cold_kernel_sum_ms_median": round(float(np.median(cold_step)), 5),
+            "roofline": _headline_roofline(kt, kernels, work, wl.name),
+            "kernels": kernels, "page_decode": bench_page_decode(dsa, wl, d, steps, warmup)}
 
 
-def bench_page_decode(dsa, wl, args):
+def bench_page_decode(dsa, wl, d, steps, warmup):
     """The same decode layer with page-level selection: the page top-k
     (k_pages = k / PS pages, max-pooled page scores), then sparse MLA over
     every valid position of those pages (page lists read directly)."""
     import torch
 
-    d = _dev_inputs(wl, "decode")
     b = wl.batches["decode"]
     T, H, PS = b.T, wl.H_mla, wl.PS
     kp = max(1, wl.k // PS)
@@ -296,8 +391,7 @@ def bench_page_decode(dsa, wl, args):
                                     d["seq_lens"], d["cu"], pages, wl.sm_scale, out=out,
                                     workspace=ws_d)
 
-    steps = max(5, args.steps // 2)
-    ms = _timed(step, steps, min(args.warmup, 3))
+    ms = _timed(step, steps, warmup)
     kt = _kernel_times(dsa, step, steps)
     return {"k_pages": kp, "ms_per_step": round(ms, 5), "tok_s": round(T / (ms * 1e-3), 1),
             "kernels_us": {nm: round(avg * 1e3, 2) for nm, (n, avg) in kt.items()}}
@@ -306,227 +400,315 @@ def bench_page_decode(dsa, wl, args):
 # ----------------------------------------------------------------------------
 # extend
 # ----------------------------------------------------------------------------
-def bench_extend(dsa, wl, args, QB, steps=None):
+class ExtendLayers:
+    """Device state of an extend workload: caches, queries, the chunk's new
+    rows, the indexer's and the locality selection, union tables per QB."""
+
+    def __init__(self, dsa, wl):
+        import numpy as np
+        import torch
+
+        import workloads as W
+
+        self.dsa, self.wl = dsa, wl
+        self.layers = len(wl.kv_cache)
+        b = wl.batches["extend"]
+        self.b = b
+        self.d = _dev_inputs(wl, "extend", layers=self.layers)
+        self.T, self.k, self.H = b.T, wl.k, wl.H_mla
+        cu = b.cu_q_lens
+        self.new_idx = _chunk_rows(wl.idx_cache, wl, cu)
+        self.new_kv = [_chunk_rows(wl.kv_cache[i], wl, cu) for i in range(self.layers)]
+        self.loc = _i32(W.locality_selection(wl.seq_lens, cu, wl.k, 100 + int(wl.seed) - 1000))
+        self.topk = torch.empty((self.T, self.k), dtype=torch.int32, device="cuda")
+        self.ws_i = torch.empty(dsa.indexer_topk_workspace(self.T, wl.S, wl.H_idx, wl.D_idx,
+                                                           wl.PS, wl.MP, self.k,
+                                                           self.d["max_q_len"]),
+                                dtype=torch.uint8, device="cuda")
+        self.ws_d = torch.empty(max(1, dsa.sparse_mla_decode_workspace(self.T, self.H, self.k)),
+                                dtype=torch.uint8, device="cuda")
+        self.outs = [torch.empty((self.T, self.H, DV), dtype=torch.bfloat16, device="cuda")
+                     for _ in range(self.layers)]
+        self.tables = {}
+        self.u_max = wl.u_max
+        for QB in (64, 256):
+            nqb = (self.T + QB - 1) // QB
+            self.tables[QB] = dict(
+                units=torch.empty((nqb, self.u_max), dtype=torch.int32, device="cuda"),
+                counts=torch.empty((nqb,), dtype=torch.int32, device="cuda"),
+                member=torch.empty((nqb, self.u_max, QB), dtype=torch.uint64, device="cuda"),
+                ws=torch.empty(max(1, dsa.block_union_workspace(self.T, wl.S, wl.MP, QB,
+                                                                self.u_max)),
+                               dtype=torch.uint8, device="cuda"))
+        self.nval = _row_valid_counts(wl, cu)
+        self.seq, _ = _rows_seq(wl, cu)
+        self.np = np
+
+    # one library call each ------------------------------------------------
+    def write(self, i, full):
+        d = self.d
+        self.dsa.paged_write_layer(self.new_idx if full else None,
+                                   d["idx_cache"] if full else None, self.new_kv[i],
+                                   d["kv_cache"][i], d["page_table"], d["seq_lens"], d["cu"])
+
+    def indexer(self):
+        d = self.d
+        self.dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
+                              d["seq_lens"], d["cu"], self.k, d["max_q_len"], out=self.topk,
+                              workspace=self.ws_i)
+
+    def union(self, sel, QB):
+        t = self.tables[QB]
+        d = self.d
+        self.dsa.block_union(sel, d["seq_lens"], d["cu"], self.wl.PS, self.wl.MP, QB,
+                             self.u_max, out=(t["units"], t["counts"], t["member"]),
+                             workspace=t["ws"])
+
+    def attend(self, i, sel, path):
+        d = self.d
+        if path == 0:
+            self.dsa.sparse_mla_decode(d["q"][i], d["kv_cache"][i], d["page_table"],
+                                       d["seq_lens"], d["cu"], sel, self.wl.sm_scale,
+                                       out=self.outs[i], workspace=self.ws_d)
+        else:
+            t = self.tables[path]
+            self.dsa.sparse_mla_extend(d["q"][i], d["kv_cache"][i], d["page_table"],
+                                       d["seq_lens"], d["cu"], t["units"], t["counts"],
+                                       t["member"], path, self.wl.sm_scale, out=self.outs[i])
+
+    # ----------------------------------------------------------------------
+    def plan(self, sel):
+        """The library's choice (0 = per query, else QB) for a selection,
+        from its unions at QB 64 and 256 (read on the host, before timing)."""
+        import torch
+
+        for QB in (64, 256):
+            self.union(sel, QB)
+        torch.cuda.synchronize()
+        counts = {QB: self.tables[QB]["counts"].cpu().numpy() for QB in (256, 64)}
+        choice = self.dsa.extend_attend_plan(counts, self.T, self.H, self.k, self.wl.PS,
+                                             self.u_max)
+        return choice, counts
+
+    def step_fn(self, sel_kind, path, layers=None, full_first=True):
+        """One pass over `layers` layers (all by default): write, then on the
+        full layer indexer top-k and the union the attention needs, then the
+        attention; `sel_kind` "locality" or "indexer" feeds union and
+        attention."""
+        n = self.layers if layers is None else layers
+        sel = self.loc if sel_kind == "locality" else self.topk
+        union_qb = path if path else 256
+
+        def step():
+            for i in range(n):
+                full = full_first and i == 0
+                self.write(i, full)
+                if full:
+                    self.indexer()
+                    self.union(sel, union_qb)
+                self.attend(i, sel, path)
+        return step
+
+    def work(self, sel_np, QB_counts):
+        """Algorithmic bytes or flops per launch of each kernel."""
+        np = self.np
+        wl = self.wl
+        T, k, H = self.T, self.k, self.H
+        n_sel = int((sel_np >= 0).sum())
+        w = {"idx_score_tiles": ("mfma", 2 * wl.H_idx * wl.D_idx * int(self.nval.sum())),
+             "topk_select": ("hbm", int(self.nval.sum()) * 4 + T * k * 4),
+             "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
+             "paged_write_rows": ("hbm", T * (wl.D_idx + DK) * 2 * 2)}
+        for QB, cnt in QB_counts.items():
+            w[f"mla_extend_qblock@{QB}"] = ("mfma", int(np.minimum(cnt, self.u_max).sum())
+                                            * QB * H * wl.PS * (DK + DV) * 2)
+        return w, n_sel
+
+    def redundancy(self, sel_np, counts):
+        np = self.np
+        keys = np.where(sel_np >= 0, self.seq[:, None] * self.wl.MP + sel_np // self.wl.PS, -1)
+        per_query = sum(len(np.unique(r[r >= 0])) for r in keys)
+        distinct = len(np.unique(keys[keys >= 0]))
+        out = {"pages_distinct": distinct,
+               "per_query": round(per_query / max(distinct, 1), 1)}
+        for QB, c in counts.items():
+            out[f"qblock_{QB}"] = round(float(c.sum()) / max(distinct, 1), 2)
+        return out
+
+
+def _attend_only(E, i, sel, path, steps):
+    """ms per launch sequence of one layer's attention alone, and its
+    per-kernel durations."""
+    f = lambda: E.attend(i, sel, path)  # noqa: E731
+    ms = _timed(f, steps, 1)
+    return ms, _kernel_times(E.dsa, f, steps)
+
+
+def bench_extend_workload(dsa, wl, steps, warmup, reps):
+    """Extend layers of a workload: the planned path, every path timed on
+    one layer, the end-to-end step (all layers), full and shared layers."""
     import numpy as np
-    import torch
 
-    layers = len(wl.kv_cache)
-    d = _dev_inputs(wl, "extend", layers=layers)
-    b = wl.batches["extend"]
-    T, k, H = b.T, wl.k, wl.H_mla
-    u_max = wl.u_max
-    nqb = (T + QB - 1) // QB
-    topk = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    units = torch.empty((nqb, u_max), dtype=torch.int32, device="cuda")
-    counts = torch.empty((nqb,), dtype=torch.int32, device="cuda")
-    member = torch.empty((nqb, u_max, QB), dtype=torch.uint64, device="cuda")
-    outs = [torch.empty((T, H, DV), dtype=torch.bfloat16, device="cuda") for _ in range(layers)]
-    ws_i = torch.empty(dsa.indexer_topk_workspace(T, wl.S, wl.H_idx, wl.D_idx, wl.PS, wl.MP, k,
-                                                  d["max_q_len"]), dtype=torch.uint8,
-                       device="cuda")
-    ws_u = torch.empty(max(1, dsa.block_union_workspace(T, wl.S, wl.MP, QB, u_max)),
-                       dtype=torch.uint8, device="cuda")
+    E = ExtendLayers(dsa, wl)
+    res = {"workload": wl.name, "layers": E.layers, "T": E.T, "k": E.k,
+           "step": "per layer: self-write; full layer: indexer top-k + union; attention"}
+    # the indexer once (its selection is the secondary feed)
+    E.indexer()
+    sel_np = {"locality": E.loc.cpu().numpy(), "indexer": E.topk.cpu().numpy()}
+    choice, counts = {}, {}
+    for kind in ("locality", "indexer"):
+        choice[kind], counts[kind] = E.plan(E.loc if kind == "locality" else E.topk)
+    res["attend_path_chosen"] = {kd: ("per_query" if c == 0 else f"qblock{c}")
+                                 for kd, c in choice.items()}
+    res["union_per_block"] = {f"{kd}_qb{QB}": {"min": int(c.min()),
+                                              "mean": round(float(c.mean()), 1),
+                                              "max": int(c.max())}
+                              for kd in counts for QB, c in counts[kd].items()}
+    res["redundant_fetch"] = {kd: E.redundancy(sel_np[kd], counts[kd]) for kd in counts}
 
-    # IndexShare: the first layer is full (indexer + union), the others are
-    # shared and attend with its tables (one slot)
-    full_slot, src_slot, n_full = dsa.index_share_map(["full"] + ["shared"] * (layers - 1))
-    assert n_full == 1
+    # end-to-end steps (all layers), locality selection first (the timed feed)
+    steps_out = {}
+    kt_main = None
+    for kind in ("locality", "indexer"):
+        path = choice[kind]
+        E.union(E.loc if kind == "locality" else E.topk, path if path else 256)
+        f = E.step_fn(kind, path)
+        ms = _timed(f, steps, warmup)
+        kt = _kernel_times(dsa, f, steps)
+        steps_out[kind] = {"ms_per_step": round(ms, 4), "ms_per_layer": round(ms / E.layers, 4),
+                           "path": res["attend_path_chosen"][kind]}
+        if kind == "locality":
+            kt_main = kt
+            if E.layers > 1:
+                ms_full = _timed(E.step_fn(kind, path, layers=1), steps, 1)
+                ms_shared = _timed(E.step_fn(kind, path, layers=1, full_first=False), steps, 1)
+                steps_out[kind].update({"ms_full_layer": round(ms_full, 4),
+                                        "ms_shared_layer": round(ms_shared, 4)})
+    res["steps"] = steps_out
+    path = choice["locality"]
+    f_main = E.step_fn("locality", path)
+    E.union(E.loc, path if path else 256)
+    warm = _kernel_stats(dsa, f_main, reps, cold=False)
+    cold = _kernel_stats(dsa, f_main, reps, cold=True)
 
-    def step():
-        for i in range(layers):
-            if i in full_slot:
-                dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
-                                 d["seq_lens"], d["cu"], k, d["max_q_len"], out=topk,
-                                 workspace=ws_i)
-                dsa.block_union(topk, d["seq_lens"], d["cu"], wl.PS, wl.MP, QB, u_max,
-                                out=(units, counts, member), workspace=ws_u)
-            dsa.sparse_mla_extend(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
-                                  d["cu"], units, counts, member, QB, wl.sm_scale, out=outs[i])
+    # every attention path on one layer, locality selection
+    w, n_sel = E.work(sel_np["locality"], counts["locality"])
+    paths = {}
+    for p in (0, 64, 256):
+        E.union(E.loc, p if p else 256)
+        ms, kt = _attend_only(E, 0, E.loc, p, max(2, steps // 2))
+        name = "per_query" if p == 0 else f"qblock{p}"
+        e = {"ms": round(ms, 4), "kernels_us": {nm: round(a * 1e3, 2) for nm, (n, a) in kt.items()}}
+        if p == 0:
+            e["roofline"] = _roofline_entry("hbm", w["mla_decode_partial"][1],
+                                            kt["mla_decode_partial"][1])
+            e["gathered_bytes"] = int(w["mla_decode_partial"][1])
+        else:
+            ex = w[f"mla_extend_qblock@{p}"][1]
+            useful = n_sel * E.H * (DK + DV) * 2
+            e["roofline_executed"] = _roofline_entry("mfma", ex, kt["mla_extend_qblock"][1])
+            e["roofline_useful"] = _roofline_entry("mfma", useful, kt["mla_extend_qblock"][1])
+            e["executed_tflop"] = round(ex / 1e12, 3)
+            e["useful_tflop"] = round(useful / 1e12, 3)
+        paths[name] = e
+    res["attend_paths_one_layer"] = paths
 
-    steps = steps or max(2, args.steps // 4)
-    ms = _timed(step, steps, min(args.warmup, 2))
-    kt = _kernel_times(dsa, step, steps)
-    cnt = counts.cpu().numpy()
-    sel = topk.cpu().numpy()
-    nval = _row_valid_counts(wl, b.cu_q_lens)
-    exec_flops = int(np.minimum(cnt, u_max).sum()) * QB * H * wl.PS * (DK + DV) * 2
-    useful_flops = int((sel >= 0).sum()) * H * (DK + DV) * 2
-    idx_flops = 2 * wl.H_idx * wl.D_idx * int(nval.sum())
-    work = {
-        "idx_score_tiles": ("mfma", idx_flops),
-        "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
-        "mla_extend_qblock": ("mfma", exec_flops),
-        "union_member": ("hbm", T * k * 4 + nqb * u_max * QB * 8),
-        "union_mark": ("hbm", T * k * 4),
-    }
-    kernels = {}
-    for name, (n, avg) in kt.items():
-        e = {"avg_us": round(avg * 1e3, 2), "launches_per_step": n // steps}
-        if name in work:
-            bound, w = work[name]
-            e.update(_roofline_entry(bound, w, avg))
-            e["work"] = w
-        kernels[name] = e
-    # redundant-fetch ratios: per-query pages vs block unions vs distinct pages
-    seq, _ = _rows_seq(wl, b.cu_q_lens)
-    keys = np.where(sel >= 0, seq[:, None] * wl.MP + sel // wl.PS, -1)
-    per_query_pages = sum(len(np.unique(r[r >= 0])) for r in keys)
-    distinct = len(np.unique(keys[keys >= 0]))
-    res = dict(ms_per_step=round(ms, 4), layers=layers, QB=QB,
-               ms_full_layer=round(ms - (layers - 1) * kt["mla_extend_qblock"][1], 4)
-               if layers > 1 else round(ms, 4),
-               ms_shared_layer=round(kt["mla_extend_qblock"][1], 4),
-               indexer_ms=round(kt.get("idx_score_tiles", (0, 0))[1]
-                                + kt.get("topk_select", (0, 0))[1], 4),
-               union_per_block={"min": int(cnt.min()), "mean": round(float(cnt.mean()), 1),
-                                "max": int(cnt.max())},
-               redundant_fetch={"per_query": round(per_query_pages / max(distinct, 1), 1),
-                                "qblock": round(float(cnt.sum()) / max(distinct, 1), 2)},
-               mfma_executed_tflop=round(exec_flops / 1e12, 3),
-               mfma_useful_tflop=round(useful_flops / 1e12, 3),
-               kernels=kernels)
-    dom = max(kt, key=lambda nm: kt[nm][1] * kt[nm][0])
-    if dom in work:
-        bound, w = work[dom]
-        roof = _roofline_entry(bound, w, kt[dom][1])
-        roof.update({"kernel": dom, "traffic": measured_traffic(dom, wl.name),
-                     "work_per_launch": w, "avg_launch_us": round(kt[dom][1] * 1e3, 2)})
-        res["roofline"] = roof
-    res["per_query"] = _per_query_attend(dsa, wl, d, topk, outs, steps, kt)
-    # the library's own choice between the two paths for these unions, and
-    # the step with the chosen path for every layer (indexer and union once)
-    res["attend_path_chosen"] = dsa.extend_attend_path(cnt, T, H, k, wl.PS, QB, u_max)
-    per_layer = (res["per_query"]["ms_per_layer"] if res["attend_path_chosen"] == "per_query"
-                 else kt["mla_extend_qblock"][1])
-    res["ms_per_step_chosen_path"] = round(ms - layers * kt["mla_extend_qblock"][1]
-                                           + layers * per_layer, 4)
-    res["cache_write"] = _cache_write(dsa, wl, d, steps)
+    work = {k_: v for k_, v in w.items() if "@" not in k_}
+    if path:
+        work["mla_extend_qblock"] = w[f"mla_extend_qblock@{path}"]
+    res["kernels"] = _kernel_table(kt_main, warm, cold, work)
+    res["roofline"] = _headline_roofline(kt_main, res["kernels"], work, wl.name)
+    res["indexer_ms"] = round(sum(kt_main[nm][1] for nm in ("idx_score_tiles", "topk_select")
+                                  if nm in kt_main), 4)
     return res
 
 
-def _cache_write(dsa, wl, d, steps):
-    """The self-write of the chunk's new tokens ahead of the layer: indexer
-    keys (one call) and latent rows (c_kv, k_rope). Timed last: it rewrites
-    the chunk's own cache slots."""
-    import torch
-
-    T = int(d["cu"][-1].item())
-    g = torch.Generator(device="cuda").manual_seed(11)
-    keys = torch.randint(-2, 3, (T, wl.D_idx), generator=g, device="cuda").to(torch.bfloat16)
-    lat = torch.randn((T, DK), generator=g, device="cuda").to(torch.bfloat16)
-
-    def step():
-        dsa.paged_write(keys, d["idx_cache"], d["page_table"], d["seq_lens"], d["cu"])
-        dsa.paged_write(lat[:, :DV], d["kv_cache"][0], d["page_table"], d["seq_lens"], d["cu"])
-        dsa.paged_write(lat[:, DV:], d["kv_cache"][0], d["page_table"], d["seq_lens"], d["cu"],
-                        col0=DV)
-
-    step()
-    kt = _kernel_times(dsa, step, steps)
-    n, avg = kt["paged_write_rows"]
-    ms = avg * n / steps  # device time of the three writes (the host calls take longer)
-    moved = T * (wl.D_idx + DK) * 2 * 2  # read and written once
-    return {"tokens": T, "launches": n // steps, "us_per_layer": round(ms * 1e3, 2),
-            "roofline": _roofline_entry("hbm", moved, ms)}
-
-
-def _per_query_attend(dsa, wl, d, topk, outs, steps, kt_qblock):
-    """The same layers attended per query: each packed row gathers its own
-    selected latent rows (the decode kernels run on the extend batch), with no
-    block union. Reported beside the query-block kernel; its outputs are
-    compared with the query-block outputs of the same selections."""
-    import torch
-
-    layers = len(outs)
-    T, k, H = topk.shape[0], topk.shape[1], outs[0].shape[1]
-    ws_d = torch.empty(max(1, dsa.sparse_mla_decode_workspace(T, H, k)), dtype=torch.uint8,
-                       device="cuda")
-    outs_pq = [torch.empty_like(o) for o in outs]
-
-    def step():
-        for i in range(layers):
-            dsa.sparse_mla_decode(d["q"][i], d["kv_cache"][i], d["page_table"], d["seq_lens"],
-                                  d["cu"], topk, wl.sm_scale, out=outs_pq[i], workspace=ws_d)
-
-    ms = _timed(step, steps, 1)
-    kt = _kernel_times(dsa, step, steps)
-    torch.cuda.synchronize()
-    diff = max(float((a.float() - b.float()).abs().max()) for a, b in zip(outs, outs_pq))
-    n_sel = int((topk >= 0).sum())
-    gather = n_sel * DK * 2 + T * k * 4 + T * H * DK * 2
-    part = kt["mla_decode_partial"][1]
-    e = {"ms_per_layer": round(ms / layers, 4),
-         "partial_us": round(part * 1e3, 2),
-         "combine_us": round(kt["mla_decode_combine"][1] * 1e3, 2),
-         "partial_roofline": _roofline_entry("hbm", gather, part),
-         "gathered_bytes_per_layer": gather,
-         "speedup_vs_qblock": round(kt_qblock["mla_extend_qblock"][1] / (ms / layers), 2),
-         "max_abs_diff_vs_qblock": round(diff, 5)}
-    return e
-
-
-def _rows_seq(wl, cu):
-    import numpy as np
-
-    T = int(cu[-1])
-    seq = np.full(T, -1, dtype=np.int64)
-    pos = np.full(T, -1, dtype=np.int64)
-    for s in range(wl.S):
-        q0, q1 = int(cu[s]), int(cu[s + 1])
-        seq[q0:q1] = s
-        pos[q0:q1] = int(wl.seq_lens[s]) - (q1 - q0) + np.arange(q1 - q0)
-    return seq, pos
-
-
 # ----------------------------------------------------------------------------
-# CPU baseline: the oracle on the host cores
+# CPU baseline: the oracle on the host cores, per stage
 # ----------------------------------------------------------------------------
 def cpu_baseline(wl, seconds):
+    """The oracle's stages on a bounded sample of the long-context layer,
+    scaled to ms per layer (same unit as the headline): score and top-k per
+    row (the indexer's own rows), the union of one query block and the
+    attention per row (the locality selection, as the timed step), each
+    extrapolated to the workload's rows, blocks and four layers."""
     import numpy as np
     import oracle
+    import workloads as W
     from threadpoolctl import threadpool_info
     from workloads import bf16_to_f64
 
-    b = wl.batches["decode"]
-    q_idx = bf16_to_f64(b.q_idx)
-    w = b.w.astype(np.float64)
+    b = wl.batches["extend"]
+    cu = b.cu_q_lens
+    T = b.T
+    QB = 256
+    seq, pos = oracle.query_rows(wl.seq_lens, cu, T)
+    q_idx, w = bf16_to_f64(b.q_idx), b.w.astype(np.float64)
     icache = wl.idx_cache.f64_view()
-    kv = wl.kv_cache[0].f64_view()
-    q = bf16_to_f64(b.q_mla[0])
-    rows_done = 0
+    budget = seconds / 3.0
+    rng = np.random.default_rng(5)
+    # score, then top-k, row by row (the oracle's own stage functions)
+    t_score = t_topk = 0.0
+    n_rows = 0
+    t_end = time.perf_counter() + budget
+    while time.perf_counter() < t_end or n_rows == 0:
+        t = int(rng.integers(T))
+        s = int(seq[t])
+        n = oracle.n_valid_keys(wl.seq_lens[s], pos[t])
+        t0 = time.perf_counter()
+        keys = np.asarray(oracle.gather_rows(icache, wl.page_table, s, np.arange(n)))
+        sc = oracle.indexer_scores(q_idx[t], w[t], keys)
+        t1 = time.perf_counter()
+        oracle.canonical_order(sc)[: min(wl.k, n)]
+        t2 = time.perf_counter()
+        t_score += t1 - t0
+        t_topk += t2 - t1
+        n_rows += 1
+    loc = W.locality_selection(wl.seq_lens, cu, wl.k, 100 + int(wl.seed) - 1000)
     t0 = time.perf_counter()
-    t_end = t0 + seconds
-    r = 0
-    while True:
-        rows = [r % b.T]
-        tk = oracle.indexer_topk(q_idx, w, icache, wl.page_table, wl.seq_lens, b.cu_q_lens, wl.k,
-                                 rows=rows)
-        oracle.sparse_mla(q, kv, wl.page_table, wl.seq_lens, b.cu_q_lens, tk, wl.sm_scale, wl.Dv,
-                          rows=rows)
-        rows_done += 1
-        r += 1
-        if time.perf_counter() >= t_end and rows_done >= 1:
-            break
-    dt = time.perf_counter() - t0
+    oracle.block_union(loc, wl.seq_lens, cu, wl.PS, wl.MP, QB, wl.u_max, blocks=[0])
+    t_union = time.perf_counter() - t0
+    q = bf16_to_f64(b.q_mla[0])
+    kv = wl.kv_cache[0].f64_view()
+    t_att, n_att = 0.0, 0
+    t_end = time.perf_counter() + budget
+    while time.perf_counter() < t_end or n_att == 0:
+        t = int(rng.integers(T))
+        t0 = time.perf_counter()
+        oracle.sparse_mla(q, kv, wl.page_table, wl.seq_lens, cu, loc, wl.sm_scale, wl.Dv,
+                          rows=[t])
+        t_att += time.perf_counter() - t0
+        n_att += 1
+    layers = len(wl.kv_cache)
+    nqb = (T + QB - 1) // QB
+    stage_ms = {"score": t_score / n_rows * T * 1e3, "topk": t_topk / n_rows * T * 1e3,
+                "union": t_union * nqb * 1e3, "attend_per_layer": t_att / n_att * T * 1e3}
+    per_layer = (stage_ms["score"] + stage_ms["topk"] + stage_ms["union"]
+                 + layers * stage_ms["attend_per_layer"]) / layers
     threads = 0
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 0)))
-    return {"value": round(rows_done / dt, 3), "unit": "tok/s", "cores": max(threads, 1),
+    return {"value": round(per_layer, 1), "unit": "ms/layer", "cores": max(threads, 1),
             "kind": "oracle",
-            "sample": f"{rows_done} decode rows (indexer top-k + sparse MLA, fp64 NumPy) of the "
-                      f"{wl.name} workload in {dt:.1f} s"}
+            "stages_ms_full_workload": {k_: round(v, 1) for k_, v in stage_ms.items()},
+            "sample": f"{wl.name}: score and top-k of {n_rows} random rows, the union of one "
+                      f"{QB}-row block, the attention of {n_att} random rows (locality "
+                      f"selection), fp64 NumPy, each stage scaled to the workload's {T} rows, "
+                      f"{nqb} blocks and {layers} layers"}
 
 
 # ----------------------------------------------------------------------------
-def copy_calibration(mib=256, reps=5):
-    """A plain device copy of known size: under a counter profiler its
-    FETCH_SIZE / WRITE_SIZE per dispatch give the counters' byte scale."""
+def copy_bandwidth(mib=1024, reps=10, verbose=False):
+    """A plain device copy of known size (the runtime's copy kernel): its
+    bandwidth, and under a counter profiler the byte scale of FETCH_SIZE /
+    WRITE_SIZE per dispatch."""
     import torch
 
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -536,17 +718,23 @@ def copy_calibration(mib=256, reps=5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    print(json.dumps({"only": "copy", "bytes_read": n * 4, "bytes_written": n * 4,
-                      "ms": round(ms, 4), "GB_s": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}),
-          flush=True)
-    return 0
+    r = {"bytes_read": n * 4, "bytes_written": n * 4, "ms": round(ms, 4),
+         "GB_s": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}
+    r["frac_of_peak"] = round(r["GB_s"] / HBM_PEAK_GBS, 4)
+    del src, dst
+    return r
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main(argv=None):
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path runs on a single MI355X here)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this "
+              "build runs the hot path on a single MI355X (the sharding design is described "
+              "but not run)", file=sys.stderr)
         return 2
     import torch
 
@@ -555,71 +743,66 @@ def main(argv=None):
 
     dsa.load()
     torch.cuda.set_device(0)
+    reps = args.cold_reps
     if args.only == "copy":
-        return copy_calibration()
-    if args.only in ("ragged", "extend", "long"):  # one side workload alone, its own line
-        if args.only == "long":
-            wll = W.config(args.long_config or 5)
-            line = bench_extend(dsa, wll, args, 256, steps=max(2, args.steps // 10))
-            line["workload"] = wll.name
-        elif args.only == "ragged":
-            wlr = W.config(args.ragged_config or 3)
-            rd = bench_decode(dsa, wlr, args)
-            line = {"workload": wlr.name, "tok_s": round(rd["tok_s"], 1),
-                    "ms_per_step": round(rd["ms"], 5), "roofline": rd["roofline"],
-                    "kernels": rd["kernels"], "page_decode": bench_page_decode(dsa, wlr, args)}
-        else:
-            wle = W.config(args.extend_config or 4)
-            qb = args.qb if args.qb in wle.QB else wle.QB[0]
-            line = bench_extend(dsa, wle, args, qb)
-            line["workload"] = wle.name
-        print(json.dumps({"only": args.only, **line}), flush=True)
+        print(json.dumps({"only": "copy", **copy_bandwidth(256, 5)}), flush=True)
         return 0
-    wl = W.config(args.config)
-    dec = bench_decode(dsa, wl, args)
+    if args.only in ("decode", "ragged"):
+        wl = W.config(2 if args.only == "decode" else 3)
+        r = bench_decode(dsa, wl, max(args.steps, 20), args.warmup, reps or 20)
+        print(json.dumps({"only": args.only, **r}), flush=True)
+        return 0
+    if args.only == "extend":
+        wl = W.config(4)
+        r = bench_extend_workload(dsa, wl, max(2, args.steps // 2), min(args.warmup, 2),
+                                  reps or 5)
+        print(json.dumps({"only": "extend", **r}), flush=True)
+        return 0
+
+    _log("long-context workload: generating")
+    wl5 = W.config(5)
+    _log("long-context workload: timing")
+    lng = bench_extend_workload(dsa, wl5, args.steps, args.warmup, reps or 3)
+    main_step = lng["steps"]["locality"]
     result = {
         "metric": METRIC,
-        "value": round(dec["tok_s"], 1),
-        "unit": "tok/s",
+        "value": main_step["ms_per_layer"],
+        "unit": "ms/layer",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["ms"], 5),
-        "higher_is_better": True,
+        "ms_per_step": main_step["ms_per_step"],
+        "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "seqs": wl.S, "kv_len": int(wl.seq_lens.max()),
-                   "page_size": wl.PS, "index_topk": wl.k, "indexer_heads": wl.H_idx,
-                   "indexer_dim": wl.D_idx, "mla_heads": wl.H_mla, "dk": DK, "dv": DV,
-                   "step": "one DSA decode layer: indexer top-k + sparse MLA"},
-        "roofline": dec["roofline"],
-        "kernels": dec["kernels"],
-        "page_decode": bench_page_decode(dsa, wl, args),
+        "config": {"workload": wl5.name, "seqs": wl5.S, "kv_len": int(wl5.seq_lens.max()),
+                   "chunk_tokens": lng["T"], "page_size": wl5.PS, "index_topk": wl5.k,
+                   "indexer_heads": wl5.H_idx, "indexer_dim": wl5.D_idx,
+                   "mla_heads": wl5.H_mla, "dk": DK, "dv": DV, "layers": lng["layers"],
+                   "indexshare": "1 full + 3 shared", "attend_feed": "locality selection",
+                   "attend_path": main_step["path"],
+                   "step": "4 layers: self-write; full layer indexer top-k + union; "
+                           "sparse MLA attention on the planned path"},
+        "roofline": lng["roofline"],
+        "long_extend": lng,
     }
-    if args.only == "all" and args.ragged_config and args.ragged_config != args.config:
-        wlr = W.config(args.ragged_config)
-        rd = bench_decode(dsa, wlr, args)
-        result["ragged_decode"] = {
-            "workload": wlr.name, "seqs": wlr.S, "tokens": int(wlr.seq_lens.sum()),
-            "tok_s": round(rd["tok_s"], 1), "ms_per_step": round(rd["ms"], 5),
-            "indexer_ms": rd["indexer_ms"], "attend_ms": rd["attend_ms"],
-            "roofline": rd["roofline"], "kernels": rd["kernels"],
-            "page_decode": bench_page_decode(dsa, wlr, args)}
-    if args.only == "all" and args.extend_config:
-        wle = W.config(args.extend_config)
-        qb = args.qb if args.qb in wle.QB else wle.QB[0]
-        ext = bench_extend(dsa, wle, args, qb)
-        ext["workload"] = wle.name
-        result["extend"] = ext
-    if args.only == "all" and args.long_config:
-        wll = W.config(args.long_config)
-        lng = bench_extend(dsa, wll, args, 256, steps=max(2, args.steps // 10))
-        lng["workload"] = wll.name
-        result["long_extend"] = lng
+    if args.only == "all":
+        del wl5
+        _log("decode batch")
+        result["decode_batch"] = bench_decode(dsa, W.config(2), max(20, 2 * args.steps),
+                                              args.warmup, reps or 20)
+        _log("ragged decode")
+        result["ragged_decode"] = bench_decode(dsa, W.config(3), max(20, 2 * args.steps),
+                                               args.warmup, reps or 20)
+        _log("chunked extend")
+        result["chunked_extend"] = bench_extend_workload(dsa, W.config(4), max(4, args.steps),
+                                                         args.warmup, reps or 5)
+        result["copy_kernel"] = copy_bandwidth()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        _log("cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(W.config(5, layers=4), args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 
