@@ -106,33 +106,49 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode: grid = (nch * HB, T), block = 256. Workgroup (c, hb, t) attends row
-// t over selections [c * CH, (c + 1) * CH) for heads 16 hb .. 16 hb + 15 and
-// leaves its partial (max m, sum l, unnormalised O) per head for the combine
-// kernel. The source slot of every selection is resolved first; stages of 32
-// selected rows then stream through a four-stage LDS ring (three stages in
-// flight while one is used, each refilled as soon as it is consumed), staged
-// like an extend page.
+// Decode: grid = (nch * HB, T), block = 256, two workgroups per compute unit.
+// Workgroup (c, hb, t) attends row t over selections [c * CH, (c + 1) * CH)
+// for heads 16 hb .. 16 hb + 15 and leaves its partial (max m, sum l,
+// unnormalised O) per head for the combine kernel. The source slot of every
+// selection is resolved first; stages of 32 selected rows then stream through
+// a two-stage LDS ring (the next stage in flight while one is used), staged
+// like an extend page. Two resident workgroups per compute unit keep two
+// stages in flight per compute unit and overlap one workgroup's arithmetic
+// and barriers with the other's loads (one workgroup with a four-stage ring
+// ran the long-context per-query attend at 3.0 ms, two with two stages at
+// 2.0 ms: rows that neighbouring queries share then come from L2).
 // S^T = K . Q^T of a stage is two 16-key tiles for the 16 heads
-// (v_mfma_f32_16x16x32_bf16: M = keys, N = heads); the contraction over the
-// 576 latent columns is split between the waves (k steps 5, 5, 4, 4 of 32
-// columns), so each staged key is read from LDS once, and the four partial
-// tiles meet through LDS, summed in the same order by every wave. A lane then
-// holds keys 4 g .. 4 g + 3 of both tiles for head `col`, which is exactly
-// its P^T operand for one 32-key step, and its O^T accumulators belong to the
-// same head, so every wave runs the same online softmax on its own: wave w
-// computes O^T += V^T . P^T for value columns 128 w .. 128 w + 127, reading
-// V^T with transposed LDS reads in the same key order. Logits are kept
-// in log2 units. Invalid selections load a valid row of the same stage and
-// are masked to probability 0; stages without any valid selection load cache
-// row 0 and skip the arithmetic.
+// (v_mfma_f32_16x16x32_bf16: M = keys, N = heads); waves 2 i and 2 i + 1
+// compute tile i over one half each of the contraction over the 576 latent
+// columns (k steps 0..8 and 9..17 of 32 columns), so each staged key is read
+// from LDS once, and the four half tiles meet through LDS, summed in the same
+// order by every wave. A lane then holds keys 4 g .. 4 g + 3 of both tiles for
+// head `col`, which is exactly its P^T operand for one 32-key step, and its
+// O^T accumulators belong to the same head, so every wave runs the same
+// online softmax on its own: wave w computes O^T += V^T . P^T for value
+// columns 128 w .. 128 w + 127, reading V^T with transposed LDS reads in the
+// same key order. Logits are kept in log2 units. Invalid selections load a
+// valid row of the same stage and are masked to probability 0; stages without
+// any valid selection load cache row 0 and skip the arithmetic.
 // ---------------------------------------------------------------------------
+#ifndef DEC_RING
+#define DEC_RING 2   // LDS stages per workgroup
+#endif
+#ifndef DEC_MAXCH
+#define DEC_MAXCH 512  // selections per workgroup at most
+#endif
+#ifndef DEC_WPC
+#define DEC_WPC 2    // workgroups per compute unit
+#endif
+#ifndef DEC_CHUNK_WPC
+#define DEC_CHUNK_WPC DEC_WPC  // workgroups per compute unit the chunk size aims at
+#endif
 constexpr int kDecRows = 32;                                  // selections per stage
-constexpr int kDecRing = 4;                                   // LDS stages
+constexpr int kDecRing = DEC_RING;                            // LDS stages
 constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
 constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
-constexpr int kDecMaxCH = 1024;
+constexpr int kDecMaxCH = DEC_MAXCH;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
 // LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
@@ -156,7 +172,7 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
 // entry i of the row (k = sel_ld * PS entries) is position
 // page[i / PS] * PS + i % PS, or none for a -1 page.
 template <int PAGED>
-__global__ __launch_bounds__(256, 1) void mla_decode_partial(
+__global__ __launch_bounds__(256, DEC_WPC) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int sel_ld, int T, int S,
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
   __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
-  __shared__ f32x4 s_part[4][2][64];  // per wave: partial S^T of both tiles
+  __shared__ f32x4 s_part[4][64];  // per wave: its half of one S^T tile
 
   const int c = blockIdx.x / HB, hb = blockIdx.x - c * HB, t = blockIdx.y;
   const int tid = threadIdx.x, l = lane_id();
@@ -174,9 +190,10 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   const int i_begin = c * CH, i_end = min(i_begin + CH, k);
   const float scale2 = sm_scale * 1.44269504088896341f;
 
-  // ---- this wave's k steps [kb, kb + nk) of 32 latent columns
-  const int kb = wave < 2 ? 5 * wave : 4 * wave + 2;
-  const int nk = wave < 2 ? 5 : 4;
+  // ---- this wave's S^T tile (keys 16 tile .. 16 tile + 15 of a stage) and
+  // its half of the 18 k steps of 32 latent columns
+  const int tile = wave >> 1;
+  const int kb = 9 * (wave & 1);
   // ---- the selection entries of this chunk (entry i = 64 (4 p + wave) + l
   // of pass p, two stages per wave and pass) and this lane's query fragments
   // (head 16 hb + col, k values 32 (kb + u) + 8 g ..) depend only on the row
@@ -198,13 +215,13 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     }
   }
   const int head = 16 * hb + col;
-  bf16x8 qf[5];
+  bf16x8 qf[9];
   {
     const uint16_t* qrow = q + ((size_t)t * H + (head < H ? head : 0)) * DK + 8 * g;
 #pragma unroll
-    for (int u = 0; u < 5; ++u)
-      qf[u] = as_bf16x8(head < H && u < nk ? *reinterpret_cast<const uint4*>(qrow + 32 * (kb + u))
-                                           : zero_u4());
+    for (int u = 0; u < 9; ++u)
+      qf[u] = as_bf16x8(head < H ? *reinterpret_cast<const uint4*>(qrow + 32 * (kb + u))
+                                 : zero_u4());
   }
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, MP * PS);
   const int nst = ri.seq >= 0 ? (i_end - i_begin + kDecRows - 1) / kDecRows : 0;
@@ -235,20 +252,19 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   // complete the query loads here: a first use inside the stage loop would
   // make the compiler wait for every outstanding load there, ring loads included
 #pragma unroll
-  for (int u = 0; u < 5; ++u) asm volatile("" : : "v"(qf[u]));
+  for (int u = 0; u < 9; ++u) asm volatile("" : : "v"(qf[u]));
   __syncthreads();
 
-  // per-lane LDS offsets. S^T reads: key row col (+16 for the second tile),
-  // chunk 4 i + g of k step i (nope_x and rope_x of row 16 + col equal those
-  // of col).
+  // per-lane LDS offsets. S^T reads: key row 16 tile + col, chunk 4 i + g of
+  // k step i (nope_x and rope_x of row 16 + col equal those of col).
   const int nx = nope_x(col), rx = rope_x(col);
-  int koff[5], kstep[5];
+  const int kr = 16 * tile + col;
+  int koff[9];
 #pragma unroll
-  for (int u = 0; u < 5; ++u) {
+  for (int u = 0; u < 9; ++u) {
     const int i = kb + u;
-    koff[u] = i < 16 ? col * NOPE_B + 16 * ((4 * i + g) ^ nx)
-                     : kDecRopeOff + col * ROPE_B + 16 * ((4 * (i - 16) + g) ^ rx);
-    kstep[u] = i < 16 ? 16 * NOPE_B : 16 * ROPE_B;
+    koff[u] = i < 16 ? kr * NOPE_B + 16 * ((4 * i + g) ^ nx)
+                     : kDecRopeOff + kr * ROPE_B + 16 * ((4 * (i - 16) + g) ^ rx);
   }
   // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3),
   // i.e. 16-byte chunk 16 wave + 2 ct + (col & 3) / 2, byte 8 (col & 1)
@@ -271,8 +287,8 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
   for (int st = 0; st < nst; ++st) {
     // stages st + 1 .. st + 2 were issued after this one
     const int later = min(kDecRing - 2, nst - 1 - st);
-    if (later >= 2) wait_vmcnt<2 * kDecLoads>();
-    else if (later == 1) wait_vmcnt<kDecLoads>();
+    if (kDecRing > 3 && later >= 2) wait_vmcnt<2 * kDecLoads>();
+    else if (kDecRing > 2 && later >= 1) wait_vmcnt<kDecLoads>();
     else wait_vmcnt<0>();
     lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
     if (st + kDecRing - 1 < nst)
@@ -281,26 +297,16 @@ __global__ __launch_bounds__(256, 1) void mla_decode_partial(
     const uint32_t mask = s_mask[st];
     if (mask == 0) continue;
     const unsigned char* buf = ring[st % kDecRing];
-    // ---- this wave's part of S^T for the stage's 32 keys (two tiles)
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // ---- this wave's half of its S^T tile (16 keys), then both tiles summed
+    // in the same order by every wave
+    f32x4 sp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      if (u < nk) {
-        s0 = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u])), qf[u], s0);
-        s1 = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u] + kstep[u])), qf[u],
-                    s1);
-      }
-    }
-    s_part[wave][0][l] = s0;
-    s_part[wave][1][l] = s1;
+    for (int u = 0; u < 9; ++u)
+      sp = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u])), qf[u], sp);
+    s_part[wave][l] = sp;
     lds_barrier();
-    s0 = s_part[0][0][l];
-    s1 = s_part[0][1][l];
-#pragma unroll
-    for (int w2 = 1; w2 < 4; ++w2) {
-      s0 += s_part[w2][0][l];
-      s1 += s_part[w2][1][l];
-    }
+    f32x4 s0 = s_part[0][l] + s_part[1][l];
+    f32x4 s1 = s_part[2][l] + s_part[3][l];
     // ---- masked online softmax over the stage's 32 keys (log2 units)
     const uint32_t m0 = mask >> (4 * g), m1 = mask >> (16 + 4 * g);
     float x0[4], x1[4];
@@ -554,12 +560,12 @@ __global__ __launch_bounds__(256) void mla_decode_combine_wide(const uint16_t* _
 }
 
 int mla_decode_chunk(int T, int k) {
-  // about one workgroup per compute unit, 1 .. 16 blocks of 64 selections
-  // each: a large batch gets long chunks, which halves both the one-time
-  // prologues (one workgroup per compute unit runs at a time) and the
-  // partials the combine reads
+  // about DEC_WPC workgroups per compute unit, 1 .. kDecMaxCH / 64 blocks of
+  // 64 selections each: a large batch gets long chunks, which cuts both the
+  // one-time prologues and the partials the combine reads
   const long nsub = (k + 63) / 64;
-  long per = ((long)T * nsub + 255) / 256;
+  const long slots = 256L * DEC_CHUNK_WPC;
+  long per = ((long)T * nsub + slots - 1) / slots;
   if (per < 1) per = 1;
   if (per > kDecMaxCH / 64) per = kDecMaxCH / 64;
   return (int)per * 64;
