@@ -244,10 +244,14 @@ def _kernel_table(kt, warm, cold, work):
     return out
 
 
+INDEXER_KERNELS = ("idx_score_stream", "idx_score_flat", "idx_score_tiles", "topk_select",
+                   "idx_score_topk", "topk_order", "topk_merge")
+
 # Sources whose text decides each kernel's machine code.
 KERNEL_SOURCES = {
     "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
     "idx_score_tiles": "indexer.hip", "topk_select": "indexer.hip",
+    "idx_score_topk": "indexer.hip", "topk_order": "indexer.hip", "topk_merge": "indexer.hip",
     "mla_decode_partial": "mla.hip", "mla_decode_combine": "mla.hip",
     "mla_decode_combine_wide": "mla.hip", "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
@@ -359,7 +363,7 @@ def bench_decode(dsa, wl, steps, warmup, reps):
                  for i in range(reps)]
     return {"workload": wl.name, "seqs": wl.S, "tokens": int(wl.seq_lens.sum()),
             "tok_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
-            "indexer_ms": round(part(("idx_score_stream", "idx_score_flat", "topk_select")), 5),
+            "indexer_ms": round(part(INDEXER_KERNELS), 5),
             "attend_ms": round(part(("mla_decode_partial", "mla_decode_combine",
                                      "mla_decode_combine_wide")), 5),
             "cold_kernel_sum_ms_median": round(float(np.median(cold_step)), 5),
@@ -515,8 +519,11 @@ class ExtendLayers:
         wl = self.wl
         T, k, H = self.T, self.k, self.H
         n_sel = int((sel_np >= 0).sum())
-        w = {"idx_score_tiles": ("mfma", 2 * wl.H_idx * wl.D_idx * int(self.nval.sum())),
+        idx_flops = 2 * wl.H_idx * wl.D_idx * int(self.nval.sum())
+        w = {"idx_score_tiles": ("mfma", idx_flops),
+             "idx_score_topk": ("mfma", idx_flops),
              "topk_select": ("hbm", int(self.nval.sum()) * 4 + T * k * 4),
+             "topk_order": ("hbm", T * k * (8 + 4)),
              "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
              "paged_write_rows": ("hbm", T * (wl.D_idx + DK) * 2 * 2)}
         for QB, cnt in QB_counts.items():
@@ -618,8 +625,7 @@ def bench_extend_workload(dsa, wl, steps, warmup, reps):
         work["mla_extend_qblock"] = w[f"mla_extend_qblock@{path}"]
     res["kernels"] = _kernel_table(kt_main, warm, cold, work)
     res["roofline"] = _headline_roofline(kt_main, res["kernels"], work, wl.name)
-    res["indexer_ms"] = round(sum(kt_main[nm][1] for nm in ("idx_score_tiles", "topk_select")
-                                  if nm in kt_main), 4)
+    res["indexer_ms"] = round(sum(kt_main[nm][1] for nm in INDEXER_KERNELS if nm in kt_main), 4)
     return res
 
 

@@ -86,8 +86,13 @@ int dsa_abi_version(void);
  *              the streaming per-row kernel when <= 1 and the MFMA tile
  *              kernel otherwise; any value gives the same result)
  *   workspace  device scratch of at least dsa_indexer_topk_workspace(...)
- *              bytes for the same arguments: the fp32 score rows and, for
- *              the tile kernel, each row's extreme scores per 2048 positions
+ *              bytes for the same arguments. For query chunks (max_q_len > 1)
+ *              whose score matrix T x ceil64(MP * PS) fp32 would exceed
+ *              256 MiB, the call takes the fused path of
+ *              dsa_indexer_topk_fused (workspace O(T * k)); otherwise it holds
+ *              the fp32 score rows and, for the tile kernel, each row's
+ *              extreme scores per 2048 positions. Both paths give the same
+ *              result.
  * Supported: 1 <= H <= 64, D in {32, 64, 128}, PS a multiple of 16,
  * MP * PS <= 2^24, 1 <= k <= 4096; otherwise DSA_ERR_UNSUPPORTED.
  */
@@ -98,6 +103,34 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
                      const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
                      int k, int max_q_len, int32_t* topk, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_indexer_topk_fused — dsa_indexer_topk without the score matrix: the
+ * scores are ranked as they are computed ("dsa_sparse_backend.py", the
+ * prefill indexer kernel note: the [T, max_kv] token scores are the dominant
+ * temporary at long context). Same result, bit for bit, as
+ * dsa_indexer_topk for the same arguments.
+ *
+ * Each row's positions are split into G segments (G <= 8, G * k <= 8192);
+ * one workgroup scores 8 consecutive rows over one segment in ascending
+ * position order and keeps, per row, a candidate list of C = k + max(k, 512)
+ * (rounded up to 64) entries: when it fills, the list is cut to its exact k
+ * best (ties by lower position) and only keys above the k-th are taken
+ * afterwards. A second kernel merges each row's lists into the canonical
+ * order. The workspace holds the lists: T * G * C * 8 + T * G * 4 bytes
+ * (about 268 MB for 8192 rows at k = 2048, against 4.3 GB of scores at a
+ * 131072-position context).
+ *
+ *   arguments as in dsa_indexer_topk, without max_q_len (any ragged layout
+ *   is accepted); workspace of dsa_indexer_topk_fused_workspace(...) bytes
+ * Supported: as dsa_indexer_topk.
+ */
+size_t dsa_indexer_topk_fused_workspace(int T, int S, int H, int D, int PS, int MP, int k);
+int dsa_indexer_topk_fused(const void* q_idx, const float* w, const void* idx_cache,
+                           int num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                           int k, int32_t* topk, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * dsa_indexer_page_topk — lightning-indexer exact top-k over pages.

@@ -17,6 +17,8 @@ from ._lib import (  # noqa: F401
     indexer_page_topk,
     indexer_page_topk_workspace,
     indexer_topk,
+    indexer_topk_fused,
+    indexer_topk_fused_workspace,
     indexer_topk_workspace,
     last_error,
     load,

@@ -33,6 +33,9 @@ SIGNATURES = {
     "dsa_indexer_topk_workspace": (_c_size, [_c_int] * 8),
     "dsa_indexer_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                          + [_vp, _vp, _c_size, _vp]),
+    "dsa_indexer_topk_fused_workspace": (_c_size, [_c_int] * 7),
+    "dsa_indexer_topk_fused": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 7
+                               + [_vp, _vp, _c_size, _vp]),
     "dsa_block_union_workspace": (_c_size, [_c_int] * 5),
     "dsa_block_union": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp, _vp, _c_size,
                                                                   _vp]),
@@ -239,6 +242,37 @@ def indexer_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int,
                                  _ptr(seq_lens), _ptr(cu_q_lens), T, S, H, D, PS, MP, k,
                                  max_q_len, _ptr(out), _ptr(ws), nbytes, _stream(stream))
     _check("dsa_indexer_topk", st)
+    return out
+
+
+def indexer_topk_fused_workspace(T, S, H, D, PS, MP, k) -> int:
+    return load().dsa_indexer_topk_fused_workspace(T, S, H, D, PS, MP, k)
+
+
+def indexer_topk_fused(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int, out=None,
+                       workspace=None, stream=None):
+    """Exact lightning-indexer top-k without the score matrix -> int32
+    [T, k] (dsa_indexer_topk_fused); the same result as indexer_topk."""
+    torch = _torch()
+    dev = q_idx.device
+    _need(q_idx, "q_idx", torch.bfloat16, 3, dev)
+    _need(w, "w", torch.float32, 2, dev)
+    _need(idx_cache, "idx_cache", torch.bfloat16, 3, dev)
+    S, MP = _ragged(page_table, seq_lens, cu_q_lens, dev)
+    T, H, D = q_idx.shape
+    P, PS, Dc = idx_cache.shape
+    if Dc != D or tuple(w.shape) != (T, H):
+        raise ValueError("q_idx [T,H,D], w [T,H], idx_cache [P,PS,D] disagree")
+    if out is None:
+        out = _empty((T, k), torch.int32, dev, stream)
+    _need(out, "out", torch.int32, 2, dev)
+    nbytes = indexer_topk_fused_workspace(T, S, H, D, PS, MP, k)
+    ws = _workspace(nbytes, dev, workspace, stream)
+    st = load().dsa_indexer_topk_fused(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P,
+                                       _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S,
+                                       H, D, PS, MP, k, _ptr(out), _ptr(ws), nbytes,
+                                       _stream(stream))
+    _check("dsa_indexer_topk_fused", st)
     return out
 
 

@@ -51,6 +51,20 @@ int check_ragged(int T, int S, int PS, int MP, int num_pages) {
   return DSA_OK;
 }
 
+// The fused indexer path (scores never stored) replaces the score matrix
+// when it would exceed this many bytes for a batch of query chunks.
+constexpr size_t kMaterializeMax = size_t(256) << 20;
+
+size_t fused_ws(int T, int MP, int PS, int k) {
+  int G = 1, L = 0, C = 0;
+  dsa::fused_plan(T, MP * PS, k, &G, &L, &C);
+  return align256((size_t)T * G * C * 8) + align256((size_t)T * G * 4);
+}
+
+bool use_fused(int T, int MP, int PS, int max_q_len) {
+  return max_q_len > 1 && (size_t)T * scores_ld(MP, PS) * 4 > kMaterializeMax;
+}
+
 size_t decode_ws(int T, int H, int k) {
   const int ch = dsa::mla_decode_chunk(T, k);
   const size_t nch = (size_t)((k + ch - 1) / ch);
@@ -79,17 +93,25 @@ int dsa_abi_version(void) { return 1; }
 // ---------------------------------------------------------------------------
 size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
                                   int max_q_len) {
-  (void)S; (void)H; (void)D; (void)k;
-  if (T <= 0 || PS <= 0 || MP <= 0) return 0;
+  (void)S; (void)H; (void)D;
+  if (T <= 0 || PS <= 0 || MP <= 0 || k <= 0) return 0;
+  if (use_fused(T, MP, PS, max_q_len)) return fused_ws(T, MP, PS, k);
   return align256((size_t)T * scores_ld(MP, PS) * 4) +
          align256((size_t)T * dsa::score_ext_ld(max_q_len, MP * PS) * 8);
 }
 
-int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
-                     const int32_t* page_table, const int32_t* seq_lens,
-                     const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP, int k,
-                     int max_q_len, int32_t* topk, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+size_t dsa_indexer_topk_fused_workspace(int T, int S, int H, int D, int PS, int MP, int k) {
+  (void)S; (void)H; (void)D;
+  if (T <= 0 || PS <= 0 || MP <= 0 || k <= 0) return 0;
+  return fused_ws(T, MP, PS, k);
+}
+
+namespace {
+int indexer_topk_impl(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
+                      const int32_t* page_table, const int32_t* seq_lens,
+                      const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP, int k,
+                      int max_q_len, bool fused, int32_t* topk, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int st = check_ragged(T, S, PS, MP, num_pages);
   if (st) return st;
   if (H < 1 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "indexer H=%d not in [1, 64]", H);
@@ -103,7 +125,8 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   if (!aligned16(q_idx) || !aligned16(idx_cache))
     return fail(DSA_ERR_INVALID_ARG, "q_idx and idx_cache must be 16-byte aligned");
-  const size_t need = dsa_indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len);
+  const size_t need = fused ? fused_ws(T, MP, PS, k)
+                            : dsa_indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len);
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "indexer workspace %zu < %zu bytes", workspace_bytes, need);
   dsa::IndexerArgs a;
@@ -116,17 +139,45 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
   a.cu = cu_q_lens;
   a.T = T; a.S = S; a.H = H; a.D = D; a.PS = PS; a.MP = MP; a.k = k;
   a.max_q_len = max_q_len;
+  a.topk = topk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused) {
+    int G = 1, L = 0, C = 0;
+    dsa::fused_plan(T, MP * PS, k, &G, &L, &C);
+    a.cand = static_cast<uint2*>(workspace);
+    a.cand_cnt = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                        align256((size_t)T * G * C * 8));
+    return hip_status(dsa::indexer_fused_topk(a, s), "fused indexer launch");
+  }
   a.scores = static_cast<float*>(workspace);
   a.ld = scores_ld(MP, PS);
   a.ext_ld = dsa::score_ext_ld(max_q_len, MP * PS);
   if (a.ext_ld > 0)
     a.ext = reinterpret_cast<uint2*>(static_cast<char*>(workspace) +
                                      align256((size_t)T * a.ld * 4));
-  a.topk = topk;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dsa::indexer_score(a, s);
   if (e != hipSuccess) return hip_status(e, "indexer score launch");
   return hip_status(dsa::indexer_select(a, s), "indexer top-k launch");
+}
+}  // namespace
+
+int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
+                     const int32_t* page_table, const int32_t* seq_lens,
+                     const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP, int k,
+                     int max_q_len, int32_t* topk, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return indexer_topk_impl(q_idx, w, idx_cache, num_pages, page_table, seq_lens, cu_q_lens, T,
+                           S, H, D, PS, MP, k, max_q_len, use_fused(T, MP, PS, max_q_len), topk,
+                           workspace, workspace_bytes, stream);
+}
+
+int dsa_indexer_topk_fused(const void* q_idx, const float* w, const void* idx_cache,
+                           int num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                           const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                           int k, int32_t* topk, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return indexer_topk_impl(q_idx, w, idx_cache, num_pages, page_table, seq_lens, cu_q_lens, T,
+                           S, H, D, PS, MP, k, 2, true, topk, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -1645,4 +1645,606 @@ hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused prefill scoring and exact top-k: the [T, cap] score matrix of a long
+// extend batch is never stored ("dsa_sparse_backend.py", the prefill indexer
+// kernel note: token scores of that size are the dominant temporary at long
+// context).
+//
+// idx_score_topk: a workgroup of 8 waves owns 8 consecutive packed rows (one
+// per wave, query fragments and head weights resident, as idx_score_tiles)
+// and one segment of the key positions, which it walks in ascending order:
+// ranges of kTileMaxRK positions, each streamed through the same four-stage
+// ring of 64-key blocks and shared by the rows of one sequence. Every wave
+// keeps its row's candidates of the segment in a global list of C entries
+// (order key, position), appending each scored key above the row's bar.
+// When the next block might not fit, the wave compacts the list to exactly k
+// entries — every key above the k-th largest key kappa, then the first keys
+// equal to kappa in list order — and the bar becomes kappa.
+//
+// Exactness. The list is in ascending position order (keys are appended in
+// position order, a compaction keeps the order), so the kept entries beat,
+// in the canonical order (key descending, position ascending), every dropped
+// entry and every later key that is not above kappa: each of those is below
+// kappa, or equal to it at a larger position than all k kept entries. So the
+// row's top k always lie in the list plus the later keys above the bar. The
+// bar starts unset (every key is taken).
+//
+// The compaction is a radix select of the k-th key over the list, one 8-bit
+// digit per pass with a 256-bin LDS histogram per wave, then an
+// order-keeping pass; list reads bypass the vector L1 (agent-scope loads),
+// so they see the wave's own earlier list stores.
+// grid = (G segments of L positions, ceil(T / 8)), block = 512.
+//
+// topk_merge: one workgroup per row sorts the G lists of the row (at most
+// G * k <= kMergeMax entries) by composite key (order key << 32 | ~position)
+// with a bitonic sort in LDS and writes the first min(k, total) positions,
+// then -1. Composite keys are distinct, so the order is the canonical one.
+// ---------------------------------------------------------------------------
+constexpr int kMergeMax = 8192;
+
+__device__ __forceinline__ uint2 list_load(const uint2* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
+// Compact list[0 .. cnt), cnt > k, to exactly k entries in list order (see
+// above); returns kappa. Wave-level: hist is this wave's 256 LDS words. Every
+// key lies in [lo, hi], so the bits above the highest bit in which lo and hi
+// differ are common to all keys and the digit passes start below them (one
+// pass per 8 bits left; none when every key is equal). Each lane has eight
+// list loads in flight at a time.
+constexpr int kListBatch = 8;
+
+// The bin d of a wave's 256-bin histogram at which the count from the top
+// bin down reaches need (1 <= need <= total), and the count above it.
+__device__ __forceinline__ void hist_find(const uint32_t* hist, int need, int* d_out,
+                                          int* above_out) {
+  const int l = lane_id();
+  // lane l holds bins 255 - 4 l - c (c < 4), descending
+  uint32_t c4[4];
+  int lane_sum = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    c4[c] = hist[255 - 4 * l - c];
+    lane_sum += (int)c4[c];
+  }
+  int incl = lane_sum;
+#pragma unroll
+  for (int off = 1; off < DSA_WAVE; off <<= 1) {
+    const int u = __shfl_up(incl, off, DSA_WAVE);
+    if (l >= off) incl += u;
+  }
+  const int excl = incl - lane_sum;
+  const uint64_t hit = __ballot(excl < need && incl >= need);
+  const int src = (int)__builtin_ctzll(hit);
+  int d = 0, above = 0;
+  if (l == src) {
+    int run = excl;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (run + (int)c4[c] >= need) {
+        d = 255 - 4 * l - c;
+        above = run;
+        break;
+      }
+      run += (int)c4[c];
+    }
+  }
+  *d_out = __shfl(d, src, DSA_WAVE);
+  *above_out = __shfl(above, src, DSA_WAVE);
+}
+
+__device__ uint32_t list_compact(uint2* list, int cnt, int k, uint32_t* hist, uint32_t lo,
+                                 uint32_t hi) {
+  const int l = lane_id();
+  uint32_t prefix = lo;
+  int need = k;  // kappa is the need-th largest key among those matching prefix
+  const uint32_t diff = lo ^ hi;
+  if (diff != 0u) {
+    const int top = 31 - __builtin_clz(diff);
+    const int start = top & ~7;
+    prefix = lo & ~((2u << top) - 1u);  // the common high bits (none when top = 31)
+    if (top == 31) prefix = 0u;
+    for (int shift = start; shift >= 0; shift -= 8) {
+      for (int i = l; i < 256; i += DSA_WAVE) hist[i] = 0u;
+      const uint32_t hmask = shift + 8 >= 32 ? 0u : ~((1u << (shift + 8)) - 1u);
+      for (int base = 0; base < cnt; base += DSA_WAVE * kListBatch) {
+        uint32_t key[kListBatch];
+#pragma unroll
+        for (int u = 0; u < kListBatch; ++u) {
+          const int i = base + u * DSA_WAVE + l;
+          key[u] = i < cnt ? list_load(list + i).x : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kListBatch; ++u) {
+          const int i = base + u * DSA_WAVE + l;
+          if (i < cnt && (key[u] & hmask) == (prefix & hmask))
+            atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+        }
+      }
+      int d, above;
+      hist_find(hist, need, &d, &above);
+      prefix = (prefix & hmask) | ((uint32_t)d << shift);
+      need -= above;
+    }
+  }
+  const uint32_t kappa = prefix;
+  // keep: keys above kappa, and the first `need` keys equal to kappa
+  int kept = 0, ties = 0;
+  for (int base = 0; base < cnt; base += DSA_WAVE * kListBatch) {
+    uint2 e[kListBatch];
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int i = base + u * DSA_WAVE + l;
+      e[u] = i < cnt ? list_load(list + i) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int i = base + u * DSA_WAVE + l;
+      const bool gt = i < cnt && e[u].x > kappa;
+      const bool eq = i < cnt && e[u].x == kappa;
+      const uint64_t beq = __ballot(eq);
+      const bool keep = gt || (eq && ties + ballot_rank(beq) < need);
+      const uint64_t bk = __ballot(keep);
+      if (keep) list[kept + ballot_rank(bk)] = e[u];  // never past index i
+      kept += __popcll(bk);
+      ties += __popcll(beq);
+    }
+  }
+  wait_vm<0>();
+  return kappa;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, DSA_WAVE));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, DSA_WAVE));
+  return v;
+}
+
+// The histogram window of a list: 256 bins of 2^shift keys from base, the
+// last bin also holding every larger key.
+__device__ __forceinline__ int window_shift(uint32_t base, uint32_t hi) {
+  const uint32_t span = hi > base ? hi - base : 0u;
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  return bits > 8 ? bits - 8 : 0;
+}
+
+__device__ __forceinline__ uint32_t window_bin(uint32_t key, uint32_t base, int shift) {
+  const uint32_t b = (key - base) >> shift;
+  return b < 255u ? b : 255u;
+}
+
+// Count the keys of list[0 .. cnt) (all >= base) into hist under the window
+// (base, shift).
+__device__ void list_hist(const uint2* list, int cnt, uint32_t base, int shift, uint32_t* hist) {
+  const int l = lane_id();
+  for (int i = l; i < 256; i += DSA_WAVE) hist[i] = 0u;
+  for (int b0 = 0; b0 < cnt; b0 += DSA_WAVE * kListBatch) {
+    uint32_t key[kListBatch];
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int i = b0 + u * DSA_WAVE + l;
+      key[u] = i < cnt ? list_load(list + i).x : base;
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u)
+      if (b0 + u * DSA_WAVE + l < cnt) atomicAdd(&hist[window_bin(key[u], base, shift)], 1u);
+  }
+}
+
+// Keep the entries of list[0 .. cnt) with key >= theta, in list order, and
+// bin them into hist under the window (theta, shift). Returns the count kept.
+__device__ int list_cut_rebin(uint2* list, int cnt, uint32_t theta, int shift, uint32_t* hist) {
+  const int l = lane_id();
+  for (int i = l; i < 256; i += DSA_WAVE) hist[i] = 0u;
+  int kept = 0;
+  for (int base = 0; base < cnt; base += DSA_WAVE * kListBatch) {
+    uint2 e[kListBatch];
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int i = base + u * DSA_WAVE + l;
+      e[u] = i < cnt ? list_load(list + i) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kListBatch; ++u) {
+      const int i = base + u * DSA_WAVE + l;
+      const bool keep = i < cnt && e[u].x >= theta;
+      const uint64_t bk = __ballot(keep);
+      if (keep) {
+        list[kept + ballot_rank(bk)] = e[u];  // never past index i
+        atomicAdd(&hist[window_bin(e[u].x, theta, shift)], 1u);
+      }
+      kept += __popcll(bk);
+    }
+  }
+  wait_vm<0>();
+  return kept;
+}
+
+template <int D, int HB>
+__global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
+    int PS, int MP, int k, int G, int L, int C, uint2* __restrict__ cand,
+    int* __restrict__ cand_cnt) {
+  constexpr int KS = D / 16, HALF = D / 2, RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;
+  constexpr int BLK = kTileKB * RB;      // bytes per staged block
+  constexpr int NLB = BLK / 1024;        // direct loads per block (D / 8)
+  constexpr int NLW = (NLB + 7) / 8;     // at most this many per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kTileRing][BLK];
+  __shared__ int s_pg[kTileMaxRK / 16 + 1];
+  __shared__ int s_seq[kTileRows], s_nv[kTileRows];
+  __shared__ uint32_t s_hist[kTileRows][256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane_id();
+  const int m = l & 31, hf = l >> 5;
+  const int t0 = blockIdx.y * kTileRows;
+  const int cap = MP * PS;
+  if (tid < kTileRows) {
+    const int t = t0 + tid;
+    RowInfo ri;
+    ri.seq = -1;
+    ri.n_valid = 0;
+    if (t < T) ri = row_info(cu, seq_lens, S, t, cap);
+    s_seq[tid] = ri.seq;
+    s_nv[tid] = ri.n_valid;
+  }
+  __syncthreads();
+  const int seg0 = blockIdx.x * L;
+  const int seg1 = min(seg0 + L, cap);
+  const int t = t0 + wave;
+  const int my_nv = __builtin_amdgcn_readfirstlane(s_nv[wave]);
+  const bool has = t < T && s_seq[wave] >= 0 && my_nv > seg0;
+  uint2* list = cand + ((size_t)(t < T ? t : 0) * G + blockIdx.x) * C;
+  int cnt = 0;            // entries in the list (wave-uniform)
+  bool barred = false;    // a bar exists: only keys above it are taken
+  uint32_t bar = 0u;
+  // bounds of the keys this lane appended (the list's keys lie between the
+  // wave's minimum, or the bar once there is one, and the wave's maximum)
+  uint32_t key_lo = 0xffffffffu, key_hi = 0u;
+  // once barred: s_hist[wave] counts the list's keys in 256 bins of
+  // 2^win_shift keys from win_base (= the bar), the last bin open above
+  uint32_t win_base = 0u;
+  int win_shift = 0;
+
+  // this wave's query fragments and head weights, once for the segment
+  bf16x8 a[HB][KS];
+  float wv[HB][16];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 32 * hb + m;
+    const bool okq = has && head < H;
+    load_q_frag<D>(q + ((size_t)(okq ? t : 0) * H + (head < H ? head : 0)) * D + hf * HALF, okq,
+                   a[hb]);
+    load_head_weights(w + (size_t)(has ? t : 0) * H, H, hb, hf, wv[hb]);
+  }
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) asm volatile("" : : "v"(a[hb][i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) asm volatile("" : : "v"(wv[hb][i]));
+  }
+  const uint32_t lds_ring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
+  const int lr = l / CPR, lc = l % CPR;
+  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+
+  for (int k0 = seg0; k0 < seg1; k0 += kTileMaxRK) {
+    int seg = 0;
+    while (seg < kTileRows) {
+      const int s = __builtin_amdgcn_readfirstlane(s_seq[seg]);
+      int seg_end = seg + 1;
+      while (seg_end < kTileRows && s_seq[seg_end] == s) ++seg_end;
+      seg_end = __builtin_amdgcn_readfirstlane(seg_end);
+      const int n_hi = s >= 0 ? __builtin_amdgcn_readfirstlane(s_nv[seg_end - 1]) : 0;
+      const int k1 = min(min(k0 + kTileMaxRK, n_hi), seg1);
+      if (s >= 0 && k0 < k1) {
+        const int32_t* ptrow = pt + (size_t)s * MP;
+        const int pg0 = k0 / PS;
+        for (int i = tid; i <= (k1 - 1) / PS - pg0; i += 512) s_pg[i] = ptrow[pg0 + i];
+        const bool act = has && wave >= seg && wave < seg_end && my_nv > k0;
+        const int nv = min(my_nv, seg1);
+        __syncthreads();  // s_pg ready
+
+        const int nb = (k1 - k0 + kTileKB - 1) / kTileKB;
+        const int nlw = wave < NLB % 8 || NLB % 8 == 0 ? NLW : NLW - 1;
+        auto stage = [&](int b) {
+          const uint32_t buf = lds_ring + (b % kTileRing) * BLK;
+#pragma unroll
+          for (int n = 0; n < NLW; ++n) {
+            const int I = wave + 8 * n;
+            if (I < NLB) {
+              int j0 = k0 + b * kTileKB + I * RPI;
+              if (j0 >= k1) j0 = k0;  // past the range: any staged row, never used
+              const int page = clamp_page(s_pg[j0 / PS - pg0], num_pages);
+              const uint64_t src =
+                  (uint64_t)(uintptr_t)(cache + ((size_t)page * PS + (j0 % PS)) * D);
+              const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
+              const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
+              gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
+                        (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                        __builtin_amdgcn_readfirstlane(buf + I * 1024));
+            }
+          }
+        };
+#pragma unroll
+        for (int b = 0; b < kTileRing - 1; ++b)
+          if (b < nb) stage(b);
+        int hist = 0;  // bit i: this wave stored list entries i + 1 iterations ago
+        for (int b = 0; b < nb; ++b) {
+          const int later = min(kTileRing - 2, nb - 1 - b);
+          wait_vm_dyn(later * nlw + __popc(hist & 7));
+          lds_sync();  // block b has landed for every wave; block b - 1 is consumed
+          if (b + kTileRing - 1 < nb) stage(b + kTileRing - 1);
+          hist <<= 1;
+          if (!act || k0 + b * kTileKB >= nv) continue;  // wave-uniform
+          const unsigned char* buf = ring[b % kTileRing];
+          float sc[kTileKB / 32];
+#pragma unroll
+          for (int sb = 0; sb < kTileKB / 32; ++sb) {
+            const int kr = sb * 32 + m;
+            bf16x8 bk[KS];
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+              const int chunk = hf * HALF / 8 + i;
+              bk[i] = as_bf16x8(
+                  *reinterpret_cast<const uint4*>(buf + kr * RB + 16 * (chunk ^ (kr % CPR))));
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+              f32x16 acc = {};
+#pragma unroll
+              for (int i = 0; i < KS; ++i)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], bk[i], acc, 0, 0, 0);
+              part += relu_weighted_sum(acc, wv[hb]);
+            }
+            sc[sb] = part + shfl_xor_f(part, 32);  // both lane halves hold key sb * 32 + m
+          }
+          // lane l holds key l of the block
+          const int j = k0 + b * kTileKB + l;
+          const uint32_t key = score_order_bits(hf ? sc[1] : sc[0]);
+          bool take = j < nv && (!barred || key > bar);
+          uint64_t bal = __ballot(take);
+          if (bal == 0ull) continue;
+          if (cnt + __popcll(bal) > C) {  // no room (cnt > C - 64 > k): cut the list
+            const uint32_t hi = wave_max_u32(key_hi);
+            if (!barred) {  // the first cut: a window over the keys seen so far
+              win_base = wave_min_u32(key_lo);
+              win_shift = window_shift(win_base, hi);
+              list_hist(list, cnt, win_base, win_shift, s_hist[wave]);
+            }
+            int d = 0, above = 0;
+            hist_find(s_hist[wave], k, &d, &above);
+            const int keep_n = above + (int)s_hist[wave][d];
+            if (keep_n <= k + (C - k) / 2) {
+              // cut at the lower edge of the window bin that holds the k-th key
+              // (every list key is >= win_base: the bar, or the minimum before
+              // the first cut)
+              bar = win_base + ((uint32_t)d << win_shift);
+              win_shift = window_shift(bar, hi);
+              cnt = list_cut_rebin(list, cnt, bar, win_shift, s_hist[wave]);
+            } else {
+              // exact cut to k entries (a crowded bin)
+              const uint32_t lo = barred ? bar : win_base;
+              bar = list_compact(list, cnt, k, s_hist[wave], lo, hi);
+              win_shift = window_shift(bar, hi);
+              cnt = list_cut_rebin(list, k, bar, win_shift, s_hist[wave]);
+            }
+            win_base = bar;
+            barred = true;
+            hist = 0;  // the cut waited for every outstanding operation
+            take = take && key > bar;
+            bal = __ballot(take);
+            if (bal == 0ull) continue;
+          }
+          if (take) {
+            list[cnt + ballot_rank(bal)] = make_uint2(key, (uint32_t)j);
+            key_lo = min(key_lo, key);
+            key_hi = max(key_hi, key);
+            if (barred) atomicAdd(&s_hist[wave][window_bin(key, win_base, win_shift)], 1u);
+          }
+          cnt += __popcll(bal);
+          hist |= 1;
+        }
+        __syncthreads();  // the ring and s_pg are free for the next pass
+      }
+      seg = seg_end;
+    }
+  }
+  if (cnt > k) {
+    const uint32_t lo = barred ? bar : wave_min_u32(key_lo);
+    list_compact(list, cnt, k, s_hist[wave], lo, wave_max_u32(key_hi));
+    cnt = k;
+  }
+  if (t < T && l == 0) cand_cnt[(size_t)t * G + blockIdx.x] = cnt;
+}
+
+constexpr int kMergeNT = 256;
+
+__global__ __launch_bounds__(kMergeNT) void topk_merge(const uint2* __restrict__ cand,
+                                                       const int* __restrict__ cand_cnt, int G,
+                                                       int C, int k, int32_t* __restrict__ topk) {
+  extern __shared__ uint64_t s_key[];  // merge_width(G, k) entries
+  __shared__ int s_off[9];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int run = 0;
+    for (int g = 0; g < G; ++g) {
+      s_off[g] = run;
+      run += cand_cnt[(size_t)t * G + g];
+    }
+    s_off[G] = run;
+  }
+  __syncthreads();
+  const int total = min(s_off[G], kMergeMax);
+  int nb = 64;
+  while (nb < total) nb <<= 1;
+  for (int i = tid; i < nb; i += kMergeNT) {
+    uint64_t v = 0ull;
+    if (i < total) {
+      int g = 0;
+      while (g + 1 < G && s_off[g + 1] <= i) ++g;
+      const uint2 e = cand[((size_t)t * G + g) * C + (i - s_off[g])];
+      v = ((uint64_t)e.x << 32) | (uint64_t)(0xffffffffu - e.y);
+    }
+    s_key[i] = v;
+  }
+  __syncthreads();
+  for (int size = 2; size <= nb; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (nb >> 1); i += kMergeNT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = s_key[lo], y = s_key[hi];
+        if ((x < y) == up) {
+          s_key[lo] = y;
+          s_key[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int n_out = min(k, total);
+  int32_t* out = topk + (size_t)t * k;
+  for (int i = tid; i < k; i += kMergeNT) out[i] = i < n_out ? topk_key_pos(s_key[i]) : -1;
+}
+
+// One list per row (G = 1): the list holds the row's top min(k, n_valid)
+// entries in ascending position order, so a stable sort by key descending
+// (rocPRIM's block radix sort, over the bits in which the keys differ) gives
+// the canonical order. grid = T, block = kMergeNT.
+template <int IPT>
+__global__ __launch_bounds__(kMergeNT) void topk_order(const uint2* __restrict__ cand,
+                                                       const int* __restrict__ cand_cnt, int C,
+                                                       int k, int32_t* __restrict__ topk) {
+  using Sorter = rocprim::block_radix_sort<uint32_t, kMergeNT, IPT, int>;
+  __shared__ typename Sorter::storage_type storage;
+  __shared__ uint32_t s_red[2][kMergeNT / DSA_WAVE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int cnt = min(cand_cnt[t], k);
+  const uint2* list = cand + (size_t)t * C;
+  uint32_t keys[IPT];
+  int vals[IPT];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    const uint2 e = idx < cnt ? list[idx] : make_uint2(0u, 0xffffffffu);
+    keys[i] = e.x;
+    vals[i] = (int)e.y;
+    if (idx < cnt) {
+      mn = min(mn, e.x);
+      mx = max(mx, e.x);
+    }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane_id() == 0) {
+    s_red[0][tid >> 6] = mn;
+    s_red[1][tid >> 6] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kMergeNT / DSA_WAVE; ++w) {
+    mn = min(mn, s_red[0][w]);
+    mx = max(mx, s_red[1][w]);
+  }
+  const uint32_t diff = cnt > 0 ? mn ^ mx : 0u;
+  if (diff != 0u)  // block-uniform; entries past cnt carry key 0 and stay last
+    Sorter().sort_desc(keys, vals, storage, 0u, 32u - (unsigned)__builtin_clz(diff));
+  int32_t* out = topk + (size_t)t * k;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    if (idx < k) out[idx] = idx < cnt ? vals[i] : -1;
+  }
+}
+
+void fused_plan(int T, int cap, int k, int* G, int* L, int* C) {
+  const int nrt = (T + kTileRows - 1) / kTileRows;
+  const int gmax_k = kMergeMax / k < 8 ? kMergeMax / k : 8;
+  const int gmax_cap = (cap + kTileMaxRK - 1) / kTileMaxRK;
+  int g = (512 + nrt - 1) / nrt;
+  if (g > gmax_k) g = gmax_k;
+  if (g > gmax_cap) g = gmax_cap;
+  if (g < 1) g = 1;
+  int len = (cap + g - 1) / g;
+  len = (len + kTileMaxRK - 1) / kTileMaxRK * kTileMaxRK;
+  *L = len;
+  *G = (cap + len - 1) / len;
+  // room above k: a cut keeps k to 1.5 k entries, so about k / 2 or more
+  // keys are taken between cuts
+  const int c = k + (k > 512 ? k : 512);
+  *C = (c + 63) / 64 * 64;
+}
+
+template <int D, int HB>
+static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
+  int G = 1, L = 0, C = 0;
+  fused_plan(a.T, a.MP * a.PS, a.k, &G, &L, &C);
+  {
+    ProfScope prof("idx_score_topk", st);
+    hipLaunchKernelGGL((idx_score_topk<D, HB>), dim3(G, (a.T + kTileRows - 1) / kTileRows),
+                       dim3(512), 0, st, a.q, a.w, a.cache, a.num_pages, a.pt, a.seq_lens, a.cu,
+                       a.T, a.S, a.H, a.PS, a.MP, a.k, G, L, C, a.cand, a.cand_cnt);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (G == 1) {
+    ProfScope prof("topk_order", st);
+    if (a.k <= kMergeNT * 8)
+      hipLaunchKernelGGL((topk_order<8>), dim3(a.T), dim3(kMergeNT), 0, st, a.cand, a.cand_cnt,
+                         C, a.k, a.topk);
+    else
+      hipLaunchKernelGGL((topk_order<16>), dim3(a.T), dim3(kMergeNT), 0, st, a.cand,
+                         a.cand_cnt, C, a.k, a.topk);
+    return hipGetLastError();
+  }
+  // the LDS sort holds the row's lists, at most G * k entries, padded to a
+  // power of two
+  int nbmax = 64;
+  while (nbmax < G * a.k) nbmax <<= 1;
+  const size_t lds = (size_t)nbmax * 8;
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done.load() & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_merge),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMergeMax * 8);
+    if (e != hipSuccess) return e;
+    attr_done.fetch_or(bit);
+  }
+  ProfScope prof("topk_merge", st);
+  hipLaunchKernelGGL(topk_merge, dim3(a.T), dim3(kMergeNT), lds, st, a.cand, a.cand_cnt, G, C,
+                     a.k, a.topk);
+  return hipGetLastError();
+}
+
+hipError_t indexer_fused_topk(const IndexerArgs& a, hipStream_t st) {
+  const int HB = (a.H + 31) / 32;
+  switch (a.D) {
+    case 32: return HB == 1 ? launch_fused<32, 1>(a, st) : launch_fused<32, 2>(a, st);
+    case 64: return HB == 1 ? launch_fused<64, 1>(a, st) : launch_fused<64, 2>(a, st);
+    case 128: return HB == 1 ? launch_fused<128, 1>(a, st) : launch_fused<128, 2>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace dsa

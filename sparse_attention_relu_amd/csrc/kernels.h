@@ -29,7 +29,15 @@ struct IndexerArgs {
   // key of the stored scores [T, ext_ld] (nullptr: not produced)
   uint2* ext = nullptr;
   int ext_ld = 0;
+  // fused scoring and top-k: per (row, segment) candidate lists [T, G, C] of
+  // (order key, position) and their lengths [T, G]
+  uint2* cand = nullptr;
+  int* cand_cnt = nullptr;
 };
+
+// Segments G of L positions and list capacity C of the fused path.
+void fused_plan(int T, int cap, int k, int* G, int* L, int* C);
+hipError_t indexer_fused_topk(const IndexerArgs& a, hipStream_t st);
 
 // Tiles per row of the per-tile extreme keys the scorer writes for rows of
 // at most `cap` positions (0 when the chosen scorer writes none).

@@ -131,24 +131,13 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // valid row of the same stage and are masked to probability 0; stages without
 // any valid selection load cache row 0 and skip the arithmetic.
 // ---------------------------------------------------------------------------
-#ifndef DEC_RING
-#define DEC_RING 2   // LDS stages per workgroup
-#endif
-#ifndef DEC_MAXCH
-#define DEC_MAXCH 512  // selections per workgroup at most
-#endif
-#ifndef DEC_WPC
-#define DEC_WPC 2    // workgroups per compute unit
-#endif
-#ifndef DEC_CHUNK_WPC
-#define DEC_CHUNK_WPC DEC_WPC  // workgroups per compute unit the chunk size aims at
-#endif
+constexpr int kDecWPC = 2;                                    // workgroups per compute unit
 constexpr int kDecRows = 32;                                  // selections per stage
-constexpr int kDecRing = DEC_RING;                            // LDS stages
+constexpr int kDecRing = 2;                                   // LDS stages
 constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
 constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
-constexpr int kDecMaxCH = DEC_MAXCH;
+constexpr int kDecMaxCH = 512;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
 // LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
@@ -172,7 +161,7 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
 // entry i of the row (k = sel_ld * PS entries) is position
 // page[i / PS] * PS + i % PS, or none for a -1 page.
 template <int PAGED>
-__global__ __launch_bounds__(256, DEC_WPC) void mla_decode_partial(
+__global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, int row_stride,
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int sel_ld, int T, int S,
@@ -560,11 +549,11 @@ __global__ __launch_bounds__(256) void mla_decode_combine_wide(const uint16_t* _
 }
 
 int mla_decode_chunk(int T, int k) {
-  // about DEC_WPC workgroups per compute unit, 1 .. kDecMaxCH / 64 blocks of
+  // about kDecWPC workgroups per compute unit, 1 .. kDecMaxCH / 64 blocks of
   // 64 selections each: a large batch gets long chunks, which cuts both the
   // one-time prologues and the partials the combine reads
   const long nsub = (k + 63) / 64;
-  const long slots = 256L * DEC_CHUNK_WPC;
+  const long slots = 256L * kDecWPC;
   long per = ((long)T * nsub + slots - 1) / slots;
   if (per < 1) per = 1;
   if (per > kDecMaxCH / 64) per = kDecMaxCH / 64;

@@ -23,7 +23,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 23
+    assert len(declared) == 25
     assert "dsa_sparse_mla_decode_static" in declared
     for name in declared:
         assert hasattr(lib, name), name

@@ -39,11 +39,20 @@ def _oracle_topk(wl, b, k=None, q_idx=None, w=None, cu=None):
 
 
 def _gpu_topk(dsa, d, q_idx, w, cu, k, max_q_len):
+    """max_q_len "fused" calls the fused entry point (scores never stored)."""
     torch = torch_mod()
-    out = dsa.indexer_topk(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache, d.page_table,
-                           d.seq_lens, i32(cu, "cuda"), k, max_q_len)
+    if max_q_len == "fused":
+        out = dsa.indexer_topk_fused(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache,
+                                     d.page_table, d.seq_lens, i32(cu, "cuda"), k)
+    else:
+        out = dsa.indexer_topk(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache, d.page_table,
+                               d.seq_lens, i32(cu, "cuda"), k, max_q_len)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def _mql(path, ql):
+    return 1 if path == "rows" else ("fused" if path == "fused" else max(2, ql))
 
 
 def _max_q_len(cu):
@@ -55,13 +64,13 @@ def _max_q_len(cu):
 # Indexer
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("bname", ["decode", "extend"])
-@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("path", ["rows", "tiles", "fused"])
 def test_indexer_tiny(dsa, bname, path):
     wl = W.config(1)
     b = wl.batches[bname]
     log(f"indexer tiny {bname} path={path}")
     d = Dev(wl)
-    mql = 1 if path == "rows" else max(2, _max_q_len(b.cu_q_lens))
+    mql = _mql(path, _max_q_len(b.cu_q_lens))
     got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, mql)
     exp = _oracle_topk(wl, b)
     assert np.array_equal(got, exp)
@@ -89,7 +98,7 @@ INDEXER_EDGE = {
 
 
 @pytest.mark.parametrize("name", sorted(INDEXER_EDGE))
-@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("path", ["rows", "tiles", "fused"])
 def test_indexer_edges(dsa, name, path):
     S, kv, PS, MP, ql, H, D, k, extra = INDEXER_EDGE[name]
     cu = np.concatenate([[0], np.cumsum(ql)]).tolist()
@@ -102,7 +111,7 @@ def test_indexer_edges(dsa, name, path):
         w = np.concatenate([w, w[:1].repeat(extra, 0)])
     log(f"indexer edge {name} path={path} T={q_idx.shape[0]}")
     d = Dev(wl)
-    mql = 1 if path == "rows" else max(2, max(ql))
+    mql = _mql(path, max(ql))
     got = _gpu_topk(dsa, d, q_idx, w, cu, k, mql)
     exp = _oracle_topk(wl, b, k=k, q_idx=q_idx, w=w, cu=np.array(cu))
     assert np.array_equal(got, exp)
@@ -156,7 +165,7 @@ def test_indexer_ties_and_negative_zero(dsa):
     w = b.w.copy()
     w[1::2] *= -1.0
     d = Dev(wl)
-    for mql in (1, 5):
+    for mql in (1, 5, "fused"):
         log(f"indexer ties mql={mql}")
         got = _gpu_topk(dsa, d, q, w, b.cu_q_lens, 64, mql)
         exp = _oracle_topk(wl, b, k=64, q_idx=q, w=w)
@@ -181,7 +190,7 @@ def test_indexer_crowded_ties(dsa, k, kv):
     rows[big] = W.f32_to_bf16(2.0 * W.bf16_to_f32(v))
     d = Dev(wl)
     exp = _oracle_topk(wl, b, k=k)
-    for mql in (1, 3):
+    for mql in (1, 3, "fused"):
         log(f"indexer crowded ties k={k} kv={kv} mql={mql}")
         got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, k, mql)
         assert np.array_equal(got, exp)
@@ -207,11 +216,61 @@ def test_indexer_long_rows_skewed(dsa, skew):
     cache.rows[at] = W.f32_to_bf16(2.0 * W.bf16_to_f32(cache.rows[at]))
     d = Dev(wl)
     exp = _oracle_topk(wl, b, k=2048)
-    for mql in (1, 3):
+    for mql in (1, 3, "fused"):
         log(f"indexer long rows skew={skew} mql={mql}")
         got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, 2048, mql)
         assert np.array_equal(got, exp)
     check_topk_rows_valid(got, wl.seq_lens, b.cu_q_lens, 2048)
+
+
+# The fused path: lists that fill and are cut many times per row (k small
+# against the row length), scores rising with position (every key beats the
+# bar, ties at every level), one score for every key (each cut is a tie cut
+# by position), and few rows over a long context (several segments per row,
+# merged).
+FUSED_CASES = {
+    # name: (S, kv_lens, PS, MP, q_lens, H, D, k, pattern)
+    "k16_rows6000": (2, [6000, 4100], 16, 400, [9, 7], 8, 32, 16, "random"),
+    "k100_rows_straddle": (3, [5000, 64, 9000], 64, 150, [5, 2, 11], 32, 128, 100, "random"),
+    "rising_steps": (1, [9000], 64, 150, [10], 1, 32, 300, "rising"),
+    "all_equal": (2, [7000, 3000], 32, 230, [6, 4], 4, 64, 257, "equal"),
+    "segments_k2048": (2, [40000, 25000], 64, 640, [4, 3], 32, 128, 2048, "random"),
+    "segments_k4096_h40": (1, [50000], 64, 800, [6], 40, 128, 4096, "random"),
+    "k4096_one_segment": (2, [2000, 700], 64, 32, [5, 3], 32, 128, 4096, "random"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_CASES))
+def test_indexer_fused_cases(dsa, name):
+    S, kv, PS, MP, ql, H, D, k, pattern = FUSED_CASES[name]
+    cu = np.concatenate([[0], np.cumsum(ql)]).tolist()
+    wl = W.build(name=name, seed=91, S=S, kv_lens=kv, PS=PS, MP=MP, batches={"b": cu}, H_idx=H,
+                 D_idx=D, k=k, with_mla=False, extra_pages=1)
+    b = wl.batches["b"]
+    q_idx, w = b.q_idx, b.w
+    if pattern == "rising":
+        # key at position j: its first m_j coordinates 2, the rest 0, with m_j
+        # rising with j; queries all 2, one head of weight 1: score 4 m_j
+        q_idx = W.f32_to_bf16(np.full(q_idx.shape, 2.0, np.float32))
+        w = np.ones(w.shape, np.float32)
+        n = wl.idx_cache.rows.shape[0]
+        flat = wl.idx_cache.slots
+        page_of = {int(p): i for i, p in enumerate(wl.page_table[0])}
+        pos = np.array([page_of[int(sl) // PS] * PS + int(sl) % PS for sl in flat])
+        m = np.minimum(D, pos * (D + 1) // kv[0])
+        vals = (np.arange(D)[None, :] < m[:, None]).astype(np.float32) * 2.0
+        wl.idx_cache.rows[:] = W.f32_to_bf16(vals)
+        assert n == flat.size
+    elif pattern == "equal":
+        wl.idx_cache.rows[:] = wl.idx_cache.rows[0]
+    d = Dev(wl)
+    log(f"indexer fused {name}: T={q_idx.shape[0]}, k={k}")
+    exp = _oracle_topk(wl, b, k=k, q_idx=q_idx, w=w, cu=np.array(cu))
+    got = _gpu_topk(dsa, d, q_idx, w, cu, k, "fused")
+    assert np.array_equal(got, exp), "fused top-k differs from the oracle"
+    check_topk_rows_valid(got, wl.seq_lens, cu, k)
+    ref = _gpu_topk(dsa, d, q_idx, w, cu, k, max(2, max(ql)))
+    assert np.array_equal(got, ref), "fused and score-matrix paths differ"
 
 
 def test_indexer_zero_rows(dsa):
