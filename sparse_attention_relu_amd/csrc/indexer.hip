@@ -1682,6 +1682,12 @@ hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t
 // then -1. Composite keys are distinct, so the order is the canonical one.
 // ---------------------------------------------------------------------------
 constexpr int kMergeMax = 8192;
+constexpr int kCutSoon = 192;  // a list this close to full asks the workgroup for a cut
+
+__device__ __forceinline__ uint32_t list_load_key(const uint2* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ uint2 list_load(const uint2* p) {
   const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
@@ -1755,7 +1761,7 @@ __device__ uint32_t list_compact(uint2* list, int cnt, int k, uint32_t* hist, ui
 #pragma unroll
         for (int u = 0; u < kListBatch; ++u) {
           const int i = base + u * DSA_WAVE + l;
-          key[u] = i < cnt ? list_load(list + i).x : 0u;
+          key[u] = list_load_key(list + min(i, cnt - 1));  // clamped: never a branch
         }
 #pragma unroll
         for (int u = 0; u < kListBatch; ++u) {
@@ -1778,7 +1784,7 @@ __device__ uint32_t list_compact(uint2* list, int cnt, int k, uint32_t* hist, ui
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u) {
       const int i = base + u * DSA_WAVE + l;
-      e[u] = i < cnt ? list_load(list + i) : make_uint2(0u, 0u);
+      e[u] = list_load(list + min(i, cnt - 1));  // clamped: never a branch
     }
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u) {
@@ -1832,7 +1838,7 @@ __device__ void list_hist(const uint2* list, int cnt, uint32_t base, int shift, 
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u) {
       const int i = b0 + u * DSA_WAVE + l;
-      key[u] = i < cnt ? list_load(list + i).x : base;
+      key[u] = list_load_key(list + min(i, cnt - 1));  // clamped: never a branch
     }
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u)
@@ -1851,7 +1857,7 @@ __device__ int list_cut_rebin(uint2* list, int cnt, uint32_t theta, int shift, u
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u) {
       const int i = base + u * DSA_WAVE + l;
-      e[u] = i < cnt ? list_load(list + i) : make_uint2(0u, 0u);
+      e[u] = list_load(list + min(i, cnt - 1));  // clamped: never a branch
     }
 #pragma unroll
     for (int u = 0; u < kListBatch; ++u) {
@@ -1884,6 +1890,7 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
   __shared__ int s_pg[kTileMaxRK / 16 + 1];
   __shared__ int s_seq[kTileRows], s_nv[kTileRows];
   __shared__ uint32_t s_hist[kTileRows][256];
+  __shared__ int s_cutreq[2];  // by block parity: the block in which waves are to cut
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1900,6 +1907,7 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
     s_seq[tid] = ri.seq;
     s_nv[tid] = ri.n_valid;
   }
+  if (tid < 2) s_cutreq[tid] = -1;
   __syncthreads();
   const int seg0 = blockIdx.x * L;
   const int seg1 = min(seg0 + L, cap);
@@ -1917,6 +1925,32 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
   // 2^win_shift keys from win_base (= the bar), the last bin open above
   uint32_t win_base = 0u;
   int win_shift = 0;
+  int gblk = 0;  // blocks walked so far (the same in every wave)
+  // Cut the list: at the lower edge of the window bin that holds the k-th key
+  // when that keeps at most k + (C - k) / 2 entries, else exactly to k. Every
+  // list key is >= win_base (the bar, or the minimum before the first cut).
+  auto cut_list = [&]() {
+    const uint32_t hi = wave_max_u32(key_hi);
+    if (!barred) {  // the first cut: a window over the keys seen so far
+      win_base = wave_min_u32(key_lo);
+      win_shift = window_shift(win_base, hi);
+      list_hist(list, cnt, win_base, win_shift, s_hist[wave]);
+    }
+    int d = 0, above = 0;
+    hist_find(s_hist[wave], k, &d, &above);
+    const int keep_n = above + (int)s_hist[wave][d];
+    if (keep_n <= k + (C - k) / 2) {
+      bar = win_base + ((uint32_t)d << win_shift);
+      win_shift = window_shift(bar, hi);
+      cnt = list_cut_rebin(list, cnt, bar, win_shift, s_hist[wave]);
+    } else {  // a crowded bin: exact cut to k entries
+      bar = list_compact(list, cnt, k, s_hist[wave], win_base, hi);
+      win_shift = window_shift(bar, hi);
+      cnt = list_cut_rebin(list, k, bar, win_shift, s_hist[wave]);
+    }
+    win_base = bar;
+    barred = true;
+  };
 
   // this wave's query fragments and head weights, once for the segment
   bf16x8 a[HB][KS];
@@ -1988,7 +2022,16 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
           lds_sync();  // block b has landed for every wave; block b - 1 is consumed
           if (b + kTileRing - 1 < nb) stage(b + kTileRing - 1);
           hist <<= 1;
+          // a cut asked for during the previous block: every wave whose list is
+          // a quarter full above k cuts now, so that the waves of the
+          // workgroup wait at the barrier for one cut rather than one each
+          const bool cut_asked = s_cutreq[gblk & 1] == gblk;
+          ++gblk;
           if (!act || k0 + b * kTileKB >= nv) continue;  // wave-uniform
+          if (cut_asked && cnt > k + (C - k) / 4) {
+            cut_list();
+            hist = 0;
+          }
           const unsigned char* buf = ring[b % kTileRing];
           float sc[kTileKB / 32];
 #pragma unroll
@@ -2019,31 +2062,7 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
           uint64_t bal = __ballot(take);
           if (bal == 0ull) continue;
           if (cnt + __popcll(bal) > C) {  // no room (cnt > C - 64 > k): cut the list
-            const uint32_t hi = wave_max_u32(key_hi);
-            if (!barred) {  // the first cut: a window over the keys seen so far
-              win_base = wave_min_u32(key_lo);
-              win_shift = window_shift(win_base, hi);
-              list_hist(list, cnt, win_base, win_shift, s_hist[wave]);
-            }
-            int d = 0, above = 0;
-            hist_find(s_hist[wave], k, &d, &above);
-            const int keep_n = above + (int)s_hist[wave][d];
-            if (keep_n <= k + (C - k) / 2) {
-              // cut at the lower edge of the window bin that holds the k-th key
-              // (every list key is >= win_base: the bar, or the minimum before
-              // the first cut)
-              bar = win_base + ((uint32_t)d << win_shift);
-              win_shift = window_shift(bar, hi);
-              cnt = list_cut_rebin(list, cnt, bar, win_shift, s_hist[wave]);
-            } else {
-              // exact cut to k entries (a crowded bin)
-              const uint32_t lo = barred ? bar : win_base;
-              bar = list_compact(list, cnt, k, s_hist[wave], lo, hi);
-              win_shift = window_shift(bar, hi);
-              cnt = list_cut_rebin(list, k, bar, win_shift, s_hist[wave]);
-            }
-            win_base = bar;
-            barred = true;
+            cut_list();
             hist = 0;  // the cut waited for every outstanding operation
             take = take && key > bar;
             bal = __ballot(take);
@@ -2057,6 +2076,7 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
           }
           cnt += __popcll(bal);
           hist |= 1;
+          if (cnt > C - kCutSoon) s_cutreq[gblk & 1] = gblk;  // ask for a cut next block
         }
         __syncthreads();  // the ring and s_pg are free for the next pass
       }
