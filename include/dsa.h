@@ -15,6 +15,11 @@
  *   allocates nothing, keeps no pointer after a call returns, and never
  *   synchronises: work is enqueued on `stream` (a hipStream_t; NULL = the
  *   default stream) and results are visible after the caller's sync.
+ * - State kept by the library: the thread-local text of dsa_last_error();
+ *   the event records of the profiling hook (idle unless enabled); and, per
+ *   GPU, the static scratch of dsa_sparse_mla_decode_static (part of the
+ *   loaded code object) with its device address. Every other entry point is
+ *   reentrant; overlapping calls of the static decode on one GPU race.
  * - bf16 tensors are raw IEEE bfloat16 (uint16 bit patterns); all layouts
  *   are dense row-major with the shapes given.
  * - Ragged batches (packed along the token axis T):
@@ -37,8 +42,12 @@
  *   launched and nothing is written; dsa_last_error() describes the cause.
  *   DSA_ERR_HIP reports a launch failure (hipGetLastError); asynchronous
  *   faults surface at the caller's next synchronisation.
- * - Each entry point takes a caller-provided device workspace of at least
- *   the size its *_workspace() query returns (any alignment >= 256 B).
+ * - Each entry point that needs scratch takes a caller-provided device
+ *   workspace of at least the size its *_workspace() query returns (any
+ *   alignment >= 256 B); the query takes the shape arguments that size it.
+ *   dsa_sparse_mla_decode_static uses the library's static scratch instead.
+ * - Status codes are returned as int (the enum values below); the host-logic
+ *   functions return a non-negative result or a negated status.
  */
 #ifndef DSA_H
 #define DSA_H
