@@ -137,7 +137,10 @@ constexpr int kDecRing = 2;                                   // LDS stages
 constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
 constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
 constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
-constexpr int kDecMaxCH = 512;
+constexpr int kDecMaxCH = 1024;
+// s_src entries: the cache slot a selection loads; an invalid selection
+// carries this bit over the slot of a valid row of its stage (or slot 0)
+constexpr int kDecInvalid = (int)0x80000000;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
 // LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
@@ -149,11 +152,11 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
 #pragma unroll
   for (int n = 0; n < kDecRows / 4; ++n) {
     const int r = 4 * n + wave;
-    const int src = __builtin_amdgcn_readfirstlane(s_src[r]);
+    const int src = __builtin_amdgcn_readfirstlane(s_src[r] & ~kDecInvalid);
     gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), kv + (size_t)src * row_stride, buf + r * NOPE_B);
   }
   const int r = 8 * wave + (l >> 3);
-  gll16_a(kv + (size_t)s_src[r] * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
+  gll16_a(kv + (size_t)(s_src[r] & ~kDecInvalid) * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
           buf + kDecRopeOff + wave * 1024);
 }
 
@@ -169,7 +172,6 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
-  __shared__ uint32_t s_mask[kDecMaxCH / kDecRows];
   __shared__ f32x4 s_part[4][64];  // per wave: its half of one S^T tile
 
   const int c = blockIdx.x / HB, hb = blockIdx.x - c * HB, t = blockIdx.y;
@@ -234,8 +236,7 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
       const int fsrc = __shfl(src[p2], first, DSA_WAVE);
       // a stage without any valid selection still stages cache row 0 (read,
       // never used), so that every stage issues the same loads
-      s_src[i] = src[p2] >= 0 ? src[p2] : (mh ? fsrc : 0);
-      if ((l & 31) == 0 && i < nst * kDecRows) s_mask[i / kDecRows] = mh;
+      s_src[i] = src[p2] >= 0 ? src[p2] : ((mh ? fsrc : 0) | kDecInvalid);
     }
   }
   // complete the query loads here: a first use inside the stage loop would
@@ -283,7 +284,8 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     if (st + kDecRing - 1 < nst)
       stage_rows(lds_ring + ((st + kDecRing - 1) % kDecRing) * kDecStage, kv, row_stride,
                  s_src + (st + kDecRing - 1) * kDecRows, wave);
-    const uint32_t mask = s_mask[st];
+    // the stage's validity mask: bit r for selection r of the stage
+    const uint32_t mask = (uint32_t)__ballot(s_src[st * kDecRows + (l & 31)] >= 0);
     if (mask == 0) continue;
     const unsigned char* buf = ring[st % kDecRing];
     // ---- this wave's half of its S^T tile (16 keys), then both tiles summed
