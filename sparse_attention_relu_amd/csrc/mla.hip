@@ -550,6 +550,59 @@ __global__ __launch_bounds__(256) void mla_decode_combine_wide(const uint16_t* _
   }
 }
 
+// Few chunks (nch <= kCombFew), many rows. grid = (ceil(T / kCombRows), ceil(H / 4)),
+// block = 256: wave w merges the partials of head h = 4 blockIdx.y + w for
+// kCombRows consecutive rows, with every load of those rows (each row's nch
+// (m, l) pairs and O chunks) issued before the first reduction; lane l sums
+// value columns 8 l .. 8 l + 7. The merge is that of mla_decode_combine.
+constexpr int kCombFew = 4;
+constexpr int kCombRows = 4;
+
+__global__ __launch_bounds__(256) void mla_decode_combine_rows(const uint16_t* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml,
+                                                               int T, int H, int nch,
+                                                               uint16_t* __restrict__ out) {
+  const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+  if (h >= H) return;  // wave-uniform
+  const int l = lane_id();
+  const int t0 = kCombRows * blockIdx.x;
+  uint4 va[kCombRows][kCombFew];
+  float2 ml[kCombRows][kCombFew];
+#pragma unroll
+  for (int r = 0; r < kCombRows; ++r) {
+    const int t = min(t0 + r, T - 1);  // a row past T reloads the last row, never stored
+#pragma unroll
+    for (int c = 0; c < kCombFew; ++c) {
+      const size_t idx = ((size_t)t * nch + min(c, nch - 1)) * H + h;
+      va[r][c] = *reinterpret_cast<const uint4*>(part_o + idx * DV + 8 * l);
+      ml[r][c] = *reinterpret_cast<const float2*>(part_ml + idx * 2);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kCombRows; ++r) {
+    const int t = t0 + r;
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kCombFew; ++c)
+      if (c < nch && ml[r][c].y > 0.f) M = fmaxf(M, ml[r][c].x);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int c = 0; c < kCombFew; ++c) {
+      const float wc = c < nch && ml[r][c].y > 0.f ? __expf(ml[r][c].x - M) : 0.f;
+      L += wc * (c < nch ? ml[r][c].y : 0.f);
+      fma_bf16x8(acc, wc, va[r][c]);
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    uint4 packed;
+    packed.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    packed.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    packed.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+    packed.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+    if (t < T) *reinterpret_cast<uint4*>(out + ((size_t)t * H + h) * DV + 8 * l) = packed;
+  }
+}
+
 int mla_decode_chunk(int T, int k) {
   // about kDecWPC workgroups per compute unit, 1 .. kDecMaxCH / 64 blocks of
   // 64 selections each: a large batch gets long chunks, which cuts both the
@@ -583,7 +636,11 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ProfScope prof("mla_decode_combine", st);
-  if (nch > kCombAhead)  // many chunks: two thread groups per (row, head) share them
+  if (nch <= kCombFew && a.T >= 1024)  // many rows of few chunks: several rows per wave
+    hipLaunchKernelGGL(mla_decode_combine_rows, dim3((a.T + kCombRows - 1) / kCombRows,
+                                                     (a.H + 3) / 4),
+                       dim3(256), 0, st, a.part_o, a.part_ml, a.T, a.H, nch, a.out);
+  else if (nch > kCombAhead)  // many chunks: two thread groups per (row, head) share them
     hipLaunchKernelGGL(mla_decode_combine_wide, dim3(a.T, a.H), dim3(256), 0, st, a.part_o,
                        a.part_ml, a.H, nch, a.out);
   else
