@@ -261,6 +261,30 @@ def _extend_config(dsa, cid, QB, n_random, n_blocks):
 
 
 @pytest.mark.timeout(600)
+def test_config4_fused_indexer_every_row(dsa):
+    """The chunked extend's indexer through the fused path (scores never
+    stored; one segment per row at T = 4096) equals the score-matrix path
+    on every row, and the oracle on the sampled rows."""
+    torch = torch_mod()
+    wl = W.config(4, with_mla=False)
+    b = wl.batches["extend"]
+    cu = b.cu_q_lens
+    d = Dev(wl, layers=0)
+    bt = d.batch("extend")
+    mql = int(np.diff(cu).max())
+    log("config 4: indexer top-k, score-matrix path and fused path")
+    tk = _topk(dsa, d, bt, wl.k, mql).cpu().numpy()
+    tf = dsa.indexer_topk_fused(bt["q_idx"], bt["w"], d.idx_cache, d.page_table, d.seq_lens,
+                                bt["cu"], wl.k)
+    torch.cuda.synchronize()
+    tf = tf.cpu().numpy()
+    assert np.array_equal(tf, tk), "fused and score-matrix top-k differ"
+    rows = _sample_rows(b.T, cu, 64, 44, wl.seq_lens)
+    exp = _oracle_rows_topk(wl, b, rows)
+    assert np.array_equal(tf[rows], exp[rows]), "fused top-k differs from the oracle"
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("QB", [64, 256])
 def test_config4_chunked_extend(dsa, QB):
     _extend_config(dsa, 4, QB, n_random=256, n_blocks=8)
