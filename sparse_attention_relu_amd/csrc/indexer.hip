@@ -52,6 +52,17 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// The scores of a 64-key block from the per-half head sums of its two
+// 32-key sub-blocks: lane (m, hf) holds p0, the sum over its half's heads
+// for key m, and p1, the same for key 32 + m. One v_permlane32_swap moves p0
+// of the upper half to the lower half and p1 of the lower half to the upper
+// half, so lane l ends up with the score of key l (half 0 + half 1).
+__device__ __forceinline__ float block_scores(float p0, float p1) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float relu_weighted_sum(const f32x16& acc, const float (&wv)[16]) {
   float part = 0.0f;
 #pragma unroll
@@ -482,8 +493,7 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 // weights in registers) and a range of up to kTileMaxRK key positions. The
 // keys stream through a four-stage LDS ring of 64-key blocks by direct
 // global->LDS loads (three blocks in flight while one is multiplied), in the
-// swizzled layout of the streaming scorer, and every staged block serves all
-// 8 rows. A wave stores its row's 64 scores of a block with one instruction
+// row-group layout of TileLayout, and every staged block serves all 8 rows. A wave stores its row's 64 scores of a block with one instruction
 // (lane l: key l), so the waits on the ring count every outstanding memory
 // operation exactly: the key loads of later blocks plus the stores of the
 // last three blocks. Rows of a tile may belong to several sequences: the
@@ -495,8 +505,68 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 // grid = (ceil(cap / kTileMaxRK), ceil(T / 8)), block = 512.
 // ---------------------------------------------------------------------------
 constexpr int kTileMaxRK = 2048;  // key range of one tile workgroup
-constexpr int kTileRows = 8;      // rows per workgroup, one per wave
+// Rows per workgroup, one per wave. The score-matrix scorer takes 8 (two
+// workgroups per compute unit). The fused scorer takes 16 with one head
+// block, so that every staged block serves 16 rows and each wave issues one
+// direct load per block, and 8 with two (their query fragments need twice
+// the registers).
+constexpr int kTileRows = 8;
+template <int HB>
+constexpr int fused_rows() { return HB == 1 ? 16 : 8; }
 constexpr int kTileKB = 64;       // keys per staged block
+
+// Staged block layout of the tile scorers. One direct load fills 1024 LDS
+// bytes with RPI = 1024 / (2 D) consecutive key rows, a row group: slot s of
+// the group holds 16-byte chunk s / RPI of row s % RPI (chunk-major), and
+// consecutive groups start GS = 1024 + 16 RPI bytes apart. The fragment a
+// lane reads for k-step i is then its own base address plus 16 RPI i, an
+// immediate offset of the LDS read, so the reads of a block need no address
+// arithmetic. A read phase (8 or 16 consecutive lanes: rows m .. m + 15 at
+// one chunk) hits distinct banks: the rows of a group are contiguous, and
+// each further group is shifted by 16 RPI bytes modulo 256.
+// Page-table entries of a key range kept in registers: entry pg0 + 64 c + i
+// of the range in lane i of pgv[c]. A direct load's source page is read back
+// with v_readlane at a wave-uniform index, so staging a block needs no LDS
+// round trip (an LDS read there queued behind the key fragment reads of all
+// the other waves).
+constexpr int kTilePgRegs = (kTileMaxRK / 16 + 1 + 63) / 64;
+
+__device__ __forceinline__ void load_page_regs(const int32_t* __restrict__ ptrow, int n, int l,
+                                               int (&pgv)[kTilePgRegs]) {
+#pragma unroll
+  for (int c = 0; c < kTilePgRegs; ++c) {
+    const int i = 64 * c + l;
+    pgv[c] = i < n ? ptrow[i] : 0;
+  }
+}
+
+// entry p (wave-uniform, p < 64 kTilePgRegs)
+__device__ __forceinline__ int page_reg(const int (&pgv)[kTilePgRegs], int p) {
+  int v = __builtin_amdgcn_readlane(pgv[0], p & 63);
+#pragma unroll
+  for (int c = 1; c < kTilePgRegs; ++c)
+    if (p >= 64 * c) v = __builtin_amdgcn_readlane(pgv[c], p & 63);
+  return v;
+}
+
+template <int D>
+struct TileLayout {
+  static constexpr int RB = 2 * D;                  // bytes per key row
+  static constexpr int RPI = 1024 / RB;             // rows per group (per load)
+  static constexpr int GS = 1024 + 16 * RPI;        // group stride
+  static constexpr int NLB = kTileKB * RB / 1024;   // groups (loads) per block
+  static constexpr int BLK = NLB * GS;              // bytes per staged block
+  static constexpr int SUB = (32 / RPI) * GS;       // bytes per 32 rows
+  // lane l of a load fetches chunk l / RPI of group row l % RPI
+  static __device__ __forceinline__ uint32_t load_off(int l) {
+    return (uint32_t)((l % RPI) * RB + 16 * (l / RPI));
+  }
+  // base of lane (m, hf)'s fragments: row m of a 32-row sub-block, the
+  // chunks of contraction half hf
+  static __device__ __forceinline__ int read_base(int m, int hf) {
+    return (m / RPI) * GS + 16 * (m % RPI) + 16 * RPI * (hf * (D / 16));
+  }
+};
 constexpr int kTileRing = 4;
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in 0 .. 15
@@ -522,26 +592,27 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
 }
 
 template <int D, int HB, bool EXT>
-__global__ __launch_bounds__(512, 2) void idx_score_tiles(
+__global__ __launch_bounds__(64 * kTileRows, 2) void idx_score_tiles(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
     int PS, int MP, float* __restrict__ scores, long ld, uint2* __restrict__ ext, int ext_ld) {
-  constexpr int KS = D / 16, HALF = D / 2, RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;
-  constexpr int BLK = kTileKB * RB;      // bytes per staged block
-  constexpr int NLB = BLK / 1024;        // direct loads per block (D / 8)
-  constexpr int NLW = (NLB + 7) / 8;     // at most this many per wave
+  using TL = TileLayout<D>;
+  constexpr int KS = D / 16, HALF = D / 2, RPI = TL::RPI;
+  constexpr int BLK = TL::BLK;           // bytes per staged block
+  constexpr int NLB = TL::NLB;           // direct loads per block (D / 8)
+  constexpr int R = kTileRows;
+  constexpr int NLW = (NLB + R - 1) / R;  // at most this many per wave
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kTileRing][BLK];
-  __shared__ int s_pg[kTileMaxRK / 16 + 1];  // page-table entries of the key range
-  __shared__ int s_seq[kTileRows], s_nv[kTileRows];
+  __shared__ int s_seq[R], s_nv[R];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int m = l & 31, hf = l >> 5;
-  const int t0 = blockIdx.y * kTileRows;
+  const int t0 = blockIdx.y * R;
   const int cap = MP * PS;
-  if (tid < kTileRows) {
+  if (tid < R) {
     const int t = t0 + tid;
     RowInfo ri;
     ri.seq = -1;
@@ -553,21 +624,21 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
   __syncthreads();
   const int k0 = blockIdx.x * kTileMaxRK;
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
-  const int lr = l / CPR, lc = l % CPR;
-  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+  const uint32_t voff = TL::load_off(l);
+  const int rbase = TL::read_base(m, hf);
 
   int seg = 0;
-  while (seg < kTileRows) {
+  while (seg < R) {
     const int s = __builtin_amdgcn_readfirstlane(s_seq[seg]);
     int seg_end = seg + 1;
-    while (seg_end < kTileRows && s_seq[seg_end] == s) ++seg_end;
+    while (seg_end < R && s_seq[seg_end] == s) ++seg_end;
     seg_end = __builtin_amdgcn_readfirstlane(seg_end);
     const int n_hi = s >= 0 ? __builtin_amdgcn_readfirstlane(s_nv[seg_end - 1]) : 0;
     const int k1 = min(k0 + kTileMaxRK, n_hi);
     if (s >= 0 && k0 < k1) {
-      const int32_t* ptrow = pt + (size_t)s * MP;
       const int pg0 = k0 / PS;
-      for (int i = tid; i <= (k1 - 1) / PS - pg0; i += 512) s_pg[i] = ptrow[pg0 + i];
+      int pgv[kTilePgRegs];
+      load_page_regs(pt + (size_t)s * MP + pg0, (k1 - 1) / PS - pg0 + 1, l, pgv);
       // this wave's row, if it belongs to the segment
       const int r = wave;
       const int nv = s_nv[r];
@@ -591,27 +662,27 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
 #pragma unroll
         for (int i = 0; i < 16; ++i) asm volatile("" : : "v"(wv[hb][i]));
       }
-      __syncthreads();  // s_pg ready
+#pragma unroll
+      for (int c = 0; c < kTilePgRegs; ++c) asm volatile("" : : "v"(pgv[c]));
 
       const int nb = (k1 - k0 + kTileKB - 1) / kTileKB;
-      const int nlw = wave < NLB % 8 || NLB % 8 == 0 ? NLW : NLW - 1;  // this wave's loads per block
-      // direct loads of block b: load I = wave + 8 n covers rows I * RPI .. of the block
+      const int nlw = wave < NLB % R || NLB % R == 0 ? NLW : NLW - 1;  // this wave's loads per block
+      // direct loads of block b: load I = wave + R n covers rows I * RPI .. of the block
       auto stage = [&](int b) {
         const uint32_t buf = lds_ring + (b % kTileRing) * BLK;
 #pragma unroll
         for (int n = 0; n < NLW; ++n) {
-          const int I = wave + 8 * n;
+          const int I = wave + R * n;
           if (I < NLB) {
             int j0 = k0 + b * kTileKB + I * RPI;
             if (j0 >= k1) j0 = k0;  // past the range: any staged row, never stored
-            const int page = clamp_page(s_pg[j0 / PS - pg0], num_pages);
+            const int page = clamp_page(page_reg(pgv, j0 / PS - pg0), num_pages);
             const uint64_t src =
                 (uint64_t)(uintptr_t)(cache + ((size_t)page * PS + (j0 % PS)) * D);
             const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
             const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
-            gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
-                      (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
-                      __builtin_amdgcn_readfirstlane(buf + I * 1024));
+            gll16_idx(voff, (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                      __builtin_amdgcn_readfirstlane(buf + I * TL::GS));
           }
         }
       };
@@ -636,14 +707,11 @@ __global__ __launch_bounds__(512, 2) void idx_score_tiles(
         float sc[kTileKB / 32];
 #pragma unroll
         for (int sb = 0; sb < kTileKB / 32; ++sb) {
-          const int kr = sb * 32 + m;
           bf16x8 bk[KS];
 #pragma unroll
-          for (int i = 0; i < KS; ++i) {
-            const int chunk = hf * HALF / 8 + i;
-            bk[i] = as_bf16x8(
-                *reinterpret_cast<const uint4*>(buf + kr * RB + 16 * (chunk ^ (kr % CPR))));
-          }
+          for (int i = 0; i < KS; ++i)
+            bk[i] = as_bf16x8(*reinterpret_cast<const uint4*>(buf + rbase + sb * TL::SUB +
+                                                             16 * RPI * i));
           float part = 0.0f;
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb) {
@@ -1464,14 +1532,15 @@ static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
 template <int D, int HB>
 static hipError_t launch_tiles(const IndexerArgs& a, hipStream_t st) {
   const int cap = a.MP * a.PS;
-  dim3 grid((cap + kTileMaxRK - 1) / kTileMaxRK, (a.T + kTileRows - 1) / kTileRows);
+  constexpr int R = kTileRows;
+  dim3 grid((cap + kTileMaxRK - 1) / kTileMaxRK, (a.T + R - 1) / R);
   ProfScope prof("idx_score_tiles", st);
   if (a.ext != nullptr)
-    hipLaunchKernelGGL((idx_score_tiles<D, HB, true>), grid, dim3(512), 0, st, a.q, a.w,
+    hipLaunchKernelGGL((idx_score_tiles<D, HB, true>), grid, dim3(64 * R), 0, st, a.q, a.w,
                        a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP,
                        a.scores, a.ld, a.ext, a.ext_ld);
   else
-    hipLaunchKernelGGL((idx_score_tiles<D, HB, false>), grid, dim3(512), 0, st, a.q, a.w,
+    hipLaunchKernelGGL((idx_score_tiles<D, HB, false>), grid, dim3(64 * R), 0, st, a.q, a.w,
                        a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS, a.MP,
                        a.scores, a.ld, nullptr, 0);
   return hipGetLastError();
@@ -1651,11 +1720,16 @@ hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t
 // kernel note: token scores of that size are the dominant temporary at long
 // context).
 //
-// idx_score_topk: a workgroup of 8 waves owns 8 consecutive packed rows (one
-// per wave, query fragments and head weights resident, as idx_score_tiles)
-// and one segment of the key positions, which it walks in ascending order:
-// ranges of kTileMaxRK positions, each streamed through the same four-stage
-// ring of 64-key blocks and shared by the rows of one sequence. Every wave
+// idx_score_topk: a workgroup of R waves (fused_rows: 16 with one head
+// block) owns R consecutive packed rows (one per wave, query fragments and
+// head weights resident, as idx_score_tiles) and one segment of the key
+// positions, which it walks in ascending order: ranges of kTileMaxRK
+// positions, each streamed through a ring of 64-key blocks in the row-group
+// layout and shared by the rows of one sequence. With 16 rows a workgroup
+// scores two blocks between barriers (a ring of five: three blocks in flight
+// beyond the two being scored), and computes both blocks' scores before it
+// takes their keys, so that head sums and products of neighbouring
+// sub-blocks overlap. Every wave
 // keeps its row's candidates of the segment in a global list of C entries
 // (order key, position), appending each scored key above the row's bar.
 // When the next block might not fit, the wave compacts the list to exactly k
@@ -1674,7 +1748,7 @@ hipError_t page_tokens(const int32_t* pages, int T, int k_pages, int PS, int32_t
 // digit per pass with a 256-bin LDS histogram per wave, then an
 // order-keeping pass; list reads bypass the vector L1 (agent-scope loads),
 // so they see the wave's own earlier list stores.
-// grid = (G segments of L positions, ceil(T / 8)), block = 512.
+// grid = (G segments of L positions, ceil(T / R)), block = 64 R.
 //
 // topk_merge: one workgroup per row sorts the G lists of the row (at most
 // G * k <= kMergeMax entries) by composite key (order key << 32 | ~position)
@@ -1876,29 +1950,38 @@ __device__ int list_cut_rebin(uint2* list, int cnt, uint32_t theta, int shift, u
 }
 
 template <int D, int HB>
-__global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
+__global__ __launch_bounds__(64 * fused_rows<HB>(), HB == 1 ? 4 : 2) void idx_score_topk(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
     int PS, int MP, int k, int G, int L, int C, uint2* __restrict__ cand,
     int* __restrict__ cand_cnt) {
-  constexpr int KS = D / 16, HALF = D / 2, RB = 2 * D, CPR = D / 8, RPI = 1024 / RB;
-  constexpr int BLK = kTileKB * RB;      // bytes per staged block
-  constexpr int NLB = BLK / 1024;        // direct loads per block (D / 8)
-  constexpr int NLW = (NLB + 7) / 8;     // at most this many per wave
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kTileRing][BLK];
-  __shared__ int s_pg[kTileMaxRK / 16 + 1];
-  __shared__ int s_seq[kTileRows], s_nv[kTileRows];
-  __shared__ uint32_t s_hist[kTileRows][256];
+  using TL = TileLayout<D>;
+  constexpr int KS = D / 16, HALF = D / 2, RPI = TL::RPI;
+  constexpr int BLK = TL::BLK;           // bytes per staged block
+  constexpr int NLB = TL::NLB;           // direct loads per block (D / 8)
+  constexpr int R = fused_rows<HB>();
+  constexpr int NLW = (NLB + R - 1) / R;  // at most this many per wave
+  // blocks scored between two barriers, and the ring: three blocks in flight
+  // beyond the ones being scored
+  constexpr int BPI = R == 16 ? 2 : 1;
+  constexpr int RING = 3 + BPI;
+  // iterations whose list stores were issued after the last load of the
+  // blocks an iteration waits for
+  constexpr int SI = BPI == 1 ? 3 : 1;
+  constexpr int kCutSoonB = kCutSoon + 64 * (BPI - 1);
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[RING][BLK];
+  __shared__ int s_seq[R], s_nv[R];
+  __shared__ uint32_t s_hist[R][256];
   __shared__ int s_cutreq[2];  // by block parity: the block in which waves are to cut
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = lane_id();
   const int m = l & 31, hf = l >> 5;
-  const int t0 = blockIdx.y * kTileRows;
+  const int t0 = blockIdx.y * R;
   const int cap = MP * PS;
-  if (tid < kTileRows) {
+  if (tid < R) {
     const int t = t0 + tid;
     RowInfo ri;
     ri.seq = -1;
@@ -1925,11 +2008,11 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
   // 2^win_shift keys from win_base (= the bar), the last bin open above
   uint32_t win_base = 0u;
   int win_shift = 0;
-  int gblk = 0;  // blocks walked so far (the same in every wave)
+  int gblk = 0;  // iterations walked so far (the same in every wave)
   // Cut the list: at the lower edge of the window bin that holds the k-th key
   // when that keeps at most k + (C - k) / 2 entries, else exactly to k. Every
   // list key is >= win_base (the bar, or the minimum before the first cut).
-  auto cut_list = [&]() {
+  auto cut_list = [&]() __attribute__((always_inline)) {
     const uint32_t hi = wave_max_u32(key_hi);
     if (!barred) {  // the first cut: a window over the keys seen so far
       win_base = wave_min_u32(key_lo);
@@ -1971,102 +2054,86 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
     for (int i = 0; i < 16; ++i) asm volatile("" : : "v"(wv[hb][i]));
   }
   const uint32_t lds_ring = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring[0];
-  const int lr = l / CPR, lc = l % CPR;
-  const uint32_t voff = (uint32_t)(lr * RB + 16 * (lc ^ (lr % CPR)));
+  const uint32_t voff = TL::load_off(l);
+  const int rbase = TL::read_base(m, hf);
 
   for (int k0 = seg0; k0 < seg1; k0 += kTileMaxRK) {
     int seg = 0;
-    while (seg < kTileRows) {
+    while (seg < R) {
       const int s = __builtin_amdgcn_readfirstlane(s_seq[seg]);
       int seg_end = seg + 1;
-      while (seg_end < kTileRows && s_seq[seg_end] == s) ++seg_end;
+      while (seg_end < R && s_seq[seg_end] == s) ++seg_end;
       seg_end = __builtin_amdgcn_readfirstlane(seg_end);
       const int n_hi = s >= 0 ? __builtin_amdgcn_readfirstlane(s_nv[seg_end - 1]) : 0;
       const int k1 = min(min(k0 + kTileMaxRK, n_hi), seg1);
       if (s >= 0 && k0 < k1) {
-        const int32_t* ptrow = pt + (size_t)s * MP;
         const int pg0 = k0 / PS;
-        for (int i = tid; i <= (k1 - 1) / PS - pg0; i += 512) s_pg[i] = ptrow[pg0 + i];
+        int pgv[kTilePgRegs];
+        load_page_regs(pt + (size_t)s * MP + pg0, (k1 - 1) / PS - pg0 + 1, l, pgv);
+#pragma unroll
+        for (int c = 0; c < kTilePgRegs; ++c) asm volatile("" : : "v"(pgv[c]));
         const bool act = has && wave >= seg && wave < seg_end && my_nv > k0;
         const int nv = min(my_nv, seg1);
-        __syncthreads();  // s_pg ready
 
         const int nb = (k1 - k0 + kTileKB - 1) / kTileKB;
-        const int nlw = wave < NLB % 8 || NLB % 8 == 0 ? NLW : NLW - 1;
+        const int nlw = wave < NLB % R || NLB % R == 0 ? NLW : NLW - 1;
         auto stage = [&](int b) {
-          const uint32_t buf = lds_ring + (b % kTileRing) * BLK;
+          const uint32_t buf = lds_ring + (b % RING) * BLK;
 #pragma unroll
           for (int n = 0; n < NLW; ++n) {
-            const int I = wave + 8 * n;
+            const int I = wave + R * n;
             if (I < NLB) {
               int j0 = k0 + b * kTileKB + I * RPI;
               if (j0 >= k1) j0 = k0;  // past the range: any staged row, never used
-              const int page = clamp_page(s_pg[j0 / PS - pg0], num_pages);
+              const int page = clamp_page(page_reg(pgv, j0 / PS - pg0), num_pages);
               const uint64_t src =
                   (uint64_t)(uintptr_t)(cache + ((size_t)page * PS + (j0 % PS)) * D);
               const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)src);
               const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(src >> 32));
-              gll16_idx(voff ^ (uint32_t)(16 * ((I * RPI) % CPR)),
-                        (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
-                        __builtin_amdgcn_readfirstlane(buf + I * 1024));
+              gll16_idx(voff, (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo),
+                        __builtin_amdgcn_readfirstlane(buf + I * TL::GS));
             }
           }
         };
+        // list stores per iteration, four bits each, the last iteration lowest
+        int sh = 0;
+        // scores of block b: lane l gets key l
+        auto score_block = [&](int b) __attribute__((always_inline)) -> float {
+          const unsigned char* buf = ring[b % RING];
+          float p[2];
 #pragma unroll
-        for (int b = 0; b < kTileRing - 1; ++b)
-          if (b < nb) stage(b);
-        int hist = 0;  // bit i: this wave stored list entries i + 1 iterations ago
-        for (int b = 0; b < nb; ++b) {
-          const int later = min(kTileRing - 2, nb - 1 - b);
-          wait_vm_dyn(later * nlw + __popc(hist & 7));
-          lds_sync();  // block b has landed for every wave; block b - 1 is consumed
-          if (b + kTileRing - 1 < nb) stage(b + kTileRing - 1);
-          hist <<= 1;
-          // a cut asked for during the previous block: every wave whose list is
-          // a quarter full above k cuts now, so that the waves of the
-          // workgroup wait at the barrier for one cut rather than one each
-          const bool cut_asked = s_cutreq[gblk & 1] == gblk;
-          ++gblk;
-          if (!act || k0 + b * kTileKB >= nv) continue;  // wave-uniform
-          if (cut_asked && cnt > k + (C - k) / 4) {
-            cut_list();
-            hist = 0;
-          }
-          const unsigned char* buf = ring[b % kTileRing];
-          float sc[kTileKB / 32];
-#pragma unroll
-          for (int sb = 0; sb < kTileKB / 32; ++sb) {
-            const int kr = sb * 32 + m;
+          for (int sb = 0; sb < 2; ++sb) {
             bf16x8 bk[KS];
 #pragma unroll
-            for (int i = 0; i < KS; ++i) {
-              const int chunk = hf * HALF / 8 + i;
+            for (int i = 0; i < KS; ++i)
               bk[i] = as_bf16x8(
-                  *reinterpret_cast<const uint4*>(buf + kr * RB + 16 * (chunk ^ (kr % CPR))));
-            }
-            float part = 0.0f;
+                  *reinterpret_cast<const uint4*>(buf + rbase + sb * TL::SUB + 16 * RPI * i));
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
               f32x16 acc = {};
 #pragma unroll
               for (int i = 0; i < KS; ++i)
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][i], bk[i], acc, 0, 0, 0);
-              part += relu_weighted_sum(acc, wv[hb]);
+              const float r = relu_weighted_sum(acc, wv[hb]);
+              p[sb] = hb == 0 ? r : p[sb] + r;
             }
-            sc[sb] = part + shfl_xor_f(part, 32);  // both lane halves hold key sb * 32 + m
           }
-          // lane l holds key l of the block
+          return block_scores(p[0], p[1]);
+        };
+        // take block b's keys (lane l: score v of key l) into the list;
+        // returns the list stores issued (0 or 1)
+        auto take_block = [&](int b, float v) __attribute__((always_inline)) -> int {
           const int j = k0 + b * kTileKB + l;
-          const uint32_t key = score_order_bits(hf ? sc[1] : sc[0]);
+          const uint32_t key = score_order_bits(v);
           bool take = j < nv && (!barred || key > bar);
           uint64_t bal = __ballot(take);
-          if (bal == 0ull) continue;
+          if (bal == 0ull) return 0;
           if (cnt + __popcll(bal) > C) {  // no room (cnt > C - 64 > k): cut the list
             cut_list();
-            hist = 0;  // the cut waited for every outstanding operation
+            sh = 0;  // the cut waited for every outstanding operation
             take = take && key > bar;
             bal = __ballot(take);
-            if (bal == 0ull) continue;
+            if (bal == 0ull) return 0;
           }
           if (take) {
             list[cnt + ballot_rank(bal)] = make_uint2(key, (uint32_t)j);
@@ -2075,10 +2142,53 @@ __global__ __launch_bounds__(512, HB == 1 ? 4 : 2) void idx_score_topk(
             if (barred) atomicAdd(&s_hist[wave][window_bin(key, win_base, win_shift)], 1u);
           }
           cnt += __popcll(bal);
-          hist |= 1;
-          if (cnt > C - kCutSoon) s_cutreq[gblk & 1] = gblk;  // ask for a cut next block
+          if (cnt > C - kCutSoonB) s_cutreq[gblk & 1] = gblk;  // ask for a cut next iteration
+          return 1;
+        };
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+          if (b < nb) stage(b);
+        for (int b = 0; b < nb; b += BPI) {
+          // outstanding after the last load of blocks b .. b + BPI - 1: the
+          // loads of the blocks staged after it and the list stores of the
+          // last SI iterations
+          const int later = min(RING - 2 * BPI, max(nb - b - BPI, 0));
+          int pend = 0;
+#pragma unroll
+          for (int i = 0; i < SI; ++i) pend += (sh >> (4 * i)) & 15;
+          wait_vm_dyn(later * nlw + pend);
+          lds_sync();  // blocks b .. b + BPI - 1 have landed; the previous ones are consumed
+#pragma unroll
+          for (int i = 0; i < BPI; ++i)
+            if (b + 3 + i < nb) stage(b + 3 + i);
+          sh <<= 4;
+          // a cut asked for during the previous iteration: every wave whose
+          // list is a quarter full above k cuts now, so that the waves of the
+          // workgroup wait at the barrier for one cut rather than one each
+          const bool cut_asked = s_cutreq[gblk & 1] == gblk;
+          ++gblk;
+          if (!act || k0 + b * kTileKB >= nv) continue;  // wave-uniform
+          if (cut_asked && cnt > k + (C - k) / 4) {
+            cut_list();
+            sh = 0;
+          }
+          // the scores of the iteration's blocks first (straight-line code,
+          // so that the head sums of one sub-block overlap the products of
+          // the next), then their keys in position order
+          const int nbk =
+              min(min(BPI, nb - b), (nv - k0 - b * kTileKB + kTileKB - 1) / kTileKB);  // >= 1
+          // (a block past the row's range scores whatever its ring slot
+          // holds, never taken: no branch between the products)
+          float v[BPI];
+#pragma unroll
+          for (int i = 0; i < BPI; ++i) v[i] = score_block(b + i);
+          int ns = 0;
+#pragma unroll
+          for (int i = 0; i < BPI; ++i)
+            if (i < nbk) ns += take_block(b + i, v[i]);
+          sh |= ns;
         }
-        __syncthreads();  // the ring and s_pg are free for the next pass
+        __syncthreads();  // the ring is free for the next pass
       }
       seg = seg_end;
     }
@@ -2196,7 +2306,7 @@ __global__ __launch_bounds__(kMergeNT) void topk_order(const uint2* __restrict__
 }
 
 void fused_plan(int T, int cap, int k, int* G, int* L, int* C) {
-  const int nrt = (T + kTileRows - 1) / kTileRows;
+  const int nrt = (T + 15) / 16;  // row tiles of 16 (of 8 with two head blocks: twice as many)
   const int gmax_k = kMergeMax / k < 8 ? kMergeMax / k : 8;
   const int gmax_cap = (cap + kTileMaxRK - 1) / kTileMaxRK;
   int g = (512 + nrt - 1) / nrt;
@@ -2219,9 +2329,10 @@ static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
   fused_plan(a.T, a.MP * a.PS, a.k, &G, &L, &C);
   {
     ProfScope prof("idx_score_topk", st);
-    hipLaunchKernelGGL((idx_score_topk<D, HB>), dim3(G, (a.T + kTileRows - 1) / kTileRows),
-                       dim3(512), 0, st, a.q, a.w, a.cache, a.num_pages, a.pt, a.seq_lens, a.cu,
-                       a.T, a.S, a.H, a.PS, a.MP, a.k, G, L, C, a.cand, a.cand_cnt);
+    constexpr int R = fused_rows<HB>();
+    hipLaunchKernelGGL((idx_score_topk<D, HB>), dim3(G, (a.T + R - 1) / R), dim3(64 * R), 0, st,
+                       a.q, a.w, a.cache, a.num_pages, a.pt, a.seq_lens, a.cu, a.T, a.S, a.H, a.PS,
+                       a.MP, a.k, G, L, C, a.cand, a.cand_cnt);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
