@@ -2180,8 +2180,12 @@ __global__ __launch_bounds__(64 * fused_rows<HB>(), HB == 1 ? 4 : 2) void idx_sc
           // (a block past the row's range scores whatever its ring slot
           // holds, never taken: no branch between the products)
           float v[BPI];
+          // the products of this wave go first when waves compete for issue
+          // (the other waves' head sums and list work fill the gaps)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int i = 0; i < BPI; ++i) v[i] = score_block(b + i);
+          __builtin_amdgcn_s_setprio(0);
           int ns = 0;
 #pragma unroll
           for (int i = 0; i < BPI; ++i)
