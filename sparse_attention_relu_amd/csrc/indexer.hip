@@ -2313,7 +2313,9 @@ void fused_plan(int T, int cap, int k, int* G, int* L, int* C) {
   const int nrt = (T + 15) / 16;  // row tiles of 16 (of 8 with two head blocks: twice as many)
   const int gmax_k = kMergeMax / k < 8 ? kMergeMax / k : 8;
   const int gmax_cap = (cap + kTileMaxRK - 1) / kTileMaxRK;
-  int g = (512 + nrt - 1) / nrt;
+  // about one workgroup per compute unit (a 16-row workgroup fills one);
+  // more segments cost a merge of their lists per row
+  int g = (256 + nrt - 1) / nrt;
   if (g > gmax_k) g = gmax_k;
   if (g > gmax_cap) g = gmax_cap;
   if (g < 1) g = 1;
