@@ -158,6 +158,32 @@ def _timed(step, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def _graph_timed(step, steps, warmup):
+    """ms per replay of one step captured as a HIP graph (torch.cuda.CUDAGraph):
+    the step's launches are replayed as one submission. The step runs eagerly
+    first, so that one-time state (kernel attributes, static scratch) is set
+    outside the capture; every buffer it uses is preallocated."""
+    import torch
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def _kernel_times(dsa, step, steps):
     """{kernel: (launches per step, average ms per launch)} over `steps`
     steps, from the library's per-launch HIP events (recorded on the launch
@@ -342,6 +368,7 @@ def bench_decode(dsa, wl, steps, warmup, reps):
     kt = _kernel_times(dsa, step, steps)
     warm = _kernel_stats(dsa, step, reps, cold=False)
     cold = _kernel_stats(dsa, step, reps, cold=True)
+    ms_graph = _graph_timed(step, steps, warmup)
 
     nval = _row_valid_counts(wl, b.cu_q_lens)
     n_sel = int((topk >= 0).sum())
@@ -363,6 +390,8 @@ def bench_decode(dsa, wl, steps, warmup, reps):
                  for i in range(reps)]
     return {"workload": wl.name, "seqs": wl.S, "tokens": int(wl.seq_lens.sum()),
             "tok_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 5),
+            "graph": {"ms_per_step": round(ms_graph, 5), "tok_s": round(T / (ms_graph * 1e-3), 1),
+                      "note": "the same step captured once as a HIP graph and replayed"},
             "indexer_ms": round(part(INDEXER_KERNELS), 5),
             "attend_ms": round(part(("mla_decode_partial", "mla_decode_combine",
                                      "mla_decode_combine_wide")), 5),
