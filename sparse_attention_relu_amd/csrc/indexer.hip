@@ -493,7 +493,8 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 // weights in registers) and a range of up to kTileMaxRK key positions. The
 // keys stream through a four-stage LDS ring of 64-key blocks by direct
 // global->LDS loads (three blocks in flight while one is multiplied), in the
-// row-group layout of TileLayout, and every staged block serves all 8 rows. A wave stores its row's 64 scores of a block with one instruction
+// row-group layout of TileLayout, and every staged block serves all 8 rows.
+// A wave stores its row's 64 scores of a block with one instruction
 // (lane l: key l), so the waits on the ring count every outstanding memory
 // operation exactly: the key loads of later blocks plus the stores of the
 // last three blocks. Rows of a tile may belong to several sequences: the
