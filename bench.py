@@ -784,20 +784,20 @@ def main(argv=None):
         return 0
     if args.only in ("decode", "ragged"):
         wl = W.config(2 if args.only == "decode" else 3)
-        r = bench_decode(dsa, wl, max(args.steps, 20), args.warmup, reps or 20)
+        r = bench_decode(dsa, wl, max(args.steps, 20), args.warmup, reps or 50)
         print(json.dumps({"only": args.only, **r}), flush=True)
         return 0
     if args.only == "extend":
         wl = W.config(4)
         r = bench_extend_workload(dsa, wl, max(2, args.steps // 2), min(args.warmup, 2),
-                                  reps or 5)
+                                  reps or 20)
         print(json.dumps({"only": "extend", **r}), flush=True)
         return 0
 
     _log("long-context workload: generating")
     wl5 = W.config(5)
     _log("long-context workload: timing")
-    lng = bench_extend_workload(dsa, wl5, args.steps, args.warmup, reps or 3)
+    lng = bench_extend_workload(dsa, wl5, args.steps, args.warmup, reps or 20)
     main_step = lng["steps"]["locality"]
     result = {
         "metric": METRIC,
@@ -827,13 +827,13 @@ def main(argv=None):
         del wl5
         _log("decode batch")
         result["decode_batch"] = bench_decode(dsa, W.config(2), max(20, 2 * args.steps),
-                                              args.warmup, reps or 20)
+                                              args.warmup, reps or 50)
         _log("ragged decode")
         result["ragged_decode"] = bench_decode(dsa, W.config(3), max(20, 2 * args.steps),
-                                               args.warmup, reps or 20)
+                                               args.warmup, reps or 50)
         _log("chunked extend")
         result["chunked_extend"] = bench_extend_workload(dsa, W.config(4), max(4, args.steps),
-                                                         args.warmup, reps or 5)
+                                                         args.warmup, reps or 20)
         result["copy_kernel"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         _log("cpu baseline")
