@@ -281,7 +281,11 @@ int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t*
  * products, fp32 accumulation, bf16 output. Empty V or a row outside every
  * sequence gives zeros. Selections must be duplicate-free (a duplicate would
  * be counted twice). Any ragged layout is accepted; "decode" names the
- * per-row execution (split over the selection list, then a combine).
+ * per-row execution: each row's selection list is split into chunks of up
+ * to 2048 entries, sized so that about 512 workgroups exist, and a combine
+ * merges the chunks' partials; when every list is one chunk (large
+ * batches) the attention writes the output itself and
+ * dsa_sparse_mla_decode_workspace returns 0 (workspace may then be NULL).
  *
  *   q          bf16 [T, H, 576]  = [q_nope absorbed (512) | q_rope (64)]
  *   kv_cache   bf16 [num_pages, PS, row_stride], row_stride >= 576

@@ -68,6 +68,7 @@ bool use_fused(int T, int MP, int PS, int max_q_len) {
 size_t decode_ws(int T, int H, int k) {
   const int ch = dsa::mla_decode_chunk(T, k);
   const size_t nch = (size_t)((k + ch - 1) / ch);
+  if (nch == 1) return 0;  // one chunk per row: the kernel writes the output itself
   return align256((size_t)T * nch * H * 512 * 2) + align256((size_t)T * nch * H * 2 * 4);
 }
 
@@ -406,7 +407,7 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   if (!page_table || !seq_lens || !cu_q_lens || !topk)
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const size_t need = dsa_sparse_mla_decode_workspace(T, H, k);
-  if (!workspace || workspace_bytes < need)
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", workspace_bytes, need);
   const int ch = dsa::mla_decode_chunk(T, k);
   const size_t nch = (size_t)((k + ch - 1) / ch);
@@ -422,9 +423,11 @@ int dsa_sparse_mla_decode(const void* q, const void* kv_cache, int row_stride, i
   a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = static_cast<uint16_t*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256((size_t)T * nch * H * 512 * 2));
+  if (need > 0) {  // split rows: partials in the workspace
+    a.part_o = static_cast<uint16_t*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256((size_t)T * nch * H * 512 * 2));
+  }
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 
@@ -500,7 +503,7 @@ int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_str
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const int k = k_pages * PS;
   const size_t need = dsa_sparse_mla_decode_workspace(T, H, k);
-  if (!workspace || workspace_bytes < need)
+  if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "decode workspace %zu < %zu bytes", workspace_bytes, need);
   const int ch = dsa::mla_decode_chunk(T, k);
   const size_t nch = (size_t)((k + ch - 1) / ch);
@@ -517,9 +520,11 @@ int dsa_sparse_mla_decode_pages(const void* q, const void* kv_cache, int row_str
   a.T = T; a.S = S; a.H = H; a.k = k; a.PS = PS; a.MP = MP;
   a.sm_scale = sm_scale;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = static_cast<uint16_t*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       align256((size_t)T * nch * H * 512 * 2));
+  if (need > 0) {  // split rows: partials in the workspace
+    a.part_o = static_cast<uint16_t*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         align256((size_t)T * nch * H * 512 * 2));
+  }
   return hip_status(dsa::mla_decode(a, static_cast<hipStream_t>(stream)), "decode launch");
 }
 

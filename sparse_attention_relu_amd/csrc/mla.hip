@@ -108,11 +108,16 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 // ---------------------------------------------------------------------------
 // Decode: grid = (nch * HB, T), block = 256, two workgroups per compute unit.
 // Workgroup (c, hb, t) attends row t over selections [c * CH, (c + 1) * CH)
-// for heads 16 hb .. 16 hb + 15 and leaves its partial (max m, sum l,
-// unnormalised O) per head for the combine kernel. The source slot of every
-// selection is resolved first; stages of 32 selected rows then stream through
-// a two-stage LDS ring (the next stage in flight while one is used), staged
-// like an extend page. Two resident workgroups per compute unit keep two
+// for heads 16 hb .. 16 hb + 15. With several chunks per row it leaves its
+// partial (max m, sum l, unnormalised O) per head for the combine kernel;
+// with one (CH = k, large batches) it writes the normalised output itself
+// and no combine runs. The source slot of every selection is resolved first;
+// stages of 32 selected rows then stream through a two-stage LDS ring (the
+// next stage in flight while one is used): the 512 nope columns of a row by
+// direct loads, staged like an extend page, and the 64 rope columns into the
+// registers of the odd waves, whose half of the contraction ends with the
+// two rope steps (so the ring holds only nope columns and the source table
+// fits 2048 entries). Two resident workgroups per compute unit keep two
 // stages in flight per compute unit and overlap one workgroup's arithmetic
 // and barriers with the other's loads (one workgroup with a four-stage ring
 // ran the long-context per-query attend at 3.0 ms, two with two stages at
@@ -134,17 +139,16 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 constexpr int kDecWPC = 2;                                    // workgroups per compute unit
 constexpr int kDecRows = 32;                                  // selections per stage
 constexpr int kDecRing = 2;                                   // LDS stages
-constexpr int kDecStage = kDecRows * (NOPE_B + ROPE_B);       // 36864 bytes
-constexpr int kDecRopeOff = kDecRows * NOPE_B;                // rope region of a stage
-constexpr int kDecLoads = kDecRows / 4 + 1;                   // direct loads per wave per stage
-constexpr int kDecMaxCH = 1024;
+constexpr int kDecStage = kDecRows * NOPE_B;                  // 32768 bytes (nope columns)
+constexpr int kDecLoads = kDecRows / 4;                       // direct loads per wave per stage
+constexpr int kDecMaxCH = 2048;
 // s_src entries: the cache slot a selection loads; an invalid selection
 // carries this bit over the slot of a valid row of its stage (or slot 0)
 constexpr int kDecInvalid = (int)0x80000000;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
-// LDS bytes [1024 r, 1024 r + 1024), and the rope parts of rows 8 wave ..
-// 8 wave + 7 at kDecRopeOff + 1024 wave.
+// LDS bytes [1024 r, 1024 r + 1024). (The rope columns of a stage go to the
+// registers of the waves whose part of the contraction holds them.)
 __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restrict__ kv,
                                            int row_stride, const int* s_src, int wave) {
   const int l = lane_id_volatile();
@@ -155,9 +159,6 @@ __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restr
     const int src = __builtin_amdgcn_readfirstlane(s_src[r] & ~kDecInvalid);
     gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), kv + (size_t)src * row_stride, buf + r * NOPE_B);
   }
-  const int r = 8 * wave + (l >> 3);
-  gll16_a(kv + (size_t)(s_src[r] & ~kDecInvalid) * row_stride + DV + 8 * ((l & 7) ^ rope_x(r)),
-          buf + kDecRopeOff + wave * 1024);
 }
 
 // PAGED = 1: the selection of a row is a list of sel_ld seq-local pages, and
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     int num_pages, const int32_t* __restrict__ pt, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ topk, int sel_ld, int T, int S,
     int H, int k, int PS, int MP, float sm_scale, int CH, int nch, int HB,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_ml) {
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing][kDecStage];
   __shared__ int s_src[kDecMaxCH];
   __shared__ f32x4 s_part[4][64];  // per wave: its half of one S^T tile
@@ -182,9 +183,11 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   const float scale2 = sm_scale * 1.44269504088896341f;
 
   // ---- this wave's S^T tile (keys 16 tile .. 16 tile + 15 of a stage) and
-  // its half of the 18 k steps of 32 latent columns
+  // its half of the 18 k steps of 32 latent columns; the odd waves' half
+  // ends with the two rope steps, whose key fragments they load to registers
   const int tile = wave >> 1;
   const int kb = 9 * (wave & 1);
+  const bool rope_wave = (wave & 1) != 0;
   // ---- the selection entries of this chunk (entry i = 64 (4 p + wave) + l
   // of pass p, two stages per wave and pass) and this lane's query fragments
   // (head 16 hb + col, k values 32 (kb + u) + 8 g ..) depend only on the row
@@ -246,16 +249,22 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   __syncthreads();
 
   // per-lane LDS offsets. S^T reads: key row 16 tile + col, chunk 4 i + g of
-  // k step i (nope_x and rope_x of row 16 + col equal those of col).
-  const int nx = nope_x(col), rx = rope_x(col);
+  // k step i (nope_x of row 16 + col equals that of col), for the nope steps
+  // i < 16; the rope steps 16 and 17 read rope chunks g and 4 + g of the row
+  // from registers.
+  const int nx = nope_x(col);
   const int kr = 16 * tile + col;
-  int koff[9];
+  int koff[7];
 #pragma unroll
-  for (int u = 0; u < 9; ++u) {
-    const int i = kb + u;
-    koff[u] = i < 16 ? kr * NOPE_B + 16 * ((4 * i + g) ^ nx)
-                     : kDecRopeOff + kr * ROPE_B + 16 * ((4 * (i - 16) + g) ^ rx);
-  }
+  for (int u = 0; u < 7; ++u) koff[u] = kr * NOPE_B + 16 * ((4 * (kb + u) + g) ^ nx);
+  // rope fragments of stage st (kernel-visible loads, waited for with the
+  // ring): this lane's two 16-byte chunks of key row kr
+  auto rope_load = [&](int st, bf16x8 (&rp)[2]) __attribute__((always_inline)) {
+    const int src = s_src[st * kDecRows + kr] & ~kDecInvalid;
+    const uint16_t* r = kv + (size_t)src * row_stride + DV + 8 * g;
+    rp[0] = as_bf16x8(*reinterpret_cast<const uint4*>(r));
+    rp[1] = as_bf16x8(*reinterpret_cast<const uint4*>(r + 32));
+  };
   // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3),
   // i.e. 16-byte chunk 16 wave + 2 ct + (col & 3) / 2, byte 8 (col & 1)
   const int vr = 4 * g + (col >> 2), vq = col & 3;
@@ -271,9 +280,12 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   float m_run = -INFINITY, l_run = 0.f;
   const uint32_t lds_ring = lds_addr_of(ring[0]);
 
+  bf16x8 rope_cur[2], rope_next[2];
+  rope_cur[0] = rope_cur[1] = rope_next[0] = rope_next[1] = as_bf16x8(zero_u4());
 #pragma unroll
   for (int s = 0; s < kDecRing - 1; ++s)
     if (s < nst) stage_rows(lds_ring + s * kDecStage, kv, row_stride, s_src + s * kDecRows, wave);
+  if (rope_wave && nst > 0) rope_load(0, rope_next);
   for (int st = 0; st < nst; ++st) {
     // stages st + 1 .. st + 2 were issued after this one
     const int later = min(kDecRing - 2, nst - 1 - st);
@@ -281,9 +293,13 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     else if (kDecRing > 2 && later >= 1) wait_vmcnt<kDecLoads>();
     else wait_vmcnt<0>();
     lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
-    if (st + kDecRing - 1 < nst)
+    rope_cur[0] = rope_next[0];
+    rope_cur[1] = rope_next[1];
+    if (st + kDecRing - 1 < nst) {
       stage_rows(lds_ring + ((st + kDecRing - 1) % kDecRing) * kDecStage, kv, row_stride,
                  s_src + (st + kDecRing - 1) * kDecRows, wave);
+      if (rope_wave) rope_load(st + kDecRing - 1, rope_next);
+    }
     // the stage's validity mask: bit r for selection r of the stage
     const uint32_t mask = (uint32_t)__ballot(s_src[st * kDecRows + (l & 31)] >= 0);
     if (mask == 0) continue;
@@ -292,8 +308,18 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     // in the same order by every wave
     f32x4 sp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 9; ++u)
+    for (int u = 0; u < 7; ++u)
       sp = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + koff[u])), qf[u], sp);
+    if (rope_wave) {
+      sp = mfma16(rope_cur[0], qf[7], sp);
+      sp = mfma16(rope_cur[1], qf[8], sp);
+    } else {
+#pragma unroll
+      for (int u = 7; u < 9; ++u)
+        sp = mfma16(as_bf16x8(*reinterpret_cast<const uint4*>(buf + kr * NOPE_B +
+                                                              16 * ((4 * (kb + u) + g) ^ nx))),
+                    qf[u], sp);
+    }
     s_part[wave][l] = sp;
     lds_barrier();
     f32x4 s0 = s_part[0][l] + s_part[1][l];
@@ -347,6 +373,20 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   // ---- partials: m (natural-log units), l summed over the lane groups, O
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
+  if (nch == 1) {  // the row's whole selection: the normalised output itself
+    if (head < H) {
+      const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      uint16_t* orow = out + ((size_t)t * H + head) * DV + 128 * wave + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        uint2 v;
+        v.x = pack_bf16x2(o[ct][0] * inv, o[ct][1] * inv);
+        v.y = pack_bf16x2(o[ct][2] * inv, o[ct][3] * inv);
+        *reinterpret_cast<uint2*>(orow + 16 * ct) = v;
+      }
+    }
+    return;
+  }
   const size_t base = ((size_t)t * nch + c) * H;
   if (head < H) {
     if (wave == 0 && g == 0) {
@@ -626,15 +666,16 @@ hipError_t mla_decode(const MlaArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((mla_decode_partial<1>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q,
                          a.kv, a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk,
                          a.k / a.PS, a.T, a.S, a.H, a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB,
-                         a.part_o, a.part_ml);
+                         a.part_o, a.part_ml, a.out);
     else
       hipLaunchKernelGGL((mla_decode_partial<0>), dim3(nch * HB, a.T), dim3(256), 0, st, a.q,
                          a.kv, a.row_stride, a.num_pages, a.pt, a.seq_lens, a.cu, a.topk, a.k,
                          a.T, a.S, a.H, a.k, a.PS, a.MP, a.sm_scale, CH, nch, HB, a.part_o,
-                         a.part_ml);
+                         a.part_ml, a.out);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nch == 1) return hipSuccess;  // the partial wrote the output
   ProfScope prof("mla_decode_combine", st);
   if (nch <= kCombFew && a.T >= 1024)  // many rows of few chunks: several rows per wave
     hipLaunchKernelGGL(mla_decode_combine_rows, dim3((a.T + kCombRows - 1) / kCombRows,

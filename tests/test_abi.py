@@ -82,7 +82,8 @@ def test_union_validation(lib):
 
 def test_mla_validation(lib):
     def dec(**kw):
-        a = dict(rs=576, H=16, k=64, T=2, q=1 << 12)
+        # k = 2048 over 2 rows is split into chunks, so a workspace is needed
+        a = dict(rs=576, H=16, k=2048, T=2, q=1 << 12)
         a.update(kw)
         return lib.dsa_sparse_mla_decode(a["q"], 1 << 12, a["rs"], 8, 1 << 12, 1 << 12, 1 << 12,
                                          1 << 12, a["T"], 2, a["H"], a["k"], 64, 4, 0.1,
@@ -113,6 +114,9 @@ def test_decode_workspace_formula(lib):
     ws = dsa.sparse_mla_decode_workspace(8, 16, 2048)
     assert ws > 0 and ws % 256 == 0
     assert dsa.sparse_mla_decode_workspace(0, 16, 2048) == 0
+    # a batch with one chunk per row (8192 rows of 2048 selections) writes its
+    # output directly: no workspace
+    assert dsa.sparse_mla_decode_workspace(8192, 16, 2048) == 0
 
 
 def test_extend_attend_path(lib):
