@@ -9,7 +9,9 @@ top-k). One step is the four layers in order, each timed end to end:
 
   full layer    the self-write of the chunk's indexer keys and latent rows
                 (one launch), the indexer top-k, the query-block union of
-                the attend's selection, and the sparse MLA attention;
+                the attend's selection (its block sizes only, which the
+                plan reads, when the attention runs per query), and the
+                sparse MLA attention;
   shared layer  the self-write of its latent rows and the attention with the
                 full layer's selection and union.
 
@@ -490,12 +492,12 @@ class ExtendLayers:
                               d["seq_lens"], d["cu"], self.k, d["max_q_len"], out=self.topk,
                               workspace=self.ws_i)
 
-    def union(self, sel, QB):
+    def union(self, sel, QB, member=True):
         t = self.tables[QB]
         d = self.d
         self.dsa.block_union(sel, d["seq_lens"], d["cu"], self.wl.PS, self.wl.MP, QB,
                              self.u_max, out=(t["units"], t["counts"], t["member"]),
-                             workspace=t["ws"])
+                             workspace=t["ws"], member=member)
 
     def attend(self, i, sel, path):
         d = self.d
@@ -525,9 +527,10 @@ class ExtendLayers:
 
     def step_fn(self, sel_kind, path, layers=None, full_first=True):
         """One pass over `layers` layers (all by default): write, then on the
-        full layer indexer top-k and the union the attention needs, then the
-        attention; `sel_kind` "locality" or "indexer" feeds union and
-        attention."""
+        full layer indexer top-k and the union (the block sizes a plan reads,
+        at QB 256, when the attention runs per query; the full tables at the
+        attention's QB otherwise), then the attention; `sel_kind` "locality"
+        or "indexer" feeds union and attention."""
         n = self.layers if layers is None else layers
         sel = self.loc if sel_kind == "locality" else self.topk
         union_qb = path if path else 256
@@ -538,7 +541,7 @@ class ExtendLayers:
                 self.write(i, full)
                 if full:
                     self.indexer()
-                    self.union(sel, union_qb)
+                    self.union(sel, union_qb, member=bool(path))
                 self.attend(i, sel, path)
         return step
 
@@ -587,7 +590,8 @@ def bench_extend_workload(dsa, wl, steps, warmup, reps):
 
     E = ExtendLayers(dsa, wl)
     res = {"workload": wl.name, "layers": E.layers, "T": E.T, "k": E.k,
-           "step": "per layer: self-write; full layer: indexer top-k + union; attention"}
+           "step": "per layer: self-write; full layer: indexer top-k + union (sizes only "
+                   "when per query); attention"}
     # the indexer once (its selection is the secondary feed)
     E.indexer()
     sel_np = {"locality": E.loc.cpu().numpy(), "indexer": E.topk.cpu().numpy()}
@@ -818,7 +822,8 @@ def main(argv=None):
                    "mla_heads": wl5.H_mla, "dk": DK, "dv": DV, "layers": lng["layers"],
                    "indexshare": "1 full + 3 shared", "attend_feed": "locality selection",
                    "attend_path": main_step["path"],
-                   "step": "4 layers: self-write; full layer indexer top-k + union; "
+                   "step": "4 layers: self-write; full layer indexer top-k + union (sizes "
+                           "only when per query); "
                            "sparse MLA attention on the planned path"},
         "roofline": lng["roofline"],
         "long_extend": lng,

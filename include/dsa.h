@@ -258,7 +258,10 @@ int dsa_paged_write_layer(const void* idx_src, int D, void* idx_cache, const voi
  *   topk        int32 [T, k]
  *   blk_units   int32 [nQB, u_max]       output
  *   blk_counts  int32 [nQB]              output
- *   blk_member  uint64 [nQB, u_max, QB]  output
+ *   blk_member  uint64 [nQB, u_max, QB]  output, or NULL: then only
+ *               blk_units and blk_counts are written and the membership
+ *               pass is not launched (the sizes a plan reads cost about
+ *               half of the full call).
  * Supported: PS <= 64 (one 64-bit membership word per page), S * MP <= 2^18,
  * 1 <= u_max <= 8192, 1 <= QB <= 1024; otherwise DSA_ERR_UNSUPPORTED.
  */

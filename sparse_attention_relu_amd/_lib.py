@@ -386,9 +386,10 @@ def block_union_workspace(T, S, MP, QB, u_max) -> int:
 
 
 def block_union(topk, seq_lens, cu_q_lens, PS: int, MP: int, QB: int, u_max: int,
-                out=None, workspace=None, stream=None):
+                out=None, workspace=None, stream=None, member: bool = True):
     """Query-block union tables -> (units [nQB,u_max] i32, counts [nQB] i32,
-    member [nQB,u_max,QB] u64) (dsa_block_union)."""
+    member [nQB,u_max,QB] u64) (dsa_block_union). member=False writes units
+    and counts only and returns None for the membership table."""
     torch = _torch()
     dev = topk.device
     _need(topk, "topk", torch.int32, 2, dev)
@@ -400,15 +401,26 @@ def block_union(topk, seq_lens, cu_q_lens, PS: int, MP: int, QB: int, u_max: int
     if out is None:
         out = (_empty((nqb, u_max), torch.int32, dev, stream),
                _empty((nqb,), torch.int32, dev, stream),
-               _empty((nqb, u_max, QB), torch.uint64, dev, stream))
-    units, counts, member = out
+               _empty((nqb, u_max, QB), torch.uint64, dev, stream) if member else None)
+    units, counts, mb = out
+    _need(units, "units", torch.int32, 2, dev)
+    _need(counts, "counts", torch.int32, 1, dev)
+    if tuple(units.shape) != (nqb, u_max) or tuple(counts.shape) != (nqb,):
+        raise ValueError(f"units {tuple(units.shape)} / counts {tuple(counts.shape)} do not "
+                         f"match nQB={nqb}, u_max={u_max}")
+    if not member:
+        mb = None
+    else:
+        _need(mb, "member", torch.uint64, 3, dev)
+        if tuple(mb.shape) != (nqb, u_max, QB):
+            raise ValueError(f"member {tuple(mb.shape)} != {(nqb, u_max, QB)}")
     nbytes = block_union_workspace(T, S, MP, QB, u_max)
     ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_block_union(_ptr(topk), _ptr(seq_lens), _ptr(cu_q_lens), T, S, k, PS, MP, QB,
-                                u_max, _ptr(units), _ptr(counts), _ptr(member), _ptr(ws), nbytes,
+                                u_max, _ptr(units), _ptr(counts), _ptr(mb), _ptr(ws), nbytes,
                                 _stream(stream))
     _check("dsa_block_union", st)
-    return units, counts, member
+    return units, counts, mb
 
 
 def _mla_common(q, kv_cache, page_table, seq_lens, cu_q_lens):
@@ -599,10 +611,11 @@ def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max
        launch): new_kv[i] into kv_cache[i] and, on a full layer, its
        new_idx[slot] into idx_cache[slot] (skipped when new_kv is None);
     2. on a full layer: the indexer top-k (dsa_indexer_topk) into the
-       layer's slot, then the block unions at each QB of qb_candidates
-       (dsa_block_union), whose sizes choose the attention
+       layer's slot, then the block union sizes at each QB of qb_candidates
+       (dsa_block_union without membership), which choose the attention
        (dsa_extend_attend_plan: a QB or the per-query path; this reads the
-       union sizes on the host, a synchronisation of `stream`);
+       union sizes on the host, a synchronisation of `stream`), and the
+       full union tables at the chosen QB only;
     3. the attention of every layer with its source slot's selection:
        dsa_sparse_mla_extend at the chosen QB, or dsa_sparse_mla_decode
        (per query) on the packed batch.
@@ -612,7 +625,8 @@ def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max
     kv_cache, new_kv are lists indexed by layer. path forces "per_query" or
     a QB for every slot. Returns (outs, info): outs[i] bf16 [T, H, 512];
     info["topk"][slot], info["choice"][slot] (0 = per query, else the QB),
-    info["counts"][slot] (QB -> blk_counts).
+    info["counts"][slot] (QB -> blk_counts: every candidate when planned,
+    else the forced QB only).
     """
     full_slot, src_slot, n_full = index_share_map(indexer_types)
     n_layers = len(indexer_types)
@@ -647,19 +661,24 @@ def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max
             tk = indexer_topk(q_idx[own], w[own], idx_cache[own], page_table, seq_lens,
                               cu_q_lens, k, max_q_len, stream=stream)
             topk[own] = tk
+            ums = {qb: (u_max if u_max is not None else min(qb * k, S * MP)) for qb in qbs}
             tabs, cnts = {}, {}
-            for qb in qbs:
-                um = u_max if u_max is not None else min(qb * k, S * MP)
-                tabs[qb] = (block_union(tk, seq_lens, cu_q_lens, PS, MP, qb, um, stream=stream),
-                            um)
-                cnts[qb] = tabs[qb][0][1]
             if path is None:
-                um0 = min(t[1] for t in tabs.values()) if tabs else (u_max or S * MP)
+                # sizes only for the plan; membership only at the chosen QB
+                for qb in qbs:
+                    cnts[qb] = block_union(tk, seq_lens, cu_q_lens, PS, MP, qb, ums[qb],
+                                           stream=stream, member=False)[1]
+                um0 = min(ums.values()) if ums else (u_max or S * MP)
                 choice[own] = extend_attend_plan(cnts, T, H, k, PS, um0)
             else:
                 choice[own] = 0 if path == "per_query" else int(path)
-                if choice[own] and choice[own] not in tabs:
+                if choice[own] and choice[own] not in ums:
                     raise ValueError(f"forced QB {path} is not among qb_candidates")
+            c = choice[own]
+            if c:
+                tabs[c] = (block_union(tk, seq_lens, cu_q_lens, PS, MP, c, ums[c],
+                                       stream=stream), ums[c])
+                cnts[c] = tabs[c][0][1]
             tables[own] = tabs
             counts[own] = cnts
         c = choice[slot]

@@ -354,7 +354,7 @@ int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t*
   if ((long)S * MP > (1L << 18))
     return fail(DSA_ERR_UNSUPPORTED, "S*MP=%ld page keys exceed 2^18", (long)S * MP);
   if (T == 0) return ok();
-  if (!topk || !seq_lens || !cu_q_lens || !blk_units || !blk_counts || !blk_member)
+  if (!topk || !seq_lens || !cu_q_lens || !blk_units || !blk_counts)
     return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
   const size_t need = dsa_block_union_workspace(T, S, MP, QB, u_max);
   if (!workspace || workspace_bytes < need)
@@ -368,7 +368,7 @@ int dsa_block_union(const int32_t* topk, const int32_t* seq_lens, const int32_t*
   a.T = T; a.S = S; a.k = k; a.PS = PS; a.MP = MP; a.QB = QB; a.u_max = u_max;
   a.units = blk_units;
   a.counts = blk_counts;
-  a.member = blk_member;
+  a.member = blk_member;  // NULL: units and counts only
   a.bits = static_cast<uint64_t*>(workspace);
   a.prefix = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(nqb * nw * 8));
   return hip_status(dsa::block_union(a, static_cast<hipStream_t>(stream)), "union launch");

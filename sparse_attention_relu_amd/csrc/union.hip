@@ -219,6 +219,7 @@ hipError_t block_union(const UnionArgs& a, hipStream_t st) {
                        a.units, a.counts);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!a.member) return hipSuccess;  // sizes only, for planning
   const int qpw = union_member_qpw(a.QB, a.u_max);
   ProfScope prof("union_member", st);
   hipLaunchKernelGGL(union_member, dim3(nqb, (a.QB + qpw - 1) / qpw), dim3(256),

@@ -65,11 +65,12 @@ def test_indexer_validation(lib):
 
 def test_union_validation(lib):
     def call(**kw):
-        a = dict(T=8, S=2, k=4, PS=64, MP=8, QB=4, u_max=16, ws=None, wsb=0)
+        a = dict(T=8, S=2, k=4, PS=64, MP=8, QB=4, u_max=16, ws=None, wsb=0, units=1 << 12,
+                 member=1 << 12)
         a.update(kw)
         return lib.dsa_block_union(1 << 12, 1 << 12, 1 << 12, a["T"], a["S"], a["k"], a["PS"],
-                                   a["MP"], a["QB"], a["u_max"], 1 << 12, 1 << 12, 1 << 12,
-                                   a["ws"], a["wsb"], None)
+                                   a["MP"], a["QB"], a["u_max"], a["units"], 1 << 12,
+                                   a["member"], a["ws"], a["wsb"], None)
 
     assert call(PS=128) == _lib.DSA_ERR_UNSUPPORTED
     assert call(QB=0) == _lib.DSA_ERR_UNSUPPORTED
@@ -77,6 +78,8 @@ def test_union_validation(lib):
     assert call(u_max=100000) == _lib.DSA_ERR_UNSUPPORTED
     assert call(S=64, MP=8192) == _lib.DSA_ERR_UNSUPPORTED
     assert call() == _lib.DSA_ERR_WORKSPACE
+    assert call(units=None) == _lib.DSA_ERR_INVALID_ARG
+    assert call(member=None) == _lib.DSA_ERR_WORKSPACE  # sizes only: membership is optional
     assert call(T=0) == _lib.DSA_OK
 
 

@@ -328,6 +328,20 @@ def test_union_cases(dsa, name):
     assert np.array_equal(c, ec)
     assert np.array_equal(u, eu)
     assert np.array_equal(m, em)
+    # sizes only (no membership pass): same units and counts, and a member
+    # table handed in stays untouched
+    torch = torch_mod()
+    nqb = len(ec)
+    out = (torch.full((nqb, u_max), -7, dtype=torch.int32, device="cuda"),
+           torch.full((nqb,), -7, dtype=torch.int32, device="cuda"),
+           torch.full((nqb, u_max, QB), 0x5A5A, dtype=torch.int64,
+                      device="cuda").view(torch.uint64))
+    u2, c2, m2 = dsa.block_union(i32(tk, "cuda"), i32(wl.seq_lens, "cuda"), i32(cu, "cuda"),
+                                 PS, MP, QB, u_max, out=out, member=False)
+    torch.cuda.synchronize()
+    assert m2 is None
+    assert np.array_equal(c2.cpu().numpy(), ec) and np.array_equal(u2.cpu().numpy(), eu)
+    assert (out[2].cpu().numpy() == 0x5A5A).all()
 
 
 # ----------------------------------------------------------------------------
