@@ -101,6 +101,15 @@ __device__ __forceinline__ void gll16_a(const void* src, uint32_t lds_addr) {
                : "memory", "m0");
 }
 
+// max of two floats as one v_max_f32 (the operands are results of
+// arithmetic or of lane permutations of such results, so no quieting of
+// signalling NaNs is needed before the compare)
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
@@ -142,22 +151,26 @@ constexpr int kDecRing = 2;                                   // LDS stages
 constexpr int kDecStage = kDecRows * NOPE_B;                  // 32768 bytes (nope columns)
 constexpr int kDecLoads = kDecRows / 4;                       // direct loads per wave per stage
 constexpr int kDecMaxCH = 2048;
+constexpr float kDecLazy = 8.0f;  // headroom of the running maximum (log2 units)
 // s_src entries: the cache slot a selection loads; an invalid selection
 // carries this bit over the slot of a valid row of its stage (or slot 0)
 constexpr int kDecInvalid = (int)0x80000000;
 
 // This wave's direct loads of one stage: nope rows r = 4 n + wave (n < 8) at
-// LDS bytes [1024 r, 1024 r + 1024). (The rope columns of a stage go to the
-// registers of the waves whose part of the contraction holds them.)
+// LDS bytes [1024 r, 1024 r + 1024). `ent` holds in lane n the stage's
+// source entry of row 4 n + wave (read from the source table beforehand, so
+// that the eight rows cost one LDS round trip, not eight). (The rope columns
+// of a stage go to the registers of the waves whose part of the contraction
+// holds them.)
+// roff[n] is the lane's swizzled byte offset within row 4 n + wave.
 __device__ __forceinline__ void stage_rows(uint32_t buf, const uint16_t* __restrict__ kv,
-                                           int row_stride, const int* s_src, int wave) {
-  const int l = lane_id_volatile();
-  const uint32_t l16 = 16u * (uint32_t)l;
+                                           int row_stride, int ent, int wave,
+                                           const uint32_t (&roff)[kDecRows / 4]) {
 #pragma unroll
   for (int n = 0; n < kDecRows / 4; ++n) {
     const int r = 4 * n + wave;
-    const int src = __builtin_amdgcn_readfirstlane(s_src[r] & ~kDecInvalid);
-    gll16_s(l16 ^ (16u * (uint32_t)nope_x(r)), kv + (size_t)src * row_stride, buf + r * NOPE_B);
+    const int src = __builtin_amdgcn_readlane(ent, n) & ~kDecInvalid;
+    gll16_s(roff[n], kv + (size_t)src * row_stride, buf + r * NOPE_B);
   }
 }
 
@@ -259,12 +272,16 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   for (int u = 0; u < 7; ++u) koff[u] = kr * NOPE_B + 16 * ((4 * (kb + u) + g) ^ nx);
   // rope fragments of stage st (kernel-visible loads, waited for with the
   // ring): this lane's two 16-byte chunks of key row kr
-  auto rope_load = [&](int st, bf16x8 (&rp)[2]) __attribute__((always_inline)) {
-    const int src = s_src[st * kDecRows + kr] & ~kDecInvalid;
-    const uint16_t* r = kv + (size_t)src * row_stride + DV + 8 * g;
+  auto rope_load = [&](int ent, bf16x8 (&rp)[2]) __attribute__((always_inline)) {
+    const uint16_t* r = kv + (size_t)(ent & ~kDecInvalid) * row_stride + DV + 8 * g;
     rp[0] = as_bf16x8(*reinterpret_cast<const uint4*>(r));
     rp[1] = as_bf16x8(*reinterpret_cast<const uint4*>(r + 32));
   };
+  // source entries of stage st: lane n < 8 of stage_rows' operand holds row
+  // 4 n + wave, the rope operand row kr, the mask operand row l % 32
+  auto ent_rows = [&](int st) { return s_src[st * kDecRows + 4 * (l & 7) + wave]; };
+  auto ent_rope = [&](int st) { return s_src[st * kDecRows + kr]; };
+  auto ent_mask = [&](int st) { return s_src[st * kDecRows + (l & 31)]; };
   // V^T reads: key row 4 g + col / 4 (+16), columns 128 wave + 16 ct + 4 (col & 3),
   // i.e. 16-byte chunk 16 wave + 2 ct + (col & 3) / 2, byte 8 (col & 1)
   const int vr = 4 * g + (col >> 2), vq = col & 3;
@@ -280,30 +297,33 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
   float m_run = -INFINITY, l_run = 0.f;
   const uint32_t lds_ring = lds_addr_of(ring[0]);
 
-  bf16x8 rope_cur[2], rope_next[2];
-  rope_cur[0] = rope_cur[1] = rope_next[0] = rope_next[1] = as_bf16x8(zero_u4());
+  // rope fragments: two register sets, used alternately by even and odd
+  // stages (the loop body is instantiated once per ring slot, so that slot
+  // offsets fold into the LDS instructions and no register copies are made)
+  bf16x8 rope_a[2], rope_b[2];
+  rope_a[0] = rope_a[1] = rope_b[0] = rope_b[1] = as_bf16x8(zero_u4());
+  static_assert(kDecRing == 2, "the stage loop issues one stage ahead");
+  uint32_t roff[kDecRows / 4];
 #pragma unroll
-  for (int s = 0; s < kDecRing - 1; ++s)
-    if (s < nst) stage_rows(lds_ring + s * kDecStage, kv, row_stride, s_src + s * kDecRows, wave);
-  if (rope_wave && nst > 0) rope_load(0, rope_next);
-  for (int st = 0; st < nst; ++st) {
-    // stages st + 1 .. st + 2 were issued after this one
-    const int later = min(kDecRing - 2, nst - 1 - st);
-    if (kDecRing > 3 && later >= 2) wait_vmcnt<2 * kDecLoads>();
-    else if (kDecRing > 2 && later >= 1) wait_vmcnt<kDecLoads>();
-    else wait_vmcnt<0>();
+  for (int n = 0; n < kDecRows / 4; ++n) roff[n] = 16u * (uint32_t)(l ^ nope_x(4 * n + wave));
+  auto run_stage = [&](const int st, const int slot, bf16x8 (&rope_cur)[2],
+                       bf16x8 (&rope_next)[2]) __attribute__((always_inline)) {
+    // the entries of the stage issued below and this stage's mask, read
+    // before the barrier, whose LDS wait covers them
+    const bool ahead = st + 1 < nst;
+    const int e_rows = ahead ? ent_rows(st + 1) : 0;
+    const int e_rope = ahead ? ent_rope(st + 1) : 0;
+    const int e_mask = ent_mask(st);
+    wait_vmcnt<0>();
     lds_barrier();  // stage st has landed for every wave; stage st - 1 is consumed
-    rope_cur[0] = rope_next[0];
-    rope_cur[1] = rope_next[1];
-    if (st + kDecRing - 1 < nst) {
-      stage_rows(lds_ring + ((st + kDecRing - 1) % kDecRing) * kDecStage, kv, row_stride,
-                 s_src + (st + kDecRing - 1) * kDecRows, wave);
-      if (rope_wave) rope_load(st + kDecRing - 1, rope_next);
+    if (ahead) {
+      stage_rows(lds_ring + (1 - slot) * kDecStage, kv, row_stride, e_rows, wave, roff);
+      if (rope_wave) rope_load(e_rope, rope_next);
     }
     // the stage's validity mask: bit r for selection r of the stage
-    const uint32_t mask = (uint32_t)__ballot(s_src[st * kDecRows + (l & 31)] >= 0);
-    if (mask == 0) continue;
-    const unsigned char* buf = ring[st % kDecRing];
+    const uint32_t mask = (uint32_t)__ballot(e_mask >= 0);
+    if (mask == 0) return;
+    const unsigned char* buf = ring[slot];
     // ---- this wave's half of its S^T tile (16 keys), then both tiles summed
     // in the same order by every wave
     f32x4 sp = {0.f, 0.f, 0.f, 0.f};
@@ -325,33 +345,55 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
     f32x4 s0 = s_part[0][l] + s_part[1][l];
     f32x4 s1 = s_part[2][l] + s_part[3][l];
     // ---- masked online softmax over the stage's 32 keys (log2 units)
-    const uint32_t m0 = mask >> (4 * g), m1 = mask >> (16 + 4 * g);
+    if (mask != 0xffffffffu) {  // wave-uniform: only stages with invalid entries
+      const uint32_t m0 = mask >> (4 * g), m1 = mask >> (16 + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (!((m0 >> r) & 1u)) s0[r] = -INFINITY;
+        if (!((m1 >> r) & 1u)) s1[r] = -INFINITY;
+      }
+    }
     float x0[4], x1[4];
-    float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x0[r] = ((m0 >> r) & 1u) ? s0[r] * scale2 : -INFINITY;
-      x1[r] = ((m1 >> r) & 1u) ? s1[r] * scale2 : -INFINITY;
-      mx = fmaxf(mx, fmaxf(x0[r], x1[r]));
+      x0[r] = s0[r] * scale2;
+      x1[r] = s1[r] * scale2;
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+    // the head's maximum over the four lane groups: rows of 16 lanes swapped
+    // in pairs, then halves
+    float mx = fmaxf(fmaxf(fmaxf(x0[0], x1[0]), fmaxf(x0[1], x1[1])),
+                     fmaxf(fmaxf(x0[2], x1[2]), fmaxf(x0[3], x1[3])));
+    {
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+      mx = max_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+      const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+      mx = max_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    }
+    // The subtracted maximum moves only when the stage's maximum exceeds it
+    // by more than kDecLazy (log2 units): softmax does not depend on the
+    // constant subtracted, so the accumulators are rescaled rarely, and the
+    // exponentials stay below 2^kDecLazy.
+    const bool grow = mx > m_run + kDecLazy;  // always at the first stage (m_run = -inf)
+    const float m_use = grow ? mx : m_run;
     float p0[4], p1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p0[r] = __builtin_amdgcn_exp2f(x0[r] - m_new);
-      p1[r] = __builtin_amdgcn_exp2f(x1[r] - m_new);
+      p0[r] = __builtin_amdgcn_exp2f(x0[r] - m_use);
+      p1[r] = __builtin_amdgcn_exp2f(x1[r] - m_use);
     }
-    l_run = l_run * alpha + ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
-    m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {
+    const float psum = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.0f;  // 0 at first
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[ct][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_use;
     }
+    l_run += psum;
     uint4 pb4;
     pb4.x = pack_bf16x2(p0[0], p0[1]);
     pb4.y = pack_bf16x2(p0[2], p0[3]);
@@ -369,6 +411,14 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
       __builtin_memcpy(reinterpret_cast<char*>(&va) + 8, &vhi, 8);
       o[ct] = mfma16(va, pb, o[ct]);
     }
+  };
+  if (nst > 0) {
+    stage_rows(lds_ring, kv, row_stride, ent_rows(0), wave, roff);
+    if (rope_wave) rope_load(ent_rope(0), rope_a);
+  }
+  for (int st = 0; st < nst; st += 2) {
+    run_stage(st, 0, rope_a, rope_b);
+    if (st + 1 < nst) run_stage(st + 1, 1, rope_b, rope_a);
   }
   // ---- partials: m (natural-log units), l summed over the lane groups, O
   l_run += shfl_xor_f(l_run, 16);
