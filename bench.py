@@ -273,13 +273,15 @@ def _kernel_table(kt, warm, cold, work):
 
 
 INDEXER_KERNELS = ("idx_score_stream", "idx_score_flat", "idx_score_tiles", "topk_select",
-                   "idx_score_topk", "topk_order", "topk_merge")
+                   "idx_score_topk", "topk_order", "topk_merge", "topk_rows_ascending",
+                   "topk_rows_bitmap")
 
 # Sources whose text decides each kernel's machine code.
 KERNEL_SOURCES = {
     "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
     "idx_score_tiles": "indexer.hip", "topk_select": "indexer.hip",
     "idx_score_topk": "indexer.hip", "topk_order": "indexer.hip", "topk_merge": "indexer.hip",
+    "topk_rows_ascending": "indexer.hip", "topk_rows_bitmap": "indexer.hip",
     "mla_decode_partial": "mla.hip", "mla_decode_combine": "mla.hip",
     "mla_decode_combine_wide": "mla.hip", "mla_extend_qblock": "mla.hip",
     "union_clear": "union.hip", "union_mark": "union.hip", "union_compact": "union.hip",
@@ -487,10 +489,11 @@ class ExtendLayers:
                                    d["kv_cache"][i], d["page_table"], d["seq_lens"], d["cu"])
 
     def indexer(self):
+        # position order, as the library's layer loop asks for its attention feed
         d = self.d
         self.dsa.indexer_topk(d["q_idx"], d["w"], d["idx_cache"], d["page_table"],
                               d["seq_lens"], d["cu"], self.k, d["max_q_len"], out=self.topk,
-                              workspace=self.ws_i)
+                              workspace=self.ws_i, order="position")
 
     def union(self, sel, QB, member=True):
         t = self.tables[QB]
@@ -556,6 +559,8 @@ class ExtendLayers:
              "idx_score_topk": ("mfma", idx_flops),
              "topk_select": ("hbm", int(self.nval.sum()) * 4 + T * k * 4),
              "topk_order": ("hbm", T * k * (8 + 4)),
+             "topk_rows_ascending": ("hbm", T * k * (4 + 4)),
+             "topk_rows_bitmap": ("hbm", T * k * (4 + 4)),
              "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
              "paged_write_rows": ("hbm", T * (wl.D_idx + DK) * 2 * 2)}
         for QB, cnt in QB_counts.items():

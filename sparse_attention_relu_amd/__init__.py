@@ -6,6 +6,8 @@ attention for decode and chunked-prefill extend. All compute runs in the HIP
 kernels; this package only marshals torch tensors into the C calls.
 """
 from ._lib import (  # noqa: F401
+    DSA_ORDER_POSITION,
+    DSA_ORDER_SCORE,
     DsaError,
     block_union,
     block_union_workspace,
@@ -34,4 +36,5 @@ from ._lib import (  # noqa: F401
     sparse_mla_extend,
     sparse_mla_extend_workspace,
     status_string,
+    topk_position_order,
 )

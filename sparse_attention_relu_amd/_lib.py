@@ -34,7 +34,10 @@ SIGNATURES = {
     "dsa_indexer_topk": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                          + [_vp, _vp, _c_size, _vp]),
     "dsa_indexer_topk_fused_workspace": (_c_size, [_c_int] * 7),
-    "dsa_indexer_topk_fused": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 7
+    "dsa_indexer_topk_ordered": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 9
+                                 + [_vp, _vp, _c_size, _vp]),
+    "dsa_topk_position_order": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
+    "dsa_indexer_topk_fused": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 8
                                + [_vp, _vp, _c_size, _vp]),
     "dsa_block_union_workspace": (_c_size, [_c_int] * 5),
     "dsa_block_union": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp, _vp, _vp, _vp, _c_size,
@@ -220,9 +223,21 @@ def indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len) -> int:
     return load().dsa_indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len)
 
 
+DSA_ORDER_SCORE, DSA_ORDER_POSITION = 0, 1
+_ORDERS = {"score": DSA_ORDER_SCORE, "position": DSA_ORDER_POSITION}
+
+
+def _order(order) -> int:
+    if order not in _ORDERS:
+        raise ValueError(f"order {order!r} is neither 'score' nor 'position'")
+    return _ORDERS[order]
+
+
 def indexer_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int,
-                 max_q_len: int, out=None, workspace=None, stream=None):
-    """Exact lightning-indexer top-k -> int32 [T, k] (dsa_indexer_topk)."""
+                 max_q_len: int, out=None, workspace=None, stream=None, order="score"):
+    """Exact lightning-indexer top-k -> int32 [T, k] (dsa_indexer_topk;
+    order="position": the same positions ascending, dsa_indexer_topk_ordered)."""
+    ordv = _order(order)
     torch = _torch()
     dev = q_idx.device
     _need(q_idx, "q_idx", torch.bfloat16, 3, dev)
@@ -238,10 +253,34 @@ def indexer_topk(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int,
     _need(out, "out", torch.int32, 2, dev)
     nbytes = indexer_topk_workspace(T, S, H, D, PS, MP, k, max_q_len)
     ws = _workspace(nbytes, dev, workspace, stream)
-    st = load().dsa_indexer_topk(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P, _ptr(page_table),
-                                 _ptr(seq_lens), _ptr(cu_q_lens), T, S, H, D, PS, MP, k,
-                                 max_q_len, _ptr(out), _ptr(ws), nbytes, _stream(stream))
-    _check("dsa_indexer_topk", st)
+    if ordv == DSA_ORDER_SCORE:
+        st = load().dsa_indexer_topk(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P, _ptr(page_table),
+                                     _ptr(seq_lens), _ptr(cu_q_lens), T, S, H, D, PS, MP, k,
+                                     max_q_len, _ptr(out), _ptr(ws), nbytes, _stream(stream))
+        _check("dsa_indexer_topk", st)
+    else:
+        st = load().dsa_indexer_topk_ordered(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P,
+                                             _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens),
+                                             T, S, H, D, PS, MP, k, max_q_len, ordv, _ptr(out),
+                                             _ptr(ws), nbytes, _stream(stream))
+        _check("dsa_indexer_topk_ordered", st)
+    return out
+
+
+def topk_position_order(topk, out=None, stream=None):
+    """Each row of a top-k table in ascending position order, -1 entries
+    last -> int32 [T, k] (dsa_topk_position_order; out may be topk)."""
+    torch = _torch()
+    dev = topk.device
+    _need(topk, "topk", torch.int32, 2, dev)
+    T, k = topk.shape
+    if out is None:
+        out = _empty((T, k), torch.int32, dev, stream)
+    _need(out, "out", torch.int32, 2, dev)
+    if tuple(out.shape) != (T, k):
+        raise ValueError(f"out {tuple(out.shape)} != {(T, k)}")
+    st = load().dsa_topk_position_order(_ptr(topk), _ptr(out), T, k, _stream(stream))
+    _check("dsa_topk_position_order", st)
     return out
 
 
@@ -250,9 +289,10 @@ def indexer_topk_fused_workspace(T, S, H, D, PS, MP, k) -> int:
 
 
 def indexer_topk_fused(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: int, out=None,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, order="score"):
     """Exact lightning-indexer top-k without the score matrix -> int32
     [T, k] (dsa_indexer_topk_fused); the same result as indexer_topk."""
+    ordv = _order(order)
     torch = _torch()
     dev = q_idx.device
     _need(q_idx, "q_idx", torch.bfloat16, 3, dev)
@@ -270,7 +310,7 @@ def indexer_topk_fused(q_idx, w, idx_cache, page_table, seq_lens, cu_q_lens, k: 
     ws = _workspace(nbytes, dev, workspace, stream)
     st = load().dsa_indexer_topk_fused(_ptr(q_idx), _ptr(w), _ptr(idx_cache), P,
                                        _ptr(page_table), _ptr(seq_lens), _ptr(cu_q_lens), T, S,
-                                       H, D, PS, MP, k, _ptr(out), _ptr(ws), nbytes,
+                                       H, D, PS, MP, k, ordv, _ptr(out), _ptr(ws), nbytes,
                                        _stream(stream))
     _check("dsa_indexer_topk_fused", st)
     return out
@@ -601,7 +641,8 @@ def sparse_mla_extend(q, kv_cache, page_table, seq_lens, cu_q_lens, units, count
 # ----------------------------------------------------------------------------
 def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max_q_len: int,
                   sm_scale: float, q_idx, w, idx_cache, q, kv_cache, new_idx=None, new_kv=None,
-                  qb_candidates=(64, 256), u_max=None, path=None, outs=None, stream=None):
+                  qb_candidates=(64, 256), u_max=None, path=None, outs=None, stream=None,
+                  topk_order="position"):
     """Run a stack of DSA layers over one packed batch with IndexShare
     ("ref.py", build_index_share_map; "dsa_sparse_backend.py", __call__:
     a shared layer attends with the top-k of the nearest preceding full
@@ -610,8 +651,10 @@ def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max
     1. the self-write of the batch's new tokens (dsa_paged_write_layer, one
        launch): new_kv[i] into kv_cache[i] and, on a full layer, its
        new_idx[slot] into idx_cache[slot] (skipped when new_kv is None);
-    2. on a full layer: the indexer top-k (dsa_indexer_topk) into the
-       layer's slot, then the block union sizes at each QB of qb_candidates
+    2. on a full layer: the indexer top-k (dsa_indexer_topk_ordered, in
+       `topk_order`: "position" by default, since union and attention only
+       see the set and gather faster in position order) into the layer's
+       slot, then the block union sizes at each QB of qb_candidates
        (dsa_block_union without membership), which choose the attention
        (dsa_extend_attend_plan: a QB or the per-query path; this reads the
        union sizes on the host, a synchronisation of `stream`), and the
@@ -659,7 +702,7 @@ def extend_layers(indexer_types, *, page_table, seq_lens, cu_q_lens, k: int, max
                               stream=stream)
         if own is not None:
             tk = indexer_topk(q_idx[own], w[own], idx_cache[own], page_table, seq_lens,
-                              cu_q_lens, k, max_q_len, stream=stream)
+                              cu_q_lens, k, max_q_len, stream=stream, order=topk_order)
             topk[own] = tk
             ums = {qb: (u_max if u_max is not None else min(qb * k, S * MP)) for qb in qbs}
             tabs, cnts = {}, {}

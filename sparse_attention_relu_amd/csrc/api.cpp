@@ -89,7 +89,7 @@ const char* dsa_status_string(int status) {
 
 const char* dsa_last_error(void) { return g_err; }
 
-int dsa_abi_version(void) { return 1; }
+int dsa_abi_version(void) { return 2; }
 
 // ---------------------------------------------------------------------------
 size_t dsa_indexer_topk_workspace(int T, int S, int H, int D, int PS, int MP, int k,
@@ -111,10 +111,13 @@ namespace {
 int indexer_topk_impl(const void* q_idx, const float* w, const void* idx_cache, int num_pages,
                       const int32_t* page_table, const int32_t* seq_lens,
                       const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP, int k,
-                      int max_q_len, bool fused, int32_t* topk, void* workspace,
+                      int max_q_len, bool fused, int order, int32_t* topk, void* workspace,
                       size_t workspace_bytes, void* stream) {
   int st = check_ragged(T, S, PS, MP, num_pages);
   if (st) return st;
+  if (order != DSA_ORDER_SCORE && order != DSA_ORDER_POSITION)
+    return fail(DSA_ERR_INVALID_ARG, "order=%d is neither DSA_ORDER_SCORE nor DSA_ORDER_POSITION",
+                order);
   if (H < 1 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "indexer H=%d not in [1, 64]", H);
   if (D != 32 && D != 64 && D != 128)
     return fail(DSA_ERR_UNSUPPORTED, "indexer D=%d not in {32, 64, 128}", D);
@@ -141,6 +144,7 @@ int indexer_topk_impl(const void* q_idx, const float* w, const void* idx_cache, 
   a.T = T; a.S = S; a.H = H; a.D = D; a.PS = PS; a.MP = MP; a.k = k;
   a.max_q_len = max_q_len;
   a.topk = topk;
+  a.by_pos = order == DSA_ORDER_POSITION;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fused) {
     int G = 1, L = 0, C = 0;
@@ -158,7 +162,9 @@ int indexer_topk_impl(const void* q_idx, const float* w, const void* idx_cache, 
                                      align256((size_t)T * a.ld * 4));
   hipError_t e = dsa::indexer_score(a, s);
   if (e != hipSuccess) return hip_status(e, "indexer score launch");
-  return hip_status(dsa::indexer_select(a, s), "indexer top-k launch");
+  e = dsa::indexer_select(a, s);
+  if (e != hipSuccess || !a.by_pos) return hip_status(e, "indexer top-k launch");
+  return hip_status(dsa::topk_rows_distinct_order(topk, T, k, MP * PS, s), "top-k order launch");
 }
 }  // namespace
 
@@ -168,17 +174,37 @@ int dsa_indexer_topk(const void* q_idx, const float* w, const void* idx_cache, i
                      int max_q_len, int32_t* topk, void* workspace, size_t workspace_bytes,
                      void* stream) {
   return indexer_topk_impl(q_idx, w, idx_cache, num_pages, page_table, seq_lens, cu_q_lens, T,
-                           S, H, D, PS, MP, k, max_q_len, use_fused(T, MP, PS, max_q_len), topk,
-                           workspace, workspace_bytes, stream);
+                           S, H, D, PS, MP, k, max_q_len, use_fused(T, MP, PS, max_q_len),
+                           DSA_ORDER_SCORE, topk, workspace, workspace_bytes, stream);
+}
+
+int dsa_indexer_topk_ordered(const void* q_idx, const float* w, const void* idx_cache,
+                             int num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                             const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
+                             int k, int max_q_len, int order, int32_t* topk, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return indexer_topk_impl(q_idx, w, idx_cache, num_pages, page_table, seq_lens, cu_q_lens, T,
+                           S, H, D, PS, MP, k, max_q_len, use_fused(T, MP, PS, max_q_len), order,
+                           topk, workspace, workspace_bytes, stream);
 }
 
 int dsa_indexer_topk_fused(const void* q_idx, const float* w, const void* idx_cache,
                            int num_pages, const int32_t* page_table, const int32_t* seq_lens,
                            const int32_t* cu_q_lens, int T, int S, int H, int D, int PS, int MP,
-                           int k, int32_t* topk, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           int k, int order, int32_t* topk, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   return indexer_topk_impl(q_idx, w, idx_cache, num_pages, page_table, seq_lens, cu_q_lens, T,
-                           S, H, D, PS, MP, k, 2, true, topk, workspace, workspace_bytes, stream);
+                           S, H, D, PS, MP, k, 2, true, order, topk, workspace, workspace_bytes,
+                           stream);
+}
+
+int dsa_topk_position_order(const int32_t* topk, int32_t* out, int T, int k, void* stream) {
+  if (T < 0) return fail(DSA_ERR_INVALID_ARG, "T=%d must be >= 0", T);
+  if (k < 1 || k > 4096) return fail(DSA_ERR_UNSUPPORTED, "k=%d not in [1, 4096]", k);
+  if (T == 0) return ok();
+  if (!topk || !out) return fail(DSA_ERR_INVALID_ARG, "NULL tensor pointer");
+  return hip_status(dsa::topk_position_order(topk, out, T, k, static_cast<hipStream_t>(stream)),
+                    "top-k order launch");
 }
 
 // ---------------------------------------------------------------------------

@@ -2210,7 +2210,8 @@ constexpr int kMergeNT = 256;
 
 __global__ __launch_bounds__(kMergeNT) void topk_merge(const uint2* __restrict__ cand,
                                                        const int* __restrict__ cand_cnt, int G,
-                                                       int C, int k, int32_t* __restrict__ topk) {
+                                                       int C, int k, int by_pos,
+                                                       int32_t* __restrict__ topk) {
   extern __shared__ uint64_t s_key[];  // merge_width(G, k) entries
   __shared__ int s_off[9];
   const int t = blockIdx.x;
@@ -2255,6 +2256,30 @@ __global__ __launch_bounds__(kMergeNT) void topk_merge(const uint2* __restrict__
   }
   const int n_out = min(k, total);
   int32_t* out = topk + (size_t)t * k;
+  if (by_pos) {  // the same entries in ascending position order: a second sort
+    int nb2 = 64;
+    while (nb2 < n_out) nb2 <<= 1;
+    for (int i = tid; i < nb2; i += kMergeNT)
+      s_key[i] = i < n_out ? (uint64_t)(uint32_t)topk_key_pos(s_key[i]) : ~0ull;
+    __syncthreads();
+    for (int size = 2; size <= nb2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < (nb2 >> 1); i += kMergeNT) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = (lo & size) == 0;
+          const uint64_t x = s_key[lo], y = s_key[hi];
+          if ((x > y) == up) {
+            s_key[lo] = y;
+            s_key[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < k; i += kMergeNT) out[i] = i < n_out ? (int)(uint32_t)s_key[i] : -1;
+    return;
+  }
   for (int i = tid; i < k; i += kMergeNT) out[i] = i < n_out ? topk_key_pos(s_key[i]) : -1;
 }
 
@@ -2265,7 +2290,8 @@ __global__ __launch_bounds__(kMergeNT) void topk_merge(const uint2* __restrict__
 template <int IPT>
 __global__ __launch_bounds__(kMergeNT) void topk_order(const uint2* __restrict__ cand,
                                                        const int* __restrict__ cand_cnt, int C,
-                                                       int k, int32_t* __restrict__ topk) {
+                                                       int k, int by_pos,
+                                                       int32_t* __restrict__ topk) {
   using Sorter = rocprim::block_radix_sort<uint32_t, kMergeNT, IPT, int>;
   __shared__ typename Sorter::storage_type storage;
   __shared__ uint32_t s_red[2][kMergeNT / DSA_WAVE];
@@ -2273,6 +2299,11 @@ __global__ __launch_bounds__(kMergeNT) void topk_order(const uint2* __restrict__
   const int tid = threadIdx.x;
   const int cnt = min(cand_cnt[t], k);
   const uint2* list = cand + (size_t)t * C;
+  if (by_pos) {  // the list is in ascending position order already
+    int32_t* out = topk + (size_t)t * k;
+    for (int i = tid; i < k; i += kMergeNT) out[i] = i < cnt ? (int)list[i].y : -1;
+    return;
+  }
   uint32_t keys[IPT];
   int vals[IPT];
   uint32_t mn = 0xffffffffu, mx = 0u;
@@ -2347,10 +2378,10 @@ static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
     ProfScope prof("topk_order", st);
     if (a.k <= kMergeNT * 8)
       hipLaunchKernelGGL((topk_order<8>), dim3(a.T), dim3(kMergeNT), 0, st, a.cand, a.cand_cnt,
-                         C, a.k, a.topk);
+                         C, a.k, a.by_pos, a.topk);
     else
       hipLaunchKernelGGL((topk_order<16>), dim3(a.T), dim3(kMergeNT), 0, st, a.cand,
-                         a.cand_cnt, C, a.k, a.topk);
+                         a.cand_cnt, C, a.k, a.by_pos, a.topk);
     return hipGetLastError();
   }
   // the LDS sort holds the row's lists, at most G * k entries, padded to a
@@ -2371,7 +2402,112 @@ static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
   }
   ProfScope prof("topk_merge", st);
   hipLaunchKernelGGL(topk_merge, dim3(a.T), dim3(kMergeNT), lds, st, a.cand, a.cand_cnt, G, C,
-                     a.k, a.topk);
+                     a.k, a.by_pos, a.topk);
+  return hipGetLastError();
+}
+
+// Each row of a top-k table in ascending position order, -1 entries last
+// (as unsigned keys they are the largest): rocPRIM's block radix sort over
+// the bits below the row's largest valid position + 1, so that -1 sorts as
+// the all-ones key of that width, above every valid one. In place is fine: a
+// row is read whole before the sort and written after it.
+// grid = T, block = kMergeNT.
+template <int IPT>
+__global__ __launch_bounds__(kMergeNT) void topk_rows_ascending(const int32_t* __restrict__ in,
+                                                                int k, int32_t* __restrict__ out) {
+  using Sorter = rocprim::block_radix_sort<uint32_t, kMergeNT, IPT>;
+  __shared__ typename Sorter::storage_type storage;
+  __shared__ uint32_t s_red[kMergeNT / DSA_WAVE];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* row = in + (size_t)t * k;
+  uint32_t keys[IPT];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    const int v = idx < k ? row[idx] : -1;
+    keys[i] = (uint32_t)v;
+    if (v >= 0) mx = max(mx, (uint32_t)v);
+  }
+  mx = wave_max_u32(mx);
+  if (lane_id() == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kMergeNT / DSA_WAVE; ++w) mx = max(mx, s_red[w]);
+  const unsigned bits = 32u - (unsigned)__builtin_clz(mx + 1u);  // mx + 1 < 2^31
+  Sorter().sort(keys, storage, 0u, bits);
+  int32_t* orow = out + (size_t)t * k;
+  const uint32_t all = bits >= 32u ? 0xffffffffu : (1u << bits) - 1u;
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int idx = tid * IPT + i;
+    if (idx < k) orow[idx] = (keys[i] & all) == all ? -1 : (int)keys[i];
+  }
+}
+
+// The same for a top-k table whose rows hold distinct positions below cap
+// (an indexer's): each row's positions become bits of an LDS bitmap of cap
+// bits, whose prefix popcounts give every position its place. In place.
+// grid = T, block = 256, dynamic LDS: 2 * ceil(cap / 32) words.
+constexpr int kRowsMaxIPT = 16;  // k <= 4096 entries per row over 256 threads
+__global__ __launch_bounds__(256) void topk_rows_bitmap(int32_t* __restrict__ topk, int k,
+                                                        int cap) {
+  extern __shared__ uint32_t s_bits[];  // nw bitmap words, then nw prefix counts
+  __shared__ int s_scan[4];
+  const int nw = (cap + 31) / 32;
+  uint32_t* s_pre = s_bits + nw;
+  const int tid = threadIdx.x;
+  int32_t* row = topk + (size_t)blockIdx.x * k;
+  for (int i = tid; i < nw; i += 256) s_bits[i] = 0u;
+  __syncthreads();
+  int v[kRowsMaxIPT];
+#pragma unroll
+  for (int e = 0; e < kRowsMaxIPT; ++e) {
+    const int i = tid + 256 * e;
+    v[e] = i < k ? row[i] : -1;
+    if (v[e] >= cap) v[e] = -1;
+    if (v[e] >= 0) atomicOr(&s_bits[v[e] >> 5], 1u << (v[e] & 31));
+  }
+  __syncthreads();
+  // exclusive prefix of the words' popcounts: each thread a contiguous range
+  const int wpt = (nw + 255) / 256, w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
+  int local = 0;
+  for (int i = w0; i < w1; ++i) local += __popc(s_bits[i]);
+  int total;
+  int run = block_inclusive_scan<256>(local, s_scan, &total) - local;
+  for (int i = w0; i < w1; ++i) {
+    s_pre[i] = (uint32_t)run;
+    run += __popc(s_bits[i]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kRowsMaxIPT; ++e)
+    if (v[e] >= 0) {
+      const int wd = v[e] >> 5;
+      row[s_pre[wd] + __popc(s_bits[wd] & ((1u << (v[e] & 31)) - 1u))] = v[e];
+    }
+  for (int i = total + tid; i < k; i += 256) row[i] = -1;
+}
+
+hipError_t topk_rows_distinct_order(int32_t* topk, int T, int k, int cap, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  const size_t lds = (size_t)2 * ((cap + 31) / 32) * 4;
+  if (cap > kRowsBitmapMaxCap) return topk_position_order(topk, topk, T, k, st);
+  ProfScope prof("topk_rows_bitmap", st);
+  hipLaunchKernelGGL(topk_rows_bitmap, dim3(T), dim3(256), lds, st, topk, k, cap);
+  return hipGetLastError();
+}
+
+hipError_t topk_position_order(const int32_t* in, int32_t* out, int T, int k, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  ProfScope prof("topk_rows_ascending", st);
+  if (k <= kMergeNT * 4)
+    hipLaunchKernelGGL((topk_rows_ascending<4>), dim3(T), dim3(kMergeNT), 0, st, in, k, out);
+  else if (k <= kMergeNT * 8)
+    hipLaunchKernelGGL((topk_rows_ascending<8>), dim3(T), dim3(kMergeNT), 0, st, in, k, out);
+  else
+    hipLaunchKernelGGL((topk_rows_ascending<16>), dim3(T), dim3(kMergeNT), 0, st, in, k, out);
   return hipGetLastError();
 }
 

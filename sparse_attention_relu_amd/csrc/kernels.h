@@ -33,11 +33,20 @@ struct IndexerArgs {
   // (order key, position) and their lengths [T, G]
   uint2* cand = nullptr;
   int* cand_cnt = nullptr;
+  // 1: each row's top-k in ascending position order (-1 last) instead of
+  // the canonical score order
+  int by_pos = 0;
 };
 
 // Segments G of L positions and list capacity C of the fused path.
 void fused_plan(int T, int cap, int k, int* G, int* L, int* C);
 hipError_t indexer_fused_topk(const IndexerArgs& a, hipStream_t st);
+// out[t] = in[t] in ascending position order, -1 entries last (in == out allowed)
+hipError_t topk_position_order(const int32_t* in, int32_t* out, int T, int k, hipStream_t st);
+// The same in place for rows of distinct positions below cap (a bitmap per
+// row up to kRowsBitmapMaxCap positions, the general sort above that).
+constexpr int kRowsBitmapMaxCap = 1 << 17;  // 32 KB of LDS
+hipError_t topk_rows_distinct_order(int32_t* topk, int T, int k, int cap, hipStream_t st);
 
 // Tiles per row of the per-tile extreme keys the scorer writes for rows of
 // at most `cap` positions (0 when the chosen scorer writes none).

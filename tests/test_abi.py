@@ -23,8 +23,9 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = _lib.header_functions()
-    assert len(declared) == 25
+    assert len(declared) == 27
     assert "dsa_sparse_mla_decode_static" in declared
+    assert "dsa_indexer_topk_ordered" in declared and "dsa_topk_position_order" in declared
     for name in declared:
         assert hasattr(lib, name), name
         assert name in _lib.SIGNATURES, f"binding lacks {name}"
@@ -34,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     assert dsa.status_string(0) == "ok"
     assert "workspace" in dsa.status_string(3)
-    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_abi_version() == 2
 
 
 def _idx_call(lib, **kw):
@@ -61,6 +62,33 @@ def test_indexer_validation(lib):
     need = dsa.indexer_topk_workspace(2, 1, 32, 128, 64, 4, 16, 1)
     assert need >= 2 * 4 * 64 * 4
     assert _idx_call(lib, ws=1 << 12, wsb=need - 1) == _lib.DSA_ERR_WORKSPACE
+
+
+def test_ordered_entries_validation(lib):
+    def ordered(order, **kw):
+        a = dict(T=2, ws=None)
+        a.update(kw)
+        return lib.dsa_indexer_topk_ordered(1 << 12, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12,
+                                            1 << 12, a["T"], 1, 32, 128, 64, 4, 16, 1, order,
+                                            1 << 12, a["ws"], 0, None)
+
+    assert ordered(2) == _lib.DSA_ERR_INVALID_ARG
+    assert "order" in dsa.last_error()
+    assert ordered(-1) == _lib.DSA_ERR_INVALID_ARG
+    assert ordered(_lib.DSA_ORDER_POSITION) == _lib.DSA_ERR_WORKSPACE  # valid order, no workspace
+    assert ordered(_lib.DSA_ORDER_SCORE, T=0) == _lib.DSA_OK
+    fused = lib.dsa_indexer_topk_fused(1 << 12, 1 << 12, 1 << 12, 4, 1 << 12, 1 << 12, 1 << 12,
+                                       2, 1, 32, 128, 64, 4, 16, 7, 1 << 12, None, 0, None)
+    assert fused == _lib.DSA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        _lib._order("descending")
+    # the row sort: k out of range, NULL pointers, nothing to do
+    assert lib.dsa_topk_position_order(1 << 12, 1 << 12, 4, 0, None) == _lib.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_position_order(1 << 12, 1 << 12, 4, 4097, None) == \
+        _lib.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_position_order(None, 1 << 12, 4, 16, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_position_order(1 << 12, 1 << 12, -1, 16, None) == _lib.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_position_order(None, None, 0, 16, None) == _lib.DSA_OK
 
 
 def test_union_validation(lib):

@@ -213,6 +213,15 @@ def _extend_config(dsa, cid, QB, n_random, n_blocks):
     log(f"config {cid}: oracle top-k on {len(rows)} rows")
     exp = _oracle_rows_topk(wl, b, rows)
     assert np.array_equal(tk[rows], exp[rows]), "top-k differs from the oracle"
+    # the same selection in position order (the attention's feed in the
+    # layer loop): every row equals the canonical row sorted by position
+    tk_pos = dsa.indexer_topk(bt["q_idx"], bt["w"], d.idx_cache, d.page_table, d.seq_lens,
+                              bt["cu"], wl.k, mql, order="position")
+    torch.cuda.synchronize()
+    big = np.iinfo(np.int64).max
+    srt = np.sort(np.where(tk >= 0, tk.astype(np.int64), big), axis=1)
+    assert np.array_equal(tk_pos.cpu().numpy(), np.where(srt == big, -1, srt)), \
+        "position-order top-k is not the canonical selection sorted"
 
     log(f"config {cid}: union QB={QB}")
     u_max = wl.u_max

@@ -38,17 +38,26 @@ def _oracle_topk(wl, b, k=None, q_idx=None, w=None, cu=None):
                                wl.k if k is None else k)
 
 
-def _gpu_topk(dsa, d, q_idx, w, cu, k, max_q_len):
+def _gpu_topk(dsa, d, q_idx, w, cu, k, max_q_len, order="score"):
     """max_q_len "fused" calls the fused entry point (scores never stored)."""
     torch = torch_mod()
     if max_q_len == "fused":
         out = dsa.indexer_topk_fused(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache,
-                                     d.page_table, d.seq_lens, i32(cu, "cuda"), k)
+                                     d.page_table, d.seq_lens, i32(cu, "cuda"), k, order=order)
     else:
         out = dsa.indexer_topk(bf16(q_idx, "cuda"), f32(w, "cuda"), d.idx_cache, d.page_table,
-                               d.seq_lens, i32(cu, "cuda"), k, max_q_len)
+                               d.seq_lens, i32(cu, "cuda"), k, max_q_len, order=order)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def _by_position(topk):
+    """Each row's non-negative entries ascending, then -1 (the position
+    order of a top-k table)."""
+    big = np.iinfo(np.int64).max
+    t = np.where(topk >= 0, topk.astype(np.int64), big)
+    t = np.sort(t, axis=1)
+    return np.where(t == big, -1, t).astype(np.int32)
 
 
 def _mql(path, ql):
@@ -74,6 +83,8 @@ def test_indexer_tiny(dsa, bname, path):
     got = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, mql)
     exp = _oracle_topk(wl, b)
     assert np.array_equal(got, exp)
+    got_p = _gpu_topk(dsa, d, b.q_idx, b.w, b.cu_q_lens, wl.k, mql, order="position")
+    assert np.array_equal(got_p, _by_position(exp))
 
 
 INDEXER_EDGE = {
@@ -116,6 +127,37 @@ def test_indexer_edges(dsa, name, path):
     exp = _oracle_topk(wl, b, k=k, q_idx=q_idx, w=w, cu=np.array(cu))
     assert np.array_equal(got, exp)
     check_topk_rows_valid(got, wl.seq_lens, cu, k)
+    # the same set in position order (the fused path's lists, or a sort of
+    # the selected rows after the score-matrix select)
+    got_p = _gpu_topk(dsa, d, q_idx, w, cu, k, mql, order="position")
+    assert np.array_equal(got_p, _by_position(exp))
+
+
+@pytest.mark.parametrize("k", [1, 7, 256, 1000, 1024, 2048, 2049, 4096])
+def test_topk_position_order_rows(dsa, k):
+    """dsa_topk_position_order against a NumPy sort: rows with -1 entries
+    anywhere, duplicates, position 0, large positions, all -1, in place and
+    out of place."""
+    torch = torch_mod()
+    rng = np.random.default_rng(k)
+    T = 37
+    hi = [1, 5, 1 << 10, 1 << 17, (1 << 31) - 2]
+    rows = []
+    for t in range(T):
+        v = rng.integers(0, hi[t % len(hi)], size=k, endpoint=True).astype(np.int64)
+        v[rng.random(k) < (t % 4) / 4.0] = -1
+        if t == 3:
+            v[:] = -1
+        rows.append(v)
+    tk = np.stack(rows).astype(np.int32)
+    log(f"top-k position order k={k}")
+    src = i32(tk, "cuda")
+    out = dsa.topk_position_order(src)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), _by_position(tk))
+    dsa.topk_position_order(src, out=src)  # in place
+    torch.cuda.synchronize()
+    assert np.array_equal(src.cpu().numpy(), _by_position(tk))
 
 
 # Ragged decode-style batches large enough (rows x 128-position stages above
