@@ -776,8 +776,9 @@ __global__ __launch_bounds__(64 * kTileRows, 2) void idx_score_tiles(
 //
 // Each thread owns M consecutive positions of a chunk (M = 8 when a score
 // row holds at most 8192 positions, else 16); the first chunk (the whole row
-// when it has at most kSelNT * M positions) is read once, before the row's
-// bounds are known, and kept in registers for every pass.
+// when it has at most kSelNT * M positions), and the second as well when a
+// row holds at most two, is read once, before the row's bounds are known,
+// and kept in registers for every pass.
 // grid = T, block = 1024, dynamic LDS = select_lds_bytes(k).
 // ---------------------------------------------------------------------------
 constexpr int kSelNT = 1024;
@@ -908,11 +909,13 @@ __device__ __forceinline__ float order_key_value(uint32_t key) {
 // than kDirectBucketMax positions. Five block barriers. When the row fits one
 // chunk, the histogram's atomic returns each key's offset inside its bucket,
 // so the candidates are placed without a second round of atomics. A row of
-// several chunks counts its first chunk alone (three more barriers), takes
-// from that count a bucket beyond which the candidates most likely do not
-// reach, and lists every key up to it during the histogram pass; when the
-// row's last candidate bucket is within that bound and the list did not
-// overflow, the candidates come from the list, else from a second pass.
+// two chunks held in registers counts both and takes its candidates from the
+// registers in a second pass. A longer row counts its first chunk alone
+// (three more barriers), takes from that count a bucket beyond which the
+// candidates most likely do not reach, and lists every key up to it during
+// the histogram pass; when the row's last candidate bucket is within that
+// bound and the list did not overflow, the candidates come from the list,
+// else from a second pass.
 constexpr int kDirectMaxN = 1 << 17;
 
 struct DirectShared {
@@ -925,8 +928,9 @@ struct DirectShared {
   int spec_b;                    // their last bucket
 };
 
-template <int NT, int M>
-__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float* row, int n,
+template <int NT, int M, int R>
+__device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const uint32_t (&k1)[M],
+                                            const float* row, int n,
                                             int k, uint32_t* lds, size_t cur_off,
                                             size_t start_off, size_t key_off, size_t spec_off,
                                             int spec_cap, DirectShared& sh,
@@ -939,11 +943,14 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
   int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + start_off);
   uint64_t* scomp = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + key_off);
   uint64_t* spec = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(lds) + spec_off);
-  // keys of chunk c0 (the first one from registers)
+  // keys of chunk c0 (the first R chunks from registers)
   auto chunk_keys = [&](int c0, uint32_t (&keys)[M]) {
     if (c0 == 0) {
 #pragma unroll
       for (int e = 0; e < M; ++e) keys[e] = k0[e];
+    } else if (R == 2 && c0 == C) {
+#pragma unroll
+      for (int e = 0; e < M; ++e) keys[e] = k1[e];
     } else {
       load_keys<M>(row, n, c0, keys);
     }
@@ -1018,6 +1025,15 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
 #pragma unroll
     for (int e = 0; e < M; ++e)
       if (j0 + e < n) atomicAdd(&cursor[bucket(k0[e])], 1u);
+  } else if (R == 2 && n <= 2 * C) {
+    // both chunks are in registers: count them here and take the candidates
+    // from the registers in phase 5 (no speculative list)
+#pragma unroll
+    for (int e = 0; e < M; ++e) atomicAdd(&cursor[bucket(k0[e])], 1u);
+    const int j1 = C + tid * M;
+#pragma unroll
+    for (int e = 0; e < M; ++e)
+      if (j1 + e < n) atomicAdd(&cursor[bucket(k1[e])], 1u);
   } else {
     // A row of several chunks. The first chunk (all valid) is counted alone;
     // the bucket at which its count reaches 1.3 k C / n + 16 estimates where
@@ -1083,7 +1099,7 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
     }
     for (int c0 = C; c0 < n; c0 += C) {
       uint32_t keys[M];
-      load_keys<M>(row, n, c0, keys);
+      chunk_keys(c0, keys);
       const int j0 = c0 + tid * M;
       uint32_t take = 0;
 #pragma unroll
@@ -1212,7 +1228,7 @@ __device__ __forceinline__ bool topk_direct(const uint32_t (&k0)[M], const float
   return true;
 }
 
-template <int IPT, int M>
+template <int IPT, int M, int R>
 __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ scores, long ld,
                                                       const int32_t* __restrict__ cu,
                                                       const int32_t* __restrict__ seq_lens,
@@ -1237,9 +1253,11 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const float* row = scores + (size_t)t * ld;
-  // chunk 0, resident for all passes; its loads overlap the row lookup
-  uint32_t k0[M];
+  // chunk 0 (and with R = 2 chunk 1), resident for all passes; the loads
+  // overlap the row lookup
+  uint32_t k0[M], k1[M];
   load_keys_ahead<M>(row, ld < (long)CHUNK ? (int)ld : CHUNK, k0);
+  if (R == 2) load_keys_ahead<M>(row + CHUNK, (int)(ld < 2l * CHUNK ? ld : 2l * CHUNK) - CHUNK, k1);
   const RowInfo ri = row_info_wave(cu, seq_lens, S, t, cap);
   // positions of the row: its valid tokens, or (unit = PS) the pages that
   // hold one
@@ -1250,7 +1268,7 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
     return;
   }
   if (n <= kDirectMaxN &&
-      topk_direct<NT, M>(k0, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
+      topk_direct<NT, M, R>(k0, k1, row, n, k, lds, Cfg::D_CUR_OFF, Cfg::D_START_OFF, Cfg::D_KEY_OFF,
                          Cfg::D_SPEC_OFF, Cfg::SPEC, s_direct,
                          ext != nullptr ? ext + (size_t)t * ext_ld : nullptr, orow))
     return;
@@ -1291,6 +1309,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
         if (c0 == 0) {
 #pragma unroll
           for (int e = 0; e < M; ++e) keys[e] = k0[e];
+        } else if (R == 2 && c0 == CHUNK) {
+#pragma unroll
+          for (int e = 0; e < M; ++e) keys[e] = k1[e];
         } else {
           load_keys<M>(row, n, c0, keys);
         }
@@ -1320,6 +1341,9 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
       if (c0 == 0) {
 #pragma unroll
         for (int e = 0; e < M; ++e) keys[e] = k0[e];
+      } else if (R == 2 && c0 == CHUNK) {
+#pragma unroll
+        for (int e = 0; e < M; ++e) keys[e] = k1[e];
       } else {
         load_keys<M>(row, n, c0, keys);
       }
@@ -1590,7 +1614,7 @@ struct SelectJob {
   int ext_ld;
 };
 
-template <int IPT, int M>
+template <int IPT, int M, int R>
 static hipError_t launch_select(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
   const size_t lds = SelectCfg<IPT>::BYTES;
   // raise the dynamic-LDS limit once per device
@@ -1600,22 +1624,25 @@ static hipError_t launch_select(const IndexerArgs& a, const SelectJob& j, hipStr
   if (e != hipSuccess) return e;
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load() & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<IPT, M>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_select<IPT, M, R>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_done.fetch_or(bit);
   }
   ProfScope prof("topk_select", st);
-  hipLaunchKernelGGL((topk_select<IPT, M>), dim3(a.T), dim3(kSelNT), lds, st, j.scores, j.ld,
+  hipLaunchKernelGGL((topk_select<IPT, M, R>), dim3(a.T), dim3(kSelNT), lds, st, j.scores, j.ld,
                      a.cu, a.seq_lens, a.S, a.MP * a.PS, j.unit, j.k, j.ext, j.ext_ld, j.out);
   return hipGetLastError();
 }
 
-// positions per thread: 8 when a whole score row fits one chunk of 8192
+// positions per thread: 8 when a whole score row fits one chunk of 8192,
+// else 16; rows of two chunks (up to 32768 scores) keep both in registers
 template <int IPT>
 static hipError_t launch_select_m(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
-  return j.ld <= (long)kSelNT * 8 ? launch_select<IPT, 8>(a, j, st)
-                                  : launch_select<IPT, 16>(a, j, st);
+  if (j.ld <= (long)kSelNT * 8) return launch_select<IPT, 8, 1>(a, j, st);
+  if (j.ld <= (long)kSelNT * 16 || j.ld > (long)kSelNT * 32)
+    return launch_select<IPT, 16, 1>(a, j, st);
+  return launch_select<IPT, 16, 2>(a, j, st);
 }
 
 static hipError_t select_job(const IndexerArgs& a, const SelectJob& j, hipStream_t st) {
