@@ -272,14 +272,14 @@ def _kernel_table(kt, warm, cold, work):
     return out
 
 
-INDEXER_KERNELS = ("idx_score_stream", "idx_score_flat", "idx_score_tiles", "topk_select",
-                   "idx_score_topk", "topk_order", "topk_merge", "topk_rows_ascending",
-                   "topk_rows_bitmap")
+INDEXER_KERNELS = ("idx_score_stream", "idx_score_flat", "idx_score_regs", "idx_score_tiles",
+                   "topk_select", "idx_score_topk", "topk_order", "topk_merge",
+                   "topk_rows_ascending", "topk_rows_bitmap")
 
 # Sources whose text decides each kernel's machine code.
 KERNEL_SOURCES = {
     "idx_score_stream": "indexer.hip", "idx_score_flat": "indexer.hip",
-    "idx_score_tiles": "indexer.hip", "topk_select": "indexer.hip",
+    "idx_score_regs": "indexer.hip", "idx_score_tiles": "indexer.hip", "topk_select": "indexer.hip",
     "idx_score_topk": "indexer.hip", "topk_order": "indexer.hip", "topk_merge": "indexer.hip",
     "topk_rows_ascending": "indexer.hip", "topk_rows_bitmap": "indexer.hip",
     "mla_decode_partial": "mla.hip", "mla_decode_combine": "mla.hip",
@@ -382,6 +382,7 @@ def bench_decode(dsa, wl, steps, warmup, reps):
     work = {
         "idx_score_stream": ("hbm", score_bytes),
         "idx_score_flat": ("hbm", score_bytes),
+        "idx_score_regs": ("hbm", score_bytes),
         "topk_select": ("hbm", int(nval.sum()) * 4 + T * k * 4),
         "mla_decode_partial": ("hbm", n_sel * DK * 2 + T * k * 4 + T * H * DK * 2),
     }

@@ -242,8 +242,9 @@ __global__ __launch_bounds__(256, 1) void idx_score_stream(
 }
 
 // ---------------------------------------------------------------------------
-// Balanced streaming scorer for ragged batches. The batch's work is the flat
-// list of (row, 128-position stage) pairs in row order; each of G persistent
+// Balanced streaming scorer for ragged batches of more sequences than the
+// register scorer below stages in LDS. The batch's work is the flat list of
+// (row, 128-position stage) pairs in row order; each of G persistent
 // workgroups (one per compute unit) takes an equal contiguous share of it, so
 // rows of any length mix without a tail of part-filled workgroups, and the
 // four-stage ring keeps streaming across row boundaries (one ring fill per
@@ -484,6 +485,221 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
     float part = relu_weighted_sum(acc, wv);
     part += shfl_xor_f(part, 32);
     if (hf == 0 && j < n_c) srow[j] = part;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-streaming scorer for ragged batches. The work items are the
+// 32-position blocks of every row, in row order, and each wave of the grid
+// takes an equal contiguous share of them. A lane loads the half of its key
+// that its MFMA operand needs (D / 2 values, D / 16 loads of 16 bytes)
+// straight into registers: no LDS staging, and no barrier or wait that
+// another wave shares stands between a block's loads and its products. The
+// keys of the next block and the page-table entries of the one after it are
+// in flight while a block is multiplied. A position past the row's valid
+// range loads the row's last valid key and is never stored. Each workgroup
+// first finds every row's valid length and the prefix of its block counts
+// (cu_q_lens and seq_lens staged in LDS, one binary search per row).
+// Scores go to a per-wave LDS buffer and are stored 32 blocks at a time
+// (1 KB per store instruction): the ragged decode's writes, spread one
+// 128-byte line per block between its key reads, cost about 8 us of 68;
+// grouped they cost about 4.
+// grid = (several workgroups per compute unit), block = 256.
+// ---------------------------------------------------------------------------
+constexpr int kRegKeys = 32;        // positions per work item
+constexpr int kRegMaxS = 1024;      // sequences the staging area holds
+constexpr int kRegWavesPerSimd = 3;
+constexpr int kRegBatch = 32;  // blocks whose scores a wave stores at once
+
+template <int D, bool P32>
+__global__ __launch_bounds__(256, kRegWavesPerSimd) void idx_score_regs(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
+    int PS, int MP, float* __restrict__ scores, long ld) {
+  constexpr int KS = D / 16, HALF = D / 2;
+  __shared__ int s_pre[kFlatMaxT + 1];
+  __shared__ int s_n[kFlatMaxT];
+  __shared__ int s_seq[kFlatMaxT];
+  __shared__ int s_cu[kRegMaxS + 1];
+  __shared__ int s_sl[kRegMaxS];
+  __shared__ int s_scan[4];
+  // per wave: the scores of up to kRegBatch blocks, stored in one pass
+  __shared__ __attribute__((aligned(16))) float s_out[4][kRegBatch * kRegKeys];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = lane_id();
+  const int m = l & 31, hf = l >> 5;
+  const int cap = MP * PS;
+
+  // ---- valid length of every row and the prefix of its block counts
+  for (int i = tid; i <= S; i += 256) s_cu[i] = cu[i];
+  for (int i = tid; i < S; i += 256) s_sl[i] = seq_lens[i];
+  __syncthreads();
+  const int R = (T + 255) / 256;  // rows per thread, consecutive
+  int cnt = 0;
+  for (int i = 0; i < R; ++i) {
+    const int t = R * tid + i;
+    if (t >= T) break;
+    int seq = -1, n = 0;
+    if (S > 0 && t >= s_cu[0] && t < s_cu[S]) {
+      int lo = 0, hi = S;  // first s with cu[s + 1] > t
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_cu[mid + 1] > t) hi = mid; else lo = mid + 1;
+      }
+      if (lo < S) {
+        const int q0 = s_cu[lo], q1 = s_cu[lo + 1];
+        const int kv = s_sl[lo];
+        const int abs_q = kv - (q1 - q0) + (t - q0);
+        const int kc = kv < 0 ? 0 : (kv > cap ? cap : kv);
+        n = abs_q + 1 < kc ? abs_q + 1 : kc;
+        n = n < 0 ? 0 : n;
+        seq = lo;
+      }
+    }
+    s_n[t] = n;
+    s_seq[t] = seq;
+    cnt += (n + kRegKeys - 1) / kRegKeys;
+  }
+  int total;
+  int run = block_inclusive_scan<256>(cnt, s_scan, &total) - cnt;
+  for (int i = 0; i < R; ++i) {
+    const int t = R * tid + i;
+    if (t >= T) break;
+    s_pre[t] = run;
+    run += (s_n[t] + kRegKeys - 1) / kRegKeys;
+  }
+  if (tid == 0) s_pre[T] = total;
+  __syncthreads();
+
+  // ---- this wave's share [i_begin, i_end) of the block list
+  const int G = gridDim.x * 4;
+  const int gw = blockIdx.x * 4 + wave;
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int i_begin = (int)((long)gw * total / G);
+  const int i_end = (int)((long)(gw + 1) * total / G);
+  if (i_begin >= i_end) return;  // no barrier follows
+  auto pre = [&](int r) { return __builtin_amdgcn_readfirstlane(s_pre[r]); };
+  int r = 0;
+  {
+    int lo = 0, hi = T - 1;  // last row with s_pre[row] <= i_begin (it has blocks)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= i_begin) lo = mid; else hi = mid - 1;
+    }
+    r = __builtin_amdgcn_readfirstlane(lo);
+  }
+  // The share is walked one row segment at a time (most waves have one).
+  // Lane (m, hf) holds, for k-step x, the 8 values 16 x + 8 hf .. of its
+  // query head m (operand A) and of its key m (operand B): the two lanes of
+  // a key read 32 consecutive bytes per load.
+  for (int i = i_begin; i < i_end;) {
+    const int base = pre(r);
+    const int seg_end = min(i_end, pre(r + 1));
+    const int nrow = __builtin_amdgcn_readfirstlane(s_n[r]);
+    const int seq = __builtin_amdgcn_readfirstlane(s_seq[r]);
+    const int32_t* ptrow = pt + (size_t)seq * MP;
+    bf16x8 a[KS];
+    float wv[16];
+    {
+      const bool okq = m < H;
+      const uint16_t* qrow = q + ((size_t)r * H + (okq ? m : 0)) * D + 8 * hf;
+#pragma unroll
+      for (int x = 0; x < KS; ++x)
+        a[x] = as_bf16x8(okq ? *reinterpret_cast<const uint4*>(qrow + 16 * x) : zero_u4());
+      load_head_weights(w + (size_t)r * H, H, 0, hf, wv);
+    }
+    const int b0 = i - base, bend = seg_end - base;
+    // block bb of the row, clamped to the segment's last block (loads past
+    // the segment repeat that block and are never multiplied)
+    auto key_j = [&](int bb) {
+      const int j = min(bb, bend - 1) * kRegKeys + m;
+      return j < nrow ? j : nrow - 1;
+    };
+    // P32 (PS a multiple of 32): a block's 32 positions share one page, whose
+    // entry is read once for the wave; positions past the row's end then
+    // stay inside that page and are never stored
+    auto entry = [&](int bb) {
+      if constexpr (P32)
+        return ptrow[__builtin_amdgcn_readfirstlane(min(bb, bend - 1) * kRegKeys) / PS];
+      else
+        return ptrow[key_j(bb) / PS];
+    };
+    const uint16_t* lane_base = cache + (size_t)m * D + 8 * hf;
+    auto load = [&](int bb, int pe, bf16x8 (&kk)[KS]) __attribute__((always_inline)) {
+      const uint16_t* src;
+      if constexpr (P32) {
+        const int j0 = __builtin_amdgcn_readfirstlane(min(bb, bend - 1) * kRegKeys);
+        const int pg = clamp_page(__builtin_amdgcn_readfirstlane(pe), num_pages);
+        src = lane_base + ((size_t)pg * PS + (size_t)(j0 % PS)) * D;
+      } else {
+        const int j = key_j(bb);
+        src = cache + ((size_t)clamp_page(pe, num_pages) * PS + (size_t)(j % PS)) * D + 8 * hf;
+      }
+#pragma unroll
+      for (int x = 0; x < KS; ++x)
+        kk[x] = as_bf16x8(*reinterpret_cast<const uint4*>(src + 16 * x));
+    };
+    float* srow = scores + (size_t)r * ld;
+    float* sbuf = s_out[wave];
+    // scores of blocks fb .. fb + nb - 1 from the wave's buffer to the row:
+    // lane l writes positions 4 l .. 4 l + 3 of the batch
+    auto flush = [&](int fb, int nb) __attribute__((always_inline)) {
+      asm volatile("" ::: "memory");
+      const int lim = min(nb * kRegKeys, nrow - fb * kRegKeys);  // valid positions of the batch
+#pragma unroll
+      for (int u = 0; u < kRegBatch / 8; ++u) {
+        const int o = 256 * u + 4 * l;           // this lane's positions in the batch
+        const int p = fb * kRegKeys + o;
+        const float4 v = *reinterpret_cast<const float4*>(sbuf + o);
+        if (o + 3 < lim) {
+          *reinterpret_cast<float4*>(srow + p) = v;
+        } else if (o < lim) {
+          srow[p] = v.x;
+          if (o + 1 < lim) srow[p + 1] = v.y;
+          if (o + 2 < lim) srow[p + 2] = v.z;
+        }
+      }
+      asm volatile("" ::: "memory");
+    };
+    auto product = [&](int bb, const bf16x8 (&kk)[KS]) __attribute__((always_inline)) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int x = 0; x < KS; ++x)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], kk[x], acc, 0, 0, 0);
+      float part = relu_weighted_sum(acc, wv);
+      part += shfl_xor_f(part, 32);
+      const int slot = (bb - b0) % kRegBatch;
+      if (hf == 0) sbuf[slot * kRegKeys + m] = part;
+      if (slot == kRegBatch - 1) flush(bb - slot, kRegBatch);
+    };
+    // keys one block ahead, page entries three
+    bf16x8 k0[KS], k1[KS];
+    int b = b0;
+    load(b, entry(b), k0);
+    int pe_b = entry(b + 1), pe_c = entry(b + 2);
+    for (; b < bend; b += 2) {
+      load(b + 1, pe_b, k1);
+      const int pe_d = entry(b + 3);
+      // keep the loads ahead of the products (the scheduler would sink them)
+      __builtin_amdgcn_sched_barrier(0);
+      product(b, k0);
+      if (b + 1 >= bend) break;
+      load(b + 2, pe_c, k0);
+      const int pe_e = entry(b + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      product(b + 1, k1);
+      pe_b = pe_d;
+      pe_c = pe_e;
+    }
+    if ((bend - b0) % kRegBatch != 0) {  // the segment's last, partial batch
+      const int nb = (bend - b0) % kRegBatch;
+      flush(bend - nb, nb);
+    }
+    i = seg_end;
+    ++r;
+    while (r < T - 1 && pre(r + 1) <= i) ++r;  // skip rows without blocks
   }
 }
 
@@ -1533,6 +1749,18 @@ template <int D, int HB>
 static hipError_t launch_rows(const IndexerArgs& a, hipStream_t st) {
   const long cap = (long)a.MP * a.PS;
   const long total = (long)a.T * ((cap + kStreamKeys - 1) / kStreamKeys);
+  if (HB == 1 && total > 2048 && total < (1L << 30) && a.T <= kFlatMaxT && a.S <= kRegMaxS) {
+    ProfScope prof("idx_score_regs", st);
+    if (a.PS % kRegKeys == 0)
+      hipLaunchKernelGGL((idx_score_regs<D, true>), dim3(compute_units() * kRegWavesPerSimd),
+                         dim3(256), 0, st, a.q, a.w, a.cache, a.num_pages, a.pt, a.seq_lens, a.cu,
+                         a.T, a.S, a.H, a.PS, a.MP, a.scores, a.ld);
+    else
+      hipLaunchKernelGGL((idx_score_regs<D, false>), dim3(compute_units() * kRegWavesPerSimd),
+                         dim3(256), 0, st, a.q, a.w, a.cache, a.num_pages, a.pt, a.seq_lens, a.cu,
+                         a.T, a.S, a.H, a.PS, a.MP, a.scores, a.ld);
+    return hipGetLastError();
+  }
   if (HB == 1 && total > 2048 && total < (1L << 30) && a.T <= kFlatMaxT &&
       a.S <= FlatShape<D>::MAX_S) {
     ProfScope prof("idx_score_flat", st);
