@@ -443,16 +443,33 @@ __global__ __launch_bounds__(256, kDecWPC) void mla_decode_partial(
       part_ml[(base + head) * 2 + 0] = m_run * 0.693147180559945309f;
       part_ml[(base + head) * 2 + 1] = l_run;
     }
-    // the unnormalised O goes out in bf16: the combine forms a convex
-    // combination of the chunks, so each value's rounding (2^-9 relative)
-    // stays that small in the result, and the partial traffic halves
-    uint16_t* orow = part_o + (base + head) * DV + 128 * wave + 4 * g;
+  }
+  // the unnormalised O goes out in bf16: the combine forms a convex
+  // combination of the chunks, so each value's rounding (2^-9 relative)
+  // stays that small in the result, and the partial traffic halves. It goes
+  // through the ring slot that the last stage did not use (every wave had
+  // consumed that slot's stage before the last stage's barrier, and no load
+  // targets it any more): written there in the accumulator layout and read
+  // back so that each store is 16 bytes per lane over whole 256-byte head
+  // segments (rows padded to 136 values against bank conflicts).
+  {
+    constexpr int TS = 136;
+    uint16_t* tb = reinterpret_cast<uint16_t*>(ring[nst & 1]) + wave * 16 * TS;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
       uint2 v;
       v.x = pack_bf16x2(o[ct][0], o[ct][1]);
       v.y = pack_bf16x2(o[ct][2], o[ct][3]);
-      *reinterpret_cast<uint2*>(orow + 16 * ct) = v;
+      *reinterpret_cast<uint2*>(tb + col * TS + 16 * ct + 4 * g) = v;
+    }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * i + (l >> 4);  // head of the block
+      const uint4 v = *reinterpret_cast<const uint4*>(tb + hh * TS + 8 * (l & 15));
+      if (16 * hb + hh < H)
+        *reinterpret_cast<uint4*>(part_o + (base + 16 * hb + hh) * DV + 128 * wave +
+                                  8 * (l & 15)) = v;
     }
   }
 }
