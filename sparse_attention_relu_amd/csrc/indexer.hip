@@ -494,10 +494,11 @@ __global__ __launch_bounds__(256, 1) void idx_score_flat(
 // takes an equal contiguous share of them. A lane loads the half of its key
 // that its MFMA operand needs (D / 2 values, D / 16 loads of 16 bytes)
 // straight into registers: no LDS staging, and no barrier or wait that
-// another wave shares stands between a block's loads and its products. The
-// keys of the next block and the page-table entries of the one after it are
-// in flight while a block is multiplied. A position past the row's valid
-// range loads the row's last valid key and is never stored. Each workgroup
+// another wave shares stands between a block's loads and its products. While
+// a block is multiplied, the keys of the next block and the page-table
+// entries of the two after it are in flight. A position past the row's valid
+// range loads a key of the row's last valid page (the last valid key when PS
+// is not a multiple of 32) and is never stored. Each workgroup
 // first finds every row's valid length and the prefix of its block counts
 // (cu_q_lens and seq_lens staged in LDS, one binary search per row).
 // Scores go to a per-wave LDS buffer and are stored 32 blocks at a time
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(256, kRegWavesPerSimd) void idx_score_regs(
       if (hf == 0) sbuf[slot * kRegKeys + m] = part;
       if (slot == kRegBatch - 1) flush(bb - slot, kRegBatch);
     };
-    // keys one block ahead, page entries three
+    // keys one block ahead of the products, page entries three
     bf16x8 k0[KS], k1[KS];
     int b = b0;
     load(b, entry(b), k0);
