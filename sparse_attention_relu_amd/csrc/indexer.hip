@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256, kRegWavesPerSimd) void idx_score_regs(
     const uint16_t* __restrict__ cache, int num_pages, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu, int T, int S, int H,
     int PS, int MP, float* __restrict__ scores, long ld) {
-  constexpr int KS = D / 16, HALF = D / 2;
+  constexpr int KS = D / 16;
   __shared__ int s_pre[kFlatMaxT + 1];
   __shared__ int s_n[kFlatMaxT];
   __shared__ int s_seq[kFlatMaxT];
@@ -1655,7 +1655,6 @@ __global__ __launch_bounds__(kSelNT) void topk_select(const float* __restrict__ 
   const uint32_t span = (kmax - kmin) >> lo;
   const int nbits = 32 - __builtin_clz(span);
   const int sh = lo + (nbits > 12 ? nbits - 12 : 0);
-  const int nbk = (int)((kmax - kmin) >> sh) + 1;
   uint32_t* cursor = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + Cfg::HIST_OFF);
   int* bstart = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + Cfg::START_OFF);
   uint32_t* skey = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(lds) + Cfg::SKEY_OFF);

@@ -149,7 +149,6 @@ constexpr int kDecWPC = 2;                                    // workgroups per 
 constexpr int kDecRows = 32;                                  // selections per stage
 constexpr int kDecRing = 2;                                   // LDS stages
 constexpr int kDecStage = kDecRows * NOPE_B;                  // 32768 bytes (nope columns)
-constexpr int kDecLoads = kDecRows / 4;                       // direct loads per wave per stage
 constexpr int kDecMaxCH = 2048;
 constexpr float kDecLazy = 8.0f;  // headroom of the running maximum (log2 units)
 // s_src entries: the cache slot a selection loads; an invalid selection
