@@ -164,8 +164,9 @@ def test_topk_position_order_rows(dsa, k):
 # 2048) for the balanced scorers: rows of very different lengths, empty
 # sequences, rows past the last sequence, H < 32, every D, page sizes that are
 # and are not multiples of 32, and many short rows so that one wave's share
-# spans many rows. Up to 1024 sequences take the register scorer; the last
-# case (1100 sequences, half of them without rows) takes the LDS-ring scorer.
+# spans many rows. Up to 1024 sequences take the register scorer (the last
+# case: its limits, 1024 rows of 1024 sequences); 1100 sequences, half of
+# them without rows, take the LDS-ring scorer.
 INDEXER_FLAT = {
     # name: (S, kv range, q_len choices, PS, MP, H, D, k, extra_rows)
     "d128_h32_mixed": (40, (0, 4000), (0, 1, 1, 2, 5), 64, 64, 32, 128, 256, 3),
@@ -173,6 +174,7 @@ INDEXER_FLAT = {
     "d32_many_short_rows": (1000, (1, 300), (1,), 16, 160, 32, 32, 64, 2),
     "d128_ps48_h7": (40, (1, 6000), (1, 2), 48, 128, 7, 128, 300, 0),
     "d128_s1100_ring": (1100, (1, 400), (0, 1), 16, 32, 32, 128, 64, 0),
+    "d64_ps32_max_rows": (1024, (1, 500), (1,), 32, 16, 32, 64, 64, 0),
 }
 
 
