@@ -105,6 +105,11 @@ INDEXER_EDGE = {
     # relative to k)
     "h32_d128_long_rows_k1000": (2, [40000, 20000], 64, 640, [3, 2], 32, 128, 1000, 0),
     "h32_d128_long_rows_k4096": (2, [40000, 33000], 64, 640, [3, 2], 32, 128, 4096, 0),
+    # score rows of two select chunks held in registers (workspace rows of
+    # 32768 positions): rows of exactly one chunk, one position past it, and
+    # the last positions of the second chunk
+    "h32_d128_two_chunk_rows": (4, [16384, 16385, 32767, 32768], 64, 512, [1, 2, 1, 2], 32,
+                                128, 2048, 0),
 }
 
 
