@@ -794,7 +794,8 @@ def main(argv=None):
         return 0
     if args.only in ("decode", "ragged"):
         wl = W.config(2 if args.only == "decode" else 3)
-        r = bench_decode(dsa, wl, max(args.steps, 20), args.warmup, reps or 50)
+        r = bench_decode(dsa, wl, max(args.steps, 200 if args.only == "decode" else 100),
+                         max(args.warmup, 10), reps or 50)
         print(json.dumps({"only": args.only, **r}), flush=True)
         return 0
     if args.only == "extend":
@@ -836,12 +837,14 @@ def main(argv=None):
     }
     if args.only == "all":
         del wl5
+        # the decode steps take tens of microseconds: time enough of them
+        # (a few milliseconds) that host and box noise average out
         _log("decode batch")
-        result["decode_batch"] = bench_decode(dsa, W.config(2), max(20, 2 * args.steps),
-                                              args.warmup, reps or 50)
+        result["decode_batch"] = bench_decode(dsa, W.config(2), max(200, 2 * args.steps),
+                                              max(20, args.warmup), reps or 50)
         _log("ragged decode")
-        result["ragged_decode"] = bench_decode(dsa, W.config(3), max(20, 2 * args.steps),
-                                               args.warmup, reps or 50)
+        result["ragged_decode"] = bench_decode(dsa, W.config(3), max(100, 2 * args.steps),
+                                               max(10, args.warmup), reps or 50)
         _log("chunked extend")
         result["chunked_extend"] = bench_extend_workload(dsa, W.config(4), max(4, args.steps),
                                                          args.warmup, reps or 20)
